@@ -1,0 +1,292 @@
+/*
+ * k3moe_oracle.c -- plain, slow CPU oracle for the Kimi K3 "Stable LatentMoE"
+ * routed-expert block.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark load this library.  The product (the HIP library) never
+ * calls it and shares no code, header or table with it.
+ *
+ * Pages it follows (cited by title and section below):
+ *   [PR676] colibri PR #676, "Kimi K3 engine: native-MXFP4 expert streaming, KDA +
+ *           gated NoPE MLA + AttnRes + LatentMoE": summary bullets, "It runs the
+ *           full model", the chunked-prefill paragraph, "What's in the commits".
+ *   [PR684] colibri PR #684, "Kimi K3: integrate coli chat, API, and Web": the
+ *           MXFP4-kernel commit message and the engine commit message.
+ *   [LC21]  llama.cpp fork PR #21, "Adding kimi-k3 arch test and saver fix": the
+ *           kimi-k3 arch commit and the PR description.
+ *
+ * Precision: decoded weights are fp32 (the closed form rounded once to fp32);
+ * every sum, the activation and the combine run in double; outputs are cast to
+ * fp32 once at the end.  The router's selection key is an fp32 value (see
+ * k3o_route).  Built at -O2 without fast-math and with FP contraction off.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ MXFP4 decode */
+
+/* e2m1 magnitudes, indexed by the code's low three bits (exponent e1 e0, mantissa m).
+ * The pages name e2m1 but do not print the table ([PR676] summary: "e2m1 nibbles +
+ * ue8m0 per-32 scales"; [LC21] arch commit: the same E2M1 code assignment as ggml's
+ * MXFP4; [PR684] int8 commit: doubled e2m1 values are exact int8).  This is the
+ * standard OCP e2m1 value set. */
+static const double E2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* One weight from a 4-bit code and its group's scale byte:
+ * w = v * 2^(s - 127), v = (-1)^bit3 * E2M1[code & 7]   ([PR684] MXFP4 commit:
+ * "bit3 = sign", "w = v * 2^(s-127)").
+ * The product is exact in double; it is then rounded once to fp32.  Every value
+ * below 2^128 has at most two significant bits and magnitude >= 2^-128, so it is
+ * representable in fp32 (subnormals included); anything >= 2^128 overflows to a
+ * signed infinity, as IEEE 754 rounding to nearest prescribes.  Code 8 is -0.0. */
+float k3o_decode(unsigned code, unsigned scale)
+{
+    double v = E2M1[code & 7u];
+    if (code & 8u) v = -v;
+    double w = v * ldexp(1.0, (int)(scale & 0xFFu) - 127);
+    if (fabs(w) >= 0x1p128) return (float)copysign(INFINITY, w);
+    return (float)w;
+}
+
+/* Fill a 16 x 256 table: table[code * 256 + s] = k3o_decode(code, s). */
+void k3o_decode_table(float *table)
+{
+    for (unsigned c = 0; c < 16; ++c)
+        for (unsigned s = 0; s < 256; ++s) table[c * 256 + s] = k3o_decode(c, s);
+}
+
+/* Dequantize one MXFP4 matrix.  Packed q is [O, I/2] bytes, the LOW nibble holding
+ * the even column and the high nibble the odd column; scales s are [O, I/32], one
+ * per 32 consecutive inputs of a row ([PR684] MXFP4 commit).  out is [O, I] fp32. */
+void k3o_dequant(const uint8_t *q, const uint8_t *s, int64_t O, int64_t I, float *out)
+{
+    for (int64_t o = 0; o < O; ++o) {
+        for (int64_t i = 0; i < I; ++i) {
+            uint8_t byte = q[o * (I / 2) + i / 2];
+            unsigned code = (i % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4);
+            unsigned scale = s[o * (I / 32) + i / 32];
+            out[o * I + i] = k3o_decode(code, scale);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ router */
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+typedef struct { float key; int32_t id; } cand_t;
+
+/* Larger key first; equal keys -> lower expert id first. */
+static int cand_cmp(const void *pa, const void *pb)
+{
+    const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+    if (a->key > b->key) return -1;
+    if (a->key < b->key) return 1;
+    return (a->id < b->id) ? -1 : (a->id > b->id);
+}
+
+/* Sigmoid router with a score-correction bias, top-K, renormalized on raw scores
+ * ([PR684] engine commit, Stable LatentMoE bullet; [PR676] summary: 896 experts
+ * per layer, top-16).
+ *   score_e = sigma(l_e)                         (double)
+ *   key_e   = fl32( fl32(score_e) + bias_e )     (the bias only steers selection)
+ *   select the K largest keys, ties to the lower id, in descending key order
+ *   w_k     = score_{e_k} / sum_j score_{e_j}    (double, cast to fp32)
+ * A NaN key counts as -inf.  gap[t] = key_(K) - key_(K+1) (inf when K == E) is
+ * the selection's margin, reported so near-ties can be counted.
+ * logits [T, E], bias [E]; idx [T, K] int32, w [T, K] fp32, gap [T] (nullable). */
+void k3o_route(const float *logits, const float *bias, int32_t T, int32_t E, int32_t K,
+               int32_t *idx, float *w, double *gap)
+{
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)E);
+    double *score = (double *)malloc(sizeof(double) * (size_t)E);
+    for (int32_t t = 0; t < T; ++t) {
+        const float *l = logits + (int64_t)t * E;
+        for (int32_t e = 0; e < E; ++e) {
+            score[e] = sigmoid((double)l[e]);
+            float s32 = (float)score[e];
+            float key = s32 + bias[e];
+            if (isnan(key)) key = -INFINITY;
+            c[e].key = key;
+            c[e].id = e;
+        }
+        qsort(c, (size_t)E, sizeof(cand_t), cand_cmp);
+        double denom = 0.0;
+        for (int32_t k = 0; k < K; ++k) denom += score[c[k].id];
+        for (int32_t k = 0; k < K; ++k) {
+            idx[(int64_t)t * K + k] = c[k].id;
+            w[(int64_t)t * K + k] = (float)(score[c[k].id] / denom);
+        }
+        if (gap) gap[t] = (K < E) ? (double)c[K - 1].key - (double)c[K].key : INFINITY;
+    }
+    free(c);
+    free(score);
+}
+
+/* -------------------------------------------------------------------- activation */
+
+/* Generic-beta SiTU-GLU: bg*tanh(g/bg) * sigma(g) * bu*tanh(u/bu).  sigma acts on
+ * the gate branch only. */
+double k3o_situ_beta(double g, double u, double bg, double bu)
+{
+    return bg * tanh(g / bg) * sigmoid(g) * bu * tanh(u / bu);
+}
+
+/* SiTU-GLU with K3's betas 4 and 25: 4*tanh(g/4)*sigma(g)*25*tanh(u/25)
+ * ([PR676] summary, Stable LatentMoE bullet; [PR684] engine commit; [LC21] PR
+ * description: situ at betas 4.0 / 25.0).  exp(+large) = inf gives sigma = 0, so
+ * the expression saturates without inf/inf; NaN propagates. */
+double k3o_situ(double g, double u) { return k3o_situ_beta(g, u, 4.0, 25.0); }
+
+/* ------------------------------------------------------------------- expert FFN */
+
+/* One routed expert on one token, on already-decoded fp32 weights
+ * Wg, Wu [F, D] and Wd [D, F]:
+ *   g_f = sum_i Wg[f,i] x_i,  u_f = sum_i Wu[f,i] x_i     (double, ascending i)
+ *   h_f = SiTU(g_f, u_f)
+ *   y_d = sum_f Wd[d,f] h_f                                (double, ascending f)
+ * ([PR684] engine commit: gate/up, SiTU-GLU, down in the 3584-dim latent space.)
+ * Any output pointer may be NULL except y. */
+void k3o_expert(const float *Wg, const float *Wu, const float *Wd, int32_t D, int32_t F,
+                const float *x, double *g, double *u, double *h, double *y)
+{
+    double *hh = (double *)malloc(sizeof(double) * (size_t)F);
+    for (int32_t f = 0; f < F; ++f) {
+        double ag = 0.0, au = 0.0;
+        for (int32_t i = 0; i < D; ++i) {
+            ag += (double)Wg[(int64_t)f * D + i] * (double)x[i];
+            au += (double)Wu[(int64_t)f * D + i] * (double)x[i];
+        }
+        if (g) g[f] = ag;
+        if (u) u[f] = au;
+        hh[f] = k3o_situ(ag, au);
+        if (h) h[f] = hh[f];
+    }
+    for (int32_t d = 0; d < D; ++d) {
+        double ay = 0.0;
+        for (int32_t f = 0; f < F; ++f) ay += (double)Wd[(int64_t)d * F + f] * hh[f];
+        y[d] = ay;
+    }
+    free(hh);
+}
+
+/* ----------------------------------------------------------------- block forward */
+
+/* The routed-expert block for T tokens given their routing (idx [T,K], w [T,K]):
+ *   y_t = sum_{k=0}^{K-1} w_{t,k} * expert_{idx[t,k]}(x_t)     (double, k order)
+ * Weights: gq/uq [E, F, D/2], gs/us [E, F, D/32], dq [E, D, F/2], ds [E, D, F/32].
+ * Each token is computed exactly as it would be alone; the loop visits the union
+ * of routed experts and decodes each of them once (the pages' chunk loads each
+ * unique expert once, [PR676] chunked-prefill paragraph), which does not change
+ * any pair's arithmetic.  ytk (nullable) receives the per-pair expert outputs
+ * [T, K, D] in double; hk (nullable) the per-pair activations [T, K, F].
+ * Returns 0, or -1 if an index is out of range or memory runs out. */
+int k3o_forward(int32_t E, int32_t D, int32_t F,
+                const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
+                const uint8_t *dq, const uint8_t *ds,
+                const float *x, int32_t T, const int32_t *idx, const float *w, int32_t K,
+                float *y, double *ytk, double *hk, int32_t nthreads)
+{
+    int64_t P = (int64_t)T * K;
+    for (int64_t p = 0; p < P; ++p)
+        if (idx[p] < 0 || idx[p] >= E) return -1;
+
+    double *yp = ytk ? ytk : (double *)malloc(sizeof(double) * (size_t)(P * D));
+    if (!yp) return -1;
+
+    /* union of routed experts, ascending */
+    int32_t *used = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t *list = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    int32_t nu = 0;
+    for (int64_t p = 0; p < P; ++p) used[idx[p]] = 1;
+    for (int32_t e = 0; e < E; ++e)
+        if (used[e]) list[nu++] = e;
+
+    const int64_t gq_n = (int64_t)F * D / 2, gs_n = (int64_t)F * D / 32;
+    const int64_t dq_n = (int64_t)D * F / 2, ds_n = (int64_t)D * F / 32;
+    int failed = 0;
+
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        float *Wg = (float *)malloc(sizeof(float) * (size_t)F * D);
+        float *Wu = (float *)malloc(sizeof(float) * (size_t)F * D);
+        float *Wd = (float *)malloc(sizeof(float) * (size_t)D * F);
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t j = 0; j < nu; ++j) {
+            if (!Wg || !Wu || !Wd) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            int32_t e = list[j];
+            k3o_dequant(gq + e * gq_n, gs + e * gs_n, F, D, Wg);
+            k3o_dequant(uq + e * gq_n, us + e * gs_n, F, D, Wu);
+            k3o_dequant(dq + e * dq_n, ds + e * ds_n, D, F, Wd);
+            for (int64_t p = 0; p < P; ++p) {
+                if (idx[p] != e) continue;
+                int64_t t = p / K;
+                k3o_expert(Wg, Wu, Wd, D, F, x + t * D, NULL, NULL,
+                           hk ? hk + p * F : NULL, yp + p * D);
+            }
+        }
+        free(Wg);
+        free(Wu);
+        free(Wd);
+    }
+
+    if (!failed) {
+        for (int32_t t = 0; t < T; ++t)
+            for (int32_t d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int32_t k = 0; k < K; ++k)
+                    acc += (double)w[(int64_t)t * K + k] * yp[((int64_t)t * K + k) * D + d];
+                y[(int64_t)t * D + d] = (float)acc;
+            }
+    }
+    free(used);
+    free(list);
+    if (!ytk) free(yp);
+    return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ chunk grouping */
+
+/* Group a chunk's (token, slot) pairs by expert with a counting sort ([PR676]
+ * chunked-prefill paragraph: the MoE loads each unique expert of the chunk once;
+ * [PR684] chunked-prefill commit: position lists via counting sort).
+ *   counts[e]   number of pairs routed to e
+ *   offsets[e]  exclusive prefix sum of counts (offsets[E] = T*K)
+ *   perm[...]   pair ids p = t*K + k, grouped by ascending expert and, within an
+ *               expert, in ascending p (a counting sort is stable)
+ *   uniq[...]   the experts with counts > 0, ascending; *n_unique their number
+ * Returns 0, or -1 if an index is out of range. */
+int k3o_group(const int32_t *idx, int32_t T, int32_t K, int32_t E, int32_t *counts,
+              int32_t *offsets, int32_t *perm, int32_t *uniq, int32_t *n_unique)
+{
+    int64_t P = (int64_t)T * K;
+    memset(counts, 0, sizeof(int32_t) * (size_t)E);
+    for (int64_t p = 0; p < P; ++p) {
+        if (idx[p] < 0 || idx[p] >= E) return -1;
+        counts[idx[p]]++;
+    }
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *fill = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    for (int64_t p = 0; p < P; ++p) {
+        int32_t e = idx[p];
+        perm[offsets[e] + fill[e]] = (int32_t)p;
+        fill[e]++;
+    }
+    free(fill);
+    int32_t nu = 0;
+    for (int32_t e = 0; e < E; ++e)
+        if (counts[e] > 0) uniq[nu++] = e;
+    *n_unique = nu;
+    return 0;
+}

@@ -1,0 +1,199 @@
+"""Seeded synthetic inputs for the MXFP4 routed-expert block.
+
+This module only draws numbers: it holds none of the block's arithmetic (no
+decode, no routing, no matmul).  Both the CPU oracle and the HIP library are fed
+from it, so the two sides always see byte-identical inputs.
+
+Workloads (shapes from the Kimi K3 engine pages: 896 routed experts per layer,
+top-16, a 3584-dim latent space; F = 3072 makes one expert 17 547 264 bytes of
+MXFP4, i.e. 16 experts x 92 MoE layers = 25.8 GB streamed per token, the volume
+colibri PR #676 reports in "It runs the full model"):
+
+  tiny        1 token,   E=8,   K=2,  D=256,  F=128, decode path
+  decode1     1 token,   E=896, K=16, D=3584, F=3072, decode path
+  prefill32   32 tokens, same shape, AR(1) hidden states, logits = h.R, chunk path
+  prefill256  256 tokens, same as prefill32, chunk path
+  batch4096   4096 tokens, i.i.d. hidden states, logits = h.R, chunk path;
+              eight "edge" experts carry scale bytes over the full 0..255 range
+
+Weights: each packed byte is drawn uniform over 0..255, i.e. both e2m1 nibbles
+independent and uniform over the 16 codes.  Scale bytes are uniform integers over
+an inclusive range.  Every (expert, tensor) pair has its own PCG64 sub-stream
+``default_rng([weight_seed, expert, tensor_id])`` so any expert can be
+regenerated alone (the oracle needs only the experts a sample touches).
+tensor_id order: gate_q, gate_s, up_q, up_s, down_q, down_s.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import os
+from typing import Dict, Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+TENSORS = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    T: int
+    E: int
+    K: int
+    D: int
+    F: int
+    weight_seed: int
+    act_seed: int
+    scale_lo: int
+    scale_hi: int
+    x_kind: str            # "normal" (i.i.d. N(0,1)) or "ar1"
+    logit_kind: str        # "normal" (i.i.d. N(0,1)) or "hR" (h_t . R)
+    bias_std: float        # score-correction bias ~ N(0, bias_std^2); 0 -> zeros
+    path: str              # "decode" or "chunk"
+    edge_experts: Tuple[int, ...] = ()
+
+    @property
+    def pairs(self) -> int:
+        return self.T * self.K
+
+    def expert_bytes(self) -> int:
+        """MXFP4 bytes of one expert: three [rows, cols/2] packed + [rows, cols/32] scales."""
+        per = self.F * self.D // 2 + self.F * self.D // 32
+        return 3 * per
+
+    def shapes(self) -> Dict[str, Tuple[int, int]]:
+        D, F = self.D, self.F
+        return {
+            "gate_q": (F, D // 2), "gate_s": (F, D // 32),
+            "up_q": (F, D // 2), "up_s": (F, D // 32),
+            "down_q": (D, F // 2), "down_s": (D, F // 32),
+        }
+
+
+_EDGE = tuple(range(0, 896, 112))  # 0, 112, ..., 784
+
+CONFIGS: Dict[str, Config] = {
+    "tiny": Config("tiny", T=1, E=8, K=2, D=256, F=128, weight_seed=101, act_seed=101,
+                   scale_lo=120, scale_hi=130, x_kind="normal", logit_kind="normal",
+                   bias_std=0.1, path="decode"),
+    "decode1": Config("decode1", T=1, E=896, K=16, D=3584, F=3072, weight_seed=102, act_seed=102,
+                      scale_lo=118, scale_hi=128, x_kind="normal", logit_kind="normal",
+                      bias_std=0.1, path="decode"),
+    "prefill32": Config("prefill32", T=32, E=896, K=16, D=3584, F=3072, weight_seed=102,
+                        act_seed=103, scale_lo=118, scale_hi=128, x_kind="ar1",
+                        logit_kind="hR", bias_std=0.0, path="chunk"),
+    "prefill256": Config("prefill256", T=256, E=896, K=16, D=3584, F=3072, weight_seed=102,
+                         act_seed=104, scale_lo=118, scale_hi=128, x_kind="ar1",
+                         logit_kind="hR", bias_std=0.0, path="chunk"),
+    "batch4096": Config("batch4096", T=4096, E=896, K=16, D=3584, F=3072, weight_seed=105,
+                        act_seed=105, scale_lo=118, scale_hi=128, x_kind="normal",
+                        logit_kind="hR", bias_std=0.0, path="chunk", edge_experts=_EDGE),
+}
+
+
+def scaled(cfg: Config, **changes) -> Config:
+    """A copy of ``cfg`` with some fields replaced (smaller T, other E/D/F ...)."""
+    return dataclasses.replace(cfg, **changes)
+
+
+# ----------------------------------------------------------------------------- weights
+def _tensor(cfg: Config, e: int, tid: int) -> np.ndarray:
+    name = TENSORS[tid]
+    shape = cfg.shapes()[name]
+    rng = np.random.default_rng([cfg.weight_seed, e, tid])
+    if name.endswith("_q"):
+        return rng.integers(0, 256, size=shape, dtype=np.uint8)
+    lo, hi = (0, 255) if e in cfg.edge_experts else (cfg.scale_lo, cfg.scale_hi)
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.uint8)
+
+
+def expert_tensors(cfg: Config, e: int) -> Dict[str, np.ndarray]:
+    """The six MXFP4 tensors of expert ``e`` (host numpy uint8)."""
+    if not 0 <= e < cfg.E:
+        raise ValueError(f"expert {e} out of range for E={cfg.E}")
+    return {name: _tensor(cfg, e, tid) for tid, name in enumerate(TENSORS)}
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def weights_host(cfg: Config, experts: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
+    """Stacked host weights ``{name: [n, rows, cols]}`` for ``experts`` (default: all)."""
+    ids = list(range(cfg.E)) if experts is None else [int(e) for e in experts]
+    out = {n: np.empty((len(ids),) + cfg.shapes()[n], dtype=np.uint8) for n in TENSORS}
+
+    def fill(j_e):
+        j, e = j_e
+        for tid, n in enumerate(TENSORS):
+            out[n][j] = _tensor(cfg, e, tid)
+
+    with _cf.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, enumerate(ids)))
+    return out
+
+
+def weights_device(cfg: Config, device, batch: int = 32):
+    """All E experts as torch uint8 tensors ``{name: [E, rows, cols]}`` on ``device``.
+
+    Generated on the host in batches of ``batch`` experts and copied up, so the
+    host never holds more than one batch.
+    """
+    import torch
+
+    dev = {n: torch.empty((cfg.E,) + cfg.shapes()[n], dtype=torch.uint8, device=device)
+           for n in TENSORS}
+    for e0 in range(0, cfg.E, batch):
+        ids = range(e0, min(cfg.E, e0 + batch))
+        host = weights_host(cfg, ids)
+        for n in TENSORS:
+            dev[n][e0:e0 + len(ids)].copy_(torch.from_numpy(host[n]), non_blocking=False)
+    return dev
+
+
+# ------------------------------------------------------------------------- activations
+def activations(cfg: Config, T: Optional[int] = None, stream: int = 0):
+    """``(x [T,D] f32, logits [T,E] f32, bias [E] f32)`` for the workload.
+
+    ``stream`` selects an independent draw of the same distribution (used to
+    build several different decode tokens for cache-cold timing).
+    """
+    T = cfg.T if T is None else int(T)
+    rng = np.random.default_rng([cfg.act_seed, 7919, stream])
+    if cfg.x_kind == "normal":
+        x64 = rng.standard_normal((T, cfg.D))
+    elif cfg.x_kind == "ar1":
+        # h_t = 0.9 h_{t-1} + 0.436 z_t, started at the stationary law h_0 ~ N(0, I)
+        z = rng.standard_normal((T, cfg.D))
+        x64 = np.empty_like(z)
+        x64[0] = z[0]
+        for t in range(1, T):
+            x64[t] = 0.9 * x64[t - 1] + 0.436 * z[t]
+    else:
+        raise ValueError(cfg.x_kind)
+    x = x64.astype(np.float32)
+
+    if cfg.logit_kind == "normal":
+        logits = rng.standard_normal((T, cfg.E)).astype(np.float32)
+    elif cfg.logit_kind == "hR":
+        # R ~ N(0, variance 1/D), so logits = h.R are ~N(0, 1) per entry
+        R = np.random.default_rng([cfg.act_seed, 104729]).standard_normal((cfg.D, cfg.E))
+        R *= np.sqrt(1.0 / cfg.D)
+        logits = (x.astype(np.float64) @ R).astype(np.float32)
+    else:
+        raise ValueError(cfg.logit_kind)
+
+    if cfg.bias_std > 0:
+        bias = (cfg.bias_std * np.random.default_rng([cfg.act_seed, 31337]).standard_normal(cfg.E)
+                ).astype(np.float32)
+    else:
+        bias = np.zeros(cfg.E, dtype=np.float32)
+    return np.ascontiguousarray(x), np.ascontiguousarray(logits), bias
+
+
+def sample_tokens(cfg: Config, n: int, must_include: Sequence[int] = (), seed: int = 0) -> np.ndarray:
+    """A sorted, seeded sample of ``n`` token ids plus every id in ``must_include``."""
+    rng = np.random.default_rng([cfg.act_seed, 271828, seed])
+    base = rng.choice(cfg.T, size=min(n, cfg.T), replace=False)
+    return np.unique(np.concatenate([base, np.asarray(must_include, dtype=np.int64)])).astype(np.int64)

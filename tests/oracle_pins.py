@@ -1,0 +1,393 @@
+"""Pins that tie the CPU oracle to what the pages and mathematics fix.
+
+Each ``check_*`` takes an oracle instance (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees.  ``test_oracle_pins.py`` runs them on
+the oracle as built; ``test_oracle_mutations.py`` runs them on copies of the
+oracle with one planted mistake each and requires that some check fails.
+
+None of these checks retypes the oracle's code: decode is compared with a value
+set derived from the e2m1 bit fields in exact rationals, the layout with a
+hand-worked fixture, sums with exact rational brute force, the activation with
+40-digit decimal arithmetic and its SwiGLU limit, the router with brute-force
+subset search, invariants and a case that separates the two readings of where
+the bias goes.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+import struct
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ---------------------------------------------------------------- reference helpers
+def e2m1_value(code: int) -> Fraction:
+    """e2m1 from its bit fields: sign bit3, exponent bits 2..1 (bias 1), mantissa bit0;
+    exponent field 0 is subnormal (m * 0.5)."""
+    e, m = (code >> 1) & 3, code & 1
+    mag = Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+    return -mag if code & 8 else mag
+
+
+def fp32_bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def closed_form_bits(code: int, s: int) -> int:
+    """fp32 bits of v * 2^(s-127), rounded to nearest (exact below 2^128, else inf)."""
+    v = e2m1_value(code)
+    mag = abs(v) * Fraction(2) ** (s - 127)
+    if mag >= 2 ** 128:
+        bits = 0x7F800000
+    else:
+        f = float(mag)
+        assert Fraction(f) == mag  # at most two significant bits: exact in double
+        bits = fp32_bits(f)
+        assert Fraction(struct.unpack("<f", struct.pack("<I", bits))[0]) == mag  # and in fp32
+    return bits | (0x80000000 if code & 8 else 0)
+
+
+def f32_bits_array(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+getcontext().prec = 40
+
+
+def _dexp(x) -> Decimal:
+    return Decimal(x).exp()
+
+
+def _dtanh(x) -> Decimal:
+    x = Decimal(x)
+    e2 = (2 * x).exp()
+    return (e2 - 1) / (e2 + 1)
+
+
+def _dsig(x) -> Decimal:
+    return 1 / (1 + _dexp(-Decimal(x)))
+
+
+def situ_decimal(g, u) -> Decimal:
+    """K3's SiTU-GLU at betas 4 and 25 in 40-digit decimal arithmetic."""
+    g, u = Decimal(repr(float(g))), Decimal(repr(float(u)))
+    return 4 * _dtanh(g / 4) * _dsig(g) * 25 * _dtanh(u / 25)
+
+
+def layout_fixture():
+    rows = []
+    with open(os.path.join(HERE, "golden", "mxfp4_layout.txt")) as fh:
+        for line in fh:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            b, s, v0, v1 = line.split()
+            conv = lambda t: float.fromhex(t) if "0x" in t else float(t)
+            rows.append((int(b, 16), int(s), conv(v0), conv(v1)))
+    return rows
+
+
+# ------------------------------------------------------------------------ P1 decode
+def check_decode_closed_form(o):
+    """All 16 codes x 256 scale bytes equal the closed form, bit for bit."""
+    table = f32_bits_array(o.decode_table())
+    for c in range(16):
+        for s in range(256):
+            want = closed_form_bits(c, s)
+            got = int(table.reshape(16, 256)[c, s])
+            assert got == want, f"decode(code={c}, s={s}): {got:#010x} != {want:#010x}"
+    # doubled e2m1 values are exact int8 (int8-activation commit, colibri PR #684)
+    for c in range(16):
+        d = 2 * e2m1_value(c)
+        assert d.denominator == 1 and -128 <= d.numerator <= 127
+
+
+def check_decode_conventions(o):
+    """The edge readings stated in the design: subnormals kept at s=0, s=255 is the
+    closed form (not NaN), code 8 is -0.0."""
+    assert fp32_bits(o.decode(1, 0)) == 0x00200000          # 0.5 * 2^-127 = 2^-128
+    assert fp32_bits(o.decode(7, 0)) == fp32_bits(1.5 * 2.0 ** -125)
+    assert fp32_bits(o.decode(0, 255)) == 0x00000000
+    assert fp32_bits(o.decode(8, 255)) == 0x80000000
+    assert fp32_bits(o.decode(1, 255)) == 0x7F000000        # 2^127
+    assert fp32_bits(o.decode(9, 255)) == 0xFF000000
+    assert fp32_bits(o.decode(2, 255)) == 0x7F800000        # 2^128 -> +inf
+    assert fp32_bits(o.decode(10, 255)) == 0xFF800000
+    for s in range(256):
+        assert fp32_bits(o.decode(8, s)) == 0x80000000
+
+
+# ------------------------------------------------------------------------ P2 layout
+def check_layout_fixture(o):
+    for byte, s, v_even, v_odd in layout_fixture():
+        q = np.full((1, 16), byte, dtype=np.uint8)
+        sc = np.full((1, 1), s, dtype=np.uint8)
+        out = o.dequant(q, sc)
+        for i in range(32):
+            want = v_even if i % 2 == 0 else v_odd
+            assert fp32_bits(float(out[0, i])) == fp32_bits(want), (hex(byte), s, i, out[0, i], want)
+
+
+def check_scale_groups(o):
+    """A scale byte applies to its own 32 columns only, and each row to its own scales."""
+    q = np.full((2, 32), 0x22, dtype=np.uint8)          # every code = 2 -> v = 1.0
+    s = np.array([[127, 129], [125, 127]], dtype=np.uint8)
+    out = o.dequant(q, s)
+    assert np.all(out[0, :32] == 1.0) and np.all(out[0, 32:] == 4.0)
+    assert np.all(out[1, :32] == 0.25) and np.all(out[1, 32:] == 1.0)
+
+
+def check_dequant_matches_codes(o):
+    """Random matrix: element (o, i) is the closed form of its own nibble and scale."""
+    rng = np.random.default_rng(11)
+    O, I = 3, 96
+    q = rng.integers(0, 256, size=(O, I // 2), dtype=np.uint8)
+    s = rng.integers(0, 256, size=(O, I // 32), dtype=np.uint8)
+    got = f32_bits_array(o.dequant(q, s))
+    for r in range(O):
+        for i in range(I):
+            byte = int(q[r, i // 2])
+            code = (byte & 0xF) if i % 2 == 0 else (byte >> 4)
+            assert int(got[r, i]) == closed_form_bits(code, int(s[r, i // 32])), (r, i)
+
+
+# ------------------------------------------------------------------------ P3 matmul
+def check_expert_brute_force(o):
+    """A 4 x 64 expert: g, u and y equal exact rational sums (relative 1e-12)."""
+    rng = np.random.default_rng(3)
+    D, F = 64, 4
+    Wg = rng.standard_normal((F, D)).astype(np.float32)
+    Wu = rng.standard_normal((F, D)).astype(np.float32)
+    Wd = rng.standard_normal((D, F)).astype(np.float32)
+    x = rng.standard_normal(D).astype(np.float32)
+    r = o.expert(Wg, Wu, Wd, x)
+    for name, W in (("g", Wg), ("u", Wu)):
+        for f in range(F):
+            exact = sum(Fraction(float(W[f, i])) * Fraction(float(x[i])) for i in range(D))
+            scale = sum(abs(Fraction(float(W[f, i])) * Fraction(float(x[i]))) for i in range(D))
+            assert abs(Fraction(r[name][f]) - exact) <= Fraction(1, 10 ** 12) * scale, (name, f)
+    for f in range(F):
+        assert r["h"][f] == o.situ(r["g"][f], r["u"][f])
+    for d in range(D):
+        exact = sum(Fraction(float(Wd[d, f])) * Fraction(float(r["h"][f])) for f in range(F))
+        scale = sum(abs(Fraction(float(Wd[d, f])) * Fraction(float(r["h"][f]))) for f in range(F))
+        assert abs(Fraction(r["y"][d]) - exact) <= Fraction(1, 10 ** 12) * scale + Fraction(1, 10 ** 300), d
+
+
+# ------------------------------------------------------------------------- P4 route
+def _brute_topk(keys, K):
+    """All K-subsets whose every member beats every non-member (ties -> lower id)."""
+    E = len(keys)
+    better = lambda a, b: keys[a] > keys[b] or (keys[a] == keys[b] and a < b)
+    sols = [S for S in itertools.combinations(range(E), K)
+            if all(better(a, b) for a in S for b in range(E) if b not in S)]
+    assert len(sols) == 1
+    return set(sols[0])
+
+
+def check_route_brute_force(o):
+    """E=8, K=2: the selection is the unique subset that dominates the rest, listed
+    in descending key order; weights sum to one."""
+    rng = np.random.default_rng(17)
+    for trial in range(20):
+        logits = rng.standard_normal((1, 8)).astype(np.float32)
+        bias = (0.1 * rng.standard_normal(8)).astype(np.float32)
+        idx, w, gap = o.route(logits, bias, 2)
+        # keys rebuilt with a textbook sigmoid in decimal, rounded to fp32, plus the bias
+        keys = [np.float32(np.float32(float(_dsig(Decimal(repr(float(l)))))) + bias[e])
+                for e, l in enumerate(logits[0])]
+        assert set(idx[0].tolist()) == _brute_topk(keys, 2), trial
+        assert keys[idx[0, 0]] > keys[idx[0, 1]] or (keys[idx[0, 0]] == keys[idx[0, 1]] and idx[0, 0] < idx[0, 1])
+        assert abs(float(w.sum(dtype=np.float64)) - 1.0) <= 2 * 2.0 ** -24
+        sel = sorted(keys, reverse=True)
+        assert abs(gap[0] - (float(sel[1]) - float(sel[2]))) <= 1e-12
+
+
+def check_route_invariants(o):
+    rng = np.random.default_rng(23)
+    T, E, K = 16, 896, 16
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    idx, w, gap = o.route(logits, bias, K)
+    for t in range(T):
+        assert len(set(idx[t].tolist())) == K
+        assert abs(float(w[t].sum(dtype=np.float64)) - 1.0) <= K * 2.0 ** -24
+        assert np.all(w[t] > 0)
+    # zero bias: selection is the top-K logits (sigmoid is monotone)
+    idx0, w0, _ = o.route(logits, np.zeros(E, np.float32), K)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))
+        assert set(idx0[t].tolist()) == set(order[:K]), t
+    # weights depend on the selection only, not on the bias ("raw-score renormalization"):
+    # lowering the bias of unselected experts keeps every selected key and the selection
+    for t in range(T):
+        b2 = bias.copy()
+        mask = np.ones(E, bool)
+        mask[idx[t]] = False
+        b2[mask] -= np.float32(1.0)
+        idx1, w1, _ = o.route(logits[t:t + 1], b2, K)
+        assert np.array_equal(idx1[0], idx[t]) and np.array_equal(w1[0], w[t]), t
+    # K = 1: weight exactly 1; equal logits: weights exactly 1/K, ties to lower ids
+    idxk, wk, _ = o.route(logits[:1], bias, 1)
+    assert wk[0, 0] == 1.0
+    flat = np.zeros((1, 10), np.float32)
+    idxf, wf, _ = o.route(flat, np.zeros(10, np.float32), 4)
+    assert idxf[0].tolist() == [0, 1, 2, 3] and np.all(wf == np.float32(0.25))
+    # K = E: w_e = sigma(l_e) / sum sigma, checked in decimal
+    l = rng.standard_normal((1, 6)).astype(np.float32)
+    idxa, wa, _ = o.route(l, np.zeros(6, np.float32), 6)
+    sig = [_dsig(Decimal(repr(float(v)))) for v in l[0]]
+    tot = sum(sig)
+    for k in range(6):
+        want = float(sig[idxa[0, k]] / tot)
+        assert abs(float(wa[0, k]) - want) <= 2.0 ** -24 * want
+
+
+def check_route_bias_reading(o):
+    """The bias corrects the SCORE sigma(l)+b, not the logit: l=(0,4), b=(0.5,0)
+    selects expert 0 (1.0 > 0.982), while sigma(l+b) would select expert 1."""
+    idx, w, _ = o.route(np.array([[0.0, 4.0]], np.float32), np.array([0.5, 0.0], np.float32), 1)
+    assert idx[0, 0] == 0 and w[0, 0] == 1.0
+    idx, w, _ = o.route(np.array([[0.0, 4.0, -1.0]], np.float32), np.array([0.5, 0.0, 0.0], np.float32), 2)
+    assert idx[0].tolist() == [0, 1]
+    s0, s1 = 1 / (1 + math.exp(-0.0)), 1 / (1 + math.exp(-4.0))
+    assert abs(float(w[0, 0]) - s0 / (s0 + s1)) <= 1e-7 and abs(float(w[0, 1]) - s1 / (s0 + s1)) <= 1e-7
+
+
+def check_route_nan(o):
+    """NaN logits rank below every number and are taken, lowest id first, only when
+    fewer than K finite keys remain."""
+    l = np.array([[np.nan, 1.0, np.nan, -2.0, np.nan]], np.float32)
+    idx, _, _ = o.route(l, np.zeros(5, np.float32), 3)
+    assert idx[0].tolist() == [1, 3, 0]
+
+
+# -------------------------------------------------------------------------- P5 SiTU
+def check_situ(o):
+    pts = [(4.0, 25.0), (1.0, 4.0), (4.0, 1.0), (-3.0, 7.0), (0.5, -30.0), (10.0, 100.0),
+           (-0.25, 0.125), (37.0, -61.0)]
+    for g, u in pts:
+        want = situ_decimal(g, u)
+        got = o.situ(g, u)
+        assert abs(Decimal(got) - want) <= Decimal("1e-14") * max(abs(want), Decimal("1e-300")), (g, u, got, want)
+    for v in (0.0, 1.5, -7.0, 300.0):
+        assert o.situ(0.0, v) == 0.0 and o.situ(v, 0.0) == 0.0
+        assert o.situ(3.0, -v) == -o.situ(3.0, v)                      # odd in u
+    for u in (1.0, -12.0, 40.0):
+        assert abs(o.situ(1e4, u) - 100.0 * math.tanh(u / 25.0)) <= 1e-13 * 100
+        assert o.situ(-1e4, u) == 0.0 and o.situ(-math.inf, u) == 0.0
+        assert abs(o.situ(math.inf, u) - 100.0 * math.tanh(u / 25.0)) <= 1e-13
+        assert math.isnan(o.situ(math.nan, u)) and math.isnan(o.situ(u, math.nan))
+    lim = 25.0 * 4.0 * math.tanh(0.5) / (1.0 + math.exp(-2.0))
+    assert abs(o.situ(2.0, math.inf) - lim) <= 1e-15 * lim
+    # generic betas -> infinity give SwiGLU g * sigma(g) * u (textbook special case)
+    for g, u in [(1.3, -0.7), (-2.0, 3.0), (0.25, 0.5)]:
+        swiglu = float(Decimal(g) * _dsig(g) * Decimal(u))
+        assert abs(o.situ_beta(g, u, 1e8, 1e8) - swiglu) <= 1e-9 * abs(swiglu)
+    # the K3 form is the generic form at betas 4 and 25
+    assert o.situ(2.5, -9.0) == o.situ_beta(2.5, -9.0, 4.0, 25.0)
+
+
+# ------------------------------------------------------------- P6/P7 forward, combine
+def _tiny():
+    import synth
+    cfg = synth.scaled(synth.CONFIGS["tiny"], T=6)
+    W = synth.weights_host(cfg)
+    x, logits, bias = synth.activations(cfg)
+    return cfg, W, x, logits, bias
+
+
+def check_forward_pairs(o):
+    """Pair (t,k) uses expert idx[t,k]'s decoded weights on token t's x; y_t is the
+    w-weighted sum of its pairs in k order."""
+    cfg, W, x, logits, bias = _tiny()
+    idx, w, _ = o.route(logits, bias, cfg.K)
+    y, ytk, hk = o.forward(W, x, idx, w, nthreads=2, want_pairs=True)
+    for t in range(cfg.T):
+        for k in range(cfg.K):
+            e = int(idx[t, k])
+            Wg = o.dequant(W["gate_q"][e], W["gate_s"][e])
+            Wu = o.dequant(W["up_q"][e], W["up_s"][e])
+            Wd = o.dequant(W["down_q"][e], W["down_s"][e])
+            r = o.expert(Wg, Wu, Wd, x[t])
+            assert np.array_equal(ytk[t, k], r["y"]) and np.array_equal(hk[t, k], r["h"]), (t, k)
+        acc = np.zeros(cfg.D)
+        for k in range(cfg.K):
+            acc = acc + np.float64(w[t, k]) * ytk[t, k]
+        assert np.array_equal(y[t], acc.astype(np.float32)), t
+
+
+def check_forward_combine(o):
+    cfg, W, x, logits, bias = _tiny()
+    idx, w, _ = o.route(logits, bias, cfg.K)
+    y = o.forward(W, x, idx, w, nthreads=2)
+    # linear in w (doubling is exact)
+    y2 = o.forward(W, x, idx, 2 * w, nthreads=2)
+    assert np.array_equal(y2, 2 * y)
+    # K = 1, w = 1: the single expert's output
+    e = int(idx[0, 0])
+    y1 = o.forward(W, x[:1], idx[:1, :1], np.ones((1, 1), np.float32), nthreads=1)
+    r = o.expert(o.dequant(W["gate_q"][e], W["gate_s"][e]), o.dequant(W["up_q"][e], W["up_s"][e]),
+                 o.dequant(W["down_q"][e], W["down_s"][e]), x[0])
+    assert np.array_equal(y1[0], r["y"].astype(np.float32))
+
+
+def check_chunk_equals_tokens(o):
+    """A chunk's output is bit-identical to running its tokens one at a time (the
+    chunked-prefill invariant, colibri PR #676 validation table)."""
+    cfg, W, x, logits, bias = _tiny()
+    idx, w, _ = o.route(logits, bias, cfg.K)
+    y = o.forward(W, x, idx, w, nthreads=3)
+    for t in range(cfg.T):
+        yt = o.forward(W, x[t:t + 1], idx[t:t + 1], w[t:t + 1], nthreads=1)
+        assert np.array_equal(yt[0], y[t]), t
+
+
+# -------------------------------------------------------------------------- P8 group
+def check_group(o):
+    rng = np.random.default_rng(29)
+    for T, K, E in [(1, 2, 8), (7, 3, 5), (33, 16, 896), (64, 4, 9)]:
+        idx = np.stack([rng.choice(E, size=K, replace=False) for _ in range(T)]).astype(np.int32)
+        g = o.group(idx, E)
+        pairs = [(int(idx[p // K, p % K]), p) for p in range(T * K)]
+        want_perm = [p for _, p in sorted(pairs)]
+        assert g["perm"].tolist() == want_perm
+        counts = [sum(1 for e, _ in pairs if e == x) for x in range(E)]
+        assert g["counts"].tolist() == counts
+        assert g["offsets"].tolist() == [sum(counts[:e]) for e in range(E + 1)]
+        union = sorted(set(idx.ravel().tolist()))
+        assert g["uniq"].tolist() == union and g["n_unique"] == len(union)
+
+
+# -------------------------------------------------------------- P9 generator moments
+def check_gate_moments(o):
+    """std(g) over rows matches sqrt(D * E[w^2]) with E[w^2] = E[v^2] * mean(4^(s-127)),
+    E[v^2] = 8.5625 over the 16 codes (1000+ rows, 3%)."""
+    import synth
+    cfg = synth.CONFIGS["decode1"]
+    ex = synth.expert_tensors(cfg, 5)
+    Wg = o.dequant(ex["gate_q"], ex["gate_s"])
+    Wd = o.dequant(ex["down_q"], ex["down_s"])
+    x = np.random.default_rng(1).standard_normal(cfg.D).astype(np.float32)
+    g = o.expert(Wg, Wg, Wd, x)["g"]
+    ev2 = float(sum(e2m1_value(c) ** 2 for c in range(16)) / 16)
+    assert ev2 == 8.5625
+    m4 = np.mean([4.0 ** (s - 127) for s in range(cfg.scale_lo, cfg.scale_hi + 1)])
+    want = math.sqrt(cfg.D * ev2 * m4 * float(np.mean(x.astype(np.float64) ** 2)))
+    got = float(np.sqrt(np.mean(g ** 2)))
+    assert abs(got / want - 1) < 0.03, (got, want)
+
+
+ALL_CHECKS = [
+    check_decode_closed_form, check_decode_conventions, check_layout_fixture, check_scale_groups,
+    check_dequant_matches_codes, check_expert_brute_force, check_route_brute_force,
+    check_route_invariants, check_route_bias_reading, check_route_nan, check_situ,
+    check_forward_pairs, check_forward_combine, check_chunk_equals_tokens, check_group,
+]
+# check_gate_moments is run separately (it pins the generator, and is the slowest)

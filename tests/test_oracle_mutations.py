@@ -1,0 +1,82 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case copies ``oracle/k3moe_oracle.c``, plants ONE mistake by a textual
+replacement, builds the copy with gcc into a temporary directory and runs every
+pin against it.  At least one pin must fail.  Everything here runs on the CPU.
+"""
+import os
+import shutil
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "k3moe_oracle.c")
+
+MUTANTS = [
+    ("nibble order swapped",
+     "(i % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4)", "(i % 2 == 0) ? (byte >> 4) : (byte & 0x0Fu)"),
+    ("sign bit ignored", "if (code & 8u) v = -v;", ""),
+    ("scale bias 128", "(int)(scale & 0xFFu) - 127", "(int)(scale & 0xFFu) - 128"),
+    ("e2m1 table entry", "{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}", "{0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 5.0}"),
+    ("s=255 read as NaN", "if (fabs(w) >= 0x1p128)", "if ((scale & 0xFFu) == 255u) return NAN;\n    if (fabs(w) >= 0x1p128)"),
+    ("subnormals flushed", "    return (float)w;\n}", "    return (fabs(w) < 0x1p-126) ? (float)copysign(0.0, w) : (float)w;\n}"),
+    ("wrong scale group", "s[o * (I / 32) + i / 32]", "s[o * (I / 32) + i / 64]"),
+    ("bias on logits", "score[e] = sigmoid((double)l[e]);\n            float s32 = (float)score[e];\n            float key = s32 + bias[e];",
+     "score[e] = sigmoid((double)l[e]);\n            float s32 = (float)sigmoid((double)l[e] + bias[e]);\n            float key = s32;"),
+    ("weights from biased keys", "denom += score[c[k].id];", "denom += c[k].key;"),
+    ("numerator from biased key", "w[(int64_t)t * K + k] = (float)(score[c[k].id] / denom);",
+     "w[(int64_t)t * K + k] = (float)(c[k].key / denom);"),
+    ("ties to higher id", "return (a->id < b->id) ? -1 : (a->id > b->id);", "return (a->id > b->id) ? -1 : (a->id < b->id);"),
+    ("renormalize over all experts", "for (int32_t k = 0; k < K; ++k) denom += score[c[k].id];",
+     "for (int32_t k = 0; k < E; ++k) denom += score[c[k].id];"),
+    ("NaN not demoted", "if (isnan(key)) key = -INFINITY;", ""),
+    ("sigmoid sign", "return 1.0 / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(z));"),
+    ("betas swapped", "k3o_situ_beta(g, u, 4.0, 25.0)", "k3o_situ_beta(g, u, 25.0, 4.0)"),
+    ("sigma on up branch", "sigmoid(g) * bu", "sigmoid(u) * bu"),
+    ("gate/up swapped", "hh[f] = k3o_situ(ag, au);", "hh[f] = k3o_situ(au, ag);"),
+    ("down transposed", "Wd[(int64_t)d * F + f]", "Wd[(int64_t)f * D + d]"),
+    ("dropped last input term", "for (int32_t i = 0; i < D; ++i) {", "for (int32_t i = 0; i < D - 1; ++i) {"),
+    ("wrong token for a pair", "x + t * D, NULL, NULL", "x + (p % T) * D, NULL, NULL"),
+    ("combine ignores weights", "acc += (double)w[(int64_t)t * K + k] * yp[", "acc += yp["),
+    ("combine drops last slot", "for (int32_t k = 0; k < K; ++k)\n                    acc +=",
+     "for (int32_t k = 0; k < K - 1; ++k)\n                    acc +="),
+    ("group order unstable", "for (int64_t p = 0; p < P; ++p) {\n        int32_t e = idx[p];\n        perm",
+     "for (int64_t p = P - 1; p >= 0; --p) {\n        int32_t e = idx[p];\n        perm"),
+    ("union misses singletons", "if (counts[e] > 0) uniq[nu++] = e;", "if (counts[e] > 1) uniq[nu++] = e;"),
+    ("offsets inclusive", "offsets[e + 1] = offsets[e] + counts[e];", "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
+]
+
+
+@pytest.fixture(scope="module")
+def tmpdir_module():
+    d = tempfile.mkdtemp(prefix="k3o_mut_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def test_mutants_are_distinct():
+    src = open(SRC).read()
+    for name, old, _ in MUTANTS:
+        assert src.count(old) == 1, f"mutation site for {name!r} must occur exactly once"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, tmpdir_module):
+    src = open(SRC).read()
+    assert src.count(old) == 1
+    tag = "".join(ch if ch.isalnum() else "_" for ch in name)
+    csrc = os.path.join(tmpdir_module, f"{tag}.c")
+    with open(csrc, "w") as fh:
+        fh.write(src.replace(old, new))
+    lib = oracle.build(force=True, src=csrc, out=os.path.join(tmpdir_module, f"{tag}.so"))
+    mut = oracle.Oracle(lib)
+    failures = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check(mut)
+        except (AssertionError, ValueError) as exc:  # ValueError: oracle rejected its own output
+            failures.append((check.__name__, str(exc)[:80]))
+    assert failures, f"no pin catches the planted mistake {name!r}"

@@ -1,0 +1,59 @@
+"""The seeded generator: determinism, per-expert independence, stated ranges."""
+import hashlib
+
+import numpy as np
+
+import synth
+
+
+def test_configs_shapes():
+    c = synth.CONFIGS["decode1"]
+    assert (c.E, c.K, c.D, c.F) == (896, 16, 3584, 3072)
+    assert c.expert_bytes() == 17_547_264                  # ~17.5 MB per expert
+    assert 16 * c.expert_bytes() * 92 / 1e9 > 25.8          # 25.8 GB per token over 92 layers
+    assert synth.CONFIGS["batch4096"].edge_experts == tuple(range(0, 896, 112))
+
+
+def test_deterministic_and_independent():
+    cfg = synth.CONFIGS["tiny"]
+    a = synth.weights_host(cfg)
+    b = synth.weights_host(cfg)
+    for n in synth.TENSORS:
+        assert np.array_equal(a[n], b[n])
+    sub = synth.weights_host(cfg, [5, 2])
+    for n in synth.TENSORS:
+        assert np.array_equal(sub[n][0], a[n][5]) and np.array_equal(sub[n][1], a[n][2])
+    h = hashlib.sha256(b"".join(a[n].tobytes() for n in synth.TENSORS)).hexdigest()
+    assert h == hashlib.sha256(b"".join(b[n].tobytes() for n in synth.TENSORS)).hexdigest()
+
+
+def test_ranges():
+    cfg = synth.CONFIGS["tiny"]
+    W = synth.weights_host(cfg)
+    for n in ("gate_s", "up_s", "down_s"):
+        assert W[n].min() >= 120 and W[n].max() <= 130
+    lo = W["gate_q"] & 0xF
+    hi = W["gate_q"] >> 4
+    assert set(np.unique(lo)) == set(range(16)) and set(np.unique(hi)) == set(range(16))
+    big = synth.CONFIGS["batch4096"]
+    edge = synth.expert_tensors(big, 112)
+    assert edge["gate_s"].min() == 0 and edge["gate_s"].max() == 255
+    normal = synth.expert_tensors(big, 1)
+    assert normal["gate_s"].min() == 118 and normal["gate_s"].max() == 128
+
+
+def test_activations():
+    cfg = synth.CONFIGS["prefill32"]
+    x, logits, bias = synth.activations(cfg)
+    assert x.shape == (32, 3584) and x.dtype == np.float32
+    assert logits.shape == (32, 896) and np.all(bias == 0)
+    assert abs(float(np.std(logits)) - 1.0) < 0.05          # h.R with var(R) = 1/D
+    assert abs(float(np.std(x)) - 1.0) < 0.05                # stationary AR(1)
+    corr = float(np.mean(x[1:] * x[:-1]))
+    assert abs(corr - 0.9) < 0.05                            # lag-1 correlation 0.9
+    c1 = synth.CONFIGS["tiny"]
+    x1, l1, b1 = synth.activations(c1)
+    assert x1.shape == (1, 256) and l1.shape == (1, 8) and b1.shape == (8,) and np.any(b1 != 0)
+    xa, _, _ = synth.activations(c1, T=4, stream=1)
+    xb, _, _ = synth.activations(c1, T=4, stream=2)
+    assert not np.array_equal(xa, xb)
