@@ -1,0 +1,194 @@
+"""Benchmark of the MI355X routed-expert block (one GPU).
+
+A step is one pass of the block's hot path for one decode token at the K3 shape
+(896 experts, top-16, D=3584, F=3072, MXFP4): the router on the token's logits,
+then the 16 selected experts' gate/up GEMVs, SiTU-GLU, down GEMVs and the
+weighted combine.  Steps rotate over 32 pre-generated tokens whose expert sets
+differ, so each step streams its 16 experts (280.76 MB) from HBM rather than from
+the 256 MB last-level cache.  The value is routed-expert weight bytes per second
+over the timed steps (inputs resident in HBM).
+
+Also reported: the 4096-token chunk pass (grouped bf16-MFMA path) in TFLOP/s,
+the roofline of the decode kernels measured with HIP events on their stream, and
+the CPU oracle timed on a bounded sample as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-expert MXFP4 GB/s + µs/layer-token (decode); TFLOP/s (chunk) vs roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--chunk-iters", type=int, default=5)
+    ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this block's kernels run on a single MI355X "
+              "(multi-GPU sharding is a design note, not implemented); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from mxfp4_routed_expert_k3moe_amd import lib
+
+    lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------- decode workload
+    cfg = synth.CONFIGS["decode1"]
+    log(f"generating {cfg.name} weights ({cfg.E} experts, {cfg.E * cfg.expert_bytes() / 1e9:.1f} GB)")
+    t0 = time.time()
+    W = lib.ExpertWeights.from_dict(synth.weights_device(cfg, dev))
+    log(f"weights resident in {time.time() - t0:.1f}s")
+    n_rot = 32
+    xs, logits, bias = synth.activations(cfg, T=n_rot, stream=5)
+    x_d = torch.from_numpy(xs).to(dev)
+    l_d = torch.from_numpy(logits).to(dev)
+    b_d = torch.from_numpy(bias).to(dev)
+    K = cfg.K
+    idx_d = torch.empty((n_rot, K), dtype=torch.int32, device=dev)
+    w_d = torch.empty((n_rot, K), dtype=torch.float32, device=dev)
+    y_d = torch.empty((n_rot, cfg.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(lib.workspace_size(lib.OP_DECODE, 1, K, W), dtype=torch.uint8, device=dev)
+    bytes_per_token = K * cfg.expert_bytes()  # 280 756 224
+
+    def step(j, ev=None):
+        lib.route(l_d[j:j + 1], b_d, K, idx=idx_d[j:j + 1], w=w_d[j:j + 1])
+        if ev is not None:
+            ev[0].record(stream)
+        lib.forward_decode(W, x_d[j], idx_d[j], w_d[j], y=y_d[j], ws=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i % n_rot)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps between two synchronizations
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i % n_rot, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])  # forward_decode per call
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = bytes_per_token * args.steps / elapsed / 1e9
+    dec_avg_us = float(np.mean(dec_ms) * 1e3)
+    achieved = bytes_per_token / (dec_avg_us * 1e-6) / 1e9
+    log(f"decode: {ms_per_step * 1e3:.1f} us/step (route + forward), forward_decode {dec_avg_us:.1f} us "
+        f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f}) -> "
+        f"{achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode1: 1 token/step (rotating over 32), 896 experts top-16, D=3584, F=3072, "
+                               "MXFP4 experts, fp32 activations",
+                   "tokens_per_step": 1, "experts": cfg.E, "top_k": K, "d_model": cfg.D, "d_ff": cfg.F,
+                   "expert_bytes_per_token": bytes_per_token},
+        "us_per_layer_token": round(ms_per_step * 1e3, 3),
+        "forward_decode_us": round(dec_avg_us, 3),
+        "roofline": {"bound": "hbm", "kernel": "forward_decode (gate/up+SiTU and down+combine kernels)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    del W, ws
+    torch.cuda.empty_cache()
+
+    # -------------------------------------------------------------- chunk workload
+    if not args.no_chunk:
+        ccfg = synth.CONFIGS["batch4096"]
+        log(f"generating {ccfg.name} weights")
+        Wc = lib.ExpertWeights.from_dict(synth.weights_device(ccfg, dev))
+        x, lg, bs = synth.activations(ccfg)
+        xc = torch.from_numpy(x).to(dev).to(torch.bfloat16)  # x holds bf16 values: exact
+        idx_c, w_c = lib.route(torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev), ccfg.K)
+        yc = torch.empty((ccfg.T, ccfg.D), dtype=torch.float32, device=dev)
+        nu = torch.zeros(1, dtype=torch.int32, device=dev)
+        wsc = torch.empty(lib.workspace_size(lib.OP_CHUNK, ccfg.T, ccfg.K, Wc), dtype=torch.uint8, device=dev)
+        lib.forward_chunk(Wc, xc, idx_c, w_c, y=yc, n_unique=nu, ws=wsc)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.chunk_iters):
+            lib.route(torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev), ccfg.K, idx=idx_c, w=w_c)
+            lib.forward_chunk(Wc, xc, idx_c, w_c, y=yc, n_unique=nu, ws=wsc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.chunk_iters
+        U = int(nu.item())
+        flops = 6.0 * ccfg.D * ccfg.F * ccfg.T * ccfg.K
+        wbytes = U * ccfg.expert_bytes()
+        result["chunk"] = {"workload": "batch4096: 4096 tokens, i.i.d. hidden states, logits = h.R, same shape, "
+                                       "bf16 MFMA grouped GEMM",
+                           "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
+                           "tflops_frac_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                           "weight_gbs": round(wbytes / ms / 1e6, 1), "unique_experts": U}
+        log(f"chunk: {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s, union {U}")
+        del Wc, wsc
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- CPU baseline
+    if not args.no_cpu:
+        import oracle
+        n_thr = oracle.default_threads()
+        xs_h, lg_h, bs_h = synth.activations(cfg, T=64, stream=9)
+        idx_h, w_h, _ = oracle.route(lg_h, bs_h, K)
+        done, t_cpu = 0, 0.0
+        while done < 64 and t_cpu < args.cpu_seconds:
+            used = np.unique(idx_h[done])
+            Wh = synth.weights_host(cfg, used)
+            local = np.searchsorted(used, idx_h[done:done + 1]).astype(np.int32)
+            t0 = time.perf_counter()
+            oracle.forward(Wh, xs_h[done:done + 1], local, w_h[done:done + 1], nthreads=n_thr)
+            t_cpu += time.perf_counter() - t0
+            done += 1
+        cpu_gbs = done * bytes_per_token / t_cpu / 1e9
+        result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": n_thr, "kind": "oracle",
+                                  "sample": f"{done} decode1 tokens (16 experts each, route excluded), "
+                                            f"{t_cpu:.1f} s on {n_thr} threads",
+                                  "us_per_layer_token": round(t_cpu / done * 1e6, 1)}
+        log(f"cpu oracle: {cpu_gbs:.3f} GB/s over {done} tokens")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

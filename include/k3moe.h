@@ -1,0 +1,177 @@
+/*
+ * k3moe.h -- C ABI of the MI355X (gfx950) routed-expert library for the Kimi K3
+ * "Stable LatentMoE" block.
+ *
+ * The block (colibri PR #684, "Kimi K3: integrate coli chat, API, and Web",
+ * engine commit, Stable LatentMoE bullet; colibri PR #676, "Kimi K3 engine:
+ * native-MXFP4 expert streaming ...", summary bullets):
+ *   1. route:   sigmoid router with a score-correction bias, top-K of E experts,
+ *               weights renormalized over the raw sigmoid scores;
+ *   2. per selected expert e: g = W_gate[e] x, u = W_up[e] x   (MXFP4 weights)
+ *   3. h = 4 tanh(g/4) sigmoid(g) * 25 tanh(u/25)              (SiTU-GLU)
+ *   4. y_e = W_down[e] h                                       (MXFP4 weights)
+ *   5. y = sum_k w_k y_{e_k}                                   (gate-weighted combine)
+ *
+ * MXFP4 tensors follow the compressed-tensors "mxfp4-pack-quantized" layout
+ * (colibri PR #684, MXFP4-kernel commit): a matrix [O, I] is stored as packed
+ * bytes [O, I/2] -- the LOW nibble holds the even column, the high nibble the odd
+ * column, bit3 of a nibble is its sign, bits 2..0 an e2m1 magnitude
+ * {0, .5, 1, 1.5, 2, 3, 4, 6} -- plus ue8m0 scale bytes [O, I/32], one per 32
+ * consecutive inputs of a row; a weight is w = v * 2^(s-127), rounded once to
+ * fp32 (subnormals kept; values >= 2^128 are +-inf; s = 255 follows the same
+ * closed form, it is not NaN).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing and keeps no state except a per-device property cache.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream).  No call synchronizes; results are ready when the stream is.
+ *   - Return value: K3MOE_OK (0) or a negative K3MOE_E_* code.  Arguments are
+ *     validated on the host BEFORE anything is launched, so on an error nothing
+ *     was enqueued.  Errors inside kernels (bad device data) cannot be returned
+ *     synchronously; where they are detected the documented output says so.
+ *   - Calls on different streams need separate workspaces; calls that share a
+ *     workspace must be ordered on one stream.
+ *   - Only gfx950 devices are supported (K3MOE_E_DEVICE otherwise).
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status codes */
+#define K3MOE_OK 0
+#define K3MOE_E_NULL (-1)       /* a required pointer is NULL                         */
+#define K3MOE_E_DIM (-2)        /* a size is out of range (see each entry point)      */
+#define K3MOE_E_ALIGN (-3)      /* a pointer or expert stride is not 16-byte aligned  */
+#define K3MOE_E_WORKSPACE (-4)  /* workspace smaller than k3moe_workspace_size()      */
+#define K3MOE_E_DEVICE (-5)     /* current device is not gfx950                       */
+#define K3MOE_E_HIP (-6)        /* the HIP runtime reported an error at launch        */
+
+/* Limits shared by the entry points. */
+#define K3MOE_MAX_K 64          /* experts per token                                  */
+#define K3MOE_MAX_E 4096        /* experts per layer                                  */
+#define K3MOE_MAX_DIM 8192      /* latent width D and expert width F                  */
+
+/* Workspace kinds for k3moe_workspace_size(). */
+#define K3MOE_OP_DECODE 1
+#define K3MOE_OP_CHUNK 2
+#define K3MOE_OP_GROUP 3
+
+/* Output element types for k3moe_dequant_mxfp4(). */
+#define K3MOE_OUT_F32 0
+#define K3MOE_OUT_BF16 1
+
+/*
+ * The routed experts of one MoE layer.  For expert e (0 <= e < n_experts):
+ *   gate, up: packed [d_ff, d_model/2] at gate_q + e*gate_q_stride (bytes),
+ *             scales [d_ff, d_model/32] at gate_s + e*gate_s_stride;
+ *   down:     packed [d_model, d_ff/2], scales [d_model, d_ff/32].
+ * The strides let the same struct address stacked [E, ...] tensors or any other
+ * placement of the six tensors (the pages store them back to back per expert).
+ * Requirements: d_model and d_ff multiples of 32 in [32, K3MOE_MAX_DIM];
+ * 1 <= n_experts <= K3MOE_MAX_E; the three packed base pointers and their
+ * strides 16-byte aligned.  The struct itself lives in host memory and is read
+ * only during the call.
+ */
+typedef struct k3moe_weights {
+    int32_t n_experts;
+    int32_t d_model;  /* D: the latent width (3584 for K3) */
+    int32_t d_ff;     /* F: the expert width               */
+    const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
+    int64_t gate_q_stride, gate_s_stride, up_q_stride, up_s_stride, down_q_stride, down_s_stride;
+} k3moe_weights_t;
+
+/*
+ * Route T tokens (step 1 above).  For each token t and expert e:
+ *   score = sigmoid(logits[t,e]) evaluated in double and rounded to fp32,
+ *   key   = fp32(score + bias[e])  (a NaN key counts as -inf; -0 counts as +0);
+ * the K largest keys are selected, equal keys going to the lower expert id, and
+ * written in descending key order to idx[t, 0..K-1]; the weights are
+ *   w[t,k] = sigmoid(l_{e_k}) / sum_j sigmoid(l_{e_j})   (double, rounded to fp32),
+ * so the bias steers selection only and each row of w sums to one.
+ * logits [T, E] fp32, bias [E] fp32, idx [T, K] int32, w [T, K] fp32 (device).
+ * Requires T >= 1, 1 <= K <= min(E, K3MOE_MAX_K), E <= K3MOE_MAX_E.
+ */
+int k3moe_route(const float *logits, const float *bias, int32_t T, int32_t E, int32_t K,
+                int32_t *idx, float *w, void *stream);
+
+/*
+ * Group a chunk's (token, slot) pairs by expert with a counting sort (colibri
+ * PR #676, chunked-prefill paragraph: the MoE loads each unique expert of a chunk
+ * once; PR #684 chunked-prefill commit: position lists via counting sort).
+ * Pair p = t*K + k is routed to idx[p].  Outputs (device, int32):
+ *   counts[E]     pairs per expert;
+ *   offsets[E+1]  exclusive prefix sum of counts (offsets[E] = T*K);
+ *   perm[T*K]     pair ids grouped by ascending expert, ascending p within one;
+ *   uniq[E]       the experts with counts > 0 in ascending order (entries past
+ *                 n_unique are left unspecified);
+ *   n_unique[1]   their number, or -1 if some idx is outside [0, E) or a token
+ *                 lists one expert twice (the other outputs are then unspecified).
+ * ws: device workspace of k3moe_workspace_size(K3MOE_OP_GROUP, T, K, W) bytes
+ * (W supplies only n_experts here).  Requires T >= 1, 1 <= K <= min(E, 64).
+ */
+int k3moe_group(const int32_t *idx, int32_t T, int32_t K, int32_t E, int32_t *counts,
+                int32_t *offsets, int32_t *perm, int32_t *uniq, int32_t *n_unique, void *ws,
+                size_t ws_bytes, void *stream);
+
+/*
+ * One token through the routed experts (steps 2-5), fp32 end to end: weights
+ * are decoded to fp32 exactly, dot products accumulate in fp32, SiTU-GLU runs in
+ * fp32 and the combine sums w_k * y_k in slot order k = 0..K-1.  This is the
+ * memory-bound decode path; every selected expert's bytes are read once.
+ * x [D] fp32, idx [K] int32 (each in [0, E), distinct), w [K] fp32, y [D] fp32.
+ * ws: k3moe_workspace_size(K3MOE_OP_DECODE, 1, K, W) bytes.  Out-of-range
+ * indices are not read; their slots contribute NaN to y.
+ */
+int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t *idx,
+                         const float *w, int32_t K, float *y, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/*
+ * A chunk of T tokens through the routed experts (steps 2-5) with the chunk's
+ * expert union deduplicated: the pairs are grouped by expert (k3moe_group), each
+ * routed expert's weights are streamed once per group of up to 128 of its
+ * tokens, and gate/up and down run as bf16 MFMA matrix products with fp32
+ * accumulation.  The activations x are bf16; the decoded weights are exact in
+ * bf16; h is rounded to bf16 (round-to-nearest-even) between the two products.
+ * The combine sums w_{t,k} * y_{t,k} in slot order in fp32.
+ * x [T, D] bf16 (raw 16-bit patterns), idx [T, K] int32, w [T, K] fp32,
+ * y [T, D] fp32; n_unique (device int32, nullable) receives the union size, or
+ * -1 for invalid routing, in which case every element of y is NaN.
+ * ws: k3moe_workspace_size(K3MOE_OP_CHUNK, T, K, W) bytes.
+ */
+int k3moe_forward_chunk(const k3moe_weights_t *W, const uint16_t *x, int32_t T, const int32_t *idx,
+                        const float *w, int32_t K, float *y, int32_t *n_unique, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/*
+ * Bytes of device workspace needed by `op` (K3MOE_OP_*) for T tokens and K slots
+ * per token on the layer described by W (n_experts, d_model, d_ff are read).
+ * Returns 0 for invalid arguments.  Pure host function.
+ */
+size_t k3moe_workspace_size(int32_t op, int32_t T, int32_t K, const k3moe_weights_t *W);
+
+/*
+ * Decode one MXFP4 matrix (q [O, I/2], s [O, I/32]) to out [O, I] as fp32
+ * (out_dtype K3MOE_OUT_F32) or bf16 (K3MOE_OUT_BF16), with the same device code
+ * the matrix products use.  Every decoded value is exactly representable in both
+ * types.  Requires O >= 1, I a positive multiple of 32, q 16-byte aligned.
+ */
+int k3moe_dequant_mxfp4(const uint8_t *q, const uint8_t *s, int32_t O, int32_t I, void *out,
+                        int32_t out_dtype, void *stream);
+
+/* Text for a status code (static storage; for K3MOE_E_HIP it includes the HIP
+ * runtime's message for the calling thread's last failure). */
+const char *k3moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K3MOE_H */

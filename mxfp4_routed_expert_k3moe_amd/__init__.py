@@ -1,0 +1,8 @@
+"""MI355X (gfx950) routed-expert block of the Kimi K3 Stable LatentMoE.
+
+The work happens in ``libk3moe.so`` (hand-written HIP kernels behind the C ABI in
+``include/k3moe.h``); ``lib`` is its ctypes binding and ``_build`` compiles it.
+"""
+from . import lib  # noqa: F401
+from .lib import (ExpertWeights, K3moeError, dequant_mxfp4, forward_chunk, forward_decode,  # noqa: F401
+                  group, load, route, status_string, workspace_size)

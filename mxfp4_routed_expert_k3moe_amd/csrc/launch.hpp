@@ -1,0 +1,79 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace k3moe {
+
+// Expert weights as the kernels see them (plain values, passed by value).
+struct DevWeights {
+    int32_t E, D, F;
+    const uint8_t *gate_q, *gate_s, *up_q, *up_s, *down_q, *down_s;
+    int64_t gate_q_stride, gate_s_stride, up_q_stride, up_s_stride, down_q_stride, down_s_stride;
+};
+
+// ------------------------------------------------------------------ route
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K, int32_t* idx,
+                        float* w, hipStream_t stream);
+
+// ------------------------------------------------------------------ decode
+constexpr int kDecodeRowsPerWaveGU = 8;    // (gate,up) row pairs per wave
+constexpr int kDecodeRowsPerWaveDown = 8;  // down rows per wave
+constexpr int kDecodeWaves = 4;            // waves per workgroup
+
+struct DecodeWorkspace {
+    float* h;            // [K, F]
+    float* ypart;        // [K, D]
+    uint32_t* counters;  // [n_counters]
+    int n_counters;
+};
+size_t decode_workspace_bytes(int K, int D, int F);
+DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F);
+hipError_t launch_decode(const DevWeights& W, const float* x, const int32_t* idx, const float* w, int K,
+                         float* y, const DecodeWorkspace& ws, hipStream_t stream);
+
+// ------------------------------------------------------------------ chunk
+constexpr int kGroupTokens = 64;   // tokens per grouping block (one u64 mask bit each)
+constexpr int kTileRows = 128;     // max rows (pairs of one expert) per GEMM tile
+
+struct GroupBuffers {
+    int nb;                 // grouping blocks = ceil(T / 64)
+    int32_t* counts_blk;    // [nb, E]
+    uint64_t* masks_blk;    // [nb, E]
+    int32_t* blkoff;        // [nb, E]
+    int32_t* err_blk;       // [nb]
+    int32_t* scalars;       // [0] n_unique (or -1), [1] n_tiles
+    int4* tiles;            // [max_tiles] (expert, row0, rows, 0)
+    int max_tiles;
+    // outputs (caller's buffers for k3moe_group, workspace for forward_chunk)
+    int32_t* counts;        // [E]
+    int32_t* offsets;       // [E + 1]
+    int32_t* perm;          // [T * K]
+    int32_t* uniq;          // [E]
+};
+
+struct ChunkWorkspace {
+    GroupBuffers g;
+    uint16_t* h_bf16;       // [T*K, F]  (grouped pair order)
+    float* ytk;             // [T*K, D]  (pair order t*K + k)
+};
+
+int group_max_tiles(int T, int K, int E);
+size_t group_workspace_bytes(int T, int K, int E, bool with_outputs);
+GroupBuffers group_workspace_carve(void* ws, int T, int K, int E, bool with_outputs);
+size_t chunk_workspace_bytes(int T, int K, int E, int D, int F);
+ChunkWorkspace chunk_workspace_carve(void* ws, int T, int K, int E, int D, int F);
+
+hipError_t launch_group(const int32_t* idx, int T, int K, int E, const GroupBuffers& g,
+                        int32_t* n_unique_out, hipStream_t stream);
+hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int32_t* idx, const float* w,
+                        int K, float* y, int32_t* n_unique_out, const ChunkWorkspace& ws,
+                        hipStream_t stream);
+
+// ------------------------------------------------------------------ dequant
+hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int O, int I, void* out, int out_bf16,
+                          hipStream_t stream);
+
+}  // namespace k3moe

@@ -1,0 +1,234 @@
+"""ctypes binding of ``libk3moe.so`` (the C ABI in ``include/k3moe.h``).
+
+Argument marshalling only: every step of the routed-expert block runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current stream.
+If the library has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libk3moe.so")
+
+K3MOE_OK = 0
+K3MOE_E_NULL = -1
+K3MOE_E_DIM = -2
+K3MOE_E_ALIGN = -3
+K3MOE_E_WORKSPACE = -4
+K3MOE_E_DEVICE = -5
+K3MOE_E_HIP = -6
+K3MOE_MAX_K = 64
+K3MOE_MAX_E = 4096
+K3MOE_MAX_DIM = 8192
+OP_DECODE, OP_CHUNK, OP_GROUP = 1, 2, 3
+OUT_F32, OUT_BF16 = 0, 1
+
+ENTRY_POINTS = ("k3moe_route", "k3moe_group", "k3moe_forward_decode", "k3moe_forward_chunk",
+                "k3moe_workspace_size", "k3moe_dequant_mxfp4", "k3moe_status_string")
+
+
+class K3moeError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {status_string(code)} (status {code})")
+        self.code = code
+
+
+class WeightsStruct(ctypes.Structure):
+    _fields_ = ([("n_experts", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32)] +
+                [(n, ctypes.c_void_p) for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")] +
+                [(n + "_stride", ctypes.c_int64)
+                 for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")])
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (__graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    wp = ctypes.POINTER(WeightsStruct)
+    lib.k3moe_route.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.k3moe_group.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.k3moe_forward_decode.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.k3moe_forward_chunk.argtypes = [wp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.k3moe_workspace_size.argtypes = [i32, i32, i32, wp]
+    lib.k3moe_workspace_size.restype = sz
+    lib.k3moe_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, i32, vp]
+    lib.k3moe_status_string.argtypes = [ctypes.c_int]
+    lib.k3moe_status_string.restype = ctypes.c_char_p
+    for name in ENTRY_POINTS:
+        if name not in ("k3moe_workspace_size", "k3moe_status_string"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().k3moe_status_string(int(code)).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != K3MOE_OK:
+        raise K3moeError(fn, rc)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+class ExpertWeights:
+    """One layer's routed experts: six uint8 device tensors
+    ``gate_q [E,F,D/2]``, ``gate_s [E,F,D/32]``, ``up_q``, ``up_s`` (same shapes),
+    ``down_q [E,D,F/2]``, ``down_s [E,D,F/32]``."""
+
+    NAMES = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
+
+    def __init__(self, gate_q, gate_s, up_q, up_s, down_q, down_s):
+        E, F, half = gate_q.shape
+        D = 2 * half
+        shapes = {"gate_q": (E, F, D // 2), "gate_s": (E, F, D // 32), "up_q": (E, F, D // 2),
+                  "up_s": (E, F, D // 32), "down_q": (E, D, F // 2), "down_s": (E, D, F // 32)}
+        self.tensors = {}
+        for n, t in zip(self.NAMES, (gate_q, gate_s, up_q, up_s, down_q, down_s)):
+            self.tensors[n] = _dev(t, torch.uint8, n, shapes[n])
+        self.E, self.D, self.F = E, D, F
+        s = WeightsStruct()
+        s.n_experts, s.d_model, s.d_ff = E, D, F
+        for n in self.NAMES:
+            t = self.tensors[n]
+            setattr(s, n, t.data_ptr())
+            setattr(s, n + "_stride", t.stride(0) * t.element_size())
+        self.struct = s
+
+    @classmethod
+    def from_dict(cls, d: Dict[str, torch.Tensor]) -> "ExpertWeights":
+        return cls(*(d[n] for n in cls.NAMES))
+
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def workspace_size(op: int, T: int, K: int, W: ExpertWeights) -> int:
+    return int(load().k3moe_workspace_size(int(op), int(T), int(K), W.ref()))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return _dev(ws, torch.uint8, "workspace")
+
+
+def route(logits: torch.Tensor, bias: torch.Tensor, K: int, idx: Optional[torch.Tensor] = None,
+          w: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sigmoid + bias top-K router: ``logits [T,E]`` -> ``(idx [T,K] int32, w [T,K] f32)``."""
+    T, E = logits.shape
+    _dev(logits, torch.float32, "logits")
+    _dev(bias, torch.float32, "bias", (E,))
+    idx = torch.empty((T, K), dtype=torch.int32, device=logits.device) if idx is None else idx
+    w = torch.empty((T, K), dtype=torch.float32, device=logits.device) if w is None else w
+    _dev(idx, torch.int32, "idx", (T, K))
+    _dev(w, torch.float32, "w", (T, K))
+    _check("k3moe_route", load().k3moe_route(_ptr(logits), _ptr(bias), T, E, K, _ptr(idx), _ptr(w),
+                                              _stream(stream)))
+    return idx, w
+
+
+def group(idx: torch.Tensor, E: int, ws: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """Counting-sort grouping of a chunk's pairs by expert (device tensors)."""
+    T, K = idx.shape
+    _dev(idx, torch.int32, "idx")
+    dev = idx.device
+    out = {"counts": torch.empty(E, dtype=torch.int32, device=dev),
+           "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+           "perm": torch.empty(T * K, dtype=torch.int32, device=dev),
+           "uniq": torch.empty(E, dtype=torch.int32, device=dev),
+           "n_unique": torch.empty(1, dtype=torch.int32, device=dev)}
+    s = WeightsStruct()
+    s.n_experts, s.d_model, s.d_ff = E, 32, 32
+    nbytes = int(load().k3moe_workspace_size(OP_GROUP, T, K, ctypes.byref(s)))
+    ws = _workspace(nbytes, dev, ws)
+    _check("k3moe_group", load().k3moe_group(_ptr(idx), T, K, E, _ptr(out["counts"]), _ptr(out["offsets"]),
+                                              _ptr(out["perm"]), _ptr(out["uniq"]), _ptr(out["n_unique"]),
+                                              _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def forward_decode(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                   y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """One token: ``x [D]`` with its ``idx [K]`` / ``w [K]`` -> ``y [D]`` (fp32 path)."""
+    x = _dev(x.reshape(-1) if x.dim() == 2 and x.shape[0] == 1 else x, torch.float32, "x", (W.D,))
+    idx = idx.reshape(-1)
+    w = w.reshape(-1)
+    K = idx.numel()
+    _dev(idx, torch.int32, "idx", (K,))
+    _dev(w, torch.float32, "w", (K,))
+    y = torch.empty(W.D, dtype=torch.float32, device=x.device) if y is None else y
+    _dev(y, torch.float32, "y", (W.D,))
+    ws = _workspace(workspace_size(OP_DECODE, 1, K, W), x.device, ws)
+    _check("k3moe_forward_decode",
+           load().k3moe_forward_decode(W.ref(), _ptr(x), _ptr(idx), _ptr(w), K, _ptr(y), _ptr(ws), ws.numel(),
+                                       _stream(stream)))
+    return y
+
+
+def forward_chunk(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                  y: Optional[torch.Tensor] = None, n_unique: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """A chunk: bf16 ``x [T,D]``, ``idx/w [T,K]`` -> fp32 ``y [T,D]`` (bf16 MFMA path)."""
+    T = x.shape[0]
+    _dev(x, torch.bfloat16, "x", (T, W.D))
+    K = idx.shape[1]
+    _dev(idx, torch.int32, "idx", (T, K))
+    _dev(w, torch.float32, "w", (T, K))
+    y = torch.empty((T, W.D), dtype=torch.float32, device=x.device) if y is None else y
+    _dev(y, torch.float32, "y", (T, W.D))
+    if n_unique is not None:
+        _dev(n_unique, torch.int32, "n_unique", (1,))
+    ws = _workspace(workspace_size(OP_CHUNK, T, K, W), x.device, ws)
+    _check("k3moe_forward_chunk",
+           load().k3moe_forward_chunk(W.ref(), _ptr(x), T, _ptr(idx), _ptr(w), K, _ptr(y), _ptr(n_unique),
+                                      _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def dequant_mxfp4(q: torch.Tensor, s: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+                  stream=None) -> torch.Tensor:
+    """Decode ``q [O, I/2]`` + ``s [O, I/32]`` to ``[O, I]`` fp32 or bf16."""
+    O, half = q.shape
+    I = 2 * half
+    _dev(q, torch.uint8, "q")
+    _dev(s, torch.uint8, "s", (O, I // 32))
+    code = {torch.float32: OUT_F32, torch.bfloat16: OUT_BF16}[out_dtype]
+    out = torch.empty((O, I), dtype=out_dtype, device=q.device)
+    _check("k3moe_dequant_mxfp4",
+           load().k3moe_dequant_mxfp4(_ptr(q), _ptr(s), O, I, _ptr(out), code, _stream(stream)))
+    return out

@@ -153,12 +153,25 @@ def weights_device(cfg: Config, device, batch: int = 32):
 
 
 # ------------------------------------------------------------------------- activations
-def activations(cfg: Config, T: Optional[int] = None, stream: int = 0):
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 (ties to even), returned as fp32.
+
+    Chunk workloads carry bf16 hidden states ("bf16 activations into the grouped
+    GEMM"); both the oracle and the device receive exactly these values."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return r.view(np.float32).reshape(np.shape(x))
+
+
+def activations(cfg: Config, T: Optional[int] = None, stream: int = 0, bf16: Optional[bool] = None):
     """``(x [T,D] f32, logits [T,E] f32, bias [E] f32)`` for the workload.
 
     ``stream`` selects an independent draw of the same distribution (used to
-    build several different decode tokens for cache-cold timing).
+    build several different decode tokens for cache-cold timing).  For chunk
+    workloads (or ``bf16=True``) the hidden states are bf16 values held in fp32,
+    and the logits are computed from those values.
     """
+    bf16 = (cfg.path == "chunk") if bf16 is None else bf16
     T = cfg.T if T is None else int(T)
     rng = np.random.default_rng([cfg.act_seed, 7919, stream])
     if cfg.x_kind == "normal":
@@ -173,6 +186,8 @@ def activations(cfg: Config, T: Optional[int] = None, stream: int = 0):
     else:
         raise ValueError(cfg.x_kind)
     x = x64.astype(np.float32)
+    if bf16:
+        x = bf16_round(x)
 
     if cfg.logit_kind == "normal":
         logits = rng.standard_normal((T, cfg.E)).astype(np.float32)

@@ -1,0 +1,79 @@
+"""Shared pieces of the GPU parity tests (not collected by pytest)."""
+from __future__ import annotations
+
+import sys
+import time
+from typing import Dict, Optional
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+_weights_cache: Dict[tuple, object] = {}
+
+
+def log(msg: str):
+    print(f"[gpu-test {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mxfp4_routed_expert_k3moe_amd import lib
+    lib.load()  # raises if the HIP library is missing: no fallback
+    return torch
+
+
+def device_weights(cfg: synth.Config):
+    """All experts of ``cfg`` on cuda:0 (cached per weight set)."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    key = (cfg.weight_seed, cfg.E, cfg.D, cfg.F, cfg.scale_lo, cfg.scale_hi, cfg.edge_experts)
+    if key not in _weights_cache:
+        if len(_weights_cache) >= 2:  # keep at most two big weight sets resident
+            _weights_cache.pop(next(iter(_weights_cache)))
+            torch.cuda.empty_cache()
+        log(f"generating weights for {cfg.name} (E={cfg.E} D={cfg.D} F={cfg.F})")
+        t0 = time.time()
+        d = synth.weights_device(cfg, "cuda:0")
+        _weights_cache[key] = lib.ExpertWeights.from_dict(d)
+        log(f"weights ready in {time.time() - t0:.1f}s")
+    return _weights_cache[key]
+
+
+def oracle_forward_subset(cfg: synth.Config, x: np.ndarray, idx: np.ndarray, w: np.ndarray,
+                          want_pairs: bool = False):
+    """The oracle on ``x [T,D]`` with routing ``idx/w [T,K]``, given host weights of
+    only the experts the routing touches (regenerated from the seeded generator)."""
+    used = np.unique(idx)
+    W = synth.weights_host(cfg, used)
+    local = np.searchsorted(used, idx).astype(np.int32)
+    return oracle.forward(W, x, local, w, want_pairs=want_pairs)
+
+
+def rel_l2(got: np.ndarray, want: np.ndarray) -> float:
+    """||got - want|| / ||want|| in float64 over elements finite in both."""
+    g = np.asarray(got, dtype=np.float64).ravel()
+    r = np.asarray(want, dtype=np.float64).ravel()
+    ok = np.isfinite(g) & np.isfinite(r)
+    den = np.linalg.norm(r[ok])
+    return float(np.linalg.norm(g[ok] - r[ok]) / den) if den > 0 else float(np.linalg.norm(g[ok]))
+
+
+def assert_close(got: np.ndarray, want: np.ndarray, tol: float, what: str, per_token: Optional[int] = None):
+    """Non-finite masks (NaN and +-inf as one class) must agree, and the rel-L2
+    over elements finite in both must be within ``tol``."""
+    g = np.asarray(got)
+    r = np.asarray(want)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    mg, mr = ~np.isfinite(g), ~np.isfinite(r)
+    n_bad = int(np.count_nonzero(mg != mr))
+    assert n_bad == 0, f"{what}: non-finite masks differ at {n_bad} elements"
+    e = rel_l2(g, r)
+    log(f"{what}: rel-L2 {e:.3e} (tol {tol:g}), non-finite {int(mr.sum())}")
+    assert e <= tol, f"{what}: rel-L2 {e:.3e} > {tol:g}"
+    return e

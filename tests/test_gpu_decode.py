@@ -1,0 +1,84 @@
+"""Decode (one token, fp32 path) on the GPU vs the oracle: rel-L2 <= 1e-5.
+
+The tolerance is the fp32-accumulate bound: a 3584-term fp32 sum carries about
+u*sqrt(n/2) ~ 2.5e-6 relative error per stage, and the oracle sums in double."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import assert_close, device_weights, log, oracle_forward_subset, torch_cuda
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def _decode_gpu(W, x, idx, w):
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    y = lib.forward_decode(W, torch.from_numpy(x).cuda(), torch.from_numpy(idx).cuda(),
+                           torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _case(cfg, x, logits, bias, what):
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    W = device_weights(cfg)
+    for t in range(x.shape[0]):
+        log(f"decode {what} token {t}: experts {idx[t].tolist()}")
+        got = _decode_gpu(W, x[t], idx[t], w[t])
+        want = oracle_forward_subset(cfg, x[t:t + 1], idx[t:t + 1], w[t:t + 1])[0]
+        assert_close(got, want, TOL, f"decode {what} token {t}")
+
+
+def test_decode_tiny():
+    cfg = synth.CONFIGS["tiny"]
+    x, logits, bias = synth.activations(cfg, T=4, stream=3)
+    _case(cfg, x, logits, bias, "tiny")
+
+
+def test_decode_k3_shape():
+    cfg = synth.CONFIGS["decode1"]
+    x, logits, bias = synth.activations(cfg)
+    _case(cfg, x, logits, bias, "decode1")
+    x2, l2, b2 = synth.activations(cfg, T=2, stream=11)
+    _case(cfg, x2, l2, b2, "decode1 extra")
+
+
+@pytest.mark.parametrize("E,K,D,F", [(5, 3, 352, 160), (64, 64, 64, 96), (4, 1, 8192, 8192), (9, 4, 4160, 2080)])
+def test_decode_shapes(E, K, D, F):
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name=f"dec{E}_{K}_{D}_{F}", E=E, K=K, D=D, F=F,
+                       weight_seed=700 + E, act_seed=700 + K)
+    x, logits, bias = synth.activations(cfg, T=1)
+    _case(cfg, x, logits, bias, f"E={E} K={K} D={D} F={F}")
+
+
+def test_decode_edge_scales():
+    """An expert whose scale bytes span 0..255: per-weight semantics (inf weights,
+    NaN from inf - inf) must match the oracle's non-finite pattern."""
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name="dec_edge", E=8, K=2, D=256, F=128,
+                       weight_seed=901, edge_experts=(1,))
+    x, logits, bias = synth.activations(cfg, T=1)
+    idx = np.array([[1, 4]], np.int32)
+    w = np.array([[0.5, 0.5]], np.float32)
+    W = device_weights(cfg)
+    got = _decode_gpu(W, x[0], idx[0], w[0])
+    want = oracle_forward_subset(cfg, x, idx, w)[0]
+    assert_close(got, want, TOL, "decode edge scales")
+
+
+def test_decode_deterministic_and_invalid_index():
+    torch = torch_cuda()
+    cfg = synth.CONFIGS["tiny"]
+    W = device_weights(cfg)
+    x, logits, bias = synth.activations(cfg)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    a = _decode_gpu(W, x[0], idx[0], w[0])
+    b = _decode_gpu(W, x[0], idx[0], w[0])
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    bad = idx[0].copy()
+    bad[1] = cfg.E + 3
+    y = _decode_gpu(W, x[0], bad, w[0])
+    assert np.all(np.isnan(y))
+    del torch

@@ -57,3 +57,13 @@ def test_activations():
     xa, _, _ = synth.activations(c1, T=4, stream=1)
     xb, _, _ = synth.activations(c1, T=4, stream=2)
     assert not np.array_equal(xa, xb)
+
+
+def test_chunk_activations_are_bf16_values():
+    x, _, _ = synth.activations(synth.CONFIGS["prefill32"])
+    assert np.all((x.view(np.uint32) & 0xFFFF) == 0)
+    xd, _, _ = synth.activations(synth.CONFIGS["decode1"])
+    assert not np.all((xd.view(np.uint32) & 0xFFFF) == 0)
+    # round to nearest, ties to even
+    v = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9], np.float32)
+    assert synth.bf16_round(v).tolist() == [1.0, 1.0 + 2.0 ** -6, 1.0]
