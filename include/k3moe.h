@@ -134,6 +134,21 @@ int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t
                          void *stream);
 
 /*
+ * The two stages of k3moe_forward_decode, callable apart (to read the SiTU-GLU
+ * activations, or to time the stages).  Same arithmetic as forward_decode.
+ * k3moe_decode_gateup (steps 2-3): h[k, f] = SiTU-GLU((W_gate[e_k] x)_f,
+ *   (W_up[e_k] x)_f) for k < K, f < F; x [D] fp32, idx [K], h [K, F] fp32.
+ *   An out-of-range idx[k] gives a NaN row h[k].
+ * k3moe_decode_down (steps 4-5): y[d] = sum_k w_k * (W_down[e_k] h[k])_d summed in
+ *   slot order; h [K, F] fp32 (16-byte aligned), y [D] fp32; ws as for
+ *   k3moe_forward_decode (it holds the per-slot down outputs).
+ */
+int k3moe_decode_gateup(const k3moe_weights_t *W, const float *x, const int32_t *idx, int32_t K,
+                        float *h, void *stream);
+int k3moe_decode_down(const k3moe_weights_t *W, const float *h, const int32_t *idx, const float *w,
+                      int32_t K, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * A chunk of T tokens through the routed experts (steps 2-5) with the chunk's
  * expert union deduplicated: the pairs are grouped by expert (k3moe_group), each
  * routed expert's weights are streamed once per group of up to 128 of its

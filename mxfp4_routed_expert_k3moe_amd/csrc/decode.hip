@@ -1,22 +1,35 @@
-// decode.hip -- one token through its K routed experts, fp32 end to end.
+// decode.hip -- one token through its K routed experts, fp32-accurate.
 //
 // The routed-expert matmuls of the Kimi K3 engine run straight on the MXFP4 bytes
 // (colibri PR #676 summary; PR #684 MXFP4-kernel commit), and decode is bound by
 // the expert bytes it streams ("It runs the full model": 25.8 GB of experts per
-// token).  Here every selected expert's bytes are read from HBM exactly once:
+// token).  Every selected expert's bytes are read from HBM exactly once.
 //
-//   kernel 1  per (expert slot k, block of F rows): g_f and u_f for the same f in
-//             one wave, SiTU-GLU in registers, h[k, f] to the workspace;
-//   kernel 2  per (expert slot k, block of D rows): (W_down h_k)[d] to a partial
-//             buffer; the last of the K slot blocks of a row block sums
-//             y[d] = sum_k w_k * part[k, d] in slot order (no float atomics, so
-//             the result is the same on every run).
+// The dot products run on the matrix cores.  Each weight is decoded exactly
+// (gfx950 scaled fp4 -> bf16 converts) straight into the B operand of
+// v_mfma_f32_16x16x32_bf16.  The fp32 activation vector v is split exactly into
+// three bf16 parts v = hi + mid + lo (8 + 8 + 8 significand bits cover fp32's 24),
+// which become rows 0..2 of the A operand; rows 3..15 are zero.  Every product
+// w * part is exact in fp32 and the MFMA accumulates in fp32, so a row's dot
+// product is sum(acc rows 0..2), accurate like an fp32 GEMV while the VALU only
+// runs the converts (half an instruction per weight).
 //
-// Row layout: a row of I inputs is I/32 chunks of 16 packed bytes (= one scale
-// group of 32 codes).  Lane l of a wave owns chunks l, l+64, ... and keeps the
-// matching activations in registers for all rows the wave visits; each row is a
-// coalesced sweep of 16-byte loads, decoded with the gfx950 scaled fp4 converts,
-// multiplied in fp32 and reduced across the wave with shuffles.
+//   kernel 1  block = (expert slot k, 64 rows of F); wave = 16 rows f: gate and up
+//             tiles for the same f, h = SiTU-GLU(g, u) in the epilogue -> h[k, f]
+//   kernel 2  block = (expert slot k, 64 rows of D); wave = 16 rows d of W_down
+//             against h[k] -> part[k, d]
+//   kernel 3  y[d] = sum_k w_k * part[k, d] in slot order (no atomics: the same
+//             bits on every run)
+//
+// Scale bytes are 1/17 of the bytes but, loaded per step, they would double the
+// number of cache-line requests; each workgroup instead copies its rows' scale
+// bytes (contiguous in memory) into LDS once, and every step reads them there.
+//
+// Operand layout per 128-column step: lane l = (n = l%16, g = l/16) loads 16 bytes
+// = 32 codes = one scale group of weight row n at columns 128s + 32g ... + 31, and
+// feeds MFMA j = 0..3 with columns 32g + 8j ... + 7 of that group.  The A operand
+// takes the same columns of the activation parts, so each MFMA pairs every
+// product exactly once.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -24,237 +37,317 @@ namespace k3moe {
 
 namespace {
 
-constexpr int RPW_GU = kDecodeRowsPerWaveGU;
-constexpr int RPW_D = kDecodeRowsPerWaveDown;
-constexpr int WAVES = kDecodeWaves;
+constexpr int WAVES = kDecodeWaves;  // 4 waves, 16 rows each
+constexpr int ROWS_PER_BLOCK = WAVES * 16;
+constexpr int PD = 4;                // pipeline depth: steps of weights in flight per wave
 
-// acc += dot(decode(q, s), xv[0..31])
-__device__ __forceinline__ float chunk_dot(uint4 q, uint32_t s, const float* xv, float acc) {
-    float wv[8];
-    fp4x8_to_f32(q.x, s, wv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(wv[j], xv[j], acc);
-    fp4x8_to_f32(q.y, s, wv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(wv[j], xv[8 + j], acc);
-    fp4x8_to_f32(q.z, s, wv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(wv[j], xv[16 + j], acc);
-    fp4x8_to_f32(q.w, s, wv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = fmaf(wv[j], xv[24 + j], acc);
-    return acc;
+// LDS layout (uint16 elements): [part 0 | part 1 | part 2] each `pstride` long, then
+// an 8-element zero block.  pstride = padded columns + 8, so the three parts start
+// 4 banks apart.
+__host__ __device__ inline int part_stride(int n) { return ((n + 127) & ~127) + 8; }
+__host__ __device__ inline size_t parts_lds_bytes(int n) { return (size_t)(3 * part_stride(n) + 8) * 2; }
+
+__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    hi = f32_to_bf16_bits(x);
+    const float r1 = x - __uint_as_float(hi << 16);
+    mid = f32_to_bf16_bits(r1);
+    const float r2 = r1 - __uint_as_float(mid << 16);
+    lo = f32_to_bf16_bits(r2);
 }
 
-// Reduce four per-lane values over the wave in 7 shuffles.  On return the total
-// of v[0] is in lanes 0..15, v[1] in 16..31, v[2] in 32..47, v[3] in 48..63.
-__device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v3, int lane) {
-    const bool hi32 = lane & 32;
-    float a = hi32 ? v2 : v0, b = hi32 ? v3 : v1;  // kept
-    float c = hi32 ? v0 : v2, d = hi32 ? v1 : v3;  // sent
-    a += __shfl_xor(c, 32, kWave);
-    b += __shfl_xor(d, 32, kWave);
-    const bool hi16 = lane & 16;
-    float keep = hi16 ? b : a, send = hi16 ? a : b;
-    keep += __shfl_xor(send, 16, kWave);
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) keep += __shfl_xor(keep, off, kWave);
-    return keep;
-}
+// Split v (fp32, n a multiple of 32, 16-byte aligned) into three bf16 parts in LDS;
+// columns [n, npad) are zero.  Two phases, so a kernel can issue these loads
+// first, then its weight prefetch, and only then wait for the activations.
+constexpr int kStageMax = 8;  // float4 loads per thread: 256 threads x 8 x 4 = 8192 columns
 
-template <int CPL>
-__device__ __forceinline__ void load_vec_chunks(const float* __restrict__ v, int nch, int lane,
-                                                float (&r)[CPL][32]) {
+struct Stage {
+    float4 r[kStageMax];
+    int n, nits;
+
+    __device__ __forceinline__ void load(const float* __restrict__ v, int n_) {
+        n = n_;
+        nits = (((n + 127) & ~127) / 4 + 255) / 256;  // block-uniform
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch < nch) {
-            const float4* p = reinterpret_cast<const float4*>(v + (size_t)ch * 32);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float4 t = p[i];
-                r[c][4 * i] = t.x; r[c][4 * i + 1] = t.y; r[c][4 * i + 2] = t.z; r[c][4 * i + 3] = t.w;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) r[c][i] = 0.0f;
+        for (int it = 0; it < kStageMax; ++it) {
+            const int i4 = min((int)threadIdx.x + it * 256, n / 4 - 1);  // clamped: no branch around the load
+            if (it < nits) r[it] = reinterpret_cast<const float4*>(v)[i4];
         }
     }
+
+    __device__ __forceinline__ void store(uint16_t* lds) const {
+        const int npad = (n + 127) & ~127, ps = part_stride(n);
+#pragma unroll
+        for (int it = 0; it < kStageMax; ++it) {
+            const int i = 4 * ((int)threadIdx.x + it * 256);
+            if (it < nits && i < npad) {
+                const bool in = i < n;
+                const float xs[4] = {in ? r[it].x : 0.f, in ? r[it].y : 0.f, in ? r[it].z : 0.f, in ? r[it].w : 0.f};
+                uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) split3(xs[c], hi[c], mid[c], lo[c]);
+                *reinterpret_cast<uint2*>(lds + i) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+                *reinterpret_cast<uint2*>(lds + ps + i) = make_uint2(mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16));
+                *reinterpret_cast<uint2*>(lds + 2 * ps + i) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+            }
+        }
+        if (threadIdx.x < 8) lds[3 * ps + threadIdx.x] = 0;
+    }
+};
+
+// Branch-free chunk load: columns past kdim read the row's last chunk instead
+// (always in bounds); the caller zeroes them with `valid` when the data is used,
+// so no load sits behind a branch and the waitcnt pass can keep many in flight.
+__device__ __forceinline__ uint4 load_row_chunk(const uint8_t* __restrict__ qrow, int col, int kdim) {
+    const int c = min(col, kdim - 32);
+    return *reinterpret_cast<const uint4*>(qrow + (c >> 1));
 }
 
-template <int CPL>
-__global__ __launch_bounds__(256, 2) void decode_gateup_kernel(DevWeights W, const float* __restrict__ x,
-                                                            const int32_t* __restrict__ idx,
-                                                            float* __restrict__ h,
-                                                            uint32_t* __restrict__ counters,
-                                                            int n_counters) {
-    const int k = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // the down kernel's arrival counters start at zero for this call
-    if (blockIdx.x == 0 && k == 0)
-        for (int i = threadIdx.x; i < n_counters; i += blockDim.x) counters[i] = 0u;
+// Copy `rows` consecutive scale rows of `sb` bytes (starting at global row r0,
+// clamped to nrows) into LDS.  Dword loads when every row is 4-byte aligned.
+template <bool DWORD>
+struct ScaleStage {
+    static constexpr int kMax = 16;  // dwords per thread: 256 x 16 x 4 B = 64 rows x 256 B (D = 8192)
+    uint32_t v[kMax];
+    int nbytes;
 
-    const int D = W.D, F = W.F, nch = D >> 5;
-    const int f0 = (blockIdx.x * WAVES + wave) * RPW_GU;
-    if (f0 >= F) return;
-    const int nf = min(RPW_GU, F - f0);
-    float* hk = h + (size_t)k * F;
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int r0, int rows, int nrows, int sb) {
+        const int rr = min(rows, nrows - r0);  // rows that exist
+        nbytes = rr * sb;
+        const uint8_t* p = base + (size_t)r0 * sb;
+#pragma unroll
+        for (int it = 0; it < kMax; ++it) {
+            const int i = (int)threadIdx.x + it * 256;
+            if (DWORD) {
+                const int c = min(i, nbytes / 4 - 1);
+                if (it * 1024 < nbytes) v[it] = reinterpret_cast<const uint32_t*>(p)[c];
+            } else {
+                // byte path: 4 bytes per thread per iteration, assembled in a dword
+                uint32_t w = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int c = min(4 * i + b, nbytes - 1);
+                    if (it * 1024 < nbytes) w |= (uint32_t)p[c] << (8 * b);
+                }
+                v[it] = w;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(uint8_t* lds) const {
+#pragma unroll
+        for (int it = 0; it < kMax; ++it) {
+            const int i = (int)threadIdx.x + it * 256;
+            if (4 * i < nbytes) *reinterpret_cast<uint32_t*>(lds + 4 * i) = v[it];
+        }
+    }
+};
+
+// One wave's weight stream: NT tiles of 16 rows, PD steps of 128 columns in flight.
+template <int NT>
+struct RowStream {
+    const uint8_t* qrow[NT];
+    const uint8_t* srow[NT];  // this lane's row of scale bytes, in LDS
+    int kdim;
+    uint4 buf[PD][NT];
+
+    // Issue the first PD steps (before anything else, so HBM is busy from the start).
+    __device__ __forceinline__ void prefetch() {
+        const int lg = (threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int u = 0; u < PD; ++u)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) buf[u][t] = load_row_chunk(qrow[t], u * 128 + 32 * lg, kdim);
+    }
+
+    // MFMAs of one step from buffer slot u.
+    __device__ __forceinline__ void step(int u, int s, const uint16_t* abase, int astep, int jstep, bool valid,
+                                         f32x4 (&acc)[NT]) {
+        const uint16_t* ap = abase + s * astep;
+        const int lg = (threadIdx.x & 63) >> 4;
+        const int sc = min(4 * s + lg, (kdim >> 5) - 1);
+        u32x4 b[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint4 q = valid ? buf[u][t] : make_uint4(0u, 0u, 0u, 0u);
+            fp4x32_to_bf16(q, srow[t][sc], b[t]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap + jstep * j);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, b[t][j]), acc[t], 0,
+                                                                 0, 0);
+        }
+    }
+
+    // acc[t] += A(parts) x B(tile t) over all steps; each buffer slot is refilled
+    // with the step PD ahead as soon as it is consumed.
+    __device__ __forceinline__ void run(const uint16_t* lds, f32x4 (&acc)[NT]) {
+        const int lane = threadIdx.x & 63;
+        const int ln = lane & 15, lg = lane >> 4;
+        const int nsteps = (kdim + 127) >> 7;
+        const int ps = part_stride(kdim);
+        // A operand: part ln (< 3) at this lane group's columns, or the zero block
+        const uint16_t* abase = (ln < 3) ? lds + ln * ps + 32 * lg : lds + 3 * ps;
+        const int astep = (ln < 3) ? 128 : 0;
+        const int jstep = (ln < 3) ? 8 : 0;
+        int s0 = 0;
+        // steady state: every refill is in range, so the body has no branches
+        for (; s0 + 2 * PD <= nsteps; s0 += PD) {
+#pragma unroll
+            for (int u = 0; u < PD; ++u) {
+                step(u, s0 + u, abase, astep, jstep, true, acc);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) buf[u][t] = load_row_chunk(qrow[t], (s0 + u + PD) * 128 + 32 * lg, kdim);
+            }
+        }
+        // tail: the last PD..2PD-1 steps (only the final step can be partial)
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int s = s0 + u;
+            if (s < nsteps) {
+                step(u, s, abase, astep, jstep, s * 128 + 32 * lg < kdim, acc);
+                if (s + PD < nsteps) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) buf[u][t] = load_row_chunk(qrow[t], (s + PD) * 128 + 32 * lg, kdim);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int s = s0 + PD + u;
+            if (s < nsteps) step(u, s, abase, astep, jstep, s * 128 + 32 * lg < kdim, acc);
+        }
+    }
+};
+
+// LDS bytes of a decode workgroup: activation parts, then NT x 64 rows of scales
+// (+16: the last scale copy may round its final dword up past its rows).
+__host__ __device__ inline size_t decode_lds_bytes(int kdim, int nt) {
+    return parts_lds_bytes(kdim) + (size_t)nt * ROWS_PER_BLOCK * (kdim / 32) + 16;
+}
+
+template <bool DS>
+__global__ __launch_bounds__(256) void decode_gateup_kernel(DevWeights W, const float* __restrict__ x,
+                                                            const int32_t* __restrict__ idx,
+                                                            float* __restrict__ h) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int k = blockIdx.y;
+    const int lane = threadIdx.x & 63, ln = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int D = W.D, F = W.F, sb = D >> 5;
+    const int fblk = blockIdx.x * ROWS_PER_BLOCK;
+    const int f0 = fblk + wave * 16;
     const int e = idx[k];
-    if (e < 0 || e >= W.E) {
-        if (lane < nf) hk[f0 + lane] = __builtin_nanf("");
+    const bool valid_e = e >= 0 && e < W.E;
+    const int ec = valid_e ? e : 0;
+    uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(D);
+
+    // activations and scale rows first: waiting for them later leaves the weights in flight
+    Stage st;
+    st.load(x, D);
+    ScaleStage<DS> sg, su;
+    sg.load(W.gate_s + (size_t)ec * W.gate_s_stride, fblk, ROWS_PER_BLOCK, F, sb);
+    su.load(W.up_s + (size_t)ec * W.up_s_stride, fblk, ROWS_PER_BLOCK, F, sb);
+    // weights: always prefetched (clamped to real rows), so no load sits behind a branch
+    const int fc = min(f0, F - 16);
+    const size_t qrow = (size_t)D >> 1;
+    RowStream<2> rs;
+    rs.kdim = D;
+    rs.qrow[0] = W.gate_q + (size_t)ec * W.gate_q_stride + (size_t)(fc + ln) * qrow;
+    rs.qrow[1] = W.up_q + (size_t)ec * W.up_q_stride + (size_t)(fc + ln) * qrow;
+    rs.srow[0] = slds + (size_t)(fc - fblk + ln) * sb;
+    rs.srow[1] = slds + (size_t)(ROWS_PER_BLOCK + fc - fblk + ln) * sb;
+    rs.prefetch();
+    st.store(lds);
+    sg.store(slds);
+    su.store(slds + ROWS_PER_BLOCK * sb);
+    __syncthreads();
+    if (f0 >= F) return;  // no barrier follows
+    float* hk = h + (size_t)k * F;
+    if (!valid_e) {
+        if (lane < 16) hk[f0 + lane] = __builtin_nanf("");
         return;
     }
-    float xr[CPL][32];
-    load_vec_chunks<CPL>(x, nch, lane, xr);
-
-    const uint8_t* __restrict__ gq = W.gate_q + (size_t)e * W.gate_q_stride;
-    const uint8_t* __restrict__ gs = W.gate_s + (size_t)e * W.gate_s_stride;
-    const uint8_t* __restrict__ uq = W.up_q + (size_t)e * W.up_q_stride;
-    const uint8_t* __restrict__ us = W.up_s + (size_t)e * W.up_s_stride;
-    const size_t qrow = (size_t)D >> 1;
-
-    for (int r = 0; r < nf; r += 2) {
-        const int fa = f0 + r;
-        const int fb = f0 + min(r + 1, nf - 1);  // duplicate of fa when nf is odd (not stored)
-        uint4 qga[CPL], qua[CPL], qgb[CPL], qub[CPL];
-        uint32_t sga[CPL], sua[CPL], sgb[CPL], sub[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int ch = lane + 64 * c;
-            if (ch < nch) {
-                qga[c] = *reinterpret_cast<const uint4*>(gq + fa * qrow + (size_t)ch * 16);
-                qua[c] = *reinterpret_cast<const uint4*>(uq + fa * qrow + (size_t)ch * 16);
-                qgb[c] = *reinterpret_cast<const uint4*>(gq + fb * qrow + (size_t)ch * 16);
-                qub[c] = *reinterpret_cast<const uint4*>(uq + fb * qrow + (size_t)ch * 16);
-                sga[c] = gs[(size_t)fa * nch + ch];
-                sua[c] = us[(size_t)fa * nch + ch];
-                sgb[c] = gs[(size_t)fb * nch + ch];
-                sub[c] = us[(size_t)fb * nch + ch];
-            }
-        }
-        float ag = 0.f, au = 0.f, bg = 0.f, bu = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int ch = lane + 64 * c;
-            if (ch < nch) {
-                ag = chunk_dot(qga[c], sga[c], xr[c], ag);
-                au = chunk_dot(qua[c], sua[c], xr[c], au);
-                bg = chunk_dot(qgb[c], sgb[c], xr[c], bg);
-                bu = chunk_dot(qub[c], sub[c], xr[c], bu);
-            }
-        }
-        const float tot = wave_sum4(ag, au, bg, bu, lane);
-        // lanes 0 (ag), 16 (au), 32 (bg), 48 (bu): gather the pair for SiTU
-        const float g_a = __shfl(tot, 0, kWave), u_a = __shfl(tot, 16, kWave);
-        const float g_b = __shfl(tot, 32, kWave), u_b = __shfl(tot, 48, kWave);
-        if (lane == 0) hk[fa] = situ_accurate(g_a, u_a);
-        if (lane == 1 && r + 1 < nf) hk[fb] = situ_accurate(g_b, u_b);
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    rs.run(lds, acc);
+    // C layout: lane l, register r -> row 4*(l/16)+r, column l%16; rows 0..2 are the
+    // hi/mid/lo sums of column (= weight row) l for lanes 0..15
+    if (lane < 16) {
+        const float g = (acc[0][0] + acc[0][1]) + acc[0][2];
+        const float u = (acc[1][0] + acc[1][1]) + acc[1][2];
+        hk[f0 + lane] = situ_accurate(g, u);
     }
 }
 
-template <int CPL>
-__global__ __launch_bounds__(256, 2) void decode_down_kernel(DevWeights W, const int32_t* __restrict__ idx,
-                                                          const float* __restrict__ wts, int K,
+template <bool DS>
+__global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const int32_t* __restrict__ idx,
                                                           const float* __restrict__ h,
-                                                          float* __restrict__ ypart,
-                                                          uint32_t* __restrict__ counters,
-                                                          float* __restrict__ y) {
-    __shared__ int s_last;
+                                                          float* __restrict__ ypart) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int k = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int D = W.D, F = W.F, nch = F >> 5;
-    const int rows_per_block = WAVES * RPW_D;
-    const int d_blk = blockIdx.x * rows_per_block;
-    const int d0 = d_blk + wave * RPW_D;
-    const int nd = max(0, min(RPW_D, D - d0));
-    float* yk = ypart + (size_t)k * D;
+    const int lane = threadIdx.x & 63, ln = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int D = W.D, F = W.F, sb = F >> 5;
+    const int dblk = blockIdx.x * ROWS_PER_BLOCK;
+    const int d0 = dblk + wave * 16;
     const int e = idx[k];
+    const bool valid_e = e >= 0 && e < W.E;
+    const int ec = valid_e ? e : 0;
+    uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(F);
 
-    if (nd > 0) {
-        if (e < 0 || e >= W.E) {
-            if (lane < nd) yk[d0 + lane] = __builtin_nanf("");
-        } else {
-            float hr[CPL][32];
-            load_vec_chunks<CPL>(h + (size_t)k * F, nch, lane, hr);
-            const uint8_t* __restrict__ dq = W.down_q + (size_t)e * W.down_q_stride;
-            const uint8_t* __restrict__ ds = W.down_s + (size_t)e * W.down_s_stride;
-            const size_t qrow = (size_t)F >> 1;
-            for (int r = 0; r < nd; r += 4) {
-                int rr[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rr[i] = d0 + min(r + i, nd - 1);
-                uint4 q[4][CPL];
-                uint32_t s[4][CPL];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        const int ch = lane + 64 * c;
-                        if (ch < nch) {
-                            q[i][c] = *reinterpret_cast<const uint4*>(dq + rr[i] * qrow + (size_t)ch * 16);
-                            s[i][c] = ds[(size_t)rr[i] * nch + ch];
-                        }
-                    }
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const int ch = lane + 64 * c;
-                    if (ch < nch) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i] = chunk_dot(q[i][c], s[i][c], hr[c], acc[i]);
-                    }
-                }
-                const float tot = wave_sum4(acc[0], acc[1], acc[2], acc[3], lane);
-                const int i = lane >> 4;
-                if ((lane & 15) == 0 && r + i < nd) yk[d0 + r + i] = tot;
-            }
-        }
-    }
-
-    // The last of the K slot blocks for this row block combines, in slot order.
-    __threadfence();
+    Stage st;
+    st.load(h + (size_t)k * F, F);
+    ScaleStage<DS> sd;
+    sd.load(W.down_s + (size_t)ec * W.down_s_stride, dblk, ROWS_PER_BLOCK, D, sb);
+    const int dc = min(d0, D - 16);
+    const size_t qrow = (size_t)F >> 1;
+    RowStream<1> rs;
+    rs.kdim = F;
+    rs.qrow[0] = W.down_q + (size_t)ec * W.down_q_stride + (size_t)(dc + ln) * qrow;
+    rs.srow[0] = slds + (size_t)(dc - dblk + ln) * sb;
+    rs.prefetch();
+    st.store(lds);
+    sd.store(slds);
     __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(&counters[blockIdx.x], 1u) == (uint32_t)(K - 1));
-    __syncthreads();
-    if (s_last) {
-        __threadfence();
-        const int d = d_blk + (int)threadIdx.x;
-        if ((int)threadIdx.x < rows_per_block && d < D) {
-            float acc = 0.0f;
-            for (int k2 = 0; k2 < K; ++k2) acc = fmaf(wts[k2], ypart[(size_t)k2 * D + d], acc);
-            y[d] = acc;
-        }
+    if (d0 >= D) return;
+    float* yk = ypart + (size_t)k * D;
+    if (!valid_e) {
+        if (lane < 16) yk[d0 + lane] = __builtin_nanf("");
+        return;
     }
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    rs.run(lds, acc);
+    if (lane < 16) yk[d0 + lane] = (acc[0][0] + acc[0][1]) + acc[0][2];
 }
 
-template <int CPL>
-hipError_t launch_gu(const DevWeights& W, const float* x, const int32_t* idx, int K, const DecodeWorkspace& ws,
-                     hipStream_t stream) {
-    const int rows_per_block = WAVES * RPW_GU;
-    dim3 grid((W.F + rows_per_block - 1) / rows_per_block, K);
-    hipLaunchKernelGGL(decode_gateup_kernel<CPL>, grid, dim3(WAVES * 64), 0, stream, W, x, idx, ws.h,
-                       ws.counters, ws.n_counters);
-    return hipGetLastError();
-}
-
-template <int CPL>
-hipError_t launch_dn(const DevWeights& W, const int32_t* idx, const float* w, int K, float* y,
-                     const DecodeWorkspace& ws, hipStream_t stream) {
-    dim3 grid(ws.n_counters, K);
-    hipLaunchKernelGGL(decode_down_kernel<CPL>, grid, dim3(WAVES * 64), 0, stream, W, idx, w, K, ws.h,
-                       ws.ypart, ws.counters, y);
-    return hipGetLastError();
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ ypart,
+                                                             const float* __restrict__ wts, int K, int D,
+                                                             float* __restrict__ y) {
+    const int d = blockIdx.x * blockDim.x + threadIdx.x;
+    if (d >= D) return;
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        float v[16], wk[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {  // all loads of a group in flight together
+            v[i] = (k0 + i < K) ? ypart[(size_t)(k0 + i) * D + d] : 0.0f;
+            wk[i] = (k0 + i < K) ? wts[k0 + i] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (k0 + i < K) acc = fmaf(wk[i], v[i], acc);
+    }
+    y[d] = acc;
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-int n_row_blocks_down(int D) { return (D + WAVES * RPW_D - 1) / (WAVES * RPW_D); }
-
 }  // namespace
 
 size_t decode_workspace_bytes(int K, int D, int F) {
-    return align256((size_t)K * F * 4) + align256((size_t)K * D * 4) +
-           align256((size_t)n_row_blocks_down(D) * 4);
+    return align256((size_t)K * F * 4) + align256((size_t)K * D * 4);
 }
 
 DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F) {
@@ -263,30 +356,42 @@ DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F) {
     r.h = reinterpret_cast<float*>(p);
     p += align256((size_t)K * F * 4);
     r.ypart = reinterpret_cast<float*>(p);
-    p += align256((size_t)K * D * 4);
-    r.counters = reinterpret_cast<uint32_t*>(p);
-    r.n_counters = n_row_blocks_down(D);
+    (void)D;
     return r;
+}
+
+hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32_t* idx, int K, float* h,
+                                hipStream_t stream) {
+    const dim3 grid((W.F + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, K);
+    const size_t lds = decode_lds_bytes(W.D, 2);
+    // dword scale copies need every scale row and expert block 4-byte aligned
+    const bool dw = (W.D % 128 == 0) && W.gate_s_stride % 4 == 0 && W.up_s_stride % 4 == 0 &&
+                    (reinterpret_cast<uintptr_t>(W.gate_s) & 3) == 0 && (reinterpret_cast<uintptr_t>(W.up_s) & 3) == 0;
+    if (dw)
+        hipLaunchKernelGGL(decode_gateup_kernel<true>, grid, dim3(WAVES * 64), lds, stream, W, x, idx, h);
+    else
+        hipLaunchKernelGGL(decode_gateup_kernel<false>, grid, dim3(WAVES * 64), lds, stream, W, x, idx, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t* idx, const float* w, int K,
+                              float* ypart, float* y, hipStream_t stream) {
+    const dim3 grid((W.D + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, K);
+    const size_t lds = decode_lds_bytes(W.F, 1);
+    const bool dw = (W.F % 128 == 0) && W.down_s_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(W.down_s) & 3) == 0;
+    if (dw)
+        hipLaunchKernelGGL(decode_down_kernel<true>, grid, dim3(WAVES * 64), lds, stream, W, idx, h, ypart);
+    else
+        hipLaunchKernelGGL(decode_down_kernel<false>, grid, dim3(WAVES * 64), lds, stream, W, idx, h, ypart);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((W.D + 255) / 256), dim3(256), 0, stream, ypart, w, K, W.D, y);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const DevWeights& W, const float* x, const int32_t* idx, const float* w, int K,
                          float* y, const DecodeWorkspace& ws, hipStream_t stream) {
-    const int cpl_d = (W.D / 32 + 63) / 64;
-    const int cpl_f = (W.F / 32 + 63) / 64;
-    hipError_t err;
-    switch (cpl_d) {
-        case 1: err = launch_gu<1>(W, x, idx, K, ws, stream); break;
-        case 2: err = launch_gu<2>(W, x, idx, K, ws, stream); break;
-        case 3: err = launch_gu<3>(W, x, idx, K, ws, stream); break;
-        default: err = launch_gu<4>(W, x, idx, K, ws, stream); break;
-    }
+    hipError_t err = launch_decode_gateup(W, x, idx, K, ws.h, stream);
     if (err != hipSuccess) return err;
-    switch (cpl_f) {
-        case 1: return launch_dn<1>(W, idx, w, K, y, ws, stream);
-        case 2: return launch_dn<2>(W, idx, w, K, y, ws, stream);
-        case 3: return launch_dn<3>(W, idx, w, K, y, ws, stream);
-        default: return launch_dn<4>(W, idx, w, K, y, ws, stream);
-    }
+    return launch_decode_down(W, ws.h, idx, w, K, ws.ypart, y, stream);
 }
 
 }  // namespace k3moe

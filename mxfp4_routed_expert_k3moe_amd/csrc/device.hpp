@@ -67,6 +67,33 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t q, uint32_t s) {
     return r;
 }
 
+// 32 codes (a 16-byte chunk = one scale group) -> 32 bf16 as 16 packed dwords,
+// out[j] holding columns 8j..8j+7.  One branch for the rare s = 255 fix-up per
+// chunk, so the common path is straight-line code.
+__device__ __forceinline__ void fp4x32_to_bf16(const uint4& q, uint32_t s, u32x4 (&out)[4]) {
+    const float sc = scale_operand(s);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        out[j].x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 0));
+        out[j].y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 1));
+        out[j].z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 2));
+        out[j].w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], sc, 3));
+    }
+    if (__builtin_expect(s == 255u, 0)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t* p = reinterpret_cast<uint32_t*>(&out[j]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(p[i] << 16) * 2.0f;
+                const float hi = __uint_as_float(p[i] & 0xFFFF0000u) * 2.0f;
+                p[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+            }
+        }
+    }
+}
+
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     uint32_t u = __float_as_uint(f);

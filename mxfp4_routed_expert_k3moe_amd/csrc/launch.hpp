@@ -19,20 +19,20 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
                         float* w, hipStream_t stream);
 
 // ------------------------------------------------------------------ decode
-constexpr int kDecodeRowsPerWaveGU = 8;    // (gate,up) row pairs per wave
-constexpr int kDecodeRowsPerWaveDown = 8;  // down rows per wave
-constexpr int kDecodeWaves = 4;            // waves per workgroup
+constexpr int kDecodeWaves = 4;  // waves per workgroup (16 weight rows each)
 
 struct DecodeWorkspace {
-    float* h;            // [K, F]
-    float* ypart;        // [K, D]
-    uint32_t* counters;  // [n_counters]
-    int n_counters;
+    float* h;      // [K, F]  SiTU-GLU outputs per slot
+    float* ypart;  // [K, D]  down-projection outputs per slot
 };
 size_t decode_workspace_bytes(int K, int D, int F);
 DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F);
 hipError_t launch_decode(const DevWeights& W, const float* x, const int32_t* idx, const float* w, int K,
                          float* y, const DecodeWorkspace& ws, hipStream_t stream);
+hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32_t* idx, int K, float* h,
+                                hipStream_t stream);
+hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t* idx, const float* w, int K,
+                              float* ypart, float* y, hipStream_t stream);
 
 // ------------------------------------------------------------------ chunk
 constexpr int kGroupTokens = 64;   // tokens per grouping block (one u64 mask bit each)

@@ -28,8 +28,9 @@ K3MOE_MAX_DIM = 8192
 OP_DECODE, OP_CHUNK, OP_GROUP = 1, 2, 3
 OUT_F32, OUT_BF16 = 0, 1
 
-ENTRY_POINTS = ("k3moe_route", "k3moe_group", "k3moe_forward_decode", "k3moe_forward_chunk",
-                "k3moe_workspace_size", "k3moe_dequant_mxfp4", "k3moe_status_string")
+ENTRY_POINTS = ("k3moe_route", "k3moe_group", "k3moe_forward_decode", "k3moe_decode_gateup",
+                "k3moe_decode_down", "k3moe_forward_chunk", "k3moe_workspace_size", "k3moe_dequant_mxfp4",
+                "k3moe_status_string")
 
 
 class K3moeError(RuntimeError):
@@ -62,6 +63,8 @@ def load() -> ctypes.CDLL:
     lib.k3moe_group.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.k3moe_forward_decode.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.k3moe_forward_chunk.argtypes = [wp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.k3moe_decode_gateup.argtypes = [wp, vp, vp, i32, vp, vp]
+    lib.k3moe_decode_down.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.k3moe_workspace_size.argtypes = [i32, i32, i32, wp]
     lib.k3moe_workspace_size.restype = sz
     lib.k3moe_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, i32, vp]
@@ -197,6 +200,36 @@ def forward_decode(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torc
     _check("k3moe_forward_decode",
            load().k3moe_forward_decode(W.ref(), _ptr(x), _ptr(idx), _ptr(w), K, _ptr(y), _ptr(ws), ws.numel(),
                                        _stream(stream)))
+    return y
+
+
+def decode_gateup(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, h: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Decode stage 1: ``h [K, F]`` = SiTU-GLU of the K experts' gate/up rows on ``x [D]``."""
+    _dev(x, torch.float32, "x", (W.D,))
+    idx = idx.reshape(-1)
+    K = idx.numel()
+    _dev(idx, torch.int32, "idx", (K,))
+    h = torch.empty((K, W.F), dtype=torch.float32, device=x.device) if h is None else h
+    _dev(h, torch.float32, "h", (K, W.F))
+    _check("k3moe_decode_gateup", load().k3moe_decode_gateup(W.ref(), _ptr(x), _ptr(idx), K, _ptr(h), _stream(stream)))
+    return h
+
+
+def decode_down(W: ExpertWeights, h: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode stage 2: ``y [D]`` = sum_k w_k W_down[e_k] h[k] (slot order)."""
+    idx = idx.reshape(-1)
+    w = w.reshape(-1)
+    K = idx.numel()
+    _dev(h, torch.float32, "h", (K, W.F))
+    _dev(idx, torch.int32, "idx", (K,))
+    _dev(w, torch.float32, "w", (K,))
+    y = torch.empty(W.D, dtype=torch.float32, device=h.device) if y is None else y
+    _dev(y, torch.float32, "y", (W.D,))
+    ws = _workspace(workspace_size(OP_DECODE, 1, K, W), h.device, ws)
+    _check("k3moe_decode_down", load().k3moe_decode_down(W.ref(), _ptr(h), _ptr(idx), _ptr(w), K, _ptr(y), _ptr(ws),
+                                                          ws.numel(), _stream(stream)))
     return y
 
 

@@ -82,3 +82,22 @@ def test_decode_deterministic_and_invalid_index():
     y = _decode_gpu(W, x[0], bad, w[0])
     assert np.all(np.isnan(y))
     del torch
+
+
+def test_decode_stages_match_oracle():
+    """Stage-wise: h from the gate/up stage vs the oracle's SiTU-GLU activations, and
+    the down stage fed with the oracle's own h."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = synth.CONFIGS["decode1"]
+    x, logits, bias = synth.activations(cfg, T=1, stream=21)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    W = device_weights(cfg)
+    log(f"decode stages: experts {idx[0].tolist()}")
+    h = lib.decode_gateup(W, torch.from_numpy(x[0]).cuda(), torch.from_numpy(idx[0]).cuda()).cpu().numpy()
+    y_o, ytk, hk = oracle_forward_subset(cfg, x, idx, w, want_pairs=True)
+    assert_close(h, hk[0], TOL, "decode stage gate/up h")
+    y = lib.decode_down(W, torch.from_numpy(hk[0].astype(np.float32)).cuda(), torch.from_numpy(idx[0]).cuda(),
+                        torch.from_numpy(w[0]).cuda()).cpu().numpy()
+    want = (w[0].astype(np.float64)[:, None] * ytk[0]).sum(axis=0)
+    assert_close(y, want, TOL, "decode stage down (oracle h in)")
