@@ -104,9 +104,10 @@ __device__ __forceinline__ uint4 load_row_chunk(const uint8_t* __restrict__ qrow
 
 // Copy `rows` consecutive scale rows of `sb` bytes (starting at global row r0,
 // clamped to nrows) into LDS.  Dword loads when every row is 4-byte aligned.
-template <bool DWORD>
+template <bool DWORD, int ROWS>
 struct ScaleStage {
-    static constexpr int kMax = 16;  // dwords per thread: 256 x 16 x 4 B = 64 rows x 256 B (D = 8192)
+    // dwords per thread: 256 threads x 4 B x kMax = ROWS rows x 256 B (the widest scale row)
+    static constexpr int kMax = ROWS / 4;
     uint32_t v[kMax];
     int nbytes;
 
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DevWeights W, const 
     // activations and scale rows first: waiting for them later leaves the weights in flight
     Stage st;
     st.load(x, D);
-    ScaleStage<DS> sg, su;
+    ScaleStage<DS, ROWS_PER_BLOCK> sg, su;
     sg.load(W.gate_s + (size_t)ec * W.gate_s_stride, fblk, ROWS_PER_BLOCK, F, sb);
     su.load(W.up_s + (size_t)ec * W.up_s_stride, fblk, ROWS_PER_BLOCK, F, sb);
     // weights: always prefetched (clamped to real rows), so no load sits behind a branch
@@ -281,6 +282,9 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DevWeights W, const 
     }
 }
 
+constexpr int DOWN_TILES = 1;  // 16-row tiles of W_down per wave
+constexpr int DOWN_ROWS_PER_BLOCK = WAVES * 16 * DOWN_TILES;
+
 template <bool DS>
 __global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const int32_t* __restrict__ idx,
                                                           const float* __restrict__ h,
@@ -290,8 +294,8 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const in
     const int lane = threadIdx.x & 63, ln = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int D = W.D, F = W.F, sb = F >> 5;
-    const int dblk = blockIdx.x * ROWS_PER_BLOCK;
-    const int d0 = dblk + wave * 16;
+    const int dblk = blockIdx.x * DOWN_ROWS_PER_BLOCK;
+    const int d0 = dblk + wave * 16 * DOWN_TILES;
     const int e = idx[k];
     const bool valid_e = e >= 0 && e < W.E;
     const int ec = valid_e ? e : 0;
@@ -299,14 +303,17 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const in
 
     Stage st;
     st.load(h + (size_t)k * F, F);
-    ScaleStage<DS> sd;
-    sd.load(W.down_s + (size_t)ec * W.down_s_stride, dblk, ROWS_PER_BLOCK, D, sb);
-    const int dc = min(d0, D - 16);
+    ScaleStage<DS, DOWN_ROWS_PER_BLOCK> sd;
+    sd.load(W.down_s + (size_t)ec * W.down_s_stride, dblk, DOWN_ROWS_PER_BLOCK, D, sb);
     const size_t qrow = (size_t)F >> 1;
-    RowStream<1> rs;
+    RowStream<DOWN_TILES> rs;
     rs.kdim = F;
-    rs.qrow[0] = W.down_q + (size_t)ec * W.down_q_stride + (size_t)(dc + ln) * qrow;
-    rs.srow[0] = slds + (size_t)(dc - dblk + ln) * sb;
+#pragma unroll
+    for (int t = 0; t < DOWN_TILES; ++t) {
+        const int dc = min(d0 + 16 * t, D - 16);  // clamped to a real tile
+        rs.qrow[t] = W.down_q + (size_t)ec * W.down_q_stride + (size_t)(dc + ln) * qrow;
+        rs.srow[t] = slds + (size_t)(dc - dblk + ln) * sb;
+    }
     rs.prefetch();
     st.store(lds);
     sd.store(slds);
@@ -314,12 +321,17 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const in
     if (d0 >= D) return;
     float* yk = ypart + (size_t)k * D;
     if (!valid_e) {
-        if (lane < 16) yk[d0 + lane] = __builtin_nanf("");
+        for (int t = 0; t < DOWN_TILES; ++t)
+            if (lane < 16 && d0 + 16 * t < D) yk[d0 + 16 * t + lane] = __builtin_nanf("");
         return;
     }
-    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc[DOWN_TILES];
+#pragma unroll
+    for (int t = 0; t < DOWN_TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     rs.run(lds, acc);
-    if (lane < 16) yk[d0 + lane] = (acc[0][0] + acc[0][1]) + acc[0][2];
+#pragma unroll
+    for (int t = 0; t < DOWN_TILES; ++t)
+        if (lane < 16 && d0 + 16 * t < D) yk[d0 + 16 * t + lane] = (acc[t][0] + acc[t][1]) + acc[t][2];
 }
 
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ ypart,
@@ -376,8 +388,8 @@ hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32
 
 hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t* idx, const float* w, int K,
                               float* ypart, float* y, hipStream_t stream) {
-    const dim3 grid((W.D + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, K);
-    const size_t lds = decode_lds_bytes(W.F, 1);
+    const dim3 grid((W.D + DOWN_ROWS_PER_BLOCK - 1) / DOWN_ROWS_PER_BLOCK, K);
+    const size_t lds = parts_lds_bytes(W.F) + (size_t)DOWN_ROWS_PER_BLOCK * (W.F / 32) + 16;
     const bool dw = (W.F % 128 == 0) && W.down_s_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(W.down_s) & 3) == 0;
     if (dw)
         hipLaunchKernelGGL(decode_down_kernel<true>, grid, dim3(WAVES * 64), lds, stream, W, idx, h, ypart);

@@ -67,6 +67,17 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t q, uint32_t s) {
     return r;
 }
 
+// 8 codes -> 8 bf16 without the s = 255 fix-up (callers guarantee s < 255, e.g.
+// after a wave-uniform check).
+__device__ __forceinline__ u32x4 fp4x8_to_bf16_nofix(uint32_t q, float sc) {
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
+    return r;
+}
+
 // 32 codes (a 16-byte chunk = one scale group) -> 32 bf16 as 16 packed dwords,
 // out[j] holding columns 8j..8j+7.  One branch for the rare s = 255 fix-up per
 // chunk, so the common path is straight-line code.

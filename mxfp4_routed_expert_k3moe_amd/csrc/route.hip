@@ -47,15 +47,27 @@ __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v,
     return ((unsigned long long)hi << 32) | lo;
 }
 
-// Maximum over the 64 lanes: DPP within each row of 16 lanes (swap neighbours,
-// swap pairs, rotate by 4, rotate by 8), then the four row maxima via readlane.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ unsigned long long dpp_keep_u64(unsigned long long v) {
+    // rows outside ROW_MASK keep their own value
+    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF,
+                                               false);
+    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Maximum over the 64 lanes, returned to every lane: DPP within each row of 16
+// (swap neighbours, swap pairs, rotate by 4, rotate by 8), then row 0 -> 1 and
+// row 2 -> 3 (row_bcast15), rows 0-1 -> 2-3 (row_bcast31); lane 63 holds the
+// maximum, which readlane hands to the whole wave.
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
     v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
     v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
     v = max_u64(v, dpp_u64<0x124>(v));  // row_ror:4
     v = max_u64(v, dpp_u64<0x128>(v));  // row_ror:8
-    return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
-                   max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
+    v = max_u64(v, dpp_keep_u64<0x142, 0xA>(v));  // row_bcast:15 into rows 1, 3
+    v = max_u64(v, dpp_keep_u64<0x143, 0xC>(v));  // row_bcast:31 into rows 2, 3
+    return readlane_u64(v, 63);
 }
 
 // K rounds of a wave max over per-lane code arrays; lane k keeps winner k in
@@ -84,6 +96,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
                                                     const float* __restrict__ bias, int T, int E, int K,
                                                     int32_t* __restrict__ idx, float* __restrict__ w) {
     __shared__ unsigned long long cand[4 * K3MOE_MAX_K_DEV];
+    extern __shared__ double sig_e[];  // [E] double sigmoid of each expert's logit
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x;
     const float* l = logits + (size_t)t * E;
@@ -96,7 +109,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         const int e = wave * Q + i;
         code[j] = 0ull;
         if (i < Q && e < E) {
-            float key = (float)sigmoid_d(l[e]) + bias[e];
+            const double sd = sigmoid_d(l[e]);
+            sig_e[e] = sd;
+            float key = (float)sd + bias[e];
             if (key != key) key = -INFINITY;
             if (key == 0.0f) key = 0.0f;  // -0 ranks as +0
             code[j] = ((unsigned long long)key_order(key) << 32) | (unsigned long long)(~(uint32_t)e);
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     unsigned long long mine = 0ull;
     wave_topk<PL>(code, K, lane, cand + wave * K, mine);
-    __syncthreads();  // the only barrier: every wave's survivors are in LDS
+    __syncthreads();  // the only barrier: survivors and sigmoids are in LDS
     if (wave != 0) return;
 
     unsigned long long mc[4];
@@ -117,7 +132,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     const int my_sel = (lane < K) ? (int)(~(uint32_t)(mine & 0xFFFFFFFFull)) : 0;
 
     // raw-score renormalization, summed in slot order in double
-    const double sig = (lane < K) ? sigmoid_d(l[my_sel]) : 0.0;
+    const double sig = (lane < K) ? sig_e[my_sel] : 0.0;
     double denom = 0.0;
     for (int k = 0; k < K; ++k) denom += __shfl(sig, k, kWave);
     if (lane < K) {
@@ -129,7 +144,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 template <int PL>
 hipError_t launch_pl(const float* logits, const float* bias, int T, int E, int K, int32_t* idx,
                      float* w, hipStream_t stream) {
-    hipLaunchKernelGGL(route_kernel<PL>, dim3(T), dim3(256), 0, stream, logits, bias, T, E, K, idx, w);
+    hipLaunchKernelGGL(route_kernel<PL>, dim3(T), dim3(256), (size_t)E * sizeof(double), stream, logits, bias, T, E,
+                       K, idx, w);
     return hipGetLastError();
 }
 
