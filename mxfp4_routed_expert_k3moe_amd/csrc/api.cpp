@@ -32,8 +32,12 @@ int check_weights(const k3moe_weights_t* W) {
     if (!W->gate_q || !W->gate_s || !W->up_q || !W->up_s || !W->down_q || !W->down_s) return K3MOE_E_NULL;
     if (W->n_experts < 1 || W->n_experts > K3MOE_MAX_E || !dim_ok(W->d_model) || !dim_ok(W->d_ff))
         return K3MOE_E_DIM;
-    if (!aligned16(W->gate_q) || !aligned16(W->up_q) || !aligned16(W->down_q)) return K3MOE_E_ALIGN;
-    if ((W->gate_q_stride | W->up_q_stride | W->down_q_stride) & 15) return K3MOE_E_ALIGN;
+    if (!aligned16(W->gate_q) || !aligned16(W->up_q) || !aligned16(W->down_q) || !aligned16(W->gate_s) ||
+        !aligned16(W->up_s) || !aligned16(W->down_s))
+        return K3MOE_E_ALIGN;
+    if ((W->gate_q_stride | W->up_q_stride | W->down_q_stride | W->gate_s_stride | W->up_s_stride |
+         W->down_s_stride) & 15)
+        return K3MOE_E_ALIGN;
     if (W->gate_q_stride < 0 || W->up_q_stride < 0 || W->down_q_stride < 0 || W->gate_s_stride < 0 ||
         W->up_s_stride < 0 || W->down_s_stride < 0)
         return K3MOE_E_DIM;

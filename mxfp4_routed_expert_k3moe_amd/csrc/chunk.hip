@@ -19,17 +19,19 @@
 //   combine        y_t = sum_k y_pair[t*K+k] in slot order
 //
 // GEMM structure (gfx950, v_mfma_f32_16x16x32_bf16, wave64):
-//   workgroup = 4 waves = one (tile, column block); the tile's rows of A
-//   (activations, shared by the 4 waves) are staged in LDS 128 columns at a time
-//   with the next step prefetched in registers.  The weight operand never
-//   touches LDS: each lane loads 16 bytes (32 codes = one scale group) of one
-//   weight row and converts them with the gfx950 scaled fp4->bf16 converts
-//   straight into four MFMA B operands.  The k order inside a 128-wide step is
-//   permuted (lane group g owns columns 32g..32g+31, MFMA j takes 8j..8j+7 of
-//   them) identically for A and B, which leaves the dot products unchanged.
-//   Workgroup ids are remapped so each XCD walks a contiguous run of
-//   (tile, column block) items: the column blocks of one tile share that XCD's L2
-//   copy of the tile's activations.
+//   workgroup = one (tile, column block): 4 waves for 128-row tiles, 8 for
+//   16-row tiles; each wave owns 32 (gate/up) or 64 (down) output columns.  The
+//   reduction runs in 128-column steps through a 4-deep ring: the tile's A rows
+//   (activations, shared by all waves) go global -> LDS directly, 16-byte pieces
+//   XOR-swizzled by row; the weight operand never touches LDS: each lane loads
+//   16 bytes (32 codes = one scale group) of one weight row into a register ring
+//   and converts them with the gfx950 scaled fp4->bf16 converts straight into
+//   four MFMA B operands.  The k order inside a step is permuted (lane group g
+//   owns columns 32g..32g+31, MFMA j takes 8j..8j+7 of them) identically for A
+//   and B, which leaves the dot products unchanged.  Scale bytes of the
+//   workgroup's weight rows are staged in LDS once.  Workgroup ids are remapped
+//   so each XCD walks a contiguous run of (tile, column block) items: the column
+//   blocks of one tile share that XCD's L2 copy of the tile's activations.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -38,11 +40,12 @@ namespace k3moe {
 namespace {
 
 constexpr int GT = kGroupTokens;
-constexpr int MT = kTileRows;
-constexpr int KS = 128;                 // reduction columns per pipeline step
-constexpr int LDS_STRIDE = KS * 2 + 16; // bytes per staged A row (pad staggers banks)
-constexpr int GEMM_THREADS = 256;
+constexpr int KS = 128;       // reduction columns per pipeline step
+constexpr int A_ROW = KS * 2;  // bytes per staged A row: 16 pieces of 16 bytes, XOR-swizzled
 constexpr int N_XCD = 8;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(int T, int K, int E, i
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ uniq,
-                                                          int4* __restrict__ tiles, int max_tiles,
+                                                          int4* __restrict__ tiles, int max_tiles, int MT,
                                                           int32_t* __restrict__ scalars,
                                                           int32_t* __restrict__ n_unique_out) {
     extern __shared__ int32_t scnt[];  // [E]
@@ -187,8 +190,8 @@ struct GemmArgs {
     int K;                  // slots per token
     const uint8_t *q0, *s0, *q1, *s1;  // GATEUP: gate, up; DOWN: down (q1/s1 unused)
     int64_t q0_stride, s0_stride, q1_stride, s1_stride;
-    int Kdim;               // reduction length
-    int N;                  // output columns per expert
+    int Kdim;               // reduction length (multiple of 32, <= 8192)
+    int N;                  // output columns per expert (multiple of 32)
     const int4* tiles;
     const int32_t* scalars;  // [1] = number of tiles
     int nblk_n;             // column blocks
@@ -197,9 +200,201 @@ struct GemmArgs {
     const float* wts;       // DOWN: [P] routing weight of each pair
 };
 
-template <int MODE>
-__global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[MT * LDS_STRIDE];
+// GATEUP: a wave owns 32 columns of h and computes them from 16-row subtiles of
+// the gate (n-subtiles 0, 1) and up (2, 3) weights.  DOWN: a wave owns 64 columns.
+template <int MODE, int WAVES>
+struct GemmShape {
+    static constexpr int WN = (MODE == GATEUP) ? 32 : 64;     // output columns per wave
+    static constexpr int BN = WAVES * WN;                     // output columns per workgroup
+    static constexpr int TENSORS = (MODE == GATEUP) ? 2 : 1;  // weight tensors read
+    static constexpr int SROWS = TENSORS * BN;                // weight rows whose scales sit in LDS
+};
+
+inline size_t gemm_lds_bytes(int mt, int nb, int srows, int kdim) {
+    return (size_t)nb * mt * A_ROW + (size_t)srows * (kdim / 32);
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
+    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Wait until at most N of this wave's vector-memory instructions are in flight.
+// The "memory" clobber keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS hand-off: this wave's LDS writes are done, then
+// s_barrier.  Unlike __syncthreads() it does not wait for the wave's global loads
+// still in flight (the weight ring and the next steps' LDS-direct loads); the
+// LDS-direct loads a step needs are waited for with wait_vmcnt first.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The reduction of one work item, with the number of 16-row subtiles (MS) fixed at
+// compile time so the step body is straight-line code.  EXACT adds the per-chunk
+// s = 255 fix-up and the masking of columns past Kdim; the fast body is taken when
+// no staged scale byte is 255 and Kdim is a multiple of 128.
+template <int MODE, int MT, int WAVES, int NB, int MS, bool EXACT>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* alds, const uint8_t* slds, int e, int row0,
+                                          int mrows, int nb0, const uint16_t* const (&asrc)[(MT * 16 + WAVES * 64 - 1) / (WAVES * 64)],
+                                          const int (&aseg)[(MT * 16 + WAVES * 64 - 1) / (WAVES * 64)]) {
+    using SH = GemmShape<MODE, WAVES>;
+    constexpr int WN = SH::WN, BN = SH::BN;
+    constexpr int PIECES = MT * 16;
+    constexpr int NQ = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
+    constexpr int PER_STEP = NQ + 4;  // vector-memory instructions per wave per step
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 15, lg = lane >> 4;
+    const int Kdim = a.Kdim, N = a.N, sb = Kdim >> 5;
+    const int n0 = nb0 + wave * WN;
+    const int nsteps = (Kdim + KS - 1) / KS;
+
+    // weight rows of this lane (clamped to real rows; columns past N are computed
+    // from a repeated row and never stored)
+    const size_t qrow = (size_t)Kdim >> 1;
+    const uint8_t* bq[4];
+    const uint8_t* bs[4];  // scale rows in LDS
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+        const int tsel = (MODE == GATEUP) ? (ns >> 1) : 0;
+        const int r = (MODE == GATEUP) ? n0 + 16 * (ns & 1) + ln : n0 + 16 * ns + ln;
+        const int row = min(r, N - 1);
+        const uint8_t* q = (tsel == 0) ? a.q0 + (size_t)e * a.q0_stride : a.q1 + (size_t)e * a.q1_stride;
+        bq[ns] = q + (size_t)row * qrow;
+        bs[ns] = slds + (size_t)tsel * BN * sb + (size_t)(row - nb0) * sb;
+    }
+
+    auto issue_a = [&](int buf, int step) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const uint16_t* src = asrc[q] + min(step * KS + aseg[q], Kdim - 8);
+            uint8_t* dst = alds + (size_t)buf * MT * A_ROW + (size_t)(((wave * NQ + q) * 64) % PIECES) * 16;
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)dst, 16, 0, 0);
+        }
+    };
+    uint4 bring[NB][4];
+    auto issue_b = [&](int slot_, int step) {
+        const int col = min(step * KS + 32 * lg, Kdim - 32);
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) bring[slot_][ns] = *reinterpret_cast<const uint4*>(bq[ns] + (col >> 1));
+    };
+
+    f32x4 acc[MS][4];
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) acc[i][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u) {
+        issue_a(u, min(u, nsteps - 1));
+        issue_b(u, min(u, nsteps - 1));
+    }
+    wait_vmcnt<(NB - 2) * PER_STEP>();
+    lds_barrier();
+
+    // one pipeline step; `u` is the ring slot of `step` (step % NB)
+    auto run_step = [&](const int u, const int step) {
+        const int ahead = min(step + NB - 1, nsteps - 1);
+        issue_a((u + NB - 1) % NB, ahead);
+        issue_b((u + NB - 1) % NB, ahead);
+        const uint8_t* abuf = alds + (size_t)u * MT * A_ROW;
+        const int sc_idx = min(4 * step + lg, sb - 1);
+        uint32_t sc[4];
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) sc[ns] = bs[ns][sc_idx];
+        const bool valid = step * KS + 32 * lg < Kdim;
+        float scf[4];
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) scf[ns] = scale_operand(sc[ns]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf16x8 bop[4];
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) {
+                if constexpr (EXACT)
+                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16(valid ? pick(bring[u][ns], j) : 0u, sc[ns]));
+                else
+                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16_nofix(pick(bring[u][ns], j), scf[ns]));
+            }
+#pragma unroll
+            for (int i = 0; i < MS; ++i) {
+                bf16x8 aop = *reinterpret_cast<const bf16x8*>(abuf + (16 * i + ln) * A_ROW + 16 * ((4 * lg + j) ^ ln));
+                if constexpr (EXACT) {
+                    if (!valid) aop = bf16x8{};
+                }
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns)
+                    acc[i][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[ns], acc[i][ns], 0, 0, 0);
+            }
+            // keep the scheduler from hoisting the next sub-step's operand reads
+            // (registers for them would push the weight ring out of VGPRs)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vmcnt<(NB - 2) * PER_STEP>();  // this wave's pieces of step + 1 are in LDS
+        lds_barrier();
+    };
+    int t0 = 0;
+    for (; t0 + NB <= nsteps; t0 += NB) {  // whole groups: straight-line body
+#pragma unroll
+        for (int u = 0; u < NB; ++u) run_step(u, t0 + u);
+    }
+#pragma unroll
+    for (int u = 0; u < NB - 1; ++u)  // remaining steps
+        if (t0 + u < nsteps) run_step(u, t0 + u);
+
+    // epilogue.  C layout: lane l, register r -> row 4*(l/16)+r, column l%16.
+    if (n0 >= N) return;
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * i + 4 * lg + r;
+            if (m >= mrows) continue;
+            if (MODE == GATEUP) {
+                uint16_t* hrow = a.h_out + (size_t)(row0 + m) * N;
+#pragma unroll
+                for (int ns = 0; ns < 2; ++ns)
+                    hrow[n0 + 16 * ns + ln] = (uint16_t)f32_to_bf16_bits(situ_fast(acc[i][ns][r], acc[i][ns + 2][r]));
+            } else {
+                const int p = a.perm[row0 + m];
+                const float wp = a.wts[p];
+                float* yrow = a.y_out + (size_t)p * N;
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns)
+                    if (n0 + 16 * ns < N) yrow[n0 + 16 * ns + ln] = acc[i][ns][r] * wp;
+            }
+        }
+    }
+}
+
+// One workgroup = one (tile of <= MT pair rows of one expert, block of BN output
+// columns), the whole reduction, in 128-column steps through an NB-deep ring:
+//   - A (activation rows, shared by all waves) goes global -> LDS directly
+//     (global_load_lds), 16-byte pieces XOR-swizzled by row so that the MFMA
+//     operand reads of 16 lanes hit distinct banks;
+//   - each lane streams the 16-byte weight chunks of its four 16-row subtiles
+//     into a register ring of the same depth and converts them in registers;
+//   - step t + NB - 1 is issued when step t starts, and one barrier per step
+//     (after the wave's own wait for step t + 1) publishes the next A buffer;
+//   - the scale bytes of the workgroup's weight rows are copied to LDS up front.
+template <int MODE, int MT, int WAVES, int NB>
+__global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(GemmArgs a) {
+    using SH = GemmShape<MODE, WAVES>;
+    constexpr int BN = SH::BN;
+    constexpr int THREADS = WAVES * 64;
+    constexpr int PIECES = MT * 16;                       // 16-byte A pieces per step
+    constexpr int NQ = (PIECES + THREADS - 1) / THREADS;  // LDS-direct loads per wave per step
+    static_assert(PIECES % 64 == 0, "whole waves of pieces");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t* alds = smem;                    // [NB][MT][A_ROW]
+    uint8_t* slds = smem + NB * MT * A_ROW;  // [TENSORS][BN][Kdim/32]
 
     // ---- work item (XCD-aware): XCD x walks items [x*per, (x+1)*per)
     const int n_items = a.scalars[1] * a.nblk_n;
@@ -209,161 +404,114 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void gemm_kernel(GemmArgs a) {
     if (slot >= per || item >= n_items) return;  // block-uniform
     const int tile = item / a.nblk_n, nblk = item % a.nblk_n;
     const int4 td = a.tiles[tile];
-    const int e = td.x, row0 = td.y, mrows = td.z;
+    const int e = td.x, row0 = td.y, mrows = td.z;  // 1 <= mrows <= MT
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Kdim = a.Kdim, N = a.N, sb = Kdim >> 5;
+    const int nb0 = nblk * BN;
+
+    // ---- A pieces of this wave: load q covers pieces c = ((wave*NQ + q)*64 + lane)
+    // mod PIECES (waves past the pieces repeat earlier ones: same bytes, same place),
+    // i.e. LDS row c/16, slot c%16, holding the row's 16-byte segment slot ^ (row%16).
+    // Rows past the tile re-read its last row; columns past Kdim are clamped when
+    // loaded and masked at use.
+    const uint16_t* asrc[NQ];
+    int aseg[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int c = ((wave * NQ + q) * 64 + lane) % PIECES;
+        const int r = c >> 4;
+        const int rc = min(r, mrows - 1);
+        const size_t row = (MODE == GATEUP) ? (size_t)(a.perm[row0 + rc] / a.K) : (size_t)(row0 + rc);
+        asrc[q] = a.A + row * (size_t)Kdim;
+        aseg[q] = 8 * ((c & 15) ^ (r & 15));
+    }
+
+    // ---- scale bytes of the workgroup's rows (srows_real * sb contiguous bytes per
+    // tensor, a multiple of 32, 16-byte aligned) -> LDS; note any byte equal to 255
+    const int srows_real = min(BN, N - nb0);
+    const int spieces = (srows_real * sb) >> 4;
+    const int stotal = SH::TENSORS * spieces;
+    int has255 = 0;
+    for (int c0 = 0; c0 < stotal; c0 += 8 * THREADS) {  // one pass for rows up to 4096 columns
+        uint4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int cc = min(c0 + k * THREADS + tid, stotal - 1);
+            const int tsel = cc >= spieces ? 1 : 0, pc = cc - tsel * spieces;
+            const uint8_t* sbase = tsel == 0 ? a.s0 + (size_t)e * a.s0_stride : a.s1 + (size_t)e * a.s1_stride;
+            v[k] = *reinterpret_cast<const uint4*>(sbase + (size_t)nb0 * sb + 16 * pc);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int c = c0 + k * THREADS + tid;
+            if (c < stotal) {
+                const int tsel = c >= spieces ? 1 : 0, pc = c - tsel * spieces;
+                *reinterpret_cast<uint4*>(slds + (size_t)tsel * BN * sb + 16 * pc) = v[k];
+                const uint32_t w4[4] = {~v[k].x, ~v[k].y, ~v[k].z, ~v[k].w};  // 255 -> zero byte
+#pragma unroll
+                for (int d = 0; d < 4; ++d) has255 |= ((w4[d] - 0x01010101u) & ~w4[d] & 0x80808080u) != 0u;
+            }
+        }
+    }
+    const bool exact = __syncthreads_or(has255) != 0 || (Kdim % KS) != 0;
+
+    if (exact) {
+        gemm_tile<MODE, MT, WAVES, NB, MT / 16, true>(a, alds, slds, e, row0, mrows, nb0, asrc, aseg);
+        return;
+    }
     const int msub = (mrows + 15) >> 4;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int ln = lane & 15, lg = lane >> 4;
-
-    // ---- this wave's output columns
-    constexpr int WN = (MODE == GATEUP) ? 32 : 64;   // per gate/up pair (GATEUP) or plain
-    const int n0 = nblk * (4 * WN) + wave * WN;
-    const int nvalid = min(WN, a.N - n0);             // multiple of 16 (N % 32 == 0)
-    const int nsub = (MODE == GATEUP) ? (nvalid > 0 ? 4 : 0) : max(0, nvalid >> 4);
-
-    // ---- B row pointers for the 4 n-subtiles of this lane
-    const size_t qrow = (size_t)a.Kdim >> 1, srow = (size_t)a.Kdim >> 5;
-    const uint8_t* bq[4];
-    const uint8_t* bs[4];
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-        int row;
-        const uint8_t *q, *s;
-        if (MODE == GATEUP) {
-            row = n0 + 16 * (ns & 1) + ln;
-            q = (ns < 2) ? a.q0 + (size_t)e * a.q0_stride : a.q1 + (size_t)e * a.q1_stride;
-            s = (ns < 2) ? a.s0 + (size_t)e * a.s0_stride : a.s1 + (size_t)e * a.s1_stride;
-        } else {
-            row = n0 + 16 * ns + ln;
-            q = a.q0 + (size_t)e * a.q0_stride;
-            s = a.s0 + (size_t)e * a.s0_stride;
-        }
-        row = min(row, a.N - 1);  // clamp for idle subtiles (never used)
-        bq[ns] = q + (size_t)row * qrow;
-        bs[ns] = s + (size_t)row * srow;
+#define K3_TILE_CASE(MSV)                                                                         \
+    case MSV:                                                                                     \
+        if constexpr (MSV <= MT / 16)                                                             \
+            gemm_tile<MODE, MT, WAVES, NB, MSV, false>(a, alds, slds, e, row0, mrows, nb0, asrc, aseg); \
+        break;
+    switch (msub) {
+        K3_TILE_CASE(1)
+        K3_TILE_CASE(2)
+        K3_TILE_CASE(3)
+        K3_TILE_CASE(4)
+        K3_TILE_CASE(5)
+        K3_TILE_CASE(6)
+        K3_TILE_CASE(7)
+        K3_TILE_CASE(8)
+        default: break;
     }
+#undef K3_TILE_CASE
+    (void)wave;
+    (void)lane;
+}
 
-    // ---- A rows this thread stages: rows r = (tid>>4) + 16*pass, 16-byte segment tid&15
-    const int seg = tid & 15, rbase = tid >> 4;
-    const uint16_t* arow[MT / 16];
-#pragma unroll
-    for (int pass = 0; pass < MT / 16; ++pass) {
-        const int r = rbase + 16 * pass;
-        arow[pass] = nullptr;
-        if (r < mrows) {
-            const size_t row = (MODE == GATEUP) ? (size_t)(a.perm[row0 + r] / a.K) : (size_t)(row0 + r);
-            arow[pass] = a.A + row * (size_t)a.Kdim;
-        }
-    }
+template <int MODE, int MT, int WAVES, int NB>
+hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
+    using SH = GemmShape<MODE, WAVES>;
+    a.nblk_n = (a.N + SH::BN - 1) / SH::BN;
+    const size_t lds = gemm_lds_bytes(MT, NB, SH::SROWS, a.Kdim);
+    const long max_items = (long)max_tiles * a.nblk_n;
+    const dim3 grid((unsigned)(((max_items + N_XCD - 1) / N_XCD) * N_XCD));
+    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, WAVES, NB>);
+    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((gemm_kernel<MODE, MT, WAVES, NB>), grid, dim3(WAVES * 64), lds, stream, a);
+    return hipGetLastError();
+}
 
-    const int nsteps = (a.Kdim + KS - 1) / KS;
-    uint4 areg[MT / 16];
-    auto load_a = [&](int step) {
-        const int kc = step * KS + seg * 8;
-#pragma unroll
-        for (int pass = 0; pass < MT / 16; ++pass) {
-            areg[pass] = make_uint4(0u, 0u, 0u, 0u);
-            if (arow[pass] != nullptr && kc < a.Kdim)
-                areg[pass] = *reinterpret_cast<const uint4*>(arow[pass] + kc);
-        }
-    };
-    auto store_a = [&]() {
-#pragma unroll
-        for (int pass = 0; pass < MT / 16; ++pass) {
-            const int r = rbase + 16 * pass;
-            if (r < mrows) *reinterpret_cast<uint4*>(lds + r * LDS_STRIDE + seg * 16) = areg[pass];
-        }
-    };
+constexpr size_t kLdsLimit = 160 * 1024;
 
-    uint4 bcur[4], bnext[4];
-    uint32_t scur[4], snext[4];
-    auto load_b = [&](int step, uint4 (&q)[4], uint32_t (&s)[4]) {
-        const int kc = step * KS + 32 * lg;
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) {
-            q[ns] = make_uint4(0u, 0u, 0u, 0u);
-            s[ns] = 127u;
-            if (ns < nsub && kc < a.Kdim) {
-                q[ns] = *reinterpret_cast<const uint4*>(bq[ns] + (kc >> 1));
-                s[ns] = bs[ns][kc >> 5];
-            }
-        }
-    };
+// 16-row tiles run eight waves per workgroup; 128-row tiles (128 accumulator
+// registers per lane) run four, one per SIMD.  The ring is four steps deep when
+// it fits in LDS beside the staged scales, else two.
+template <int MODE, int MT>
+hipError_t launch_gemm_mt(const GemmArgs& a, int max_tiles, hipStream_t stream) {
+    constexpr int WAVES = MT == 16 ? 8 : 4;
+    if (gemm_lds_bytes(MT, 4, GemmShape<MODE, WAVES>::SROWS, a.Kdim) <= kLdsLimit)
+        return launch_gemm_t<MODE, MT, WAVES, 4>(a, max_tiles, stream);
+    return launch_gemm_t<MODE, MT, WAVES, 2>(a, max_tiles, stream);
+}
 
-    f32x4 acc[MT / 16][4];
-#pragma unroll
-    for (int i = 0; i < MT / 16; ++i)
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) acc[i][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    load_a(0);
-    load_b(0, bcur, scur);
-    store_a();
-    __syncthreads();
-
-    for (int step = 0; step < nsteps; ++step) {
-        const bool more = step + 1 < nsteps;
-        if (more) {
-            load_a(step + 1);
-            load_b(step + 1, bnext, snext);
-        }
-        if (nsub > 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x8 bop[4];
-#pragma unroll
-                for (int ns = 0; ns < 4; ++ns) {
-                    const uint32_t qw = (j == 0) ? bcur[ns].x : (j == 1) ? bcur[ns].y : (j == 2) ? bcur[ns].z : bcur[ns].w;
-                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16(qw, scur[ns]));
-                }
-#pragma unroll
-                for (int i = 0; i < MT / 16; ++i) {
-                    if (i < msub) {
-                        const bf16x8 aop = *reinterpret_cast<const bf16x8*>(
-                            lds + (16 * i + ln) * LDS_STRIDE + 64 * lg + 16 * j);
-#pragma unroll
-                        for (int ns = 0; ns < 4; ++ns)
-                            if (ns < nsub)
-                                acc[i][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[ns], acc[i][ns], 0, 0, 0);
-                    }
-                }
-            }
-        }
-        if (more) {
-            __syncthreads();
-            store_a();
-            __syncthreads();
-#pragma unroll
-            for (int ns = 0; ns < 4; ++ns) { bcur[ns] = bnext[ns]; scur[ns] = snext[ns]; }
-        }
-    }
-
-    // ---- epilogue.  C layout: lane l, register r -> row 4*(l/16)+r, column l%16.
-    if (nsub == 0) return;
-#pragma unroll
-    for (int i = 0; i < MT / 16; ++i) {
-        if (i >= msub) break;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 16 * i + 4 * lg + r;
-            if (m >= mrows) continue;
-            if (MODE == GATEUP) {
-                uint16_t* hrow = a.h_out + (size_t)(row0 + m) * a.N;
-#pragma unroll
-                for (int ns = 0; ns < 2; ++ns) {
-                    const float hv = situ_fast(acc[i][ns][r], acc[i][ns + 2][r]);
-                    hrow[n0 + 16 * ns + ln] = (uint16_t)f32_to_bf16_bits(hv);
-                }
-            } else {
-                const int p = a.perm[row0 + m];
-                const float wp = a.wts[p];
-                float* yrow = a.y_out + (size_t)p * a.N;
-#pragma unroll
-                for (int ns = 0; ns < 4; ++ns)
-                    if (ns < nsub) yrow[n0 + 16 * ns + ln] = acc[i][ns][r] * wp;
-            }
-        }
-    }
+template <int MODE>
+hipError_t launch_gemm(const GemmArgs& a, int mt, int max_tiles, hipStream_t stream) {
+    return mt == 16 ? launch_gemm_mt<MODE, 16>(a, max_tiles, stream) : launch_gemm_mt<MODE, 128>(a, max_tiles, stream);
 }
 
 // -------------------------------------------------------------------------- combine
@@ -400,7 +548,8 @@ int grid_for(size_t n, int per_block) {
 // ------------------------------------------------------------------ workspace layout
 int group_max_tiles(int T, int K, int E) {
     const long P = (long)T * K;
-    return (int)((P + MT - 1) / MT + (E < P ? E : P));
+    const int mt = tile_rows(T, K, E);
+    return (int)((P + mt - 1) / mt + (E < P ? E : P));
 }
 
 size_t group_workspace_bytes(int T, int K, int E, bool with_outputs) {
@@ -424,6 +573,7 @@ GroupBuffers group_workspace_carve(void* ws, int T, int K, int E, bool with_outp
     g.err_blk = reinterpret_cast<int32_t*>(p); p += align256(nb * 4);
     g.scalars = reinterpret_cast<int32_t*>(p); p += align256(2 * 4);
     g.max_tiles = group_max_tiles(T, K, E);
+    g.mt = tile_rows(T, K, E);
     g.tiles = reinterpret_cast<int4*>(p); p += align256((size_t)g.max_tiles * 16);
     if (with_outputs) {
         g.counts = reinterpret_cast<int32_t*>(p); p += align256((size_t)E * 4);
@@ -456,7 +606,7 @@ hipError_t launch_group(const int32_t* idx, int T, int K, int E, const GroupBuff
                        g.counts_blk, reinterpret_cast<unsigned long long*>(g.masks_blk), g.err_blk);
     hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(1024), (size_t)E * 4, stream, T, K, E, g.nb,
                        g.counts_blk, g.blkoff, g.err_blk, g.counts, g.offsets, g.uniq, g.tiles,
-                       g.max_tiles, g.scalars, n_unique_out);
+                       g.max_tiles, g.mt, g.scalars, n_unique_out);
     hipLaunchKernelGGL(group_scatter_kernel, dim3(g.nb), dim3(256), 0, stream, idx, T, K, E,
                        reinterpret_cast<const unsigned long long*>(g.masks_blk), g.blkoff, g.offsets,
                        g.scalars, g.perm);
@@ -480,11 +630,9 @@ hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int
     gu.N = W.F;
     gu.tiles = ws.g.tiles;
     gu.scalars = ws.g.scalars;
-    gu.nblk_n = (W.F + 4 * 32 - 1) / (4 * 32);
     gu.h_out = ws.h_bf16;
-    const int max_items_gu = ws.g.max_tiles * gu.nblk_n;
-    hipLaunchKernelGGL(gemm_kernel<GATEUP>, dim3(((max_items_gu + N_XCD - 1) / N_XCD) * N_XCD),
-                       dim3(GEMM_THREADS), 0, stream, gu);
+    err = launch_gemm<GATEUP>(gu, ws.g.mt, ws.g.max_tiles, stream);
+    if (err != hipSuccess) return err;
 
     GemmArgs dn{};
     dn.A = ws.h_bf16;
@@ -496,12 +644,10 @@ hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int
     dn.N = W.D;
     dn.tiles = ws.g.tiles;
     dn.scalars = ws.g.scalars;
-    dn.nblk_n = (W.D + 4 * 64 - 1) / (4 * 64);
     dn.y_out = ws.ytk;
     dn.wts = w;
-    const int max_items_dn = ws.g.max_tiles * dn.nblk_n;
-    hipLaunchKernelGGL(gemm_kernel<DOWN>, dim3(((max_items_dn + N_XCD - 1) / N_XCD) * N_XCD),
-                       dim3(GEMM_THREADS), 0, stream, dn);
+    err = launch_gemm<DOWN>(dn, ws.g.mt, ws.g.max_tiles, stream);
+    if (err != hipSuccess) return err;
 
     const size_t n4 = (size_t)T * W.D / 4;
     hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, ws.ytk, T, K, W.D,

@@ -36,7 +36,10 @@ hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t
 
 // ------------------------------------------------------------------ chunk
 constexpr int kGroupTokens = 64;   // tokens per grouping block (one u64 mask bit each)
-constexpr int kTileRows = 128;     // max rows (pairs of one expert) per GEMM tile
+// GEMM tile height (pairs of one expert per tile): 16 when experts average at most
+// 16 pairs, else 128.  A pure function of (T, K, E) so that the workspace size,
+// the tile list and the GEMM instantiation always agree.
+inline int tile_rows(int T, int K, int E) { return (long)T * K <= 16L * E ? 16 : 128; }
 
 struct GroupBuffers {
     int nb;                 // grouping blocks = ceil(T / 64)
@@ -47,6 +50,7 @@ struct GroupBuffers {
     int32_t* scalars;       // [0] n_unique (or -1), [1] n_tiles
     int4* tiles;            // [max_tiles] (expert, row0, rows, 0)
     int max_tiles;
+    int mt;                 // tile height, tile_rows(T, K, E)
     // outputs (caller's buffers for k3moe_group, workspace for forward_chunk)
     int32_t* counts;        // [E]
     int32_t* offsets;       // [E + 1]
