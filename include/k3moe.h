@@ -75,8 +75,9 @@ extern "C" {
  * The strides let the same struct address stacked [E, ...] tensors or any other
  * placement of the six tensors (the pages store them back to back per expert).
  * Requirements: d_model and d_ff multiples of 32 in [32, K3MOE_MAX_DIM];
- * 1 <= n_experts <= K3MOE_MAX_E; the three packed base pointers and their
- * strides 16-byte aligned.  The struct itself lives in host memory and is read
+ * 1 <= n_experts <= K3MOE_MAX_E; all six base pointers and all six strides
+ * 16-byte aligned (true for stacked [E, ...] tensors: every row length is a
+ * multiple of 16 bytes).  The struct itself lives in host memory and is read
  * only during the call.
  */
 typedef struct k3moe_weights {

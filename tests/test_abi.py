@@ -96,6 +96,13 @@ def test_validation_before_any_device_call():
     assert lib.k3moe_forward_decode(ctypes.byref(_struct(ptr=264)), p, p, p, 16, p, p, ws, None) == k3.K3MOE_E_ALIGN
     assert lib.k3moe_forward_decode(ctypes.byref(_struct(stride=8)), p, p, p, 16, p, p, ws, None) == k3.K3MOE_E_ALIGN
     assert lib.k3moe_forward_decode(ctypes.byref(s), ctypes.c_void_p(260), p, p, 16, p, p, ws, None) == k3.K3MOE_E_ALIGN
+    for name in ("gate_s", "up_s", "down_s"):
+        bad_s = _struct()
+        setattr(bad_s, name, 264)
+        assert lib.k3moe_forward_decode(ctypes.byref(bad_s), p, p, p, 16, p, p, ws, None) == k3.K3MOE_E_ALIGN
+        bad_s = _struct()
+        setattr(bad_s, name + "_stride", 3584 * 3072 // 32 + 4)
+        assert lib.k3moe_forward_chunk(ctypes.byref(bad_s), p, 32, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_ALIGN
     assert lib.k3moe_forward_decode(ctypes.byref(s), p, p, p, 16, p, p, 100, None) == k3.K3MOE_E_WORKSPACE
     assert lib.k3moe_forward_chunk(ctypes.byref(s), p, 0, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_DIM
     assert lib.k3moe_forward_chunk(ctypes.byref(s), p, 32, p, p, 16, p, None, p, 100, None) == k3.K3MOE_E_WORKSPACE
