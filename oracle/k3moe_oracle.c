@@ -32,15 +32,15 @@
 /* ------------------------------------------------------------------ MXFP4 decode */
 
 /* e2m1 magnitudes, indexed by the code's low three bits (exponent e1 e0, mantissa m).
- * The pages name e2m1 but do not print the table ([PR676] summary: "e2m1 nibbles +
- * ue8m0 per-32 scales"; [LC21] arch commit: the same E2M1 code assignment as ggml's
- * MXFP4; [PR684] int8 commit: doubled e2m1 values are exact int8).  This is the
- * standard OCP e2m1 value set. */
+ * The pages name e2m1 but do not print the table ([PR676] summary: 4-bit e2m1 codes
+ * with one ue8m0 scale per 32 inputs; [LC21] arch commit: the code assignment is
+ * the one ggml's MXFP4 uses; [PR684] int8 commit: twice every e2m1 value is an
+ * exact int8).  This is the standard OCP e2m1 value set. */
 static const double E2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 
 /* One weight from a 4-bit code and its group's scale byte:
- * w = v * 2^(s - 127), v = (-1)^bit3 * E2M1[code & 7]   ([PR684] MXFP4 commit:
- * "bit3 = sign", "w = v * 2^(s-127)").
+ * w = v * 2^(s - 127), v = (-1)^bit3 * E2M1[code & 7]   ([PR684] MXFP4 commit: the
+ * code's bit 3 is the sign, the scale byte is a biased power-of-two exponent).
  * The product is exact in double; it is then rounded once to fp32.  Every value
  * below 2^128 has at most two significant bits and magnitude >= 2^-128, so it is
  * representable in fp32 (subnormals included); anything >= 2^128 overflows to a

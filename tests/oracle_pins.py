@@ -224,7 +224,7 @@ def check_route_invariants(o):
     for t in range(T):
         order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))
         assert set(idx0[t].tolist()) == set(order[:K]), t
-    # weights depend on the selection only, not on the bias ("raw-score renormalization"):
+    # weights depend on the selection only, not on the bias (they renormalize the raw sigmoid scores):
     # lowering the bias of unselected experts keeps every selected key and the selection
     for t in range(T):
         b2 = bias.copy()
