@@ -34,6 +34,101 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+TRAFFIC_FILE = os.path.join("profiles", "decode_gateup_traffic.json")
+# sources whose change invalidates the counter figures
+TRAFFIC_SOURCES = ("mxfp4_routed_expert_k3moe_amd/csrc/decode.hip", "mxfp4_routed_expert_k3moe_amd/csrc/device.hpp",
+                   "mxfp4_routed_expert_k3moe_amd/csrc/launch.hpp")
+PROBE_TOKENS = 8
+COPY_BYTES = 1 << 30
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_bytes():
+    """HBM bytes per decode gate/up launch from the committed counter runs, or None
+    when they are missing or were taken on other kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("sources_sha256") != sources_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def counters_probe(torch, synth, lib, dev):
+    """A short run for rocprofv3 --pmc: PROBE_TOKENS decode tokens through route,
+    gate/up and down (only the experts they touch are generated), then a plain
+    device copy of COPY_BYTES twice, whose counter readings calibrate the bytes."""
+    cfg = synth.CONFIGS["decode1"]
+    xs, logits, bias = synth.activations(cfg, T=PROBE_TOKENS, stream=5)
+    l_d, b_d = torch.from_numpy(logits).to(dev), torch.from_numpy(bias).to(dev)
+    idx, w = lib.route(l_d, b_d, cfg.K)
+    used = np.unique(idx.cpu().numpy())
+    W = lib.ExpertWeights.from_dict(synth.weights_device(cfg, dev, experts=used))
+    x_d = torch.from_numpy(xs).to(dev)
+    h = torch.empty((cfg.K, cfg.F), dtype=torch.float32, device=dev)
+    y = torch.empty((PROBE_TOKENS, cfg.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(lib.workspace_size(lib.OP_DECODE, 1, cfg.K, W), dtype=torch.uint8, device=dev)
+    for j in range(PROBE_TOKENS):
+        lib.decode_gateup(W, x_d[j], idx[j], h=h)
+        lib.decode_down(W, h, idx[j], w[j], y=y[j], ws=ws)
+    a = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"counters probe: {PROBE_TOKENS} tokens, {len(used)} experts, copy {COPY_BYTES} B x 2")
+
+
+def _pmc_rows(folder, counter):
+    """(kernel name, value in bytes) per dispatch from a rocprofv3 csv folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"]) * 1024.0))  # KiB -> B
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir):
+    cfg_k, cfg_f, cfg_d = 16, 3072, 3584
+    algo = cfg_k * 2 * (cfg_f * cfg_d // 2 + cfg_f * cfg_d // 32) + cfg_d * 4 + cfg_k * cfg_f * 4
+    out = {"kernel": "decode_gateup_kernel", "algorithmic_bytes_per_launch": algo,
+           "sources_sha256": sources_digest(), "copy_bytes": COPY_BYTES}
+    per = {}
+    for key, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = _pmc_rows(folder, counter)
+        copy = [v for n, v in rows if "copy" in n.lower() and v > COPY_BYTES / 4]
+        gu = [v for n, v in rows if "decode_gateup_kernel" in n]
+        if not copy or not gu:
+            raise SystemExit(f"{counter}: copy dispatches {len(copy)}, gate/up dispatches {len(gu)}")
+        factor = COPY_BYTES / float(np.median(copy))
+        per[key] = {"counter": counter, "raw_bytes_per_launch": float(np.mean(gu)), "copy_raw_bytes": float(np.median(copy)),
+                    "calibration_factor": factor, "bytes_per_launch": float(np.mean(gu)) * factor, "launches": len(gu)}
+    out.update(per)
+    out["bytes_per_launch"] = round(per["fetch"]["bytes_per_launch"] + per["write"]["bytes_per_launch"])
+    out["traffic_over_algorithmic"] = round(out["bytes_per_launch"] / algo, 4)
+    with open(os.path.join(ROOT, TRAFFIC_FILE), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -43,7 +138,14 @@ def main():
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--counters-probe", action="store_true",
+                    help="run only a few decode steps and the copy calibration (for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders into " + TRAFFIC_FILE)
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this block's kernels run on a single MI355X "
               "(multi-GPU sharding is a design note, not implemented); use --gpus 1", file=sys.stderr)
@@ -58,6 +160,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.counters_probe:
+        counters_probe(torch, synth, lib, dev)
+        return
 
     # ------------------------------------------------------------- decode workload
     cfg = synth.CONFIGS["decode1"]
@@ -133,7 +238,7 @@ def main():
         "us_per_layer_token": round(ms_per_step * 1e3, 3),
         "roofline": {"bound": "hbm", "kernel": "decode_gateup_kernel (16 experts' gate/up GEMV + SiTU-GLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(),
                      "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_us, 3)},
     }
     del W, ws
@@ -146,7 +251,8 @@ def main():
         Wc = lib.ExpertWeights.from_dict(synth.weights_device(ccfg, dev))
         x, lg, bs = synth.activations(ccfg)
         xc = torch.from_numpy(x).to(dev).to(torch.bfloat16)  # x holds bf16 values: exact
-        idx_c, w_c = lib.route(torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev), ccfg.K)
+        lg_c, bs_c = torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev)
+        idx_c, w_c = lib.route(lg_c, bs_c, ccfg.K)
         yc = torch.empty((ccfg.T, ccfg.D), dtype=torch.float32, device=dev)
         nu = torch.zeros(1, dtype=torch.int32, device=dev)
         wsc = torch.empty(lib.workspace_size(lib.OP_CHUNK, ccfg.T, ccfg.K, Wc), dtype=torch.uint8, device=dev)
@@ -155,7 +261,7 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.chunk_iters):
-            lib.route(torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev), ccfg.K, idx=idx_c, w=w_c)
+            lib.route(lg_c, bs_c, ccfg.K, idx=idx_c, w=w_c)
             lib.forward_chunk(Wc, xc, idx_c, w_c, y=yc, n_unique=nu, ws=wsc)
         e1.record(stream)
         torch.cuda.synchronize()
@@ -164,8 +270,9 @@ def main():
         flops = 6.0 * ccfg.D * ccfg.F * ccfg.T * ccfg.K
         wbytes = U * ccfg.expert_bytes()
         result["chunk"] = {"workload": "batch4096: 4096 tokens, i.i.d. hidden states, logits = h.R, same shape, "
-                                       "bf16 MFMA grouped GEMM",
-                           "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2),
+                                       "bf16 MFMA grouped GEMM (route + group + gate/up + down + combine)",
+                           "ms": round(ms, 4), "us_per_layer_token": round(ms * 1e3 / ccfg.T, 4),
+                           "tflops": round(flops / ms / 1e9, 2),
                            "tflops_frac_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
                            "weight_gbs": round(wbytes / ms / 1e6, 1), "unique_experts": U}
         log(f"chunk: {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s, union {U}")

@@ -134,21 +134,29 @@ def weights_host(cfg: Config, experts: Optional[Iterable[int]] = None) -> Dict[s
     return out
 
 
-def weights_device(cfg: Config, device, batch: int = 32):
-    """All E experts as torch uint8 tensors ``{name: [E, rows, cols]}`` on ``device``.
+def weights_device(cfg: Config, device, batch: int = 32, experts: Optional[Iterable[int]] = None):
+    """Experts as torch uint8 tensors ``{name: [E, rows, cols]}`` on ``device``.
 
-    Generated on the host in batches of ``batch`` experts and copied up, so the
-    host never holds more than one batch.
+    All E experts by default; with ``experts`` only those are generated and the
+    others are left zero (for short runs that touch a known subset).  Generated on
+    the host in batches of ``batch`` experts and copied up, so the host never
+    holds more than one batch.
     """
     import torch
 
-    dev = {n: torch.empty((cfg.E,) + cfg.shapes()[n], dtype=torch.uint8, device=device)
-           for n in TENSORS}
-    for e0 in range(0, cfg.E, batch):
-        ids = range(e0, min(cfg.E, e0 + batch))
+    alloc = torch.empty if experts is None else torch.zeros
+    dev = {n: alloc((cfg.E,) + cfg.shapes()[n], dtype=torch.uint8, device=device) for n in TENSORS}
+    ids_all = list(range(cfg.E)) if experts is None else sorted({int(e) for e in experts})
+    for b0 in range(0, len(ids_all), batch):
+        ids = ids_all[b0:b0 + batch]
         host = weights_host(cfg, ids)
         for n in TENSORS:
-            dev[n][e0:e0 + len(ids)].copy_(torch.from_numpy(host[n]), non_blocking=False)
+            src = torch.from_numpy(host[n])
+            if ids == list(range(ids[0], ids[0] + len(ids))):
+                dev[n][ids[0]:ids[0] + len(ids)].copy_(src, non_blocking=False)
+            else:
+                for j, e in enumerate(ids):
+                    dev[n][e].copy_(src[j], non_blocking=False)
     return dev
 
 
@@ -156,8 +164,8 @@ def weights_device(cfg: Config, device, batch: int = 32):
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """fp32 values rounded to the nearest bf16 (ties to even), returned as fp32.
 
-    Chunk workloads carry bf16 hidden states ("bf16 activations into the grouped
-    GEMM"); both the oracle and the device receive exactly these values."""
+    Chunk workloads carry bf16 hidden states (the grouped GEMM takes bf16
+    activations); both the oracle and the device receive exactly these values."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
     return r.view(np.float32).reshape(np.shape(x))
