@@ -32,6 +32,8 @@
 //   workgroup's weight rows are staged in LDS once.  Workgroup ids are remapped
 //   so each XCD walks a contiguous run of (tile, column block) items: the column
 //   blocks of one tile share that XCD's L2 copy of the tile's activations.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -44,8 +46,6 @@ constexpr int KS = 128;       // reduction columns per pipeline step
 constexpr int A_ROW = KS * 2;  // bytes per staged A row: 16 pieces of 16 bytes, XOR-swizzled
 constexpr int N_XCD = 8;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -210,6 +210,8 @@ struct GemmShape {
     static constexpr int SROWS = TENSORS * BN;                // weight rows whose scales sit in LDS
 };
 
+constexpr size_t kLdsLimit = 160 * 1024;
+
 inline size_t gemm_lds_bytes(int mt, int nb, int srows, int kdim) {
     return (size_t)nb * mt * A_ROW + (size_t)srows * (kdim / 32);
 }
@@ -218,35 +220,130 @@ __device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
     return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-// Wait until at most N of this wave's vector-memory instructions are in flight.
-// The "memory" clobber keeps the compiler from moving memory accesses across it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier for LDS hand-off: this wave's LDS writes are done, then
+// Workgroup barrier for LDS hand-off: this wave's LDS accesses are done, then
 // s_barrier.  Unlike __syncthreads() it does not wait for the wave's global loads
-// still in flight (the weight ring and the next steps' LDS-direct loads); the
-// LDS-direct loads a step needs are waited for with wait_vmcnt first.
+// still in flight (the weight ring and the activation prefetch); the compiler
+// waits for each of those where its registers are used.  The "memory" clobber
+// keeps memory accesses from moving across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// The reduction of one work item, with the number of 16-row subtiles (MS) fixed at
-// compile time so the step body is straight-line code.  EXACT adds the per-chunk
-// s = 255 fix-up and the masking of columns past Kdim; the fast body is taken when
-// no staged scale byte is 255 and Kdim is a multiple of 128.
-template <int MODE, int MT, int WAVES, int NB, int MS, bool EXACT>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* alds, const uint8_t* slds, int e, int row0,
-                                          int mrows, int nb0, const uint16_t* const (&asrc)[(MT * 16 + WAVES * 64 - 1) / (WAVES * 64)],
-                                          const int (&aseg)[(MT * 16 + WAVES * 64 - 1) / (WAVES * 64)]) {
-    using SH = GemmShape<MODE, WAVES>;
+
+// A pieces of one loading thread (index lt of NT loading threads): piece
+// c = (lt + i*NT) mod PIECES is tile row c/16, 16-byte segment c%16 of a step; it
+// is stored at LDS slot seg ^ (row % 16) of the row, so the 16 lanes that read
+// one MFMA fragment (16 rows, same segment) hit 16 different bank groups.
+// Threads past the pieces repeat earlier ones (same bytes to the same place).
+// Rows past the tile re-read its last row; columns past Kdim are clamped on load
+// and stored as zeros.
+template <int MODE, int MT, int NT>
+struct APieces {
+    static constexpr int PIECES = MT * 16;
+    static constexpr int SLOTS = (PIECES + NT - 1) / NT;
+    const uint16_t* src[SLOTS];  // row start
+    int col[SLOTS];              // element offset of the piece within a step
+    int lds[SLOTS];              // byte offset in one LDS buffer
+    __device__ __forceinline__ void init(const GemmArgs& a, int lt, int row0, int mrows) {
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int c = (lt + i * NT) % PIECES;
+            const int r = c >> 4, seg = c & 15;
+            const int rc = min(r, mrows - 1);
+            const size_t row = (MODE == GATEUP) ? (size_t)(a.perm[row0 + rc] / a.K) : (size_t)(row0 + rc);
+            src[i] = a.A + row * (size_t)a.Kdim;
+            col[i] = 8 * seg;
+            lds[i] = r * A_ROW + 16 * (seg ^ (r & 15));
+        }
+    }
+    __device__ __forceinline__ void load(uint4 (&v)[SLOTS], int step, int Kdim) const {
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i)
+            v[i] = *reinterpret_cast<const uint4*>(src[i] + min(step * KS + col[i], Kdim - 8));
+    }
+    __device__ __forceinline__ void store(const uint4 (&v)[SLOTS], uint8_t* buf, int step, int Kdim) const {
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            // mask word by word: a select between two uint4 objects would keep the
+            // register arrays in memory
+            const uint32_t m = step * KS + col[i] < Kdim ? 0xFFFFFFFFu : 0u;
+            *reinterpret_cast<uint4*>(buf + lds[i]) = make_uint4(v[i].x & m, v[i].y & m, v[i].z & m, v[i].w & m);
+        }
+    }
+};
+
+// Run body(U{}, step) for step = 0 .. nsteps-1 with U = step % P as a type, so every
+// register-array index inside is a constant: whole groups of P as a straight-line
+// loop body, then the remaining steps.
+template <typename Body, int... I>
+__device__ __forceinline__ void steps_group(Body& body, int t0, std::integer_sequence<int, I...>) {
+    (body(std::integral_constant<int, I>{}, t0 + I), ...);
+}
+template <typename Body, int... I>
+__device__ __forceinline__ void steps_tail(Body& body, int t0, int nsteps, std::integer_sequence<int, I...>) {
+    ((t0 + I < nsteps ? body(std::integral_constant<int, I>{}, t0 + I) : void()), ...);
+}
+template <int P, typename Body>
+__device__ __forceinline__ void for_steps(int nsteps, Body&& body) {
+    int t0 = 0;
+    for (; t0 + P <= nsteps; t0 += P) steps_group(body, t0, std::make_integer_sequence<int, P>{});
+    steps_tail(body, t0, nsteps, std::make_integer_sequence<int, P - 1>{});
+}
+
+// Loader waves (LW > 0): keep A two steps ahead in registers; during step t store
+// A(t + 1) into LDS buffer (t + 1) % 2 (read last in step t - 1) and load A(t + 3)
+// into the register set A(t) used.  One barrier per step, matching the compute
+// waves' barriers one for one.
+template <int MODE, int MT, int LW>
+__device__ __forceinline__ void gemm_loader(const GemmArgs& a, uint8_t* alds, int row0, int mrows, int lt) {
+    using AP = APieces<MODE, MT, LW * 64>;
+    const int Kdim = a.Kdim;
+    const int nsteps = (Kdim + KS - 1) / KS;
+    AP ap;
+    ap.init(a, lt, row0, mrows);
+    uint4 areg[3][AP::SLOTS];
+    ap.load(areg[0], 0, Kdim);
+    ap.load(areg[1], min(1, nsteps - 1), Kdim);
+    ap.load(areg[2], min(2, nsteps - 1), Kdim);
+    ap.store(areg[0], alds, 0, Kdim);
+    lds_barrier();
+    // three register sets, four-step bodies: the set of step t is t % 3, tracked at
+    // run time and switched on (a uniform branch) so the arrays stay in registers
+    int set1 = 1;  // set holding A(t + 1)
+    for (int step = 0; step < nsteps; ++step) {
+        uint8_t* nbuf = alds + (size_t)((step + 1) & 1) * MT * A_ROW;
+        const int ahead = min(step + 3, nsteps - 1);
+        if (set1 == 1) {
+            ap.store(areg[1], nbuf, step + 1, Kdim);
+            ap.load(areg[0], ahead, Kdim);
+        } else if (set1 == 2) {
+            ap.store(areg[2], nbuf, step + 1, Kdim);
+            ap.load(areg[1], ahead, Kdim);
+        } else {
+            ap.store(areg[0], nbuf, step + 1, Kdim);
+            ap.load(areg[2], ahead, Kdim);
+        }
+        set1 = set1 == 2 ? 0 : set1 + 1;
+        lds_barrier();
+    }
+}
+
+// The reduction of one work item by the compute waves, with the number of 16-row
+// subtiles (MS) fixed at compile time so the step body is straight-line code.
+// EXACT adds the per-chunk s = 255 fix-up and the masking of weight columns past
+// Kdim; the fast body is taken when no staged scale byte is 255 and Kdim is a
+// multiple of 128.
+//
+// Per step t: load the weights of step t + NBB - 1 into the ring slot step t - 1
+// used, compute step t from LDS buffer t % 2 and ring slot t % NBB, barrier.  Without
+// loader waves (LW = 0) the compute waves also keep A one step ahead: load A(t + 1)
+// at the start of step t, store it into buffer (t + 1) % 2 at the end.
+template <int MODE, int MT, int CW, int LW, int NBB, int MS, bool EXACT>
+__device__ __forceinline__ void gemm_compute(const GemmArgs& a, uint8_t* alds, const uint8_t* slds, int e, int row0,
+                                             int mrows, int nb0) {
+    using SH = GemmShape<MODE, CW>;
+    using AP = APieces<MODE, MT, CW * 64>;
     constexpr int WN = SH::WN, BN = SH::BN;
-    constexpr int PIECES = MT * 16;
-    constexpr int NQ = (PIECES + WAVES * 64 - 1) / (WAVES * 64);
-    constexpr int PER_STEP = NQ + 4;  // vector-memory instructions per wave per step
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -269,21 +366,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* alds, cons
         bq[ns] = q + (size_t)row * qrow;
         bs[ns] = slds + (size_t)tsel * BN * sb + (size_t)(row - nb0) * sb;
     }
+    uint4 bring[NBB][4];
+#define K3_ISSUE_B(SLOT, STEP)                                                                   \
+    do {                                                                                         \
+        const int col_ = min((STEP) * KS + 32 * lg, Kdim - 32);                                  \
+        _Pragma("unroll") for (int ns = 0; ns < 4; ++ns) bring[SLOT][ns] =                       \
+            *reinterpret_cast<const uint4*>(bq[ns] + (col_ >> 1));                               \
+    } while (0)
 
-    auto issue_a = [&](int buf, int step) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const uint16_t* src = asrc[q] + min(step * KS + aseg[q], Kdim - 8);
-            uint8_t* dst = alds + (size_t)buf * MT * A_ROW + (size_t)(((wave * NQ + q) * 64) % PIECES) * 16;
-            __builtin_amdgcn_global_load_lds((glb_ptr_t)src, (lds_ptr_t)dst, 16, 0, 0);
-        }
-    };
-    uint4 bring[NB][4];
-    auto issue_b = [&](int slot_, int step) {
-        const int col = min(step * KS + 32 * lg, Kdim - 32);
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns) bring[slot_][ns] = *reinterpret_cast<const uint4*>(bq[ns] + (col >> 1));
-    };
+    AP ap;
+    uint4 areg[AP::SLOTS];
+    if constexpr (LW == 0) ap.init(a, tid, row0, mrows);
 
     f32x4 acc[MS][4];
 #pragma unroll
@@ -291,20 +384,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* alds, cons
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) acc[i][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (LW == 0) ap.load(areg, 0, Kdim);
 #pragma unroll
-    for (int u = 0; u < NB - 1; ++u) {
-        issue_a(u, min(u, nsteps - 1));
-        issue_b(u, min(u, nsteps - 1));
-    }
-    wait_vmcnt<(NB - 2) * PER_STEP>();
+    for (int u = 0; u < NBB - 1; ++u) K3_ISSUE_B(u, min(u, nsteps - 1));
+    if constexpr (LW == 0) ap.store(areg, alds, 0, Kdim);
     lds_barrier();
 
-    // one pipeline step; `u` is the ring slot of `step` (step % NB)
-    auto run_step = [&](const int u, const int step) {
-        const int ahead = min(step + NB - 1, nsteps - 1);
-        issue_a((u + NB - 1) % NB, ahead);
-        issue_b((u + NB - 1) % NB, ahead);
-        const uint8_t* abuf = alds + (size_t)u * MT * A_ROW;
+    for_steps<NBB>(nsteps, [&](auto uc, const int step) {
+        constexpr int u = decltype(uc)::value;
+        if constexpr (LW == 0) ap.load(areg, min(step + 1, nsteps - 1), Kdim);
+        K3_ISSUE_B((u + NBB - 1) % NBB, min(step + NBB - 1, nsteps - 1));
+        const uint8_t* abuf = alds + (size_t)(step & 1) * MT * A_ROW;
         const int sc_idx = min(4 * step + lg, sb - 1);
         uint32_t sc[4];
 #pragma unroll
@@ -325,10 +415,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* alds, cons
             }
 #pragma unroll
             for (int i = 0; i < MS; ++i) {
-                bf16x8 aop = *reinterpret_cast<const bf16x8*>(abuf + (16 * i + ln) * A_ROW + 16 * ((4 * lg + j) ^ ln));
-                if constexpr (EXACT) {
-                    if (!valid) aop = bf16x8{};
-                }
+                const bf16x8 aop =
+                    *reinterpret_cast<const bf16x8*>(abuf + (16 * i + ln) * A_ROW + 16 * ((4 * lg + j) ^ ln));
 #pragma unroll
                 for (int ns = 0; ns < 4; ++ns)
                     acc[i][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[ns], acc[i][ns], 0, 0, 0);
@@ -337,17 +425,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* alds, cons
             // (registers for them would push the weight ring out of VGPRs)
             __builtin_amdgcn_sched_barrier(0);
         }
-        wait_vmcnt<(NB - 2) * PER_STEP>();  // this wave's pieces of step + 1 are in LDS
+        if constexpr (LW == 0) ap.store(areg, alds + (size_t)((step + 1) & 1) * MT * A_ROW, step + 1, Kdim);
         lds_barrier();
-    };
-    int t0 = 0;
-    for (; t0 + NB <= nsteps; t0 += NB) {  // whole groups: straight-line body
-#pragma unroll
-        for (int u = 0; u < NB; ++u) run_step(u, t0 + u);
-    }
-#pragma unroll
-    for (int u = 0; u < NB - 1; ++u)  // remaining steps
-        if (t0 + u < nsteps) run_step(u, t0 + u);
+    });
+#undef K3_ISSUE_B
 
     // epilogue.  C layout: lane l, register r -> row 4*(l/16)+r, column l%16.
     if (n0 >= N) return;
@@ -375,26 +456,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* alds, cons
 }
 
 // One workgroup = one (tile of <= MT pair rows of one expert, block of BN output
-// columns), the whole reduction, in 128-column steps through an NB-deep ring:
-//   - A (activation rows, shared by all waves) goes global -> LDS directly
-//     (global_load_lds), 16-byte pieces XOR-swizzled by row so that the MFMA
-//     operand reads of 16 lanes hit distinct banks;
-//   - each lane streams the 16-byte weight chunks of its four 16-row subtiles
-//     into a register ring of the same depth and converts them in registers;
-//   - step t + NB - 1 is issued when step t starts, and one barrier per step
-//     (after the wave's own wait for step t + 1) publishes the next A buffer;
-//   - the scale bytes of the workgroup's weight rows are copied to LDS up front.
-template <int MODE, int MT, int WAVES, int NB>
-__global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(GemmArgs a) {
-    using SH = GemmShape<MODE, WAVES>;
+// columns), the whole reduction, in 128-column steps:
+//   - CW compute waves each stream the 16-byte weight chunks of their four 16-row
+//     subtiles through a 4-deep register ring and convert them in registers into
+//     MFMA B operands; A fragments come from a double-buffered LDS tile (16-byte
+//     pieces XOR-swizzled by row);
+//   - LW loader waves (128-row tiles) keep the tile's activation rows two steps
+//     ahead in registers and store them into LDS, so the compute waves' loads are
+//     weights only; with LW = 0 (16-row tiles) the compute waves do it themselves;
+//   - one barrier per step; the scale bytes of the workgroup's weight rows are
+//     copied to LDS up front.
+template <int MODE, int MT, int CW, int LW, int NBB>
+__global__ __launch_bounds__((CW + LW) * 64, 1) void gemm_kernel(GemmArgs a) {
+    using SH = GemmShape<MODE, CW>;
     constexpr int BN = SH::BN;
-    constexpr int THREADS = WAVES * 64;
-    constexpr int PIECES = MT * 16;                       // 16-byte A pieces per step
-    constexpr int NQ = (PIECES + THREADS - 1) / THREADS;  // LDS-direct loads per wave per step
-    static_assert(PIECES % 64 == 0, "whole waves of pieces");
+    constexpr int THREADS = (CW + LW) * 64;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* alds = smem;                    // [NB][MT][A_ROW]
-    uint8_t* slds = smem + NB * MT * A_ROW;  // [TENSORS][BN][Kdim/32]
+    uint8_t* alds = smem;                   // [2][MT][A_ROW]
+    uint8_t* slds = smem + 2 * MT * A_ROW;  // [TENSORS][BN][Kdim/32]
 
     // ---- work item (XCD-aware): XCD x walks items [x*per, (x+1)*per)
     const int n_items = a.scalars[1] * a.nblk_n;
@@ -405,27 +484,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(GemmArgs a) {
     const int tile = item / a.nblk_n, nblk = item % a.nblk_n;
     const int4 td = a.tiles[tile];
     const int e = td.x, row0 = td.y, mrows = td.z;  // 1 <= mrows <= MT
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x;
     const int Kdim = a.Kdim, N = a.N, sb = Kdim >> 5;
     const int nb0 = nblk * BN;
-
-    // ---- A pieces of this wave: load q covers pieces c = ((wave*NQ + q)*64 + lane)
-    // mod PIECES (waves past the pieces repeat earlier ones: same bytes, same place),
-    // i.e. LDS row c/16, slot c%16, holding the row's 16-byte segment slot ^ (row%16).
-    // Rows past the tile re-read its last row; columns past Kdim are clamped when
-    // loaded and masked at use.
-    const uint16_t* asrc[NQ];
-    int aseg[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int c = ((wave * NQ + q) * 64 + lane) % PIECES;
-        const int r = c >> 4;
-        const int rc = min(r, mrows - 1);
-        const size_t row = (MODE == GATEUP) ? (size_t)(a.perm[row0 + rc] / a.K) : (size_t)(row0 + rc);
-        asrc[q] = a.A + row * (size_t)Kdim;
-        aseg[q] = 8 * ((c & 15) ^ (r & 15));
-    }
 
     // ---- scale bytes of the workgroup's rows (srows_real * sb contiguous bytes per
     // tensor, a multiple of 32, 16-byte aligned) -> LDS; note any byte equal to 255
@@ -433,7 +494,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(GemmArgs a) {
     const int spieces = (srows_real * sb) >> 4;
     const int stotal = SH::TENSORS * spieces;
     int has255 = 0;
-    for (int c0 = 0; c0 < stotal; c0 += 8 * THREADS) {  // one pass for rows up to 4096 columns
+    for (int c0 = 0; c0 < stotal; c0 += 8 * THREADS) {  // one pass for the usual sizes
         uint4 v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -456,15 +517,24 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(GemmArgs a) {
     }
     const bool exact = __syncthreads_or(has255) != 0 || (Kdim % KS) != 0;
 
+    if constexpr (LW > 0) {
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        if (wave >= CW) {  // wave-uniform
+            gemm_loader<MODE, MT, LW>(a, alds, row0, mrows, tid - CW * 64);
+            return;
+        }
+    }
     if (exact) {
-        gemm_tile<MODE, MT, WAVES, NB, MT / 16, true>(a, alds, slds, e, row0, mrows, nb0, asrc, aseg);
+        gemm_compute<MODE, MT, CW, LW, NBB, MT / 16, true>(a, alds, slds, e, row0, mrows, nb0);
         return;
     }
-    const int msub = (mrows + 15) >> 4;
-#define K3_TILE_CASE(MSV)                                                                         \
-    case MSV:                                                                                     \
-        if constexpr (MSV <= MT / 16)                                                             \
-            gemm_tile<MODE, MT, WAVES, NB, MSV, false>(a, alds, slds, e, row0, mrows, nb0, asrc, aseg); \
+    // tiles hold at most MT rows; the clamp keeps every compute wave on a path
+    // with the loader waves' barrier count even if that were ever violated
+    const int msub = min((mrows + 15) >> 4, MT / 16);
+#define K3_TILE_CASE(MSV)                                                                        \
+    case MSV:                                                                                    \
+        if constexpr (MSV <= MT / 16)                                                            \
+            gemm_compute<MODE, MT, CW, LW, NBB, MSV, false>(a, alds, slds, e, row0, mrows, nb0);      \
         break;
     switch (msub) {
         K3_TILE_CASE(1)
@@ -478,40 +548,33 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_kernel(GemmArgs a) {
         default: break;
     }
 #undef K3_TILE_CASE
-    (void)wave;
-    (void)lane;
 }
 
-template <int MODE, int MT, int WAVES, int NB>
+template <int MODE, int MT, int CW, int LW, int NBB>
 hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
-    using SH = GemmShape<MODE, WAVES>;
+    using SH = GemmShape<MODE, CW>;
     a.nblk_n = (a.N + SH::BN - 1) / SH::BN;
-    const size_t lds = gemm_lds_bytes(MT, NB, SH::SROWS, a.Kdim);
+    const size_t lds = gemm_lds_bytes(MT, 2, SH::SROWS, a.Kdim);
     const long max_items = (long)max_tiles * a.nblk_n;
     const dim3 grid((unsigned)(((max_items + N_XCD - 1) / N_XCD) * N_XCD));
-    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, WAVES, NB>);
+    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, LW, NBB>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_kernel<MODE, MT, WAVES, NB>), grid, dim3(WAVES * 64), lds, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, LW, NBB>), grid, dim3((CW + LW) * 64), lds, stream, a);
     return hipGetLastError();
 }
 
-constexpr size_t kLdsLimit = 160 * 1024;
-
-// 16-row tiles run eight waves per workgroup; 128-row tiles (128 accumulator
-// registers per lane) run four, one per SIMD.  The ring is four steps deep when
-// it fits in LDS beside the staged scales, else two.
-template <int MODE, int MT>
-hipError_t launch_gemm_mt(const GemmArgs& a, int max_tiles, hipStream_t stream) {
-    constexpr int WAVES = MT == 16 ? 8 : 4;
-    if (gemm_lds_bytes(MT, 4, GemmShape<MODE, WAVES>::SROWS, a.Kdim) <= kLdsLimit)
-        return launch_gemm_t<MODE, MT, WAVES, 4>(a, max_tiles, stream);
-    return launch_gemm_t<MODE, MT, WAVES, 2>(a, max_tiles, stream);
-}
-
+// Eight compute waves (two per SIMD) that also stage A.  16-row tiles: a 4-deep
+// weight ring.  96-row tiles (96 accumulator registers per lane): a 3-deep ring,
+// which is what fits two waves per SIMD.  LDS: two A buffers plus the staged
+// scales; when the scales of eight waves' rows do not fit (long rows, e.g. a
+// gate/up reduction of 8192), four waves with half the rows.
 template <int MODE>
 hipError_t launch_gemm(const GemmArgs& a, int mt, int max_tiles, hipStream_t stream) {
-    return mt == 16 ? launch_gemm_mt<MODE, 16>(a, max_tiles, stream) : launch_gemm_mt<MODE, 128>(a, max_tiles, stream);
+    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 0, 4>(a, max_tiles, stream);
+    if (gemm_lds_bytes(kTileRowsLarge, 2, GemmShape<MODE, 8>::SROWS, a.Kdim) <= kLdsLimit)
+        return launch_gemm_t<MODE, kTileRowsLarge, 8, 0, 3>(a, max_tiles, stream);
+    return launch_gemm_t<MODE, kTileRowsLarge, 4, 0, 3>(a, max_tiles, stream);
 }
 
 // -------------------------------------------------------------------------- combine

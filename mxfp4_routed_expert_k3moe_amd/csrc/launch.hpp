@@ -37,9 +37,10 @@ hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t
 // ------------------------------------------------------------------ chunk
 constexpr int kGroupTokens = 64;   // tokens per grouping block (one u64 mask bit each)
 // GEMM tile height (pairs of one expert per tile): 16 when experts average at most
-// 16 pairs, else 128.  A pure function of (T, K, E) so that the workspace size,
-// the tile list and the GEMM instantiation always agree.
-inline int tile_rows(int T, int K, int E) { return (long)T * K <= 16L * E ? 16 : 128; }
+// 16 pairs, else kTileRowsLarge.  A pure function of (T, K, E) so that the
+// workspace size, the tile list and the GEMM instantiation always agree.
+constexpr int kTileRowsLarge = 96;
+inline int tile_rows(int T, int K, int E) { return (long)T * K <= 16L * E ? 16 : kTileRowsLarge; }
 
 struct GroupBuffers {
     int nb;                 // grouping blocks = ceil(T / 64)
