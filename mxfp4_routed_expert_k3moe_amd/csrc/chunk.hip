@@ -46,6 +46,9 @@ constexpr int KS = 128;       // reduction columns per pipeline step
 constexpr int A_ROW = KS * 2;  // bytes per staged A row: 16 pieces of 16 bytes, XOR-swizzled
 constexpr int N_XCD = 8;
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* glb_ptr_t;
+
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -212,8 +215,9 @@ struct GemmShape {
 
 constexpr size_t kLdsLimit = 160 * 1024;
 
+// A buffers, the row table, and the scale rows rounded up to whole 1 KiB copies.
 inline size_t gemm_lds_bytes(int mt, int nb, int srows, int kdim) {
-    return (size_t)nb * mt * A_ROW + (size_t)srows * (kdim / 32);
+    return (size_t)nb * mt * A_ROW + (size_t)mt * 8 + (((size_t)srows * (kdim / 32) + 1023) & ~(size_t)1023);
 }
 
 __device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
@@ -290,61 +294,36 @@ __device__ __forceinline__ void for_steps(int nsteps, Body&& body) {
     steps_tail(body, t0, nsteps, std::make_integer_sequence<int, P - 1>{});
 }
 
-// Loader waves (LW > 0): keep A two steps ahead in registers; during step t store
-// A(t + 1) into LDS buffer (t + 1) % 2 (read last in step t - 1) and load A(t + 3)
-// into the register set A(t) used.  One barrier per step, matching the compute
-// waves' barriers one for one.
-template <int MODE, int MT, int LW>
-__device__ __forceinline__ void gemm_loader(const GemmArgs& a, uint8_t* alds, int row0, int mrows, int lt) {
-    using AP = APieces<MODE, MT, LW * 64>;
-    const int Kdim = a.Kdim;
-    const int nsteps = (Kdim + KS - 1) / KS;
+// Per-lane state of one work item that outlives the prologue: the activation
+// pieces this thread stages, the weight rows this lane streams, and both rings.
+template <int MODE, int MT, int CW, int NBB>
+struct GemmState {
+    using AP = APieces<MODE, MT, CW * 64>;
+    static_assert(NBB == 2 || NBB == 4, "ring depth must be a multiple of the two A register sets");
     AP ap;
-    ap.init(a, lt, row0, mrows);
-    uint4 areg[3][AP::SLOTS];
-    ap.load(areg[0], 0, Kdim);
-    ap.load(areg[1], min(1, nsteps - 1), Kdim);
-    ap.load(areg[2], min(2, nsteps - 1), Kdim);
-    ap.store(areg[0], alds, 0, Kdim);
-    lds_barrier();
-    // three register sets, four-step bodies: the set of step t is t % 3, tracked at
-    // run time and switched on (a uniform branch) so the arrays stay in registers
-    int set1 = 1;  // set holding A(t + 1)
-    for (int step = 0; step < nsteps; ++step) {
-        uint8_t* nbuf = alds + (size_t)((step + 1) & 1) * MT * A_ROW;
-        const int ahead = min(step + 3, nsteps - 1);
-        if (set1 == 1) {
-            ap.store(areg[1], nbuf, step + 1, Kdim);
-            ap.load(areg[0], ahead, Kdim);
-        } else if (set1 == 2) {
-            ap.store(areg[2], nbuf, step + 1, Kdim);
-            ap.load(areg[1], ahead, Kdim);
-        } else {
-            ap.store(areg[0], nbuf, step + 1, Kdim);
-            ap.load(areg[2], ahead, Kdim);
-        }
-        set1 = set1 == 2 ? 0 : set1 + 1;
-        lds_barrier();
-    }
-}
+    uint4 areg[2][AP::SLOTS];
+    const uint8_t* bq[4];  // weight rows in HBM
+    const uint8_t* bs[4];  // their scale rows in LDS
+    uint4 bring[NBB][4];
+};
 
-// The reduction of one work item by the compute waves, with the number of 16-row
+// The reduction of one work item after the prologue, with the number of 16-row
 // subtiles (MS) fixed at compile time so the step body is straight-line code.
 // EXACT adds the per-chunk s = 255 fix-up and the masking of weight columns past
 // Kdim; the fast body is taken when no staged scale byte is 255 and Kdim is a
 // multiple of 128.
 //
-// Per step t: load the weights of step t + NBB - 1 into the ring slot step t - 1
-// used, compute step t from LDS buffer t % 2 and ring slot t % NBB, barrier.  Without
-// loader waves (LW = 0) the compute waves also keep A one step ahead: load A(t + 1)
-// at the start of step t, store it into buffer (t + 1) % 2 at the end.
-template <int MODE, int MT, int CW, int LW, int NBB, int MS, bool EXACT>
-__device__ __forceinline__ void gemm_compute(const GemmArgs& a, uint8_t* alds, const uint8_t* slds, int e, int row0,
-                                             int mrows, int nb0) {
+// Per step t: load A(t + 2) into the register set A(t) used and the weights of
+// step t + NBB - 1 into the ring slot step t - 1 used; read the scale bytes of
+// step t + 1; compute step t from LDS buffer t % 2 and ring slot t % NBB; store
+// A(t + 1) into buffer (t + 1) % 2 (read last in step t - 1); barrier.  All loads
+// are ordinary vector loads, so the compiler's per-register waits stay exact
+// across the loop.
+template <int MODE, int MT, int CW, int NBB, int MS, bool EXACT>
+__device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT, CW, NBB>& st, uint8_t* alds,
+                                           const int32_t* rperm, const float* rw, int row0, int mrows, int nb0) {
     using SH = GemmShape<MODE, CW>;
-    using AP = APieces<MODE, MT, CW * 64>;
-    constexpr int WN = SH::WN, BN = SH::BN;
-
+    constexpr int WN = SH::WN;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lg = lane >> 4;
@@ -352,53 +331,34 @@ __device__ __forceinline__ void gemm_compute(const GemmArgs& a, uint8_t* alds, c
     const int n0 = nb0 + wave * WN;
     const int nsteps = (Kdim + KS - 1) / KS;
 
-    // weight rows of this lane (clamped to real rows; columns past N are computed
-    // from a repeated row and never stored)
-    const size_t qrow = (size_t)Kdim >> 1;
-    const uint8_t* bq[4];
-    const uint8_t* bs[4];  // scale rows in LDS
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-        const int tsel = (MODE == GATEUP) ? (ns >> 1) : 0;
-        const int r = (MODE == GATEUP) ? n0 + 16 * (ns & 1) + ln : n0 + 16 * ns + ln;
-        const int row = min(r, N - 1);
-        const uint8_t* q = (tsel == 0) ? a.q0 + (size_t)e * a.q0_stride : a.q1 + (size_t)e * a.q1_stride;
-        bq[ns] = q + (size_t)row * qrow;
-        bs[ns] = slds + (size_t)tsel * BN * sb + (size_t)(row - nb0) * sb;
-    }
-    uint4 bring[NBB][4];
-#define K3_ISSUE_B(SLOT, STEP)                                                                   \
-    do {                                                                                         \
-        const int col_ = min((STEP) * KS + 32 * lg, Kdim - 32);                                  \
-        _Pragma("unroll") for (int ns = 0; ns < 4; ++ns) bring[SLOT][ns] =                       \
-            *reinterpret_cast<const uint4*>(bq[ns] + (col_ >> 1));                               \
-    } while (0)
-
-    AP ap;
-    uint4 areg[AP::SLOTS];
-    if constexpr (LW == 0) ap.init(a, tid, row0, mrows);
-
     f32x4 acc[MS][4];
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) acc[i][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (LW == 0) ap.load(areg, 0, Kdim);
+    uint32_t scn[4];  // scale bytes of the next step
 #pragma unroll
-    for (int u = 0; u < NBB - 1; ++u) K3_ISSUE_B(u, min(u, nsteps - 1));
-    if constexpr (LW == 0) ap.store(areg, alds, 0, Kdim);
-    lds_barrier();
+    for (int ns = 0; ns < 4; ++ns) scn[ns] = st.bs[ns][min(lg, sb - 1)];
 
     for_steps<NBB>(nsteps, [&](auto uc, const int step) {
         constexpr int u = decltype(uc)::value;
-        if constexpr (LW == 0) ap.load(areg, min(step + 1, nsteps - 1), Kdim);
-        K3_ISSUE_B((u + NBB - 1) % NBB, min(step + NBB - 1, nsteps - 1));
-        const uint8_t* abuf = alds + (size_t)(step & 1) * MT * A_ROW;
-        const int sc_idx = min(4 * step + lg, sb - 1);
+        st.ap.load(st.areg[u & 1], min(step + 2, nsteps - 1), Kdim);
+        {
+            const int col = min((step + NBB - 1) * KS + 32 * lg, Kdim - 32);
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns)
+                st.bring[(u + NBB - 1) % NBB][ns] = *reinterpret_cast<const uint4*>(st.bq[ns] + (col >> 1));
+        }
         uint32_t sc[4];
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) sc[ns] = bs[ns][sc_idx];
+        for (int ns = 0; ns < 4; ++ns) sc[ns] = scn[ns];
+        {
+            const int nidx = min(4 * (step + 1) + lg, sb - 1);
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) scn[ns] = st.bs[ns][nidx];
+        }
+        const uint8_t* abuf = alds + (size_t)(u & 1) * MT * A_ROW;
         const bool valid = step * KS + 32 * lg < Kdim;
         float scf[4];
 #pragma unroll
@@ -409,9 +369,9 @@ __device__ __forceinline__ void gemm_compute(const GemmArgs& a, uint8_t* alds, c
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
                 if constexpr (EXACT)
-                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16(valid ? pick(bring[u][ns], j) : 0u, sc[ns]));
+                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16(valid ? pick(st.bring[u][ns], j) : 0u, sc[ns]));
                 else
-                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16_nofix(pick(bring[u][ns], j), scf[ns]));
+                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16_nofix(pick(st.bring[u][ns], j), scf[ns]));
             }
 #pragma unroll
             for (int i = 0; i < MS; ++i) {
@@ -425,10 +385,9 @@ __device__ __forceinline__ void gemm_compute(const GemmArgs& a, uint8_t* alds, c
             // (registers for them would push the weight ring out of VGPRs)
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (LW == 0) ap.store(areg, alds + (size_t)((step + 1) & 1) * MT * A_ROW, step + 1, Kdim);
+        st.ap.store(st.areg[(u + 1) & 1], alds + (size_t)((step + 1) & 1) * MT * A_ROW, step + 1, Kdim);
         lds_barrier();
     });
-#undef K3_ISSUE_B
 
     // epilogue.  C layout: lane l, register r -> row 4*(l/16)+r, column l%16.
     if (n0 >= N) return;
@@ -444,8 +403,8 @@ __device__ __forceinline__ void gemm_compute(const GemmArgs& a, uint8_t* alds, c
                 for (int ns = 0; ns < 2; ++ns)
                     hrow[n0 + 16 * ns + ln] = (uint16_t)f32_to_bf16_bits(situ_fast(acc[i][ns][r], acc[i][ns + 2][r]));
             } else {
-                const int p = a.perm[row0 + m];
-                const float wp = a.wts[p];
+                const int p = rperm[m];
+                const float wp = rw[m];
                 float* yrow = a.y_out + (size_t)p * N;
 #pragma unroll
                 for (int ns = 0; ns < 4; ++ns)
@@ -457,23 +416,26 @@ __device__ __forceinline__ void gemm_compute(const GemmArgs& a, uint8_t* alds, c
 
 // One workgroup = one (tile of <= MT pair rows of one expert, block of BN output
 // columns), the whole reduction, in 128-column steps:
-//   - CW compute waves each stream the 16-byte weight chunks of their four 16-row
-//     subtiles through a 4-deep register ring and convert them in registers into
-//     MFMA B operands; A fragments come from a double-buffered LDS tile (16-byte
-//     pieces XOR-swizzled by row);
-//   - LW loader waves (128-row tiles) keep the tile's activation rows two steps
-//     ahead in registers and store them into LDS, so the compute waves' loads are
-//     weights only; with LW = 0 (16-row tiles) the compute waves do it themselves;
+//   - each of CW waves streams the 16-byte weight chunks of its four 16-row
+//     subtiles through an NBB-deep register ring and converts them in registers
+//     into MFMA B operands;
+//   - the tile's activation rows (shared by all waves) are loaded two steps
+//     ahead into registers and stored into a double-buffered LDS tile, 16-byte
+//     pieces XOR-swizzled by row; A fragments are read from there;
 //   - one barrier per step; the scale bytes of the workgroup's weight rows are
-//     copied to LDS up front.
-template <int MODE, int MT, int CW, int LW, int NBB>
-__global__ __launch_bounds__((CW + LW) * 64, 1) void gemm_kernel(GemmArgs a) {
+//     copied to LDS up front, while the first activation and weight loads are
+//     already in flight.
+template <int MODE, int MT, int CW, int NBB>
+__global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
     using SH = GemmShape<MODE, CW>;
-    constexpr int BN = SH::BN;
-    constexpr int THREADS = (CW + LW) * 64;
+    using ST = GemmState<MODE, MT, CW, NBB>;
+    constexpr int WN = SH::WN, BN = SH::BN;
+    constexpr int THREADS = CW * 64;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* alds = smem;                   // [2][MT][A_ROW]
-    uint8_t* slds = smem + 2 * MT * A_ROW;  // [TENSORS][BN][Kdim/32]
+    int32_t* rperm = reinterpret_cast<int32_t*>(smem + 2 * MT * A_ROW);  // [MT] pair of each tile row
+    float* rw = reinterpret_cast<float*>(rperm + MT);                      // [MT] its routing weight
+    uint8_t* slds = reinterpret_cast<uint8_t*>(rw + MT);                   // [TENSORS][rows][Kdim/32]
 
     // ---- work item (XCD-aware): XCD x walks items [x*per, (x+1)*per)
     const int n_items = a.scalars[1] * a.nblk_n;
@@ -484,57 +446,88 @@ __global__ __launch_bounds__((CW + LW) * 64, 1) void gemm_kernel(GemmArgs a) {
     const int tile = item / a.nblk_n, nblk = item % a.nblk_n;
     const int4 td = a.tiles[tile];
     const int e = td.x, row0 = td.y, mrows = td.z;  // 1 <= mrows <= MT
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ln = lane & 15;
     const int Kdim = a.Kdim, N = a.N, sb = Kdim >> 5;
     const int nb0 = nblk * BN;
+    const int n0 = nb0 + wave * WN;
+    const int nsteps = (Kdim + KS - 1) / KS;
 
-    // ---- scale bytes of the workgroup's rows (srows_real * sb contiguous bytes per
-    // tensor, a multiple of 32, 16-byte aligned) -> LDS; note any byte equal to 255
+    ST st;
+    st.ap.init(a, tid, row0, mrows);  // pair ids of the staged rows (first loads)
+
+    // ---- scale bytes of the workgroup's rows: srows_real * sb contiguous bytes per
+    // tensor (a multiple of 32, 16-byte aligned), copied global -> LDS directly
+    // (global_load_lds) with tensor 1 right after tensor 0, so 16-byte piece c lands
+    // at byte 16*c.  A wave whose 64 pieces all lie past the end skips the copy;
+    // the lanes of the last wave that run past it re-copy the last piece into the
+    // rounded-up tail of the region.
     const int srows_real = min(BN, N - nb0);
     const int spieces = (srows_real * sb) >> 4;
     const int stotal = SH::TENSORS * spieces;
-    int has255 = 0;
-    for (int c0 = 0; c0 < stotal; c0 += 8 * THREADS) {  // one pass for the usual sizes
-        uint4 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int cc = min(c0 + k * THREADS + tid, stotal - 1);
+    for (int c0 = 0; c0 < stotal; c0 += THREADS) {
+        if (c0 + wave * 64 < stotal) {  // wave-uniform
+            const int cc = min(c0 + tid, stotal - 1);
             const int tsel = cc >= spieces ? 1 : 0, pc = cc - tsel * spieces;
             const uint8_t* sbase = tsel == 0 ? a.s0 + (size_t)e * a.s0_stride : a.s1 + (size_t)e * a.s1_stride;
-            v[k] = *reinterpret_cast<const uint4*>(sbase + (size_t)nb0 * sb + 16 * pc);
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)(sbase + (size_t)nb0 * sb + 16 * pc),
+                                             (lds_ptr_t)(slds + 16 * (c0 + wave * 64)), 16, 0, 0);
         }
+    }
+
+    // ---- weight rows of this lane (clamped to real rows; columns past N are
+    // computed from a repeated row and never stored), and the first ring steps
+    const size_t qrow = (size_t)Kdim >> 1;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int c = c0 + k * THREADS + tid;
-            if (c < stotal) {
-                const int tsel = c >= spieces ? 1 : 0, pc = c - tsel * spieces;
-                *reinterpret_cast<uint4*>(slds + (size_t)tsel * BN * sb + 16 * pc) = v[k];
-                const uint32_t w4[4] = {~v[k].x, ~v[k].y, ~v[k].z, ~v[k].w};  // 255 -> zero byte
+    for (int ns = 0; ns < 4; ++ns) {
+        const int tsel = (MODE == GATEUP) ? (ns >> 1) : 0;
+        const int r = (MODE == GATEUP) ? n0 + 16 * (ns & 1) + ln : n0 + 16 * ns + ln;
+        const int row = min(r, N - 1);
+        const uint8_t* q = (tsel == 0) ? a.q0 + (size_t)e * a.q0_stride : a.q1 + (size_t)e * a.q1_stride;
+        st.bq[ns] = q + (size_t)row * qrow;
+        st.bs[ns] = slds + (size_t)tsel * srows_real * sb + (size_t)(row - nb0) * sb;
+    }
+    {
+        const int lg = lane >> 4;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) has255 |= ((w4[d] - 0x01010101u) & ~w4[d] & 0x80808080u) != 0u;
-            }
+        for (int u = 0; u < NBB - 1; ++u) {
+            const int col = min(min(u, nsteps - 1) * KS + 32 * lg, Kdim - 32);
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) st.bring[u][ns] = *reinterpret_cast<const uint4*>(st.bq[ns] + (col >> 1));
         }
+    }
+    st.ap.load(st.areg[0], 0, Kdim);
+    st.ap.load(st.areg[1], min(1, nsteps - 1), Kdim);
+    if (MODE == DOWN && tid < mrows) {  // pair id and routing weight of each tile row
+        const int p = a.perm[row0 + tid];
+        rperm[tid] = p;
+        rw[tid] = a.wts[p];
+    }
+    st.ap.store(st.areg[0], alds, 0, Kdim);
+    __syncthreads();  // scales, the first A buffer and the row table are in LDS
+
+    // ---- any scale byte equal to 255 in the staged rows?
+    int has255 = 0;
+    for (int c = tid; c < stotal; c += THREADS) {
+        const uint4 v = *reinterpret_cast<const uint4*>(slds + 16 * c);
+        const uint32_t w4[4] = {~v.x, ~v.y, ~v.z, ~v.w};  // 255 -> zero byte
+#pragma unroll
+        for (int d = 0; d < 4; ++d) has255 |= ((w4[d] - 0x01010101u) & ~w4[d] & 0x80808080u) != 0u;
     }
     const bool exact = __syncthreads_or(has255) != 0 || (Kdim % KS) != 0;
 
-    if constexpr (LW > 0) {
-        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        if (wave >= CW) {  // wave-uniform
-            gemm_loader<MODE, MT, LW>(a, alds, row0, mrows, tid - CW * 64);
-            return;
-        }
-    }
     if (exact) {
-        gemm_compute<MODE, MT, CW, LW, NBB, MT / 16, true>(a, alds, slds, e, row0, mrows, nb0);
+        gemm_steps<MODE, MT, CW, NBB, MT / 16, true>(a, st, alds, rperm, rw, row0, mrows, nb0);
         return;
     }
-    // tiles hold at most MT rows; the clamp keeps every compute wave on a path
-    // with the loader waves' barrier count even if that were ever violated
+    // tiles hold at most MT rows; the clamp keeps every wave on a path with the
+    // same barrier count even if that were ever violated
     const int msub = min((mrows + 15) >> 4, MT / 16);
-#define K3_TILE_CASE(MSV)                                                                        \
-    case MSV:                                                                                    \
-        if constexpr (MSV <= MT / 16)                                                            \
-            gemm_compute<MODE, MT, CW, LW, NBB, MSV, false>(a, alds, slds, e, row0, mrows, nb0);      \
+#define K3_TILE_CASE(MSV)                                                                       \
+    case MSV:                                                                                   \
+        if constexpr (MSV <= MT / 16)                                                           \
+            gemm_steps<MODE, MT, CW, NBB, MSV, false>(a, st, alds, rperm, rw, row0, mrows, nb0); \
         break;
     switch (msub) {
         K3_TILE_CASE(1)
@@ -550,31 +543,31 @@ __global__ __launch_bounds__((CW + LW) * 64, 1) void gemm_kernel(GemmArgs a) {
 #undef K3_TILE_CASE
 }
 
-template <int MODE, int MT, int CW, int LW, int NBB>
+template <int MODE, int MT, int CW, int NBB>
 hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
     using SH = GemmShape<MODE, CW>;
     a.nblk_n = (a.N + SH::BN - 1) / SH::BN;
     const size_t lds = gemm_lds_bytes(MT, 2, SH::SROWS, a.Kdim);
     const long max_items = (long)max_tiles * a.nblk_n;
     const dim3 grid((unsigned)(((max_items + N_XCD - 1) / N_XCD) * N_XCD));
-    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, LW, NBB>);
+    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, NBB>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, LW, NBB>), grid, dim3((CW + LW) * 64), lds, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, NBB>), grid, dim3(CW * 64), lds, stream, a);
     return hipGetLastError();
 }
 
-// Eight compute waves (two per SIMD) that also stage A.  16-row tiles: a 4-deep
-// weight ring.  96-row tiles (96 accumulator registers per lane): a 3-deep ring,
-// which is what fits two waves per SIMD.  LDS: two A buffers plus the staged
-// scales; when the scales of eight waves' rows do not fit (long rows, e.g. a
-// gate/up reduction of 8192), four waves with half the rows.
+// Eight waves (two per SIMD).  16-row tiles: a 4-deep weight ring.  96-row tiles
+// (96 accumulator registers per lane): a 2-deep ring, which is what fits two
+// waves per SIMD beside two sets of activation registers.  LDS: two A buffers plus
+// the staged scales; when the scales of eight waves' rows do not fit (long rows,
+// e.g. a gate/up reduction of 8192), four waves with half the rows.
 template <int MODE>
 hipError_t launch_gemm(const GemmArgs& a, int mt, int max_tiles, hipStream_t stream) {
-    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 0, 4>(a, max_tiles, stream);
+    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 4>(a, max_tiles, stream);
     if (gemm_lds_bytes(kTileRowsLarge, 2, GemmShape<MODE, 8>::SROWS, a.Kdim) <= kLdsLimit)
-        return launch_gemm_t<MODE, kTileRowsLarge, 8, 0, 3>(a, max_tiles, stream);
-    return launch_gemm_t<MODE, kTileRowsLarge, 4, 0, 3>(a, max_tiles, stream);
+        return launch_gemm_t<MODE, kTileRowsLarge, 8, 2>(a, max_tiles, stream);
+    return launch_gemm_t<MODE, kTileRowsLarge, 4, 2>(a, max_tiles, stream);
 }
 
 // -------------------------------------------------------------------------- combine
