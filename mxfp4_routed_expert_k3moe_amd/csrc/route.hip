@@ -11,9 +11,9 @@
 // key and, among equal keys, the lower id.
 //
 // One workgroup of 4 waves per token: wave w holds experts [w*Q, (w+1)*Q) in
-// registers and finds their top-K with K rounds of a wave max (the owning lane
-// retires each winner); wave 0 then merges the 4*K survivors the same way and
-// renormalizes the selected raw scores.
+// registers and finds their top-K with K rounds of a 32-bit wave max on the key
+// (a second reduction on the id only when keys tie); the 4*K survivors then rank
+// themselves against each other in parallel.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -30,114 +30,132 @@ __device__ __forceinline__ uint32_t key_order(float k) {
 
 __device__ __forceinline__ double sigmoid_d(float l) { return 1.0 / (1.0 + exp(-(double)l)); }
 
-template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) {
-    return a > b ? a : b;
-}
-
-__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-    return ((unsigned long long)hi << 32) | lo;
-}
-
+// Maximum of a 32-bit unsigned value over the 64 lanes, returned to every lane:
+// DPP within each row of 16 (swap neighbours, swap pairs, rotate by 4, rotate by
+// 8), then row 0 -> 1 and row 2 -> 3 (row_bcast15), rows 0-1 -> 2-3
+// (row_bcast31); lane 63 holds the maximum.  Rows outside a broadcast's row mask
+// keep their own value.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ unsigned long long dpp_keep_u64(unsigned long long v) {
-    // rows outside ROW_MASK keep their own value
-    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xF,
-                                               false);
-    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+    v = max(v, dpp_u32<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+    v = max(v, dpp_u32<0x124, 0xF>(v));  // row_ror:4
+    v = max(v, dpp_u32<0x128, 0xF>(v));  // row_ror:8
+    v = max(v, dpp_u32<0x142, 0xA>(v));  // row_bcast:15 into rows 1, 3
+    v = max(v, dpp_u32<0x143, 0xC>(v));  // row_bcast:31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// A candidate: order-preserving key bits (high word) and ~id (low word), so one
+// unsigned comparison ranks larger keys first and, among equal keys, lower ids.
+__device__ __forceinline__ unsigned long long make_code(uint32_t korder, int e) {
+    return ((unsigned long long)korder << 32) | (unsigned long long)(~(uint32_t)e);
 }
 
-// Maximum over the 64 lanes, returned to every lane: DPP within each row of 16
-// (swap neighbours, swap pairs, rotate by 4, rotate by 8), then row 0 -> 1 and
-// row 2 -> 3 (row_bcast15), rows 0-1 -> 2-3 (row_bcast31); lane 63 holds the
-// maximum, which readlane hands to the whole wave.
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-    v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
-    v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
-    v = max_u64(v, dpp_u64<0x124>(v));  // row_ror:4
-    v = max_u64(v, dpp_u64<0x128>(v));  // row_ror:8
-    v = max_u64(v, dpp_keep_u64<0x142, 0xA>(v));  // row_bcast:15 into rows 1, 3
-    v = max_u64(v, dpp_keep_u64<0x143, 0xC>(v));  // row_bcast:31 into rows 2, 3
-    return readlane_u64(v, 63);
-}
-
-// K rounds of a wave max over per-lane code arrays; lane k keeps winner k in
-// `mine` and, if `out` is given, lane 0 also writes it to out[k].  Codes equal to
-// 0 are absent (a round that finds none yields 0).
+// Top-K of the codes a wave holds (PL per lane, 0 = absent), K rounds: each lane
+// offers its best code; the wave maximum of the key words picks the winning key,
+// and only when several lanes offer that key a second reduction picks the lowest
+// id among them.  The winner's lane retires it.  Winner k goes to out[k].
 template <int PL>
-__device__ __forceinline__ void wave_topk(unsigned long long (&code)[PL], int K, int lane,
-                                          unsigned long long* out, unsigned long long& mine) {
+__device__ __forceinline__ void wave_topk(unsigned long long (&code)[PL], int K, int lane, unsigned long long* out) {
+    unsigned long long head = 0ull;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) head = code[j] > head ? code[j] : head;
     for (int k = 0; k < K; ++k) {
-        unsigned long long best = 0ull;
+        const uint32_t hk = (uint32_t)(head >> 32);
+        const uint32_t mk = wave_max_u32(hk);
+        const unsigned long long tie = __ballot(hk == mk);
+        uint32_t win_lo;
+        int win_lane;
+        if (__builtin_expect(__popcll(tie) == 1, 1)) {
+            win_lane = __ffsll((long long)tie) - 1;
+            win_lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)head, win_lane);
+        } else {  // equal keys in several lanes: the lowest id has the largest ~id
+            const uint32_t lo = (hk == mk) ? (uint32_t)head : 0u;
+            win_lo = wave_max_u32(lo);
+            win_lane = __ffsll((long long)__ballot(hk == mk && (uint32_t)head == win_lo)) - 1;
+        }
+        const unsigned long long best = ((unsigned long long)mk << 32) | win_lo;
+        if (lane == 0) out[k] = (mk == 0u && win_lo == 0u) ? 0ull : best;
+        if (lane == win_lane && head != 0ull) {  // retire it and find this lane's next best
+            unsigned long long nh = 0ull;
 #pragma unroll
-        for (int j = 0; j < PL; ++j) best = code[j] > best ? code[j] : best;
-        best = wave_max_u64(best);
-        if (out != nullptr && lane == 0) out[k] = best;
-        if (lane == k) mine = best;
-        if (best != 0ull) {
-#pragma unroll
-            for (int j = 0; j < PL; ++j)
-                if (code[j] == best) code[j] = 0ull;  // codes are unique (they carry the id)
+            for (int j = 0; j < PL; ++j) {
+                if (code[j] == head) code[j] = 0ull;
+                nh = code[j] > nh ? code[j] : nh;
+            }
+            head = nh;
         }
     }
 }
 
+// One workgroup of 4 waves per token: wave w holds experts [w*Q, (w+1)*Q) and finds
+// their top-K; then every survivor counts the survivors that beat it (its rank),
+// and the K best take the output slots in rank order.  The routing weights
+// renormalize the selected raw sigmoids, summed in slot order in double.
 template <int PL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E, int K,
                                                     int32_t* __restrict__ idx, float* __restrict__ w) {
     __shared__ unsigned long long cand[4 * K3MOE_MAX_K_DEV];
+    __shared__ double sel_sig[K3MOE_MAX_K_DEV];
+    __shared__ int sel_id[K3MOE_MAX_K_DEV];
     extern __shared__ double sig_e[];  // [E] double sigmoid of each expert's logit
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x;
     const float* l = logits + (size_t)t * E;
     const int Q = (E + 3) / 4;  // experts per wave
 
+    float lv[PL], bv[PL];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {  // issue every load before the first use
+        const int i = lane + 64 * j, e = wave * Q + i;
+        const bool ok = i < Q && e < E;
+        lv[j] = ok ? l[e] : 0.f;
+        bv[j] = ok ? bias[e] : 0.f;
+    }
     unsigned long long code[PL];
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
-        const int i = lane + 64 * j;
-        const int e = wave * Q + i;
+        const int i = lane + 64 * j, e = wave * Q + i;
         code[j] = 0ull;
         if (i < Q && e < E) {
-            const double sd = sigmoid_d(l[e]);
+            const double sd = sigmoid_d(lv[j]);
             sig_e[e] = sd;
-            float key = (float)sd + bias[e];
+            float key = (float)sd + bv[j];
             if (key != key) key = -INFINITY;
             if (key == 0.0f) key = 0.0f;  // -0 ranks as +0
-            code[j] = ((unsigned long long)key_order(key) << 32) | (unsigned long long)(~(uint32_t)e);
+            code[j] = make_code(key_order(key), e);
         }
     }
-    unsigned long long mine = 0ull;
-    wave_topk<PL>(code, K, lane, cand + wave * K, mine);
-    __syncthreads();  // the only barrier: survivors and sigmoids are in LDS
-    if (wave != 0) return;
+    wave_topk<PL>(code, K, lane, cand + wave * K);
+    __syncthreads();  // survivors and sigmoids are in LDS
 
-    unsigned long long mc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = lane + 64 * j;
-        mc[j] = (i < 4 * K) ? cand[i] : 0ull;
+    // rank of each survivor among all 4K (codes are unique; 0 = absent)
+    const int nc = 4 * K;
+    if ((int)threadIdx.x < nc) {
+        const unsigned long long c = cand[threadIdx.x];
+        if (c != 0ull) {
+            int rank = 0;
+            for (int i = 0; i < nc; ++i) rank += cand[i] > c;
+            if (rank < K) {
+                const int e = (int)(~(uint32_t)(c & 0xFFFFFFFFull));
+                sel_id[rank] = e;
+                sel_sig[rank] = sig_e[e];
+            }
+        }
     }
-    wave_topk<4>(mc, K, lane, nullptr, mine);
-    const int my_sel = (lane < K) ? (int)(~(uint32_t)(mine & 0xFFFFFFFFull)) : 0;
-
-    // raw-score renormalization, summed in slot order in double
-    const double sig = (lane < K) ? sig_e[my_sel] : 0.0;
-    double denom = 0.0;
-    for (int k = 0; k < K; ++k) denom += __shfl(sig, k, kWave);
+    __syncthreads();
+    if (wave != 0) return;
+    double denom = 0.0;  // slot order, as in the definition
+    for (int k = 0; k < K; ++k) denom += sel_sig[k];
     if (lane < K) {
-        idx[(size_t)t * K + lane] = my_sel;
-        w[(size_t)t * K + lane] = (float)(sig / denom);
+        idx[(size_t)t * K + lane] = sel_id[lane];
+        w[(size_t)t * K + lane] = (float)(sel_sig[lane] / denom);
     }
 }
 
