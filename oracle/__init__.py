@@ -58,6 +58,9 @@ def _bind(path: str):
     lib.k3o_route.restype = None
     lib.k3o_route.argtypes = [_F32P, _F32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                               _I32P, _F32P, _F64P]
+    lib.k3o_route_topp.restype = None
+    lib.k3o_route_topp.argtypes = [_F32P, _F32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                   _I32P, _F32P, _I32P, _F64P]
     lib.k3o_situ.restype = ctypes.c_double
     lib.k3o_situ.argtypes = [ctypes.c_double, ctypes.c_double]
     lib.k3o_situ_beta.restype = ctypes.c_double
@@ -129,6 +132,24 @@ class Oracle:
         self.lib.k3o_route(logits, bias, T, E, K, idx, w, gap)
         return idx, w, gap
 
+    def route_topp(self, logits: np.ndarray, bias: np.ndarray, K: int,
+                   p: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+        """Router plus top-p pruning: ``(idx, w, n_kept [T] int32, gap)``; pruned
+        slots (after the kept ones) hold id -1 and weight 0."""
+        logits = _c(logits, np.float32)
+        if logits.ndim == 1:
+            logits = logits[None]
+        T, E = logits.shape
+        bias = _c(bias, np.float32)
+        if bias.shape != (E,) or not 1 <= K <= E:
+            raise ValueError("bad route arguments")
+        idx = np.empty((T, K), dtype=np.int32)
+        w = np.empty((T, K), dtype=np.float32)
+        n_kept = np.empty(T, dtype=np.int32)
+        gap = np.empty(T, dtype=np.float64)
+        self.lib.k3o_route_topp(logits, bias, T, E, K, float(p), idx, w, n_kept, gap)
+        return idx, w, n_kept, gap
+
     # --------------------------------------------------------------------- activation
     def situ(self, g: float, u: float) -> float:
         return self.lib.k3o_situ(float(g), float(u))
@@ -188,12 +209,13 @@ class Oracle:
         T, K = idx.shape
         counts = np.empty(E, dtype=np.int32)
         offsets = np.empty(E + 1, dtype=np.int32)
-        perm = np.empty(T * K, dtype=np.int32)
+        perm = np.full(T * K, -1, dtype=np.int32)
         uniq = np.full(E, -1, dtype=np.int32)
         nu = ctypes.c_int32(0)
         rc = self.lib.k3o_group(idx, T, K, E, counts, offsets, perm, uniq, ctypes.byref(nu))
         if rc != 0:
             raise ValueError("expert index out of range")
+        perm = perm[:offsets[E]].copy()  # pruned slots are not placed
         return {"counts": counts, "offsets": offsets, "perm": perm,
                 "uniq": uniq[:nu.value].copy(), "n_unique": int(nu.value)}
 
@@ -225,6 +247,10 @@ def dequant(q, s):
 
 def route(logits, bias, K):
     return instance().route(logits, bias, K)
+
+
+def route_topp(logits, bias, K, p):
+    return instance().route_topp(logits, bias, K, p)
 
 
 def situ(g, u):

@@ -101,22 +101,28 @@ static int cand_cmp(const void *pa, const void *pb)
  * A NaN key counts as -inf.  gap[t] = key_(K) - key_(K+1) (inf when K == E) is
  * the selection's margin, reported so near-ties can be counted.
  * logits [T, E], bias [E]; idx [T, K] int32, w [T, K] fp32, gap [T] (nullable). */
+/* Scores and the top-K candidates (descending key, ties to the lower id) of one
+ * token; c[0..K-1] is the selection in slot order. */
+static void select_token(const float *l, const float *bias, int32_t E, cand_t *c, double *score)
+{
+    for (int32_t e = 0; e < E; ++e) {
+        score[e] = sigmoid((double)l[e]);
+        float s32 = (float)score[e];
+        float key = s32 + bias[e];
+        if (isnan(key)) key = -INFINITY;
+        c[e].key = key;
+        c[e].id = e;
+    }
+    qsort(c, (size_t)E, sizeof(cand_t), cand_cmp);
+}
+
 void k3o_route(const float *logits, const float *bias, int32_t T, int32_t E, int32_t K,
                int32_t *idx, float *w, double *gap)
 {
     cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)E);
     double *score = (double *)malloc(sizeof(double) * (size_t)E);
     for (int32_t t = 0; t < T; ++t) {
-        const float *l = logits + (int64_t)t * E;
-        for (int32_t e = 0; e < E; ++e) {
-            score[e] = sigmoid((double)l[e]);
-            float s32 = (float)score[e];
-            float key = s32 + bias[e];
-            if (isnan(key)) key = -INFINITY;
-            c[e].key = key;
-            c[e].id = e;
-        }
-        qsort(c, (size_t)E, sizeof(cand_t), cand_cmp);
+        select_token(logits + (int64_t)t * E, bias, E, c, score);
         double denom = 0.0;
         for (int32_t k = 0; k < K; ++k) denom += score[c[k].id];
         for (int32_t k = 0; k < K; ++k) {
@@ -127,6 +133,75 @@ void k3o_route(const float *logits, const float *bias, int32_t T, int32_t E, int
     }
     free(c);
     free(score);
+}
+
+/* The router followed by top-p pruning ([PR676] K3_TOPP paragraph; [PR684] engine
+ * commit, K3_TOPP bullet): of the K selected experts, keep those with the largest
+ * routing weights until their cumulative weight reaches p, drop the low-weight
+ * tail, and renormalize the kept raw scores.  Readings of the rule:
+ *   - weight order: descending raw score sigma (equal scores: lower slot first);
+ *   - kept count m: the smallest m whose running sum of scores in that order
+ *     reaches p * S, S = sum of the K scores in slot order (double; the running
+ *     sum adds in weight order); so the expert that crosses p is kept, and m >= 1;
+ *   - p <= 0 or p >= 1 turns pruning off (m = K): the result equals k3o_route;
+ *   - output: the kept experts in their original slot order in slots 0..m-1,
+ *     w = score / (sum of kept scores in slot order); slots m..K-1 hold id -1
+ *     (pruned) and weight 0.
+ * n_kept [T] (nullable) receives m; gap as in k3o_route. */
+void k3o_route_topp(const float *logits, const float *bias, int32_t T, int32_t E, int32_t K, double p,
+                    int32_t *idx, float *w, int32_t *n_kept, double *gap)
+{
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)E);
+    double *score = (double *)malloc(sizeof(double) * (size_t)E);
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    int *kept = (int *)malloc(sizeof(int) * (size_t)K);
+    for (int32_t t = 0; t < T; ++t) {
+        select_token(logits + (int64_t)t * E, bias, E, c, score);
+        double S = 0.0;
+        for (int32_t k = 0; k < K; ++k) S += score[c[k].id];
+        int32_t m = K;
+        if (p > 0.0 && p < 1.0) {
+            /* slots in weight order: insertion sort, stable, larger score first */
+            for (int32_t k = 0; k < K; ++k) {
+                int32_t j = k;
+                while (j > 0 && score[c[order[j - 1]].id] < score[c[k].id]) {
+                    order[j] = order[j - 1];
+                    --j;
+                }
+                order[j] = k;
+            }
+            const double thr = p * S;
+            double cum = 0.0;
+            for (m = 0; m < K;) {
+                cum += score[c[order[m]].id];
+                ++m;
+                if (cum >= thr) break;
+            }
+        }
+        for (int32_t k = 0; k < K; ++k) kept[k] = (m == K);
+        if (m < K)
+            for (int32_t r = 0; r < m; ++r) kept[order[r]] = 1;
+        double Sk = 0.0;
+        for (int32_t k = 0; k < K; ++k)
+            if (kept[k]) Sk += score[c[k].id];
+        int32_t j = 0;
+        for (int32_t k = 0; k < K; ++k) {
+            if (!kept[k]) continue;
+            idx[(int64_t)t * K + j] = c[k].id;
+            w[(int64_t)t * K + j] = (float)(score[c[k].id] / Sk);
+            ++j;
+        }
+        for (; j < K; ++j) {
+            idx[(int64_t)t * K + j] = -1;
+            w[(int64_t)t * K + j] = 0.0f;
+        }
+        if (n_kept) n_kept[t] = m;
+        if (gap) gap[t] = (K < E) ? (double)c[K - 1].key - (double)c[K].key : INFINITY;
+    }
+    free(c);
+    free(score);
+    free(order);
+    free(kept);
 }
 
 /* -------------------------------------------------------------------- activation */
@@ -180,6 +255,7 @@ void k3o_expert(const float *Wg, const float *Wu, const float *Wd, int32_t D, in
 
 /* The routed-expert block for T tokens given their routing (idx [T,K], w [T,K]):
  *   y_t = sum_{k=0}^{K-1} w_{t,k} * expert_{idx[t,k]}(x_t)     (double, k order)
+ * A slot holding id -1 was pruned (k3o_route_topp) and contributes nothing.
  * Weights: gq/uq [E, F, D/2], gs/us [E, F, D/32], dq [E, D, F/2], ds [E, D, F/32].
  * Each token is computed exactly as it would be alone; the loop visits the union
  * of routed experts and decodes each of them once (the pages' chunk loads each
@@ -195,7 +271,7 @@ int k3o_forward(int32_t E, int32_t D, int32_t F,
 {
     int64_t P = (int64_t)T * K;
     for (int64_t p = 0; p < P; ++p)
-        if (idx[p] < 0 || idx[p] >= E) return -1;
+        if (idx[p] != -1 && (idx[p] < 0 || idx[p] >= E)) return -1;
 
     double *yp = ytk ? ytk : (double *)malloc(sizeof(double) * (size_t)(P * D));
     if (!yp) return -1;
@@ -204,7 +280,8 @@ int k3o_forward(int32_t E, int32_t D, int32_t F,
     int32_t *used = (int32_t *)calloc((size_t)E, sizeof(int32_t));
     int32_t *list = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
     int32_t nu = 0;
-    for (int64_t p = 0; p < P; ++p) used[idx[p]] = 1;
+    for (int64_t p = 0; p < P; ++p)
+        if (idx[p] >= 0) used[idx[p]] = 1;
     for (int32_t e = 0; e < E; ++e)
         if (used[e]) list[nu++] = e;
 
@@ -245,7 +322,8 @@ int k3o_forward(int32_t E, int32_t D, int32_t F,
             for (int32_t d = 0; d < D; ++d) {
                 double acc = 0.0;
                 for (int32_t k = 0; k < K; ++k)
-                    acc += (double)w[(int64_t)t * K + k] * yp[((int64_t)t * K + k) * D + d];
+                    if (idx[(int64_t)t * K + k] >= 0)
+                        acc += (double)w[(int64_t)t * K + k] * yp[((int64_t)t * K + k) * D + d];
                 y[(int64_t)t * D + d] = (float)acc;
             }
     }
@@ -260,8 +338,8 @@ int k3o_forward(int32_t E, int32_t D, int32_t F,
 /* Group a chunk's (token, slot) pairs by expert with a counting sort ([PR676]
  * chunked-prefill paragraph: the MoE loads each unique expert of the chunk once;
  * [PR684] chunked-prefill commit: position lists via counting sort).
- *   counts[e]   number of pairs routed to e
- *   offsets[e]  exclusive prefix sum of counts (offsets[E] = T*K)
+ *   counts[e]   number of pairs routed to e (pruned slots, id -1, are skipped)
+ *   offsets[e]  exclusive prefix sum of counts (offsets[E] = pairs placed)
  *   perm[...]   pair ids p = t*K + k, grouped by ascending expert and, within an
  *               expert, in ascending p (a counting sort is stable)
  *   uniq[...]   the experts with counts > 0, ascending; *n_unique their number
@@ -272,6 +350,7 @@ int k3o_group(const int32_t *idx, int32_t T, int32_t K, int32_t E, int32_t *coun
     int64_t P = (int64_t)T * K;
     memset(counts, 0, sizeof(int32_t) * (size_t)E);
     for (int64_t p = 0; p < P; ++p) {
+        if (idx[p] == -1) continue;
         if (idx[p] < 0 || idx[p] >= E) return -1;
         counts[idx[p]]++;
     }
@@ -280,6 +359,7 @@ int k3o_group(const int32_t *idx, int32_t T, int32_t K, int32_t E, int32_t *coun
     int32_t *fill = (int32_t *)calloc((size_t)E, sizeof(int32_t));
     for (int64_t p = 0; p < P; ++p) {
         int32_t e = idx[p];
+        if (e == -1) continue;
         perm[offsets[e] + fill[e]] = (int32_t)p;
         fill[e]++;
     }

@@ -49,9 +49,9 @@ def oracle_forward_subset(cfg: synth.Config, x: np.ndarray, idx: np.ndarray, w: 
                           want_pairs: bool = False):
     """The oracle on ``x [T,D]`` with routing ``idx/w [T,K]``, given host weights of
     only the experts the routing touches (regenerated from the seeded generator)."""
-    used = np.unique(idx)
+    used = np.unique(idx[idx >= 0])  # pruned slots (id -1) touch no expert
     W = synth.weights_host(cfg, used)
-    local = np.searchsorted(used, idx).astype(np.int32)
+    local = np.where(idx >= 0, np.searchsorted(used, np.maximum(idx, 0)), -1).astype(np.int32)
     return oracle.forward(W, x, local, w, want_pairs=want_pairs)
 
 

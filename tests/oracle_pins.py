@@ -384,10 +384,114 @@ def check_gate_moments(o):
     assert abs(got / want - 1) < 0.03, (got, want)
 
 
+# ------------------------------------------------------------------- P10 top-p pruning
+def _topp_exact(logits_row, bias_row, K, p):
+    """The top-p rule ([PR676] K3_TOPP paragraph) in 40-digit decimal arithmetic on
+    sigmoids computed here: selection by fp32 key as in the router, then the
+    smallest weight-ordered prefix whose score sum reaches p of the total.  Returns
+    (kept experts in slot order, their weights, decision margin)."""
+    E = len(logits_row)
+    sig = [_dsig(float(l)) for l in logits_row]
+    keys = []
+    for e in range(E):
+        k = np.float32(np.float32(float(sig[e])) + np.float32(bias_row[e]))
+        keys.append(-np.inf if np.isnan(k) else float(k))
+    slots = sorted(range(E), key=lambda e: (-keys[e], e))[:K]
+    S = sum(sig[e] for e in slots)
+    order = sorted(range(K), key=lambda k: (-sig[slots[k]], k))
+    thr = Decimal(repr(p)) * S
+    cum, m, margin = Decimal(0), 0, None
+    for r in order:
+        cum += sig[slots[r]]
+        m += 1
+        margin = abs(cum - thr) / S if margin is None else min(margin, abs(cum - thr) / S)
+        if cum >= thr:
+            break
+    kept_slots = sorted(order[:m])
+    Sk = sum(sig[slots[k]] for k in kept_slots)
+    return [slots[k] for k in kept_slots], [float(sig[slots[k]] / Sk) for k in kept_slots], margin
+
+
+def check_route_topp_definition(o):
+    """Kept experts = the smallest weight-ordered prefix of the top-K reaching p
+    (the crossing expert kept), listed in slot order, renormalized over the kept
+    raw scores; pruned slots hold id -1 and weight 0."""
+    rng = np.random.default_rng(41)
+    E, K, T = 32, 8, 24
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    skipped = 0
+    for p in (0.3, 0.5, 0.7, 0.9):
+        idx, w, n_kept, _ = o.route_topp(logits, bias, K, p)
+        for t in range(T):
+            want_ids, want_w, margin = _topp_exact(logits[t], bias, K, p)
+            if margin < 1e-12:
+                skipped += 1
+                continue
+            m = int(n_kept[t])
+            assert m == len(want_ids) and 1 <= m <= K, (p, t)
+            assert idx[t, :m].tolist() == want_ids, (p, t)
+            assert np.all(idx[t, m:] == -1) and np.all(w[t, m:] == 0.0), (p, t)
+            np.testing.assert_allclose(w[t, :m], want_w, rtol=1e-6, atol=0)
+            assert abs(float(np.sum(w[t, :m], dtype=np.float64)) - 1.0) < 1e-6
+    assert skipped < 4
+
+
+def check_route_topp_off_and_monotone(o):
+    """p outside (0, 1) prunes nothing (the plain router's output, bit for bit); the
+    kept count never falls as p grows; p -> 0 keeps exactly the largest weight."""
+    rng = np.random.default_rng(43)
+    E, K, T = 48, 16, 16
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    idx0, w0, _ = o.route(logits, bias, K)
+    for p in (0.0, 1.0, 1.5, -0.2):
+        idx, w, n_kept, _ = o.route_topp(logits, bias, K, p)
+        assert np.array_equal(idx, idx0) and np.array_equal(w.view(np.uint32), w0.view(np.uint32))
+        assert np.all(n_kept == K)
+    prev = np.zeros(T, dtype=np.int32)
+    for p in (1e-9, 0.2, 0.4, 0.6, 0.8, 0.95, 0.999):
+        _, _, n_kept, _ = o.route_topp(logits, bias, K, p)
+        assert np.all(n_kept >= prev)
+        prev = n_kept
+    idx, w, n_kept, _ = o.route_topp(logits, bias, K, 1e-9)
+    assert np.all(n_kept == 1) and np.all(w[:, 0] == 1.0)
+    sig = 1.0 / (1.0 + np.exp(-logits.astype(np.float64)))
+    for t in range(T):
+        assert idx[t, 0] == idx0[t][np.argmax(sig[t, idx0[t]])]
+
+
+def check_forward_pruned(o):
+    """A pruned slot (id -1) contributes nothing: the output equals the one with that
+    slot routed to any expert at weight 0."""
+    cfg, W, x, logits, bias = _tiny()
+    idx, w, _ = o.route(logits, bias, cfg.K)
+    idx_p, w_p = idx.copy(), w.copy()
+    idx_p[:, -1] = -1
+    w_p[:, -1] = 0.0
+    w_z = w.copy()
+    w_z[:, -1] = 0.0
+    assert np.array_equal(o.forward(W, x, idx_p, w_p), o.forward(W, x, idx, w_z))
+
+
+def check_group_pruned(o):
+    """Grouping skips pruned slots: counts, offsets and perm are those of the other pairs."""
+    rng = np.random.default_rng(47)
+    T, K, E = 19, 6, 11
+    idx = np.stack([rng.choice(E, size=K, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[rng.random((T, K)) < 0.3] = -1
+    g = o.group(idx, E)
+    pairs = [(int(idx[p // K, p % K]), p) for p in range(T * K) if idx[p // K, p % K] >= 0]
+    assert g["perm"].tolist() == [p for _, p in sorted(pairs)]
+    counts = [sum(1 for e, _ in pairs if e == x) for x in range(E)]
+    assert g["counts"].tolist() == counts and int(g["offsets"][E]) == len(pairs)
+
+
 ALL_CHECKS = [
     check_decode_closed_form, check_decode_conventions, check_layout_fixture, check_scale_groups,
     check_dequant_matches_codes, check_expert_brute_force, check_route_brute_force,
     check_route_invariants, check_route_bias_reading, check_route_nan, check_situ,
     check_forward_pairs, check_forward_combine, check_chunk_equals_tokens, check_group,
+    check_route_topp_definition, check_route_topp_off_and_monotone, check_forward_pruned, check_group_pruned,
 ]
 # check_gate_moments is run separately (it pins the generator, and is the slowest)

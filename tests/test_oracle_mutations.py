@@ -24,8 +24,8 @@ MUTANTS = [
     ("s=255 read as NaN", "if (fabs(w) >= 0x1p128)", "if ((scale & 0xFFu) == 255u) return NAN;\n    if (fabs(w) >= 0x1p128)"),
     ("subnormals flushed", "    return (float)w;\n}", "    return (fabs(w) < 0x1p-126) ? (float)copysign(0.0, w) : (float)w;\n}"),
     ("wrong scale group", "s[o * (I / 32) + i / 32]", "s[o * (I / 32) + i / 64]"),
-    ("bias on logits", "score[e] = sigmoid((double)l[e]);\n            float s32 = (float)score[e];\n            float key = s32 + bias[e];",
-     "score[e] = sigmoid((double)l[e]);\n            float s32 = (float)sigmoid((double)l[e] + bias[e]);\n            float key = s32;"),
+    ("bias on logits", "score[e] = sigmoid((double)l[e]);\n        float s32 = (float)score[e];\n        float key = s32 + bias[e];",
+     "score[e] = sigmoid((double)l[e]);\n        float s32 = (float)sigmoid((double)l[e] + bias[e]);\n        float key = s32;"),
     ("weights from biased keys", "denom += score[c[k].id];", "denom += c[k].key;"),
     ("numerator from biased key", "w[(int64_t)t * K + k] = (float)(score[c[k].id] / denom);",
      "w[(int64_t)t * K + k] = (float)(c[k].key / denom);"),
@@ -41,11 +41,16 @@ MUTANTS = [
     ("dropped last input term", "for (int32_t i = 0; i < D; ++i) {", "for (int32_t i = 0; i < D - 1; ++i) {"),
     ("wrong token for a pair", "x + t * D, NULL, NULL", "x + (p % T) * D, NULL, NULL"),
     ("combine ignores weights", "acc += (double)w[(int64_t)t * K + k] * yp[", "acc += yp["),
-    ("combine drops last slot", "for (int32_t k = 0; k < K; ++k)\n                    acc +=",
-     "for (int32_t k = 0; k < K - 1; ++k)\n                    acc +="),
-    ("group order unstable", "for (int64_t p = 0; p < P; ++p) {\n        int32_t e = idx[p];\n        perm",
-     "for (int64_t p = P - 1; p >= 0; --p) {\n        int32_t e = idx[p];\n        perm"),
+    ("combine drops last slot", "for (int32_t k = 0; k < K; ++k)\n                    if (idx[(int64_t)t * K + k] >= 0)",
+     "for (int32_t k = 0; k < K - 1; ++k)\n                    if (idx[(int64_t)t * K + k] >= 0)"),
+    ("group order unstable", "for (int64_t p = 0; p < P; ++p) {\n        int32_t e = idx[p];\n        if (e == -1) continue;",
+     "for (int64_t p = P - 1; p >= 0; --p) {\n        int32_t e = idx[p];\n        if (e == -1) continue;"),
     ("union misses singletons", "if (counts[e] > 0) uniq[nu++] = e;", "if (counts[e] > 1) uniq[nu++] = e;"),
+    ("top-p in slot order", "while (j > 0 && score[c[order[j - 1]].id] < score[c[k].id])", "while (0)"),
+    ("top-p drops the crossing expert", "++m;\n                if (cum >= thr) break;", "if (cum >= thr) break;\n                ++m;"),
+    ("top-p renormalizes over all K", "if (kept[k]) Sk += score[c[k].id];", "Sk += score[c[k].id];"),
+    ("top-p threshold on weights of all experts", "const double thr = p * S;", "const double thr = p * S * 1.05;"),
+    ("group keeps pruned pairs", "if (idx[p] == -1) continue;\n        if (idx[p] < 0", "if (idx[p] == -1) { counts[0]++; continue; }\n        if (idx[p] < 0"),
     ("offsets inclusive", "offsets[e + 1] = offsets[e] + counts[e];", "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
 ]
 
