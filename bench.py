@@ -138,6 +138,7 @@ def main():
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--top-p", type=float, default=0.7, help="also time decode with top-p pruning (0 = skip)")
     ap.add_argument("--counters-probe", action="store_true",
                     help="run only a few decode steps and the copy calibration (for rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -241,6 +242,37 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(),
                      "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_us, 3)},
     }
+
+    # top-p pruning (colibri PR #676, K3_TOPP paragraph) on the same tokens: the
+    # router drops the low-weight tail and the decode kernels skip pruned slots
+    top_p = args.top_p
+    if top_p > 0.0:
+        n_kept = torch.empty(1, dtype=torch.int32, device=dev)
+        kept_all = []
+        for j in range(n_rot):
+            lib.route_topp(l_d[j:j + 1], b_d, K, top_p, idx=idx_d[j:j + 1], w=w_d[j:j + 1], n_kept=n_kept)
+            kept_all.append(int(n_kept.item()))
+
+        def step_topp(j):
+            lib.route_topp(l_d[j:j + 1], b_d, K, top_p, idx=idx_d[j:j + 1], w=w_d[j:j + 1], n_kept=n_kept)
+            lib.decode_gateup(W, x_d[j], idx_d[j], h=h_d)
+            lib.decode_down(W, h_d, idx_d[j], w_d[j], y=y_d[j], ws=ws)
+
+        for i in range(args.warmup):
+            step_topp(i % n_rot)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step_topp(i % n_rot)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        kept_mean = float(np.mean([kept_all[i % n_rot] for i in range(args.steps)]))
+        us = el * 1e6 / args.steps
+        result["decode_topp"] = {"top_p": top_p, "mean_experts_kept": round(kept_mean, 3), "of": K,
+                                 "us_per_layer_token": round(us, 3),
+                                 "kept_expert_gbs": round(kept_mean * cfg.expert_bytes() / us / 1e3, 1),
+                                 "speedup_vs_top16": round(ms_per_step * 1e3 / us, 3)}
+        log(f"decode top-p {top_p}: {kept_mean:.2f} of {K} experts kept, {us:.1f} us/step")
     del W, ws
     torch.cuda.empty_cache()
 

@@ -55,6 +55,7 @@ extern "C" {
 
 /* Limits shared by the entry points. */
 #define K3MOE_MAX_K 64          /* experts per token                                  */
+#define K3MOE_PRUNED (-1)       /* routing slot dropped by top-p (k3moe_route_topp)   */
 #define K3MOE_MAX_E 4096        /* experts per layer                                  */
 #define K3MOE_MAX_DIM 8192      /* latent width D and expert width F                  */
 
@@ -103,13 +104,35 @@ int k3moe_route(const float *logits, const float *bias, int32_t T, int32_t E, in
                 int32_t *idx, float *w, void *stream);
 
 /*
+ * k3moe_route followed by top-p pruning (colibri PR #676, K3_TOPP paragraph; PR
+ * #684 engine commit, K3_TOPP bullet): of each token's K selected experts, keep
+ * those with the largest routing weights until their cumulative weight reaches
+ * top_p, drop the low-weight tail and renormalize the kept raw scores.  Exactly:
+ *   S   = sum of the K selected sigmoid scores in slot order (double);
+ *   order the K slots by descending score (equal scores: lower slot first) and
+ *   keep the shortest prefix whose running sum (double) reaches top_p * S, so
+ *   the expert that crosses top_p is kept and at least one expert is;
+ *   the kept experts stay in their slot order in idx[t, 0..m-1] with
+ *   w = score / (sum of kept scores in slot order); slots m..K-1 hold
+ *   K3MOE_PRUNED with weight 0; n_kept[t] = m (device int32, nullable).
+ * top_p <= 0 or >= 1 keeps all K (the output equals k3moe_route's).  Every
+ * entry point below skips K3MOE_PRUNED slots: no weights are read for them and
+ * they contribute nothing.  A NaN top_p is rejected (K3MOE_E_DIM).
+ */
+int k3moe_route_topp(const float *logits, const float *bias, int32_t T, int32_t E, int32_t K,
+                     double top_p, int32_t *idx, float *w, int32_t *n_kept, void *stream);
+
+/*
  * Group a chunk's (token, slot) pairs by expert with a counting sort (colibri
  * PR #676, chunked-prefill paragraph: the MoE loads each unique expert of a chunk
  * once; PR #684 chunked-prefill commit: position lists via counting sort).
- * Pair p = t*K + k is routed to idx[p].  Outputs (device, int32):
+ * Pair p = t*K + k is routed to idx[p]; K3MOE_PRUNED slots are not pairs.
+ * Outputs (device, int32):
  *   counts[E]     pairs per expert;
- *   offsets[E+1]  exclusive prefix sum of counts (offsets[E] = T*K);
- *   perm[T*K]     pair ids grouped by ascending expert, ascending p within one;
+ *   offsets[E+1]  exclusive prefix sum of counts (offsets[E] = pairs placed,
+ *                 T*K when nothing is pruned);
+ *   perm[T*K]     pair ids grouped by ascending expert, ascending p within one
+ *                 (entries past offsets[E] are left unspecified);
  *   uniq[E]       the experts with counts > 0 in ascending order (entries past
  *                 n_unique are left unspecified);
  *   n_unique[1]   their number, or -1 if some idx is outside [0, E) or a token
@@ -126,9 +149,10 @@ int k3moe_group(const int32_t *idx, int32_t T, int32_t K, int32_t E, int32_t *co
  * are decoded to fp32 exactly, dot products accumulate in fp32, SiTU-GLU runs in
  * fp32 and the combine sums w_k * y_k in slot order k = 0..K-1.  This is the
  * memory-bound decode path; every selected expert's bytes are read once.
- * x [D] fp32, idx [K] int32 (each in [0, E), distinct), w [K] fp32, y [D] fp32.
- * ws: k3moe_workspace_size(K3MOE_OP_DECODE, 1, K, W) bytes.  Out-of-range
- * indices are not read; their slots contribute NaN to y.
+ * x [D] fp32, idx [K] int32 (each in [0, E), distinct, or K3MOE_PRUNED),
+ * w [K] fp32, y [D] fp32.  ws: k3moe_workspace_size(K3MOE_OP_DECODE, 1, K, W)
+ * bytes.  Pruned slots are skipped; other out-of-range indices are not read and
+ * their slots contribute NaN to y.
  */
 int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t *idx,
                          const float *w, int32_t K, float *y, void *ws, size_t ws_bytes,
@@ -139,7 +163,8 @@ int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t
  * activations, or to time the stages).  Same arithmetic as forward_decode.
  * k3moe_decode_gateup (steps 2-3): h[k, f] = SiTU-GLU((W_gate[e_k] x)_f,
  *   (W_up[e_k] x)_f) for k < K, f < F; x [D] fp32, idx [K], h [K, F] fp32.
- *   An out-of-range idx[k] gives a NaN row h[k].
+ *   An out-of-range idx[k] gives a NaN row h[k]; a pruned slot's row is not
+ *   written.
  * k3moe_decode_down (steps 4-5): y[d] = sum_k w_k * (W_down[e_k] h[k])_d summed in
  *   slot order; h [K, F] fp32 (16-byte aligned), y [D] fp32; ws as for
  *   k3moe_forward_decode (it holds the per-slot down outputs).
@@ -152,13 +177,14 @@ int k3moe_decode_down(const k3moe_weights_t *W, const float *h, const int32_t *i
 /*
  * A chunk of T tokens through the routed experts (steps 2-5) with the chunk's
  * expert union deduplicated: the pairs are grouped by expert (k3moe_group), each
- * routed expert's weights are streamed once per group of up to 128 of its
+ * routed expert's weights are streamed once per group of up to 96 of its
  * tokens, and gate/up and down run as bf16 MFMA matrix products with fp32
  * accumulation.  The activations x are bf16; the decoded weights are exact in
  * bf16; h is rounded to bf16 (round-to-nearest-even) between the two products.
  * The combine sums w_{t,k} * y_{t,k} in slot order in fp32.
- * x [T, D] bf16 (raw 16-bit patterns), idx [T, K] int32, w [T, K] fp32,
- * y [T, D] fp32; n_unique (device int32, nullable) receives the union size, or
+ * x [T, D] bf16 (raw 16-bit patterns), idx [T, K] int32 (K3MOE_PRUNED slots
+ * skipped), w [T, K] fp32, y [T, D] fp32; n_unique (device int32, nullable)
+ * receives the union size, or
  * -1 for invalid routing, in which case every element of y is NaN.
  * ws: k3moe_workspace_size(K3MOE_OP_CHUNK, T, K, W) bytes.
  */

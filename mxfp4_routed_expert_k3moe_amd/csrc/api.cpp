@@ -90,7 +90,17 @@ int k3moe_route(const float* logits, const float* bias, int32_t T, int32_t E, in
     if (T < 1 || E < 1 || E > K3MOE_MAX_E || K < 1 || K > E || K > K3MOE_MAX_K) return K3MOE_E_DIM;
     int rc = check_device();
     if (rc != K3MOE_OK) return rc;
-    return finish(k3moe::launch_route(logits, bias, T, E, K, idx, w, static_cast<hipStream_t>(stream)));
+    return finish(k3moe::launch_route(logits, bias, T, E, K, 0.0, idx, w, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int k3moe_route_topp(const float* logits, const float* bias, int32_t T, int32_t E, int32_t K, double top_p,
+                     int32_t* idx, float* w, int32_t* n_kept, void* stream) {
+    if (!logits || !bias || !idx || !w) return K3MOE_E_NULL;
+    if (T < 1 || E < 1 || E > K3MOE_MAX_E || K < 1 || K > E || K > K3MOE_MAX_K) return K3MOE_E_DIM;
+    if (top_p != top_p) return K3MOE_E_DIM;  // NaN
+    int rc = check_device();
+    if (rc != K3MOE_OK) return rc;
+    return finish(k3moe::launch_route(logits, bias, T, E, K, top_p, idx, w, n_kept, static_cast<hipStream_t>(stream)));
 }
 
 size_t k3moe_workspace_size(int32_t op, int32_t T, int32_t K, const k3moe_weights_t* W) {

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void group_count_kernel(const int32_t* __restr
     const int t0 = b * GT, t1 = min(T, t0 + GT);
     for (int p = t0 * K + (int)threadIdx.x; p < t1 * K; p += blockDim.x) {
         const int e = idx[p];
+        if (e == K3MOE_PRUNED) continue;  // a pruned slot is not a pair
         if (e < 0 || e >= E) {
             atomicOr(&s_err, 1);
             continue;
@@ -177,6 +178,7 @@ __global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t* __res
     const int t0 = b * GT, t1 = min(T, t0 + GT);
     for (int p = t0 * K + (int)threadIdx.x; p < t1 * K; p += blockDim.x) {
         const int e = idx[p];
+        if (e == K3MOE_PRUNED) continue;
         const int ti = p / K - t0;
         const unsigned long long m = masks_blk[(size_t)b * E + e];
         const int rank = __popcll(m & ((1ull << ti) - 1ull));
@@ -571,8 +573,9 @@ hipError_t launch_gemm(const GemmArgs& a, int mt, int max_tiles, hipStream_t str
 }
 
 // -------------------------------------------------------------------------- combine
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ytk, int T, int K, int D,
-                                                      const int32_t* __restrict__ scalars,
+// y_t = sum over slots in order of the weighted pair rows; pruned slots are skipped.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ytk, const int32_t* __restrict__ idx,
+                                                      int T, int K, int D, const int32_t* __restrict__ scalars,
                                                       float* __restrict__ y) {
     const bool bad = scalars[0] < 0;
     const size_t n4 = (size_t)T * D / 4;
@@ -586,6 +589,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             acc = make_float4(nan, nan, nan, nan);
         } else {
             for (int k = 0; k < K; ++k) {
+                if (idx[t * K + k] == K3MOE_PRUNED) continue;
                 const float4 v = reinterpret_cast<const float4*>(ytk + ((t * K + k) * (size_t)D))[dd];
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
@@ -706,7 +710,7 @@ hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int
     if (err != hipSuccess) return err;
 
     const size_t n4 = (size_t)T * W.D / 4;
-    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, ws.ytk, T, K, W.D,
+    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, ws.ytk, idx, T, K, W.D,
                        ws.g.scalars, y);
     return hipGetLastError();
 }

@@ -241,6 +241,7 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DevWeights W, const 
     const int fblk = blockIdx.x * ROWS_PER_BLOCK;
     const int f0 = fblk + wave * 16;
     const int e = idx[k];
+    if (e == K3MOE_PRUNED) return;  // block-uniform: a pruned slot reads and writes nothing
     const bool valid_e = e >= 0 && e < W.E;
     const int ec = valid_e ? e : 0;
     uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(D);
@@ -297,6 +298,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const in
     const int dblk = blockIdx.x * DOWN_ROWS_PER_BLOCK;
     const int d0 = dblk + wave * 16 * DOWN_TILES;
     const int e = idx[k];
+    if (e == K3MOE_PRUNED) return;  // block-uniform
     const bool valid_e = e >= 0 && e < W.E;
     const int ec = valid_e ? e : 0;
     uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(F);
@@ -334,22 +336,26 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const in
         if (lane < 16 && d0 + 16 * t < D) yk[d0 + 16 * t + lane] = (acc[t][0] + acc[t][1]) + acc[t][2];
 }
 
+// y[d] = sum over slots in order of w_k * part[k, d]; pruned slots are skipped.
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ ypart,
-                                                             const float* __restrict__ wts, int K, int D,
+                                                             const float* __restrict__ wts,
+                                                             const int32_t* __restrict__ idx, int K, int D,
                                                              float* __restrict__ y) {
     const int d = blockIdx.x * blockDim.x + threadIdx.x;
     if (d >= D) return;
     float acc = 0.0f;
     for (int k0 = 0; k0 < K; k0 += 16) {
         float v[16], wk[16];
+        bool use[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {  // all loads of a group in flight together
-            v[i] = (k0 + i < K) ? ypart[(size_t)(k0 + i) * D + d] : 0.0f;
-            wk[i] = (k0 + i < K) ? wts[k0 + i] : 0.0f;
+            use[i] = k0 + i < K && idx[k0 + i] != K3MOE_PRUNED;
+            v[i] = use[i] ? ypart[(size_t)(k0 + i) * D + d] : 0.0f;
+            wk[i] = use[i] ? wts[k0 + i] : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            if (k0 + i < K) acc = fmaf(wk[i], v[i], acc);
+            if (use[i]) acc = fmaf(wk[i], v[i], acc);
     }
     y[d] = acc;
 }
@@ -395,7 +401,7 @@ hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t
         hipLaunchKernelGGL(decode_down_kernel<true>, grid, dim3(WAVES * 64), lds, stream, W, idx, h, ypart);
     else
         hipLaunchKernelGGL(decode_down_kernel<false>, grid, dim3(WAVES * 64), lds, stream, W, idx, h, ypart);
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((W.D + 255) / 256), dim3(256), 0, stream, ypart, w, K, W.D, y);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((W.D + 255) / 256), dim3(256), 0, stream, ypart, w, idx, K, W.D, y);
     return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "k3moe.h"  // status codes, limits and the pruned-slot marker shared with the kernels
+
 namespace k3moe {
 
 // Expert weights as the kernels see them (plain values, passed by value).
@@ -15,8 +17,8 @@ struct DevWeights {
 };
 
 // ------------------------------------------------------------------ route
-hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K, int32_t* idx,
-                        float* w, hipStream_t stream);
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K, double top_p, int32_t* idx,
+                        float* w, int32_t* n_kept, hipStream_t stream);
 
 // ------------------------------------------------------------------ decode
 constexpr int kDecodeWaves = 4;  // waves per workgroup (16 weight rows each)

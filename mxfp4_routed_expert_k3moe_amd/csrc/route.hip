@@ -100,7 +100,8 @@ __device__ __forceinline__ void wave_topk(unsigned long long (&code)[PL], int K,
 template <int PL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int E, int K,
-                                                    int32_t* __restrict__ idx, float* __restrict__ w) {
+                                                    double top_p, int32_t* __restrict__ idx,
+                                                    float* __restrict__ w, int32_t* __restrict__ n_kept) {
     __shared__ unsigned long long cand[4 * K3MOE_MAX_K_DEV];
     __shared__ double sel_sig[K3MOE_MAX_K_DEV];
     __shared__ int sel_id[K3MOE_MAX_K_DEV];
@@ -151,32 +152,70 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     __syncthreads();
     if (wave != 0) return;
-    double denom = 0.0;  // slot order, as in the definition
-    for (int k = 0; k < K; ++k) denom += sel_sig[k];
-    if (lane < K) {
-        idx[(size_t)t * K + lane] = sel_id[lane];
-        w[(size_t)t * K + lane] = (float)(sel_sig[lane] / denom);
+    double S = 0.0;  // slot order, as in the definition
+    for (int k = 0; k < K; ++k) S += sel_sig[k];
+    const double sig = lane < K ? sel_sig[lane] : 0.0;
+    int m = K;
+    double Sk = S;
+    bool kept = lane < K;
+    if (top_p > 0.0 && top_p < 1.0) {
+        // top-p: this slot's place in descending-score order (ties: lower slot first),
+        // then the running sum in that order until it reaches p of the total
+        int pos = K;
+        if (lane < K) {
+            pos = 0;
+            for (int j = 0; j < K; ++j) {
+                const double sj = sel_sig[j];
+                pos += (sj > sig) || (sj == sig && j < lane);
+            }
+        }
+        const double thr = top_p * S;
+        double cum = 0.0;
+        for (m = 0; m < K;) {
+            const int src = __ffsll((long long)__ballot(pos == m)) - 1;
+            cum += __longlong_as_double(((long long)(uint32_t)__builtin_amdgcn_readlane(
+                                             (int)(__double_as_longlong(sig) >> 32), src) << 32) |
+                                        (uint32_t)__builtin_amdgcn_readlane((int)__double_as_longlong(sig), src));
+            ++m;
+            if (cum >= thr) break;
+        }
+        kept = pos < m;
+        Sk = 0.0;  // kept scores, slot order
+        const unsigned long long km = __ballot(kept);
+        for (int k = 0; k < K; ++k)
+            if ((km >> k) & 1ull) Sk += sel_sig[k];
     }
+    const unsigned long long km = __ballot(kept);
+    if (kept) {  // kept slots, compacted in slot order
+        const int slot = __popcll(km & ((1ull << lane) - 1ull));
+        idx[(size_t)t * K + slot] = sel_id[lane];
+        w[(size_t)t * K + slot] = (float)(sig / Sk);
+    }
+    if (lane >= m && lane < K) {  // the pruned tail (lane here is the output slot)
+        idx[(size_t)t * K + lane] = K3MOE_PRUNED;
+        w[(size_t)t * K + lane] = 0.0f;
+    }
+    if (n_kept != nullptr && lane == 0) n_kept[t] = m;
 }
 
 template <int PL>
-hipError_t launch_pl(const float* logits, const float* bias, int T, int E, int K, int32_t* idx,
-                     float* w, hipStream_t stream) {
+hipError_t launch_pl(const float* logits, const float* bias, int T, int E, int K, double top_p, int32_t* idx,
+                     float* w, int32_t* n_kept, hipStream_t stream) {
     hipLaunchKernelGGL(route_kernel<PL>, dim3(T), dim3(256), (size_t)E * sizeof(double), stream, logits, bias, T, E,
-                       K, idx, w);
+                       K, top_p, idx, w, n_kept);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K, int32_t* idx,
-                        float* w, hipStream_t stream) {
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int K, double top_p, int32_t* idx,
+                        float* w, int32_t* n_kept, hipStream_t stream) {
     const int per_lane = ((E + 3) / 4 + 63) / 64;  // candidates per lane in each of 4 waves
-    if (per_lane <= 1) return launch_pl<1>(logits, bias, T, E, K, idx, w, stream);
-    if (per_lane <= 2) return launch_pl<2>(logits, bias, T, E, K, idx, w, stream);
-    if (per_lane <= 4) return launch_pl<4>(logits, bias, T, E, K, idx, w, stream);
-    if (per_lane <= 8) return launch_pl<8>(logits, bias, T, E, K, idx, w, stream);
-    return launch_pl<16>(logits, bias, T, E, K, idx, w, stream);
+    if (per_lane <= 1) return launch_pl<1>(logits, bias, T, E, K, top_p, idx, w, n_kept, stream);
+    if (per_lane <= 2) return launch_pl<2>(logits, bias, T, E, K, top_p, idx, w, n_kept, stream);
+    if (per_lane <= 4) return launch_pl<4>(logits, bias, T, E, K, top_p, idx, w, n_kept, stream);
+    if (per_lane <= 8) return launch_pl<8>(logits, bias, T, E, K, top_p, idx, w, n_kept, stream);
+    return launch_pl<16>(logits, bias, T, E, K, top_p, idx, w, n_kept, stream);
 }
 
 }  // namespace k3moe

@@ -28,7 +28,9 @@ K3MOE_MAX_DIM = 8192
 OP_DECODE, OP_CHUNK, OP_GROUP = 1, 2, 3
 OUT_F32, OUT_BF16 = 0, 1
 
-ENTRY_POINTS = ("k3moe_route", "k3moe_group", "k3moe_forward_decode", "k3moe_decode_gateup",
+PRUNED = -1  # K3MOE_PRUNED: a routing slot dropped by top-p
+
+ENTRY_POINTS = ("k3moe_route", "k3moe_route_topp", "k3moe_group", "k3moe_forward_decode", "k3moe_decode_gateup",
                 "k3moe_decode_down", "k3moe_forward_chunk", "k3moe_workspace_size", "k3moe_dequant_mxfp4",
                 "k3moe_status_string")
 
@@ -162,6 +164,26 @@ def route(logits: torch.Tensor, bias: torch.Tensor, K: int, idx: Optional[torch.
     _check("k3moe_route", load().k3moe_route(_ptr(logits), _ptr(bias), T, E, K, _ptr(idx), _ptr(w),
                                               _stream(stream)))
     return idx, w
+
+
+def route_topp(logits: torch.Tensor, bias: torch.Tensor, K: int, top_p: float, idx: Optional[torch.Tensor] = None,
+               w: Optional[torch.Tensor] = None, n_kept: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Router plus top-p pruning: ``(idx [T,K], w [T,K], n_kept [T])``; pruned slots
+    (after the kept ones) hold ``PRUNED`` and weight 0."""
+    T, E = logits.shape
+    _dev(logits, torch.float32, "logits")
+    _dev(bias, torch.float32, "bias", (E,))
+    dev = logits.device
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev) if idx is None else idx
+    w = torch.empty((T, K), dtype=torch.float32, device=dev) if w is None else w
+    n_kept = torch.empty(T, dtype=torch.int32, device=dev) if n_kept is None else n_kept
+    _dev(idx, torch.int32, "idx", (T, K))
+    _dev(w, torch.float32, "w", (T, K))
+    _dev(n_kept, torch.int32, "n_kept", (T,))
+    _check("k3moe_route_topp", load().k3moe_route_topp(_ptr(logits), _ptr(bias), T, E, K, ctypes.c_double(top_p),
+                                                        _ptr(idx), _ptr(w), _ptr(n_kept), _stream(stream)))
+    return idx, w, n_kept
 
 
 def group(idx: torch.Tensor, E: int, ws: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:

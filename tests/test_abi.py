@@ -39,6 +39,7 @@ def test_header_constants_match_binding():
     assert int(consts["K3MOE_E_DEVICE"]) == k3.K3MOE_E_DEVICE
     assert int(consts["K3MOE_E_HIP"]) == k3.K3MOE_E_HIP
     assert int(consts["K3MOE_MAX_K"]) == k3.K3MOE_MAX_K
+    assert int(consts["K3MOE_PRUNED"]) == k3.PRUNED
     assert int(consts["K3MOE_OP_DECODE"]) == k3.OP_DECODE
     assert int(consts["K3MOE_OP_CHUNK"]) == k3.OP_CHUNK
     assert int(consts["K3MOE_OP_GROUP"]) == k3.OP_GROUP
@@ -87,6 +88,10 @@ def test_validation_before_any_device_call():
     assert lib.k3moe_route(p, p, 1, 896, 65, p, p, None) == k3.K3MOE_E_DIM
     assert lib.k3moe_route(p, p, 1, 8, 9, p, p, None) == k3.K3MOE_E_DIM
     assert lib.k3moe_route(p, p, 1, 5000, 16, p, p, None) == k3.K3MOE_E_DIM
+    d = ctypes.c_double
+    assert lib.k3moe_route_topp(None, p, 1, 896, 16, d(0.7), p, p, None, None) == k3.K3MOE_E_NULL
+    assert lib.k3moe_route_topp(p, p, 1, 896, 16, d(float("nan")), p, p, None, None) == k3.K3MOE_E_DIM
+    assert lib.k3moe_route_topp(p, p, 1, 8, 9, d(0.7), p, p, None, None) == k3.K3MOE_E_DIM
     ws = 1 << 20
     assert lib.k3moe_forward_decode(None, p, p, p, 16, p, p, ws, None) == k3.K3MOE_E_NULL
     assert lib.k3moe_forward_decode(ctypes.byref(s), None, p, p, 16, p, p, ws, None) == k3.K3MOE_E_NULL

@@ -25,7 +25,7 @@ def _compare(idx, E, what):
     assert nu == want["n_unique"]
     assert np.array_equal(got["counts"], want["counts"])
     assert np.array_equal(got["offsets"], want["offsets"])
-    assert np.array_equal(got["perm"], want["perm"])
+    assert np.array_equal(got["perm"][:len(want["perm"])], want["perm"])  # placed pairs only
     assert np.array_equal(got["uniq"][:nu], want["uniq"])
     P = idx.size
     log(f"group {what}: union {nu} experts, dedup {P / max(nu, 1):.2f}x")
@@ -64,7 +64,7 @@ def test_group_invalid(kind):
     if kind == "out_of_range":
         idx[66, 2] = E
     elif kind == "negative":
-        idx[3, 0] = -1
+        idx[3, 0] = -2  # -1 marks a pruned slot, any other negative is invalid
     else:
         idx[40, 1] = idx[40, 3]
     got = _group_gpu(idx, E)

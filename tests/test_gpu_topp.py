@@ -1,0 +1,100 @@
+"""Top-p pruning on the GPU vs the oracle (colibri PR #676, K3_TOPP paragraph):
+kept sets and counts bit-exact, weights to 2 ulp; decode and chunk outputs with
+pruned slots within their path's tolerance; grouping skips pruned slots."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import assert_close, device_weights, log, oracle_forward_subset, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _route_topp_gpu(logits, bias, K, p):
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    idx, w, n = lib.route_topp(torch.from_numpy(logits).cuda(), torch.from_numpy(bias).cuda(), K, p)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy(), n.cpu().numpy()
+
+
+def _compare(logits, bias, K, p, what):
+    idx_o, w_o, n_o, gap = oracle.route_topp(logits, bias, K, p)
+    idx_g, w_g, n_g = _route_topp_gpu(logits, bias, K, p)
+    log(f"topp {what} p={p}: mean kept {n_o.mean():.2f} of {K}")
+    assert np.array_equal(n_g, n_o)
+    assert np.array_equal(idx_g, idx_o), np.nonzero(np.any(idx_g != idx_o, axis=1))[0][:10]
+    kept = idx_o >= 0
+    assert np.all(w_g[~kept] == 0.0)
+    rel = np.abs(w_g[kept].astype(np.float64) - w_o[kept]) / np.abs(w_o[kept])
+    assert rel.max() <= 2 * 2.0 ** -24, rel.max()
+    return idx_o, w_o
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode1", "prefill256"])
+@pytest.mark.parametrize("p", [0.3, 0.7, 0.9])
+def test_route_topp_configs(name, p):
+    cfg = synth.CONFIGS[name]
+    _, logits, bias = synth.activations(cfg, T=max(cfg.T, 32) if name != "prefill256" else None, stream=17)
+    _compare(logits, bias, cfg.K, p, name)
+
+
+@pytest.mark.parametrize("p", [0.0, 1.0, 2.0])
+def test_route_topp_off_equals_route(p):
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = synth.CONFIGS["decode1"]
+    _, logits, bias = synth.activations(cfg, T=16, stream=19)
+    idx_g, w_g, n_g = _route_topp_gpu(logits, bias, cfg.K, p)
+    i2, w2 = lib.route(torch.from_numpy(logits).cuda(), torch.from_numpy(bias).cuda(), cfg.K)
+    assert np.array_equal(idx_g, i2.cpu().numpy())
+    assert np.array_equal(w_g.view(np.uint32), w2.cpu().numpy().view(np.uint32))
+    assert np.all(n_g == cfg.K)
+
+
+@pytest.mark.parametrize("T,E,K", [(9, 64, 64), (5, 4096, 16), (6, 20, 1), (4, 100, 33)])
+def test_route_topp_shapes(T, E, K):
+    rng = np.random.default_rng(T * 7 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    for p in (0.05, 0.5, 0.95):
+        _compare(logits, bias, K, p, f"{T}x{E} K={K}")
+
+
+def test_decode_topp():
+    """One K3-shape token per pruning level through forward_decode (pruned slots skipped)."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = synth.CONFIGS["decode1"]
+    x, logits, bias = synth.activations(cfg, T=2, stream=23)
+    W = device_weights(cfg)
+    for p in (0.5, 0.8):
+        idx, w = _compare(logits, bias, cfg.K, p, "decode1 tokens")
+        for t in range(x.shape[0]):
+            y = lib.forward_decode(W, torch.from_numpy(x[t]).cuda(), torch.from_numpy(idx[t]).cuda(),
+                                   torch.from_numpy(w[t]).cuda())
+            torch.cuda.synchronize()
+            want = oracle_forward_subset(cfg, x[t:t + 1], idx[t:t + 1], w[t:t + 1])[0]
+            assert_close(y.cpu().numpy(), want, 1e-5, f"decode top-p {p} token {t}")
+
+
+def test_chunk_topp():
+    """A 32-token chunk routed with top-p 0.7 through forward_chunk and k3moe_group."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = synth.CONFIGS["prefill32"]
+    x, logits, bias = synth.activations(cfg)
+    idx, w = _compare(logits, bias, cfg.K, 0.7, "prefill32")
+    W = device_weights(cfg)
+    y = lib.forward_chunk(W, torch.from_numpy(x).cuda().to(torch.bfloat16), torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(w).cuda())
+    g = lib.group(torch.from_numpy(idx).cuda(), cfg.E)
+    torch.cuda.synchronize()
+    want = oracle_forward_subset(cfg, x, idx, w)
+    assert_close(y.cpu().numpy(), want, 5e-3, "chunk top-p 0.7")
+    go = oracle.group(idx, cfg.E)
+    assert int(g["n_unique"].item()) == go["n_unique"]
+    assert np.array_equal(g["counts"].cpu().numpy(), go["counts"])
+    assert np.array_equal(g["offsets"].cpu().numpy(), go["offsets"])
+    assert np.array_equal(g["perm"].cpu().numpy()[:len(go["perm"])], go["perm"])
