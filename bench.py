@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--top-p", type=float, default=0.7, help="also time decode with top-p pruning (0 = skip)")
+    ap.add_argument("--pool-slots", type=int, default=128,
+                    help="also time decode with experts in pinned host memory behind an HBM pool (0 = skip)")
     ap.add_argument("--counters-probe", action="store_true",
                     help="run only a few decode steps and the copy calibration (for rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -273,6 +275,53 @@ def main():
                                  "kept_expert_gbs": round(kept_mean * cfg.expert_bytes() / us / 1e3, 1),
                                  "speedup_vs_top16": round(ms_per_step * 1e3 / us, 3)}
         log(f"decode top-p {top_p}: {kept_mean:.2f} of {K} experts kept, {us:.1f} us/step")
+
+    # expert residency (colibri PR #676, It runs the full model; PR #684 engine
+    # commit): the layer's experts live in pinned host memory in the slot layout,
+    # an LRU pool of HBM slots holds a subset, each token's misses are copied in
+    # on a copy stream while its resident experts compute
+    if args.pool_slots > 0:
+        layout = lib.slot_layout(cfg.D, cfg.F)
+        host = torch.empty((cfg.E, layout[6]), dtype=torch.uint8, pin_memory=True)
+        for ti, name in enumerate(lib.ExpertWeights.NAMES):
+            src = W.tensors[name].reshape(cfg.E, -1)
+            host[:, layout[ti]:layout[ti] + src.shape[1]].copy_(src)
+        torch.cuda.synchronize()
+        slots_mem = torch.empty(args.pool_slots * layout[6], dtype=torch.uint8, device=dev)
+        pool = lib.Pool(args.pool_slots, cfg.D, cfg.F, slots_mem)
+        copy_stream = torch.cuda.Stream()
+        ws_p = torch.empty(lib.workspace_size(lib.OP_DECODE, 1, K, W) + 768, dtype=torch.uint8, device=dev)
+        for j in range(n_rot):  # the plain routing again (the top-p leg rewrote idx/w)
+            lib.route(l_d[j:j + 1], b_d, K, idx=idx_d[j:j + 1], w=w_d[j:j + 1])
+
+        def step_pooled(j):
+            lib.route(l_d[j:j + 1], b_d, K, idx=idx_d[j:j + 1], w=w_d[j:j + 1])
+            lib.forward_decode_pooled(pool, 0, host, 0, host.stride(0), x_d[j], idx_d[j], w_d[j], y=y_d[j],
+                                      ws=ws_p, copy_stream=copy_stream)
+
+        n_pool = min(args.steps, 64)
+        for i in range(min(args.warmup, 8)):
+            step_pooled(i % n_rot)
+        torch.cuda.synchronize()
+        st0 = pool.stats()
+        t0 = time.perf_counter()
+        for i in range(n_pool):
+            step_pooled(i % n_rot)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        st1 = pool.stats()
+        miss = st1["misses"] - st0["misses"]
+        hit = st1["hits"] - st0["hits"]
+        copied = st1["bytes"] - st0["bytes"]
+        result["decode_pooled"] = {"pool_slots": args.pool_slots, "pool_gb": round(args.pool_slots * layout[6] / 1e9, 2),
+                                   "tokens": n_pool, "hit_rate": round(hit / max(1, hit + miss), 4),
+                                   "us_per_layer_token": round(el * 1e6 / n_pool, 2),
+                                   "host_to_hbm_gbs": round(copied / el / 1e9, 2),
+                                   "resident_us_per_layer_token": round(ms_per_step * 1e3, 2)}
+        log(f"decode pooled ({args.pool_slots} slots): hit rate {hit / max(1, hit + miss):.3f}, "
+            f"{el * 1e6 / n_pool:.1f} us/token, host->HBM {copied / el / 1e9:.1f} GB/s")
+        pool.close()
+        del host, slots_mem, pool
     del W, ws
     torch.cuda.empty_cache()
 

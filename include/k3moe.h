@@ -193,6 +193,51 @@ int k3moe_forward_chunk(const k3moe_weights_t *W, const uint16_t *x, int32_t T, 
                         size_t ws_bytes, void *stream);
 
 /*
+ * Expert residency (colibri PR #676, "It runs the full model"; PR #684 engine
+ * commit: routed experts stream through a per-layer LRU of whole-expert slots,
+ * one read per expert because its six tensors sit back to back, with the reads
+ * of a token's misses overlapping the compute of experts already loaded).  Here
+ * the slow tier is pinned host memory and the slots live in HBM.
+ *
+ * k3moe_slot_layout: byte offsets of gate_q, gate_s, up_q, up_s, down_q, down_s
+ *   within one slot (offsets[0..5], each 256-byte aligned) and the slot size
+ *   (offsets[6]).  Host experts must use the same layout, at host + layer *
+ *   layer_stride + expert * expert_stride.  Pure host function.
+ * k3moe_pool_create: a pool of n_slots slots over caller-owned device memory
+ *   `slots` (n_slots * offsets[6] bytes, 256-byte aligned); returns NULL on bad
+ *   arguments.  The pool is a host object; it allocates a small pinned staging
+ *   buffer and two events on first use (released by k3moe_pool_destroy).  One
+ *   host thread at a time may use a pool.
+ * k3moe_pool_plan: the placement step alone (no device work): for a token's K
+ *   experts of `layer` (host int32, K3MOE_PRUNED skipped) writes the slot of each
+ *   (slots[K], host) and whether it had to be loaded (missed[K]); hits are
+ *   refreshed first, each miss evicts the least recently used slot not used by
+ *   this token.  Requires K <= n_slots.
+ * k3moe_pool_weights: a k3moe_weights_t addressing the slots as n_slots experts.
+ * k3moe_pool_stats: out[0] hits, out[1] misses, out[2] bytes copied.
+ * k3moe_forward_decode_pooled: k3moe_forward_decode for one token of `layer`
+ *   whose experts live in host memory: copies idx (device, [K]) to the host and
+ *   waits for `stream` (the one host synchronisation), plans the slots, issues
+ *   one host-to-device copy per missing expert on copy_stream (after the kernels
+ *   of the previous pooled call, which may still read evicted slots), runs the
+ *   gate/up products of the resident experts on `stream` while the copies run,
+ *   then those of the copied experts, then down and the combine.  The output
+ *   equals k3moe_forward_decode's on the same experts bit for bit.  ws:
+ *   k3moe_workspace_size(K3MOE_OP_DECODE, 1, K, W) + 768 bytes.
+ */
+typedef struct k3moe_pool k3moe_pool_t;
+int k3moe_slot_layout(int32_t d_model, int32_t d_ff, int64_t *offsets);
+k3moe_pool_t *k3moe_pool_create(int32_t n_slots, int32_t d_model, int32_t d_ff, void *slots);
+void k3moe_pool_destroy(k3moe_pool_t *pool);
+int k3moe_pool_plan(k3moe_pool_t *pool, int32_t layer, const int32_t *experts, int32_t K, int32_t *slots,
+                    int32_t *missed);
+int k3moe_pool_weights(const k3moe_pool_t *pool, k3moe_weights_t *W);
+int k3moe_pool_stats(const k3moe_pool_t *pool, int64_t *out);
+int k3moe_forward_decode_pooled(k3moe_pool_t *pool, int32_t layer, const uint8_t *host, int64_t layer_stride,
+                                int64_t expert_stride, const float *x, const int32_t *idx, const float *w,
+                                int32_t K, float *y, void *ws, size_t ws_bytes, void *stream, void *copy_stream);
+
+/*
  * Bytes of device workspace needed by `op` (K3MOE_OP_*) for T tokens and K slots
  * per token on the layer described by W (n_experts, d_model, d_ff are read).
  * Returns 0 for invalid arguments.  Pure host function.

@@ -32,7 +32,8 @@ PRUNED = -1  # K3MOE_PRUNED: a routing slot dropped by top-p
 
 ENTRY_POINTS = ("k3moe_route", "k3moe_route_topp", "k3moe_group", "k3moe_forward_decode", "k3moe_decode_gateup",
                 "k3moe_decode_down", "k3moe_forward_chunk", "k3moe_workspace_size", "k3moe_dequant_mxfp4",
-                "k3moe_status_string")
+                "k3moe_status_string", "k3moe_slot_layout", "k3moe_pool_create", "k3moe_pool_destroy",
+                "k3moe_pool_plan", "k3moe_pool_weights", "k3moe_pool_stats", "k3moe_forward_decode_pooled")
 
 
 class K3moeError(RuntimeError):
@@ -72,8 +73,19 @@ def load() -> ctypes.CDLL:
     lib.k3moe_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, i32, vp]
     lib.k3moe_status_string.argtypes = [ctypes.c_int]
     lib.k3moe_status_string.restype = ctypes.c_char_p
+    i64 = ctypes.c_int64
+    lib.k3moe_route_topp.argtypes = [vp, vp, i32, i32, i32, ctypes.c_double, vp, vp, vp, vp]
+    lib.k3moe_slot_layout.argtypes = [i32, i32, vp]
+    lib.k3moe_pool_create.argtypes = [i32, i32, i32, vp]
+    lib.k3moe_pool_create.restype = vp
+    lib.k3moe_pool_destroy.argtypes = [vp]
+    lib.k3moe_pool_destroy.restype = None
+    lib.k3moe_pool_plan.argtypes = [vp, i32, vp, i32, vp, vp]
+    lib.k3moe_pool_weights.argtypes = [vp, wp]
+    lib.k3moe_pool_stats.argtypes = [vp, vp]
+    lib.k3moe_forward_decode_pooled.argtypes = [vp, i32, vp, i64, i64, vp, vp, vp, i32, vp, vp, sz, vp, vp]
     for name in ENTRY_POINTS:
-        if name not in ("k3moe_workspace_size", "k3moe_status_string"):
+        if name not in ("k3moe_workspace_size", "k3moe_status_string", "k3moe_pool_create", "k3moe_pool_destroy"):
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -136,6 +148,17 @@ class ExpertWeights:
     @classmethod
     def from_dict(cls, d: Dict[str, torch.Tensor]) -> "ExpertWeights":
         return cls(*(d[n] for n in cls.NAMES))
+
+    @classmethod
+    def from_struct(cls, struct: "WeightsStruct", keepalive=None) -> "ExpertWeights":
+        """Weights described by a filled k3moe_weights_t (e.g. a residency pool's
+        slots); ``keepalive`` holds the memory it points into."""
+        self = cls.__new__(cls)
+        self.tensors = {}
+        self.E, self.D, self.F = struct.n_experts, struct.d_model, struct.d_ff
+        self.struct = struct
+        self.keepalive = keepalive
+        return self
 
     def ref(self):
         return ctypes.byref(self.struct)
@@ -287,3 +310,84 @@ def dequant_mxfp4(q: torch.Tensor, s: torch.Tensor, out_dtype: torch.dtype = tor
     _check("k3moe_dequant_mxfp4",
            load().k3moe_dequant_mxfp4(_ptr(q), _ptr(s), O, I, _ptr(out), code, _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------- expert residency
+def slot_layout(D: int, F: int):
+    """Byte offsets of the six tensors within an expert slot, and the slot size."""
+    off = (ctypes.c_int64 * 7)()
+    _check("k3moe_slot_layout", load().k3moe_slot_layout(int(D), int(F), off))
+    return [int(v) for v in off]
+
+
+class Pool:
+    """An LRU pool of ``n_slots`` HBM expert slots over the uint8 device tensor
+    ``slots`` (at least ``n_slots * slot_bytes`` bytes, 256-byte aligned)."""
+
+    def __init__(self, n_slots: int, D: int, F: int, slots: torch.Tensor):
+        _dev(slots, torch.uint8, "slots")
+        self.layout = slot_layout(D, F)
+        if slots.numel() < n_slots * self.layout[6]:
+            raise ValueError("slots tensor too small")
+        self.slots = slots
+        self.n_slots, self.D, self.F = n_slots, D, F
+        self.handle = load().k3moe_pool_create(int(n_slots), int(D), int(F), _ptr(slots))
+        if not self.handle:
+            raise ValueError("k3moe_pool_create rejected its arguments")
+
+    def plan(self, layer: int, experts):
+        import numpy as np
+        e = np.ascontiguousarray(experts, dtype=np.int32)
+        slots = np.empty_like(e)
+        missed = np.empty_like(e)
+        _check("k3moe_pool_plan", load().k3moe_pool_plan(self.handle, int(layer), e.ctypes.data, e.size,
+                                                          slots.ctypes.data, missed.ctypes.data))
+        return slots, missed
+
+    def weights(self) -> ExpertWeights:
+        s = WeightsStruct()
+        _check("k3moe_pool_weights", load().k3moe_pool_weights(self.handle, ctypes.byref(s)))
+        return ExpertWeights.from_struct(s, keepalive=self.slots)
+
+    def stats(self):
+        out = (ctypes.c_int64 * 3)()
+        _check("k3moe_pool_stats", load().k3moe_pool_stats(self.handle, out))
+        return {"hits": int(out[0]), "misses": int(out[1]), "bytes": int(out[2])}
+
+    def close(self):
+        if getattr(self, "handle", None):
+            load().k3moe_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def forward_decode_pooled(pool: Pool, layer: int, host: torch.Tensor, layer_stride: int, expert_stride: int,
+                          x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor, y: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None, stream=None, copy_stream=None) -> torch.Tensor:
+    """``forward_decode`` for one token whose layer-``layer`` experts live in the
+    pinned host tensor ``host`` (slot layout, at layer*layer_stride +
+    expert*expert_stride); missing experts are copied into the pool on
+    ``copy_stream`` while the resident ones compute."""
+    if not isinstance(host, torch.Tensor) or host.is_cuda or not host.is_pinned():
+        raise TypeError("host must be a pinned CPU tensor")
+    x = _dev(x, torch.float32, "x", (pool.D,))
+    idx = idx.reshape(-1)
+    w = w.reshape(-1)
+    K = idx.numel()
+    _dev(idx, torch.int32, "idx", (K,))
+    _dev(w, torch.float32, "w", (K,))
+    y = torch.empty(pool.D, dtype=torch.float32, device=x.device) if y is None else y
+    _dev(y, torch.float32, "y", (pool.D,))
+    W = pool.weights()
+    ws = _workspace(workspace_size(OP_DECODE, 1, K, W) + 768, x.device, ws)
+    cs = _stream(copy_stream if copy_stream is not None else stream)
+    _check("k3moe_forward_decode_pooled",
+           load().k3moe_forward_decode_pooled(pool.handle, int(layer), ctypes.c_void_p(host.data_ptr()),
+                                              int(layer_stride), int(expert_stride), _ptr(x), _ptr(idx), _ptr(w),
+                                              K, _ptr(y), _ptr(ws), ws.numel(), _stream(stream), cs))
+    return y
