@@ -221,6 +221,30 @@ double k3o_situ(double g, double u) { return k3o_situ_beta(g, u, 4.0, 25.0); }
 
 /* ------------------------------------------------------------------- expert FFN */
 
+static void expert_gateup(const float *Wg, const float *Wu, int32_t D, int32_t F, const float *x,
+                          double *g, double *u, double *h)
+{
+    for (int32_t f = 0; f < F; ++f) {
+        double ag = 0.0, au = 0.0;
+        for (int32_t i = 0; i < D; ++i) {
+            ag += (double)Wg[(int64_t)f * D + i] * (double)x[i];
+            au += (double)Wu[(int64_t)f * D + i] * (double)x[i];
+        }
+        if (g) g[f] = ag;
+        if (u) u[f] = au;
+        h[f] = k3o_situ(ag, au);
+    }
+}
+
+static void expert_down(const float *Wd, int32_t D, int32_t F, const double *h, double *y)
+{
+    for (int32_t d = 0; d < D; ++d) {
+        double ay = 0.0;
+        for (int32_t f = 0; f < F; ++f) ay += (double)Wd[(int64_t)d * F + f] * h[f];
+        y[d] = ay;
+    }
+}
+
 /* One routed expert on one token, on already-decoded fp32 weights
  * Wg, Wu [F, D] and Wd [D, F]:
  *   g_f = sum_i Wg[f,i] x_i,  u_f = sum_i Wu[f,i] x_i     (double, ascending i)
@@ -232,23 +256,125 @@ void k3o_expert(const float *Wg, const float *Wu, const float *Wd, int32_t D, in
                 const float *x, double *g, double *u, double *h, double *y)
 {
     double *hh = (double *)malloc(sizeof(double) * (size_t)F);
-    for (int32_t f = 0; f < F; ++f) {
-        double ag = 0.0, au = 0.0;
-        for (int32_t i = 0; i < D; ++i) {
-            ag += (double)Wg[(int64_t)f * D + i] * (double)x[i];
-            au += (double)Wu[(int64_t)f * D + i] * (double)x[i];
-        }
-        if (g) g[f] = ag;
-        if (u) u[f] = au;
-        hh[f] = k3o_situ(ag, au);
-        if (h) h[f] = hh[f];
-    }
-    for (int32_t d = 0; d < D; ++d) {
-        double ay = 0.0;
-        for (int32_t f = 0; f < F; ++f) ay += (double)Wd[(int64_t)d * F + f] * hh[f];
-        y[d] = ay;
-    }
+    expert_gateup(Wg, Wu, D, F, x, g, u, hh);
+    if (h)
+        for (int32_t f = 0; f < F; ++f) h[f] = hh[f];
+    expert_down(Wd, D, F, hh, y);
     free(hh);
+}
+
+/* ---------------------------------------------------- MXFP8 activations (variant) */
+
+/* The low-precision-activation variant of the chunk path: the GPU analog of the
+ * pages' per-32 int8 activations ([PR684] int8-activation commit, K3_IDOT: the
+ * activations are quantized in groups of 32 and multiplied with the MXFP4
+ * weights as they are).  Here the groups are OCP MX: 32 consecutive values share
+ * one E8M0 scale 2^(s-127) and each value is an FP8 E4M3 code (bias 7, three
+ * mantissa bits, subnormals, largest finite 448, 0x7F/0xFF NaN).  For a group:
+ *   amax = max |v|;  amax = 0: s = 0 and every code 0;
+ *   otherwise s = clamp(floor(log2 amax) - 8 + 127, 0, 254) (8 = E4M3's largest
+ *   exponent), y = v / 2^(s-127), clamped to [-448, 448], rounded to the nearest
+ *   E4M3 value with ties to the even code;
+ *   a group holding a NaN or an infinity gets the E8M0 NaN scale s = 255 and
+ *   NaN codes 0x7F.
+ * Every step is exact in double (power-of-two scaling, one rounding). */
+double k3o_e4m3_decode(unsigned code)
+{
+    const unsigned e = (code >> 3) & 15u, m = code & 7u;
+    if ((code & 0x7Fu) == 0x7Fu) return NAN;
+    const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, (int)e - 7);
+    return (code & 0x80u) ? -mag : mag;
+}
+
+static unsigned e4m3_encode(double y) /* |y| <= 448, finite */
+{
+    const unsigned sign = (y < 0.0 || (y == 0.0 && signbit(y))) ? 0x80u : 0u;
+    const double a = fabs(y);
+    if (a < ldexp(1.0, -6)) {          /* subnormal range: quantum 2^-9 */
+        const double q = nearbyint(ldexp(a, 9));   /* ties to even (default mode) */
+        return sign | (unsigned)q;     /* q = 8 is the smallest normal, code 0x08 */
+    }
+    int e2;
+    (void)frexp(a, &e2);               /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                    /* floor(log2 a), in [-6, 8] */
+    double m = nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+    if (m == 8.0) {
+        m = 0.0;
+        ++e;
+    }
+    unsigned code = (unsigned)((e + 7) << 3) | (unsigned)m;
+    if (code > 0x7Eu) code = 0x7Eu;    /* saturate at 448 */
+    return sign | code;
+}
+
+void k3o_mx_quant(const float *v, int64_t n, uint8_t *codes, uint8_t *scales)
+{
+    for (int64_t b = 0; b < n / 32; ++b) {
+        const float *g = v + 32 * b;
+        double amax = 0.0;
+        int finite = 1;
+        for (int i = 0; i < 32; ++i) {
+            if (!isfinite(g[i])) finite = 0;
+            else if (fabs((double)g[i]) > amax) amax = fabs((double)g[i]);
+        }
+        if (!finite) {
+            scales[b] = 255;
+            for (int i = 0; i < 32; ++i) codes[32 * b + i] = 0x7F;
+            continue;
+        }
+        if (amax == 0.0) {
+            scales[b] = 0;
+            for (int i = 0; i < 32; ++i) codes[32 * b + i] = (uint8_t)(signbit(g[i]) ? 0x80 : 0);
+            continue;
+        }
+        int e2;
+        (void)frexp(amax, &e2);
+        int s = (e2 - 1) - 8 + 127;
+        if (s < 0) s = 0;
+        if (s > 254) s = 254;
+        scales[b] = (uint8_t)s;
+        for (int i = 0; i < 32; ++i) {
+            double y = ldexp((double)g[i], 127 - s);
+            if (y > 448.0) y = 448.0;
+            if (y < -448.0) y = -448.0;
+            codes[32 * b + i] = (uint8_t)e4m3_encode(y);
+        }
+    }
+}
+
+/* v -> MXFP8 -> back to float, for a vector of n values (n % 32 == 0).  Every
+ * MXFP8 value of a finite fp32 input is an fp32 value: the scale exponent stays
+ * within [-127, 119] and E4M3 carries four significant bits. */
+static void mx_roundtrip(const float *v, int64_t n, float *out)
+{
+    uint8_t *c = (uint8_t *)malloc((size_t)n), *sc = (uint8_t *)malloc((size_t)(n / 32));
+    k3o_mx_quant(v, n, c, sc);
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = sc[i / 32] == 255 ? NAN : (float)(k3o_e4m3_decode(c[i]) * ldexp(1.0, (int)sc[i / 32] - 127));
+    free(c);
+    free(sc);
+}
+
+/* k3o_expert with MXFP8 activations: x is quantized as above, g and u are exact
+ * sums over the quantized x, h = SiTU(g, u) is rounded to fp32 and quantized the
+ * same way (in groups of 32 consecutive f), and y is the exact sum over it. */
+void k3o_expert_mx(const float *Wg, const float *Wu, const float *Wd, int32_t D, int32_t F,
+                   const float *x, double *h, double *y)
+{
+    float *xq = (float *)malloc(sizeof(float) * (size_t)D);
+    float *hf = (float *)malloc(sizeof(float) * (size_t)F);
+    double *hd = (double *)malloc(sizeof(double) * (size_t)F);
+    mx_roundtrip(x, D, xq);
+    expert_gateup(Wg, Wu, D, F, xq, NULL, NULL, hd);
+    for (int32_t f = 0; f < F; ++f) hf[f] = (float)hd[f];
+    mx_roundtrip(hf, F, hf);
+    for (int32_t f = 0; f < F; ++f) hd[f] = hf[f];
+    if (h)
+        for (int32_t f = 0; f < F; ++f) h[f] = hd[f];
+    expert_down(Wd, D, F, hd, y);
+    free(xq);
+    free(hf);
+    free(hd);
 }
 
 /* ----------------------------------------------------------------- block forward */
@@ -263,11 +389,11 @@ void k3o_expert(const float *Wg, const float *Wu, const float *Wd, int32_t D, in
  * any pair's arithmetic.  ytk (nullable) receives the per-pair expert outputs
  * [T, K, D] in double; hk (nullable) the per-pair activations [T, K, F].
  * Returns 0, or -1 if an index is out of range or memory runs out. */
-int k3o_forward(int32_t E, int32_t D, int32_t F,
-                const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
-                const uint8_t *dq, const uint8_t *ds,
-                const float *x, int32_t T, const int32_t *idx, const float *w, int32_t K,
-                float *y, double *ytk, double *hk, int32_t nthreads)
+static int forward_impl(int32_t E, int32_t D, int32_t F,
+                        const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
+                        const uint8_t *dq, const uint8_t *ds,
+                        const float *x, int32_t T, const int32_t *idx, const float *w, int32_t K,
+                        float *y, double *ytk, double *hk, int32_t nthreads, int mx)
 {
     int64_t P = (int64_t)T * K;
     for (int64_t p = 0; p < P; ++p)
@@ -308,8 +434,11 @@ int k3o_forward(int32_t E, int32_t D, int32_t F,
             for (int64_t p = 0; p < P; ++p) {
                 if (idx[p] != e) continue;
                 int64_t t = p / K;
-                k3o_expert(Wg, Wu, Wd, D, F, x + t * D, NULL, NULL,
-                           hk ? hk + p * F : NULL, yp + p * D);
+                if (mx)
+                    k3o_expert_mx(Wg, Wu, Wd, D, F, x + t * D, hk ? hk + p * F : NULL, yp + p * D);
+                else
+                    k3o_expert(Wg, Wu, Wd, D, F, x + t * D, NULL, NULL,
+                               hk ? hk + p * F : NULL, yp + p * D);
             }
         }
         free(Wg);
@@ -331,6 +460,26 @@ int k3o_forward(int32_t E, int32_t D, int32_t F,
     free(list);
     if (!ytk) free(yp);
     return failed ? -1 : 0;
+}
+
+int k3o_forward(int32_t E, int32_t D, int32_t F,
+                const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
+                const uint8_t *dq, const uint8_t *ds,
+                const float *x, int32_t T, const int32_t *idx, const float *w, int32_t K,
+                float *y, double *ytk, double *hk, int32_t nthreads)
+{
+    return forward_impl(E, D, F, gq, gs, uq, us, dq, ds, x, T, idx, w, K, y, ytk, hk, nthreads, 0);
+}
+
+/* k3o_forward with MXFP8 activations (k3o_expert_mx for every pair); hk receives
+ * the dequantized h. */
+int k3o_forward_mx(int32_t E, int32_t D, int32_t F,
+                   const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
+                   const uint8_t *dq, const uint8_t *ds,
+                   const float *x, int32_t T, const int32_t *idx, const float *w, int32_t K,
+                   float *y, double *ytk, double *hk, int32_t nthreads)
+{
+    return forward_impl(E, D, F, gq, gs, uq, us, dq, ds, x, T, idx, w, K, y, ytk, hk, nthreads, 1);
 }
 
 /* ------------------------------------------------------------------ chunk grouping */

@@ -487,11 +487,158 @@ def check_group_pruned(o):
     assert g["counts"].tolist() == counts and int(g["offsets"][E]) == len(pairs)
 
 
+# --------------------------------------------------------------- P10 MXFP8 activations
+def e4m3_value(code: int):
+    """OCP FP8 E4M3 from its bit fields: sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN
+    and there are no infinities.  Returns a Fraction, or None for NaN."""
+    if code & 0x7F == 0x7F:
+        return None
+    e, m = (code >> 3) & 15, code & 7
+    mag = Fraction(m, 8) * Fraction(1, 64) if e == 0 else Fraction(2) ** (e - 7) * (1 + Fraction(m, 8))
+    return -mag if code & 0x80 else mag
+
+
+_E4M3_MAGS = [e4m3_value(c) for c in range(0x7F)]  # increasing in the code
+
+
+def brute_mx_block(v):
+    """One MX block of 32 fp32 values by search: the E8M0 scale is the s for which
+    amax / 2^(s-127) lies in [256, 512) (so the largest value lands in E4M3's top
+    binade), clamped to [0, 254]; each value goes to the nearest E4M3 magnitude after
+    clamping to 448, ties to the even code, sign kept."""
+    vals = [float(t) for t in v]
+    if any(math.isnan(t) or math.isinf(t) for t in vals):
+        return [0x7F] * 32, 255
+    amax = max(Fraction(abs(t)) for t in vals)
+    if amax == 0:
+        return [0x80 if math.copysign(1.0, t) < 0 else 0 for t in vals], 0
+    s = 0
+    while s < 254 and amax >= 512 * Fraction(2) ** (s - 127):
+        s += 1
+    codes = []
+    for t in vals:
+        y = min(Fraction(abs(t)) / Fraction(2) ** (s - 127), Fraction(448))
+        best = min(range(0x7F), key=lambda c: (abs(_E4M3_MAGS[c] - y), c & 1))
+        codes.append(best | (0x80 if math.copysign(1.0, t) < 0 else 0))
+    return codes, s
+
+
+def mx_dequant_py(codes, s):
+    return [float(e4m3_value(c) * Fraction(2) ** (s - 127)) for c in codes]
+
+
+def check_e4m3_decode(o):
+    """All 256 E4M3 codes decode to their bit-field values; the format's landmarks:
+    448 largest finite, 2^-6 smallest normal, 2^-9 smallest subnormal."""
+    for c in range(256):
+        want, got = e4m3_value(c), o.e4m3(c)
+        if want is None:
+            assert math.isnan(got), c
+        else:
+            assert Fraction(got) == want, c
+    assert o.e4m3(0x7E) == 448.0 and o.e4m3(0x08) == 2.0 ** -6 and o.e4m3(0x01) == 2.0 ** -9
+    assert o.e4m3(0x38) == 1.0 and o.e4m3(0xB8) == -1.0
+
+
+def check_mx_quant_exact_values(o):
+    """A block whose largest magnitude is 448 has scale 2^0, and every E4M3 value in
+    it is kept bit for bit (quantization is the inverse of decoding there)."""
+    finite = [c for c in range(256) if c & 0x7F != 0x7F]
+    blocks = []
+    for i in range(0, len(finite), 31):
+        part = finite[i:i + 31]
+        part = part + [0] * (31 - len(part))
+        blocks.append([0x7E] + part)
+    val = lambda c: math.copysign(float(e4m3_value(c)), -1.0 if c & 0x80 else 1.0)  # keeps -0
+    v = np.array([[val(c) for c in b] for b in blocks], np.float32)
+    codes, scales = o.mx_quant(v.reshape(-1))
+    assert scales.tolist() == [127] * len(blocks)
+    assert codes.tolist() == [c for b in blocks for c in b]
+
+
+def check_mx_quant_brute(o):
+    """Random blocks over a wide spread of magnitudes, with exact ties, values past
+    the saturation point and subnormal outputs: codes and scales equal the search."""
+    rng = np.random.default_rng(53)
+    blocks = []
+    for b in range(48):
+        v = rng.standard_normal(32) * np.exp2(rng.integers(-30, 30, size=32) * (b % 3 == 0))
+        v *= 2.0 ** int(rng.integers(-95, 95))
+        blocks.append(v)
+    # ties: midpoints of adjacent E4M3 magnitudes under scale 2^0 (448 fixes the scale)
+    mids = [float((_E4M3_MAGS[c] + _E4M3_MAGS[c + 1]) / 2) for c in range(0, 0x7E)]
+    for i in range(0, len(mids), 31):
+        part = mids[i:i + 31]
+        blocks.append(np.array([448.0] + part + [0.0] * (31 - len(part))))
+    # saturation: amax in (448, 512) times a power of two
+    blocks.append(np.array([470.0, -500.0, 463.9, 464.0] + [1.0] * 28) * 2.0 ** 20)
+    # tiny blocks: scale clamps at 0, subnormal fp32 inputs
+    blocks.append(np.array([1e-39, -3e-40, 2e-45] + [0.0] * 29))
+    blocks.append(np.array([-0.0] * 32))
+    v = np.concatenate(blocks).astype(np.float32)
+    codes, scales = o.mx_quant(v)
+    for b in range(len(blocks)):
+        want_c, want_s = brute_mx_block(v[32 * b:32 * b + 32])
+        assert int(scales[b]) == want_s, (b, int(scales[b]), want_s)
+        assert codes[32 * b:32 * b + 32].tolist() == want_c, b
+
+
+def check_mx_quant_special(o):
+    """Zero block: scale 0 and zero codes; a NaN or an infinity anywhere in a block
+    makes the whole block NaN (E8M0 NaN scale 255, codes 0x7F), other blocks untouched."""
+    v = np.zeros(128, np.float32)
+    v[40] = np.nan
+    v[64 + 3] = np.inf
+    v[96:] = 1.0
+    codes, scales = o.mx_quant(v)
+    assert scales.tolist() == [0, 255, 255, 119]
+    assert codes[:32].tolist() == [0] * 32 and codes[32:96].tolist() == [0x7F] * 64
+    assert codes[96:].tolist() == [0x78] * 32  # 1.0 under scale 2^-8 is 256: exponent field 15
+
+
+def check_forward_mx(o):
+    """The MXFP8 variant on a small block: every pair's h is the MX round trip of the
+    fp32-rounded SiTU of exact sums over the MX round trip of x, and y is the exact
+    w-weighted sum of the down rows over that h (fsum of exact products)."""
+    import synth
+    cfg = synth.scaled(synth.CONFIGS["tiny"], T=2, E=4, K=2, D=64, F=64)
+    W = synth.weights_host(cfg)
+    x, logits, bias = synth.activations(cfg)
+    idx, w, _ = o.route(logits, bias, cfg.K)
+    y, ytk, hk = o.forward(W, x, idx, w, nthreads=1, want_pairs=True, mx=True)
+    for t in range(cfg.T):
+        xc, xs = zip(*[brute_mx_block(x[t, 32 * b:32 * b + 32]) for b in range(cfg.D // 32)])
+        xq = [val for b in range(cfg.D // 32) for val in mx_dequant_py(xc[b], xs[b])]
+        for k in range(cfg.K):
+            e = int(idx[t, k])
+            Wg = o.dequant(W["gate_q"][e], W["gate_s"][e]).astype(np.float64)
+            Wu = o.dequant(W["up_q"][e], W["up_s"][e]).astype(np.float64)
+            Wd = o.dequant(W["down_q"][e], W["down_s"][e]).astype(np.float64)
+            hf = np.array([o.situ(math.fsum(Wg[f] * xq), math.fsum(Wu[f] * xq)) for f in range(cfg.F)],
+                          np.float32)
+            hq = []
+            for b in range(cfg.F // 32):
+                c, s_ = brute_mx_block(hf[32 * b:32 * b + 32])
+                hq += mx_dequant_py(c, s_)
+            assert hk[t, k].tolist() == hq, (t, k)
+            for d in range(cfg.D):
+                terms = Wd[d] * np.array(hq)
+                exact = math.fsum(terms)
+                assert abs(ytk[t, k, d] - exact) <= 1e-12 * math.fsum(np.abs(terms)) + 1e-300, (t, k, d)
+        acc = np.zeros(cfg.D)
+        for k in range(cfg.K):
+            acc = acc + np.float64(w[t, k]) * ytk[t, k]
+        assert np.array_equal(y[t], acc.astype(np.float32)), t
+
+
 ALL_CHECKS = [
     check_decode_closed_form, check_decode_conventions, check_layout_fixture, check_scale_groups,
     check_dequant_matches_codes, check_expert_brute_force, check_route_brute_force,
     check_route_invariants, check_route_bias_reading, check_route_nan, check_situ,
     check_forward_pairs, check_forward_combine, check_chunk_equals_tokens, check_group,
     check_route_topp_definition, check_route_topp_off_and_monotone, check_forward_pruned, check_group_pruned,
+    check_e4m3_decode, check_mx_quant_exact_values, check_mx_quant_brute, check_mx_quant_special,
+    check_forward_mx,
 ]
 # check_gate_moments is run separately (it pins the generator, and is the slowest)

@@ -36,7 +36,7 @@ MUTANTS = [
     ("sigmoid sign", "return 1.0 / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(z));"),
     ("betas swapped", "k3o_situ_beta(g, u, 4.0, 25.0)", "k3o_situ_beta(g, u, 25.0, 4.0)"),
     ("sigma on up branch", "sigmoid(g) * bu", "sigmoid(u) * bu"),
-    ("gate/up swapped", "hh[f] = k3o_situ(ag, au);", "hh[f] = k3o_situ(au, ag);"),
+    ("gate/up swapped", "h[f] = k3o_situ(ag, au);", "h[f] = k3o_situ(au, ag);"),
     ("down transposed", "Wd[(int64_t)d * F + f]", "Wd[(int64_t)f * D + d]"),
     ("dropped last input term", "for (int32_t i = 0; i < D; ++i) {", "for (int32_t i = 0; i < D - 1; ++i) {"),
     ("wrong token for a pair", "x + t * D, NULL, NULL", "x + (p % T) * D, NULL, NULL"),
@@ -51,6 +51,13 @@ MUTANTS = [
     ("top-p renormalizes over all K", "if (kept[k]) Sk += score[c[k].id];", "Sk += score[c[k].id];"),
     ("top-p threshold on weights of all experts", "const double thr = p * S;", "const double thr = p * S * 1.05;"),
     ("group keeps pruned pairs", "if (idx[p] == -1) continue;\n        if (idx[p] < 0", "if (idx[p] == -1) { counts[0]++; continue; }\n        if (idx[p] < 0"),
+    ("mx scale offset 7", "int s = (e2 - 1) - 8 + 127;", "int s = (e2 - 1) - 7 + 127;"),
+    ("mx ties away from zero", "double m = nearbyint((ldexp(a, -e) - 1.0) * 8.0);", "double m = round((ldexp(a, -e) - 1.0) * 8.0);"),
+    ("mx subnormal boundary", "if (a < ldexp(1.0, -6)) {", "if (a < ldexp(1.0, -7)) {"),
+    ("e4m3 exponent bias 8", "ldexp(1.0 + m / 8.0, (int)e - 7)", "ldexp(1.0 + m / 8.0, (int)e - 8)"),
+    ("mx zero block scale", "            scales[b] = 0;\n", "            scales[b] = 127;\n"),
+    ("mx h kept in fp32", "    mx_roundtrip(hf, F, hf);", ""),
+    ("mx x kept in fp32", "    mx_roundtrip(x, D, xq);", "    memcpy(xq, x, sizeof(float) * (size_t)D);"),
     ("offsets inclusive", "offsets[e + 1] = offsets[e] + counts[e];", "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
 ]
 
