@@ -73,7 +73,9 @@ def _bind(path: str):
                                 [_F32P, ctypes.c_int32, _I32P, _F32P, ctypes.c_int32, _F32P,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32])
     lib.k3o_forward_mx.restype = ctypes.c_int
-    lib.k3o_forward_mx.argtypes = lib.k3o_forward.argtypes
+    lib.k3o_forward_mx.argtypes = lib.k3o_forward.argtypes + [ctypes.c_int32]
+    lib.k3o_mx_quant_parts.restype = None
+    lib.k3o_mx_quant_parts.argtypes = [_F32P, ctypes.c_int64, ctypes.c_int32, _U8P, _U8P]
     lib.k3o_mx_quant.restype = None
     lib.k3o_mx_quant.argtypes = [_F32P, ctypes.c_int64, _U8P, _U8P]
     lib.k3o_e4m3_decode.restype = ctypes.c_double
@@ -177,12 +179,13 @@ class Oracle:
 
     # ------------------------------------------------------------------------ forward
     def forward(self, weights: Dict[str, np.ndarray], x: np.ndarray, idx: np.ndarray, w: np.ndarray,
-                nthreads: Optional[int] = None, want_pairs: bool = False, mx: bool = False):
+                nthreads: Optional[int] = None, want_pairs: bool = False, mx: int = 0):
         """Routed-expert block on host weights ``{name: [E, rows, cols]}``.
 
         Returns ``y [T, D] f32``; with ``want_pairs`` also ``(ytk [T,K,D], hk [T,K,F])``
-        in float64.  ``mx=True`` runs the MXFP8-activation variant (``k3o_forward_mx``:
-        x and h quantized per 32 to E4M3 with an E8M0 scale).
+        in float64.  ``mx=1`` or ``mx=2`` runs the MXFP8-activation variant in that many
+        parts (``k3o_forward_mx``: x and h quantized per 32 to E4M3 with an E8M0 scale,
+        weight scale byte 255 read as NaN).
         """
         names = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
         arrs = [_c(weights[n], np.uint8) for n in names]
@@ -201,27 +204,28 @@ class Oracle:
         y = np.empty((T, D), dtype=np.float32)
         ytk = np.empty((T, K, D)) if want_pairs else None
         hk = np.empty((T, K, F)) if want_pairs else None
-        fwd = self.lib.k3o_forward_mx if mx else self.lib.k3o_forward
-        rc = fwd(E, D, F, *arrs, x, T, idx, w, K, y,
-                                 ytk.ctypes.data if want_pairs else None,
-                                 hk.ctypes.data if want_pairs else None,
-                                 int(nthreads or default_threads()))
+        args = [E, D, F, *arrs, x, T, idx, w, K, y, ytk.ctypes.data if want_pairs else None,
+                hk.ctypes.data if want_pairs else None, int(nthreads or default_threads())]
+        rc = self.lib.k3o_forward_mx(*args, int(mx)) if mx else self.lib.k3o_forward(*args)
         if rc != 0:
             raise ValueError("oracle forward failed (expert index out of range or out of memory)")
         return (y, ytk, hk) if want_pairs else y
 
     # ------------------------------------------------------------ MXFP8 activations
-    def mx_quant(self, v: np.ndarray):
-        """OCP MXFP8 (E4M3, E8M0 scale per 32) of a float32 vector whose length is a
-        multiple of 32 (or of rows of one).  Returns ``(codes u8, scales u8)`` of
-        shapes ``v.shape`` and ``v.shape[:-1] + (n/32,)``."""
+    def mx_quant(self, v: np.ndarray, parts: int = 1):
+        """OCP MXFP8 (E4M3, E8M0 scale per 32) of a float32 array whose last dimension
+        is a multiple of 32, in ``parts`` parts (2: the second part quantizes the
+        residual).  Returns ``(codes u8, scales u8)``; with one part of shapes
+        ``v.shape`` and ``v.shape[:-1] + (n/32,)``, with two parts with a leading 2."""
         v = _c(v, np.float32)
         if v.shape[-1] % 32:
             raise ValueError("last dimension must be a multiple of 32")
-        codes = np.empty(v.shape, np.uint8)
-        scales = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
-        self.lib.k3o_mx_quant(v, v.size, codes, scales)
-        return codes, scales
+        if parts not in (1, 2):
+            raise ValueError("parts must be 1 or 2")
+        codes = np.empty((parts,) + v.shape, np.uint8)
+        scales = np.empty((parts,) + v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+        self.lib.k3o_mx_quant_parts(v, v.size, parts, codes, scales)
+        return (codes[0], scales[0]) if parts == 1 else (codes, scales)
 
     def e4m3(self, code: int) -> float:
         return float(self.lib.k3o_e4m3_decode(int(code)))

@@ -221,14 +221,14 @@ double k3o_situ(double g, double u) { return k3o_situ_beta(g, u, 4.0, 25.0); }
 
 /* ------------------------------------------------------------------- expert FFN */
 
-static void expert_gateup(const float *Wg, const float *Wu, int32_t D, int32_t F, const float *x,
+static void expert_gateup(const float *Wg, const float *Wu, int32_t D, int32_t F, const double *x,
                           double *g, double *u, double *h)
 {
     for (int32_t f = 0; f < F; ++f) {
         double ag = 0.0, au = 0.0;
         for (int32_t i = 0; i < D; ++i) {
-            ag += (double)Wg[(int64_t)f * D + i] * (double)x[i];
-            au += (double)Wu[(int64_t)f * D + i] * (double)x[i];
+            ag += (double)Wg[(int64_t)f * D + i] * x[i];
+            au += (double)Wu[(int64_t)f * D + i] * x[i];
         }
         if (g) g[f] = ag;
         if (u) u[f] = au;
@@ -256,7 +256,10 @@ void k3o_expert(const float *Wg, const float *Wu, const float *Wd, int32_t D, in
                 const float *x, double *g, double *u, double *h, double *y)
 {
     double *hh = (double *)malloc(sizeof(double) * (size_t)F);
-    expert_gateup(Wg, Wu, D, F, x, g, u, hh);
+    double *xd = (double *)calloc((size_t)D, sizeof(double));
+    for (int32_t i = 0; i < D; ++i) xd[i] = x[i];
+    expert_gateup(Wg, Wu, D, F, xd, g, u, hh);
+    free(xd);
     if (h)
         for (int32_t f = 0; f < F; ++f) h[f] = hh[f];
     expert_down(Wd, D, F, hh, y);
@@ -342,33 +345,67 @@ void k3o_mx_quant(const float *v, int64_t n, uint8_t *codes, uint8_t *scales)
     }
 }
 
-/* v -> MXFP8 -> back to float, for a vector of n values (n % 32 == 0).  Every
- * MXFP8 value of a finite fp32 input is an fp32 value: the scale exponent stays
- * within [-127, 119] and E4M3 carries four significant bits. */
-static void mx_roundtrip(const float *v, int64_t n, float *out)
+/* Value of one MXFP8 element (scale byte 255 is the E8M0 NaN).  Every value of a
+ * block quantized from finite fp32 input is an fp32 value: its scale exponent
+ * lies in [-127, 119] and E4M3 carries four significant bits. */
+static float mx_value(uint8_t code, uint8_t scale)
 {
-    uint8_t *c = (uint8_t *)malloc((size_t)n), *sc = (uint8_t *)malloc((size_t)(n / 32));
-    k3o_mx_quant(v, n, c, sc);
-    for (int64_t i = 0; i < n; ++i)
-        out[i] = sc[i / 32] == 255 ? NAN : (float)(k3o_e4m3_decode(c[i]) * ldexp(1.0, (int)sc[i / 32] - 127));
+    return scale == 255 ? NAN : (float)(k3o_e4m3_decode(code) * ldexp(1.0, (int)scale - 127));
+}
+
+/* Quantization in `parts` MXFP8 parts (1 or 2): part 0 is v quantized as above;
+ * part 1 is the fp32 residual v - part0 quantized the same way (the residual is
+ * exact in fp32: part 0 is v rounded to nearest on a grid coarser than v's, so
+ * it lies within a factor two of v or is zero).  codes [parts][n],
+ * scales [parts][n/32]. */
+void k3o_mx_quant_parts(const float *v, int64_t n, int32_t parts, uint8_t *codes, uint8_t *scales)
+{
+    k3o_mx_quant(v, n, codes, scales);
+    if (parts < 2) return;
+    float *r = (float *)malloc(sizeof(float) * (size_t)n);
+    for (int64_t i = 0; i < n; ++i) r[i] = v[i] - mx_value(codes[i], scales[i / 32]);
+    k3o_mx_quant(r, n, codes + n, scales + n / 32);
+    free(r);
+}
+
+/* v -> MXFP8 in `parts` parts -> the sum of the parts' values, in double. */
+static void mx_roundtrip(const float *v, int64_t n, int32_t parts, double *out)
+{
+    uint8_t *c = (uint8_t *)malloc((size_t)(2 * n)), *sc = (uint8_t *)malloc((size_t)(2 * (n / 32)));
+    k3o_mx_quant_parts(v, n, parts, c, sc);
+    for (int64_t i = 0; i < n; ++i) {
+        out[i] = mx_value(c[i], sc[i / 32]);
+        if (parts > 1) out[i] += mx_value(c[n + i], sc[n / 32 + i / 32]);
+    }
     free(c);
     free(sc);
 }
 
-/* k3o_expert with MXFP8 activations: x is quantized as above, g and u are exact
- * sums over the quantized x, h = SiTU(g, u) is rounded to fp32 and quantized the
- * same way (in groups of 32 consecutive f), and y is the exact sum over it. */
-void k3o_expert_mx(const float *Wg, const float *Wu, const float *Wd, int32_t D, int32_t F,
-                   const float *x, double *h, double *y)
+/* In the MXFP8 variant the weights are OCP MXFP4: the same e2m1 codes and scale
+ * bytes, but scale byte 255 is the E8M0 NaN, so every weight of such a group is
+ * NaN (the exact path reads it as 2^128 instead). */
+static void mx_weight_nan(const uint8_t *s, int64_t O, int64_t I, float *W)
 {
-    float *xq = (float *)malloc(sizeof(float) * (size_t)D);
+    for (int64_t o = 0; o < O; ++o)
+        for (int64_t b = 0; b < I / 32; ++b)
+            if (s[o * (I / 32) + b] == 255)
+                for (int64_t i = 0; i < 32; ++i) W[o * I + 32 * b + i] = NAN;
+}
+
+/* k3o_expert with MXFP8 activations in `parts` parts: x is quantized as above,
+ * g and u are sums over the quantized x, h = SiTU(g, u) is rounded to fp32 and
+ * quantized the same way (in groups of 32 consecutive f), and y is the sum over
+ * that h; sums in double, ascending index. */
+void k3o_expert_mx(const float *Wg, const float *Wu, const float *Wd, int32_t D, int32_t F,
+                   int32_t parts, const float *x, double *h, double *y)
+{
+    double *xq = (double *)malloc(sizeof(double) * (size_t)D);
     float *hf = (float *)malloc(sizeof(float) * (size_t)F);
     double *hd = (double *)malloc(sizeof(double) * (size_t)F);
-    mx_roundtrip(x, D, xq);
+    mx_roundtrip(x, D, parts, xq);
     expert_gateup(Wg, Wu, D, F, xq, NULL, NULL, hd);
     for (int32_t f = 0; f < F; ++f) hf[f] = (float)hd[f];
-    mx_roundtrip(hf, F, hf);
-    for (int32_t f = 0; f < F; ++f) hd[f] = hf[f];
+    mx_roundtrip(hf, F, parts, hd);
     if (h)
         for (int32_t f = 0; f < F; ++f) h[f] = hd[f];
     expert_down(Wd, D, F, hd, y);
@@ -393,7 +430,7 @@ static int forward_impl(int32_t E, int32_t D, int32_t F,
                         const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
                         const uint8_t *dq, const uint8_t *ds,
                         const float *x, int32_t T, const int32_t *idx, const float *w, int32_t K,
-                        float *y, double *ytk, double *hk, int32_t nthreads, int mx)
+                        float *y, double *ytk, double *hk, int32_t nthreads, int32_t mx_parts)
 {
     int64_t P = (int64_t)T * K;
     for (int64_t p = 0; p < P; ++p)
@@ -431,11 +468,16 @@ static int forward_impl(int32_t E, int32_t D, int32_t F,
             k3o_dequant(gq + e * gq_n, gs + e * gs_n, F, D, Wg);
             k3o_dequant(uq + e * gq_n, us + e * gs_n, F, D, Wu);
             k3o_dequant(dq + e * dq_n, ds + e * ds_n, D, F, Wd);
+            if (mx_parts) {
+                mx_weight_nan(gs + e * gs_n, F, D, Wg);
+                mx_weight_nan(us + e * gs_n, F, D, Wu);
+                mx_weight_nan(ds + e * ds_n, D, F, Wd);
+            }
             for (int64_t p = 0; p < P; ++p) {
                 if (idx[p] != e) continue;
                 int64_t t = p / K;
-                if (mx)
-                    k3o_expert_mx(Wg, Wu, Wd, D, F, x + t * D, hk ? hk + p * F : NULL, yp + p * D);
+                if (mx_parts)
+                    k3o_expert_mx(Wg, Wu, Wd, D, F, mx_parts, x + t * D, hk ? hk + p * F : NULL, yp + p * D);
                 else
                     k3o_expert(Wg, Wu, Wd, D, F, x + t * D, NULL, NULL,
                                hk ? hk + p * F : NULL, yp + p * D);
@@ -471,15 +513,16 @@ int k3o_forward(int32_t E, int32_t D, int32_t F,
     return forward_impl(E, D, F, gq, gs, uq, us, dq, ds, x, T, idx, w, K, y, ytk, hk, nthreads, 0);
 }
 
-/* k3o_forward with MXFP8 activations (k3o_expert_mx for every pair); hk receives
- * the dequantized h. */
+/* k3o_forward with MXFP8 activations in `parts` (1 or 2) parts and MXFP4 weights
+ * read as OCP MX (k3o_expert_mx for every pair); hk receives the dequantized h. */
 int k3o_forward_mx(int32_t E, int32_t D, int32_t F,
                    const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
                    const uint8_t *dq, const uint8_t *ds,
                    const float *x, int32_t T, const int32_t *idx, const float *w, int32_t K,
-                   float *y, double *ytk, double *hk, int32_t nthreads)
+                   float *y, double *ytk, double *hk, int32_t nthreads, int32_t parts)
 {
-    return forward_impl(E, D, F, gq, gs, uq, us, dq, ds, x, T, idx, w, K, y, ytk, hk, nthreads, 1);
+    if (parts < 1 || parts > 2) return -1;
+    return forward_impl(E, D, F, gq, gs, uq, us, dq, ds, x, T, idx, w, K, y, ytk, hk, nthreads, parts);
 }
 
 /* ------------------------------------------------------------------ chunk grouping */

@@ -597,39 +597,108 @@ def check_mx_quant_special(o):
     assert codes[96:].tolist() == [0x78] * 32  # 1.0 under scale 2^-8 is 256: exponent field 15
 
 
+def brute_mx_parts(v, parts):
+    """``parts`` MX parts by search: part 0 of v, then part 1 of the exact residual
+    (which must be an fp32 value).  Returns the list of (codes, scale) and the
+    exact value of the sum of the parts per element (None for NaN)."""
+    c0, s0 = brute_mx_block(v)
+    out = [(c0, s0)]
+    vals = [None if s0 == 255 else e4m3_value(c) * Fraction(2) ** (s0 - 127) for c in c0]
+    if parts == 2:
+        res = []
+        for t, q in zip(v, vals):
+            r = float("nan") if q is None else Fraction(float(t)) - q
+            if q is not None:
+                assert Fraction(float(np.float32(float(r)))) == r  # the residual is exact in fp32
+                r = float(r)
+            res.append(r)
+        c1, s1 = brute_mx_block(np.array(res, np.float32))
+        out.append((c1, s1))
+        vals = [None if (q is None or s1 == 255) else q + e4m3_value(c) * Fraction(2) ** (s1 - 127)
+                for q, c in zip(vals, c1)]
+    return out, vals
+
+
+def check_mx_quant_two_parts(o):
+    """Two parts: part 1 quantizes the exact residual of part 0; the sum of the two
+    parts is within half a part-1 quantum of v (an error near 2^-8 of the block's
+    largest magnitude instead of 2^-4)."""
+    rng = np.random.default_rng(59)
+    v = (rng.standard_normal(32 * 24) * np.exp2(rng.integers(-12, 12, size=32 * 24))).astype(np.float32)
+    v[32 * 5:32 * 6] = 0.0
+    v[32 * 7 + 3] = np.nan
+    codes, scales = o.mx_quant(v, parts=2)
+    assert codes.shape == (2, v.size) and scales.shape == (2, v.size // 32)
+    for b in range(v.size // 32):
+        blk = v[32 * b:32 * b + 32]
+        parts, vals = brute_mx_parts(blk, 2)
+        for pt in range(2):
+            assert codes[pt, 32 * b:32 * b + 32].tolist() == parts[pt][0], (b, pt)
+            assert int(scales[pt, b]) == parts[pt][1], (b, pt)
+        if parts[0][1] != 255 and parts[0][1] > 0:
+            amax = max(abs(Fraction(float(t))) for t in blk)
+            for t, q in zip(blk, vals):
+                assert abs(Fraction(float(t)) - q) <= amax * Fraction(1, 2 ** 7), b
+
+
 def check_forward_mx(o):
-    """The MXFP8 variant on a small block: every pair's h is the MX round trip of the
-    fp32-rounded SiTU of exact sums over the MX round trip of x, and y is the exact
-    w-weighted sum of the down rows over that h (fsum of exact products)."""
+    """The MXFP8 variant on a small block, one and two parts: every pair's h is the MX
+    round trip of the fp32-rounded SiTU of exact sums over the MX round trip of x,
+    and y is the exact w-weighted sum of the down rows over that h (fsum of exact
+    products)."""
     import synth
     cfg = synth.scaled(synth.CONFIGS["tiny"], T=2, E=4, K=2, D=64, F=64)
     W = synth.weights_host(cfg)
     x, logits, bias = synth.activations(cfg)
     idx, w, _ = o.route(logits, bias, cfg.K)
-    y, ytk, hk = o.forward(W, x, idx, w, nthreads=1, want_pairs=True, mx=True)
+    for parts in (1, 2):
+        y, ytk, hk = o.forward(W, x, idx, w, nthreads=1, want_pairs=True, mx=parts)
+        for t in range(cfg.T):
+            xq = [float(q) for b in range(cfg.D // 32) for q in brute_mx_parts(x[t, 32 * b:32 * b + 32], parts)[1]]
+            for k in range(cfg.K):
+                e = int(idx[t, k])
+                Wg = o.dequant(W["gate_q"][e], W["gate_s"][e]).astype(np.float64)
+                Wu = o.dequant(W["up_q"][e], W["up_s"][e]).astype(np.float64)
+                Wd = o.dequant(W["down_q"][e], W["down_s"][e]).astype(np.float64)
+                hf = np.array([o.situ(math.fsum(Wg[f] * xq), math.fsum(Wu[f] * xq)) for f in range(cfg.F)],
+                              np.float32)
+                hq = [float(q) for b in range(cfg.F // 32) for q in brute_mx_parts(hf[32 * b:32 * b + 32], parts)[1]]
+                assert np.allclose(hk[t, k], hq, rtol=2.0 ** -52, atol=0), (parts, t, k)
+                for d in range(cfg.D):
+                    terms = Wd[d] * np.array(hq)
+                    exact = math.fsum(terms)
+                    assert abs(ytk[t, k, d] - exact) <= 1e-12 * math.fsum(np.abs(terms)) + 1e-300, (parts, t, k, d)
+            acc = np.zeros(cfg.D)
+            for k in range(cfg.K):
+                acc = acc + np.float64(w[t, k]) * ytk[t, k]
+            assert np.array_equal(y[t], acc.astype(np.float32)), (parts, t)
+
+
+def check_forward_mx_weight_nan(o):
+    """In the MX variant a weight group with scale byte 255 is NaN (OCP E8M0), where
+    the exact path reads it as 2^128: with all-zero codes in such a down group the
+    exact output is unchanged and the MX output of the pairs using it is NaN."""
+    import synth
+    cfg = synth.scaled(synth.CONFIGS["tiny"], T=2, E=4, K=2, D=64, F=64)
+    W = {k: v.copy() for k, v in synth.weights_host(cfg).items()}
+    x, logits, bias = synth.activations(cfg)
+    idx, w, _ = o.route(logits, bias, cfg.K)
+    e = int(idx[0, 0])
+    y0 = o.forward(W, x, idx, w, nthreads=1)
+    W["down_q"][e, 5, 0:16] = 0
+    W["down_s"][e, 5, 0] = 255
+    W_ref = {k: v.copy() for k, v in W.items()}
+    W_ref["down_s"][e, 5, 0] = 127
+    assert np.array_equal(o.forward(W, x, idx, w, nthreads=1), o.forward(W_ref, x, idx, w, nthreads=1))
+    ym = o.forward(W, x, idx, w, nthreads=1, mx=1)
+    ym_ref = o.forward(W_ref, x, idx, w, nthreads=1, mx=1)
+    uses = (idx == e).any(axis=1)
     for t in range(cfg.T):
-        xc, xs = zip(*[brute_mx_block(x[t, 32 * b:32 * b + 32]) for b in range(cfg.D // 32)])
-        xq = [val for b in range(cfg.D // 32) for val in mx_dequant_py(xc[b], xs[b])]
-        for k in range(cfg.K):
-            e = int(idx[t, k])
-            Wg = o.dequant(W["gate_q"][e], W["gate_s"][e]).astype(np.float64)
-            Wu = o.dequant(W["up_q"][e], W["up_s"][e]).astype(np.float64)
-            Wd = o.dequant(W["down_q"][e], W["down_s"][e]).astype(np.float64)
-            hf = np.array([o.situ(math.fsum(Wg[f] * xq), math.fsum(Wu[f] * xq)) for f in range(cfg.F)],
-                          np.float32)
-            hq = []
-            for b in range(cfg.F // 32):
-                c, s_ = brute_mx_block(hf[32 * b:32 * b + 32])
-                hq += mx_dequant_py(c, s_)
-            assert hk[t, k].tolist() == hq, (t, k)
-            for d in range(cfg.D):
-                terms = Wd[d] * np.array(hq)
-                exact = math.fsum(terms)
-                assert abs(ytk[t, k, d] - exact) <= 1e-12 * math.fsum(np.abs(terms)) + 1e-300, (t, k, d)
-        acc = np.zeros(cfg.D)
-        for k in range(cfg.K):
-            acc = acc + np.float64(w[t, k]) * ytk[t, k]
-        assert np.array_equal(y[t], acc.astype(np.float32)), t
+        if uses[t]:
+            assert np.isnan(ym[t, 5]) and np.array_equal(np.delete(ym[t], 5), np.delete(ym_ref[t], 5)), t
+        else:
+            assert np.array_equal(ym[t], ym_ref[t]), t
+    assert np.isfinite(y0).all()
 
 
 ALL_CHECKS = [
@@ -639,6 +708,6 @@ ALL_CHECKS = [
     check_forward_pairs, check_forward_combine, check_chunk_equals_tokens, check_group,
     check_route_topp_definition, check_route_topp_off_and_monotone, check_forward_pruned, check_group_pruned,
     check_e4m3_decode, check_mx_quant_exact_values, check_mx_quant_brute, check_mx_quant_special,
-    check_forward_mx,
+    check_mx_quant_two_parts, check_forward_mx, check_forward_mx_weight_nan,
 ]
 # check_gate_moments is run separately (it pins the generator, and is the slowest)

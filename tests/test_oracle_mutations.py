@@ -56,8 +56,12 @@ MUTANTS = [
     ("mx subnormal boundary", "if (a < ldexp(1.0, -6)) {", "if (a < ldexp(1.0, -7)) {"),
     ("e4m3 exponent bias 8", "ldexp(1.0 + m / 8.0, (int)e - 7)", "ldexp(1.0 + m / 8.0, (int)e - 8)"),
     ("mx zero block scale", "            scales[b] = 0;\n", "            scales[b] = 127;\n"),
-    ("mx h kept in fp32", "    mx_roundtrip(hf, F, hf);", ""),
-    ("mx x kept in fp32", "    mx_roundtrip(x, D, xq);", "    memcpy(xq, x, sizeof(float) * (size_t)D);"),
+    ("mx h kept in fp32", "    mx_roundtrip(hf, F, parts, hd);", "    for (int32_t f = 0; f < F; ++f) hd[f] = hf[f];"),
+    ("mx x kept in fp32", "    mx_roundtrip(x, D, parts, xq);", "    for (int32_t i = 0; i < D; ++i) xq[i] = x[i];"),
+    ("mx weights keep scale 255", "            if (mx_parts) {\n                mx_weight_nan(", "            if (0) {\n                mx_weight_nan("),
+    ("mx second part dropped", "        if (parts > 1) out[i] += mx_value(", "        if (0) out[i] += mx_value("),
+    ("mx residual of the input", "    for (int64_t i = 0; i < n; ++i) r[i] = v[i] - mx_value(codes[i], scales[i / 32]);",
+     "    for (int64_t i = 0; i < n; ++i) r[i] = v[i];"),
     ("offsets inclusive", "offsets[e + 1] = offsets[e] + counts[e];", "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
 ]
 
