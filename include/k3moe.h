@@ -63,10 +63,15 @@ extern "C" {
 #define K3MOE_OP_DECODE 1
 #define K3MOE_OP_CHUNK 2
 #define K3MOE_OP_GROUP 3
+#define K3MOE_OP_CHUNK_MX 4
 
 /* Output element types for k3moe_dequant_mxfp4(). */
 #define K3MOE_OUT_F32 0
 #define K3MOE_OUT_BF16 1
+
+/* input element types of k3moe_mx_quant */
+#define K3MOE_IN_F32 0
+#define K3MOE_IN_BF16 1
 
 /*
  * The routed experts of one MoE layer.  For expert e (0 <= e < n_experts):
@@ -191,6 +196,37 @@ int k3moe_decode_down(const k3moe_weights_t *W, const float *h, const int32_t *i
 int k3moe_forward_chunk(const k3moe_weights_t *W, const uint16_t *x, int32_t T, const int32_t *idx,
                         const float *w, int32_t K, float *y, int32_t *n_unique, void *ws,
                         size_t ws_bytes, void *stream);
+
+/*
+ * The chunk path with MXFP8 activations (the GPU form of the pages' per-32
+ * low-precision activations, colibri PR #684 int8-activation commit): x and h are
+ * quantized in groups of 32 consecutive values to OCP MXFP8 (E4M3 codes, one
+ * E8M0 scale byte per group; see k3moe_mx_quant) in `parts` parts (1, or 2 where
+ * the second part quantizes the first's fp32 residual), and the products run on
+ * the scaled FP8 x FP4 MFMA with the MXFP4 weights as stored, fp32 accumulation.
+ * In this path a weight scale byte of 255 is the E8M0 NaN (OCP MX), so every
+ * output that reads such a group is NaN; the other entry points read it as
+ * 2^128.  Arguments, outputs and the combine as in k3moe_forward_chunk, plus
+ * parts.  Requires d_model and d_ff multiples of 128.
+ * ws: k3moe_workspace_size(K3MOE_OP_CHUNK_MX, T, K, W) bytes (for either parts).
+ */
+int k3moe_forward_chunk_mx(const k3moe_weights_t *W, const uint16_t *x, int32_t T, const int32_t *idx,
+                           const float *w, int32_t K, int32_t parts, float *y, int32_t *n_unique, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/*
+ * OCP MXFP8 quantization as the MX chunk path does it, on n values (n a positive
+ * multiple of 32) of fp32 (in_dtype K3MOE_IN_F32) or bf16 (K3MOE_IN_BF16, raw
+ * 16-bit patterns).  For each group of 32 with largest magnitude amax: scale byte
+ * s = max(floor(log2 amax) - 8 + 127, 0), codes = the values times 2^(127-s),
+ * clamped to +-448, rounded to the nearest E4M3 value, ties to even, sign kept;
+ * an all-zero group gets s = 0, a group holding a NaN or an infinity s = 255 and
+ * codes 0x7F.  With parts = 2 the second part quantizes the exact fp32 residual
+ * v - value(part 0) the same way.  codes [parts][n] and scales [parts][n/32]
+ * (device, part planes back to back); v and codes 16-byte aligned.
+ */
+int k3moe_mx_quant(const void *v, int32_t in_dtype, int64_t n, int32_t parts, uint8_t *codes, uint8_t *scales,
+                   void *stream);
 
 /*
  * Expert residency (colibri PR #676, "It runs the full model"; PR #684 engine

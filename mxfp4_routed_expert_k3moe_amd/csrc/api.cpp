@@ -116,6 +116,9 @@ size_t k3moe_workspace_size(int32_t op, int32_t T, int32_t K, const k3moe_weight
             return k3moe::chunk_workspace_bytes(T, K, W->n_experts, W->d_model, W->d_ff);
         case K3MOE_OP_GROUP:
             return k3moe::group_workspace_bytes(T, K, W->n_experts, false);
+        case K3MOE_OP_CHUNK_MX:
+            if (!dim_ok(W->d_model) || !dim_ok(W->d_ff) || W->d_model % 128 || W->d_ff % 128) return 0;
+            return k3moe::chunk_mx_workspace_bytes(T, K, W->n_experts, W->d_model, W->d_ff);
         default:
             return 0;
     }
@@ -196,6 +199,39 @@ int k3moe_forward_chunk(const k3moe_weights_t* W, const uint16_t* x, int32_t T, 
     const DevWeights dw = dev_weights(W);
     const k3moe::ChunkWorkspace cws = k3moe::chunk_workspace_carve(ws, T, K, dw.E, dw.D, dw.F);
     return finish(k3moe::launch_chunk(dw, x, T, idx, w, K, y, n_unique, cws, static_cast<hipStream_t>(stream)));
+}
+
+int k3moe_forward_chunk_mx(const k3moe_weights_t* W, const uint16_t* x, int32_t T, const int32_t* idx,
+                           const float* w, int32_t K, int32_t parts, float* y, int32_t* n_unique, void* ws,
+                           size_t ws_bytes, void* stream) {
+    int rc = check_weights(W);
+    if (rc != K3MOE_OK) return rc;
+    if (!x || !idx || !w || !y || !ws) return K3MOE_E_NULL;
+    if (T < 1 || K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return K3MOE_E_DIM;
+    if (parts != 1 && parts != 2) return K3MOE_E_DIM;
+    if (W->d_model % 128 || W->d_ff % 128) return K3MOE_E_DIM;
+    if ((long long)T * K > (1ll << 30)) return K3MOE_E_DIM;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return K3MOE_E_ALIGN;
+    if (ws_bytes < k3moe::chunk_mx_workspace_bytes(T, K, W->n_experts, W->d_model, W->d_ff))
+        return K3MOE_E_WORKSPACE;
+    rc = check_device();
+    if (rc != K3MOE_OK) return rc;
+    const DevWeights dw = dev_weights(W);
+    const k3moe::ChunkMxWorkspace cws = k3moe::chunk_mx_workspace_carve(ws, T, K, dw.E, dw.D, dw.F);
+    return finish(k3moe::launch_chunk_mx(dw, x, T, idx, w, K, parts, y, n_unique, cws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int k3moe_mx_quant(const void* v, int32_t in_dtype, int64_t n, int32_t parts, uint8_t* codes, uint8_t* scales,
+                   void* stream) {
+    if (!v || !codes || !scales) return K3MOE_E_NULL;
+    if (n < 32 || n % 32 != 0 || (parts != 1 && parts != 2)) return K3MOE_E_DIM;
+    if (in_dtype != K3MOE_IN_F32 && in_dtype != K3MOE_IN_BF16) return K3MOE_E_DIM;
+    if (!aligned16(v) || !aligned16(codes)) return K3MOE_E_ALIGN;
+    int rc = check_device();
+    if (rc != K3MOE_OK) return rc;
+    return finish(k3moe::launch_mx_quant(v, in_dtype == K3MOE_IN_BF16, (size_t)n, parts, codes, scales, (size_t)n,
+                                         (size_t)n / 32, static_cast<hipStream_t>(stream)));
 }
 
 int k3moe_dequant_mxfp4(const uint8_t* q, const uint8_t* s, int32_t O, int32_t I, void* out,

@@ -35,19 +35,16 @@
 #include <type_traits>
 
 #include "device.hpp"
+#include "gemm.hpp"
 #include "launch.hpp"
 
 namespace k3moe {
 
 namespace {
 
-constexpr int GT = kGroupTokens;
-constexpr int KS = 128;       // reduction columns per pipeline step
-constexpr int A_ROW = KS * 2;  // bytes per staged A row: 16 pieces of 16 bytes, XOR-swizzled
-constexpr int N_XCD = 8;
+using namespace gemm;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* glb_ptr_t;
+constexpr int GT = kGroupTokens;
 
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -215,25 +212,13 @@ struct GemmShape {
     static constexpr int SROWS = TENSORS * BN;                // weight rows whose scales sit in LDS
 };
 
-constexpr size_t kLdsLimit = 160 * 1024;
 
 // A buffers, the row table, and the scale rows rounded up to whole 1 KiB copies.
 inline size_t gemm_lds_bytes(int mt, int nb, int srows, int kdim) {
     return (size_t)nb * mt * A_ROW + (size_t)mt * 8 + (((size_t)srows * (kdim / 32) + 1023) & ~(size_t)1023);
 }
 
-__device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
-    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-}
 
-// Workgroup barrier for LDS hand-off: this wave's LDS accesses are done, then
-// s_barrier.  Unlike __syncthreads() it does not wait for the wave's global loads
-// still in flight (the weight ring and the activation prefetch); the compiler
-// waits for each of those where its registers are used.  The "memory" clobber
-// keeps memory accesses from moving across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 
 // A pieces of one loading thread (index lt of NT loading threads): piece
@@ -278,23 +263,6 @@ struct APieces {
     }
 };
 
-// Run body(U{}, step) for step = 0 .. nsteps-1 with U = step % P as a type, so every
-// register-array index inside is a constant: whole groups of P as a straight-line
-// loop body, then the remaining steps.
-template <typename Body, int... I>
-__device__ __forceinline__ void steps_group(Body& body, int t0, std::integer_sequence<int, I...>) {
-    (body(std::integral_constant<int, I>{}, t0 + I), ...);
-}
-template <typename Body, int... I>
-__device__ __forceinline__ void steps_tail(Body& body, int t0, int nsteps, std::integer_sequence<int, I...>) {
-    ((t0 + I < nsteps ? body(std::integral_constant<int, I>{}, t0 + I) : void()), ...);
-}
-template <int P, typename Body>
-__device__ __forceinline__ void for_steps(int nsteps, Body&& body) {
-    int t0 = 0;
-    for (; t0 + P <= nsteps; t0 += P) steps_group(body, t0, std::make_integer_sequence<int, P>{});
-    steps_tail(body, t0, nsteps, std::make_integer_sequence<int, P - 1>{});
-}
 
 // Per-lane state of one work item that outlives the prologue: the activation
 // pieces this thread stages, the weight rows this lane streams, and both rings.
@@ -440,11 +408,8 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
     uint8_t* slds = reinterpret_cast<uint8_t*>(rw + MT);                   // [TENSORS][rows][Kdim/32]
 
     // ---- work item (XCD-aware): XCD x walks items [x*per, (x+1)*per)
-    const int n_items = a.scalars[1] * a.nblk_n;
-    const int xcd = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD;
-    const int per = (n_items + N_XCD - 1) / N_XCD;
-    const int item = xcd * per + slot;
-    if (slot >= per || item >= n_items) return;  // block-uniform
+    const int item = xcd_item(a.scalars[1] * a.nblk_n);
+    if (item < 0) return;  // block-uniform
     const int tile = item / a.nblk_n, nblk = item % a.nblk_n;
     const int4 td = a.tiles[tile];
     const int e = td.x, row0 = td.y, mrows = td.z;  // 1 <= mrows <= MT
@@ -551,7 +516,7 @@ hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
     a.nblk_n = (a.N + SH::BN - 1) / SH::BN;
     const size_t lds = gemm_lds_bytes(MT, 2, SH::SROWS, a.Kdim);
     const long max_items = (long)max_tiles * a.nblk_n;
-    const dim3 grid((unsigned)(((max_items + N_XCD - 1) / N_XCD) * N_XCD));
+    const dim3 grid(xcd_grid(max_items));
     const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, NBB>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
@@ -709,9 +674,13 @@ hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int
     err = launch_gemm<DOWN>(dn, ws.g.mt, ws.g.max_tiles, stream);
     if (err != hipSuccess) return err;
 
-    const size_t n4 = (size_t)T * W.D / 4;
-    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, ws.ytk, idx, T, K, W.D,
-                       ws.g.scalars, y);
+    return launch_combine(ws.ytk, idx, T, K, W.D, ws.g.scalars, y, stream);
+}
+
+hipError_t launch_combine(const float* ytk, const int32_t* idx, int T, int K, int D, const int32_t* scalars,
+                          float* y, hipStream_t stream) {
+    const size_t n4 = (size_t)T * D / 4;
+    hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n4, 256)), dim3(256), 0, stream, ytk, idx, T, K, D, scalars, y);
     return hipGetLastError();
 }
 

@@ -116,6 +116,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// One DPP move of a 32-bit value (lanes outside ROW_MASK's rows keep their own).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Maximum over each row of 16 lanes, returned to every lane of the row: swap
+// neighbours, swap pairs, rotate by 4, rotate by 8.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+    v = max(v, dpp_u32<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+    v = max(v, dpp_u32<0x124, 0xF>(v));  // row_ror:4
+    v = max(v, dpp_u32<0x128, 0xF>(v));  // row_ror:8
+    return v;
+}
+
 // Sum over the 64 lanes of a wave; every lane receives the total.  Fixed
 // butterfly order, so the result is deterministic.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -79,6 +79,26 @@ hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int
                         int K, float* y, int32_t* n_unique_out, const ChunkWorkspace& ws,
                         hipStream_t stream);
 
+hipError_t launch_combine(const float* ytk, const int32_t* idx, int T, int K, int D, const int32_t* scalars,
+                          float* y, hipStream_t stream);
+
+// ------------------------------------------------------------------ chunk, MXFP8 activations
+struct ChunkMxWorkspace {
+    GroupBuffers g;
+    uint8_t* xq;            // [2][T, D]     activation codes per part
+    uint8_t* xs;            // [2][T, D/32]  their scales
+    uint8_t* hq;            // [2][T*K, F]   SiTU-GLU output codes (grouped pair order)
+    uint8_t* hs;            // [2][T*K, F/32]
+    float* ytk;             // [T*K, D]      (pair order t*K + k)
+};
+size_t chunk_mx_workspace_bytes(int T, int K, int E, int D, int F);
+ChunkMxWorkspace chunk_mx_workspace_carve(void* ws, int T, int K, int E, int D, int F);
+hipError_t launch_mx_quant(const void* v, bool bf16, size_t n, int parts, uint8_t* codes, uint8_t* scales,
+                           size_t code_plane, size_t scale_plane, hipStream_t stream);
+hipError_t launch_chunk_mx(const DevWeights& W, const uint16_t* x, int T, const int32_t* idx, const float* w,
+                           int K, int parts, float* y, int32_t* n_unique_out, const ChunkMxWorkspace& ws,
+                           hipStream_t stream);
+
 // ------------------------------------------------------------------ dequant
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int O, int I, void* out, int out_bf16,
                           hipStream_t stream);

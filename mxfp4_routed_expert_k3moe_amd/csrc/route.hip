@@ -35,15 +35,8 @@ __device__ __forceinline__ double sigmoid_d(float l) { return 1.0 / (1.0 + exp(-
 // 8), then row 0 -> 1 and row 2 -> 3 (row_bcast15), rows 0-1 -> 2-3
 // (row_bcast31); lane 63 holds the maximum.  Rows outside a broadcast's row mask
 // keep their own value.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
-}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp_u32<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
-    v = max(v, dpp_u32<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
-    v = max(v, dpp_u32<0x124, 0xF>(v));  // row_ror:4
-    v = max(v, dpp_u32<0x128, 0xF>(v));  // row_ror:8
+    v = row16_max_u32(v);
     v = max(v, dpp_u32<0x142, 0xA>(v));  // row_bcast:15 into rows 1, 3
     v = max(v, dpp_u32<0x143, 0xC>(v));  // row_bcast:31 into rows 2, 3
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);

@@ -25,15 +25,17 @@ K3MOE_E_HIP = -6
 K3MOE_MAX_K = 64
 K3MOE_MAX_E = 4096
 K3MOE_MAX_DIM = 8192
-OP_DECODE, OP_CHUNK, OP_GROUP = 1, 2, 3
+OP_DECODE, OP_CHUNK, OP_GROUP, OP_CHUNK_MX = 1, 2, 3, 4
 OUT_F32, OUT_BF16 = 0, 1
+IN_F32, IN_BF16 = 0, 1
 
 PRUNED = -1  # K3MOE_PRUNED: a routing slot dropped by top-p
 
 ENTRY_POINTS = ("k3moe_route", "k3moe_route_topp", "k3moe_group", "k3moe_forward_decode", "k3moe_decode_gateup",
                 "k3moe_decode_down", "k3moe_forward_chunk", "k3moe_workspace_size", "k3moe_dequant_mxfp4",
                 "k3moe_status_string", "k3moe_slot_layout", "k3moe_pool_create", "k3moe_pool_destroy",
-                "k3moe_pool_plan", "k3moe_pool_weights", "k3moe_pool_stats", "k3moe_forward_decode_pooled")
+                "k3moe_pool_plan", "k3moe_pool_weights", "k3moe_pool_stats", "k3moe_forward_decode_pooled",
+                "k3moe_forward_chunk_mx", "k3moe_mx_quant")
 
 
 class K3moeError(RuntimeError):
@@ -84,6 +86,8 @@ def load() -> ctypes.CDLL:
     lib.k3moe_pool_weights.argtypes = [vp, wp]
     lib.k3moe_pool_stats.argtypes = [vp, vp]
     lib.k3moe_forward_decode_pooled.argtypes = [vp, i32, vp, i64, i64, vp, vp, vp, i32, vp, vp, sz, vp, vp]
+    lib.k3moe_forward_chunk_mx.argtypes = [wp, vp, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.k3moe_mx_quant.argtypes = [vp, i32, i64, i32, vp, vp, vp]
     for name in ENTRY_POINTS:
         if name not in ("k3moe_workspace_size", "k3moe_status_string", "k3moe_pool_create", "k3moe_pool_destroy"):
             getattr(lib, name).restype = ctypes.c_int
@@ -296,6 +300,43 @@ def forward_chunk(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch
            load().k3moe_forward_chunk(W.ref(), _ptr(x), T, _ptr(idx), _ptr(w), K, _ptr(y), _ptr(n_unique),
                                       _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def forward_chunk_mx(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor, parts: int = 1,
+                     y: Optional[torch.Tensor] = None, n_unique: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """A chunk with MXFP8 activations in ``parts`` parts: bf16 ``x [T,D]``,
+    ``idx/w [T,K]`` -> fp32 ``y [T,D]`` (scaled FP8 x FP4 MFMA path)."""
+    T = x.shape[0]
+    _dev(x, torch.bfloat16, "x", (T, W.D))
+    K = idx.shape[1]
+    _dev(idx, torch.int32, "idx", (T, K))
+    _dev(w, torch.float32, "w", (T, K))
+    y = torch.empty((T, W.D), dtype=torch.float32, device=x.device) if y is None else y
+    _dev(y, torch.float32, "y", (T, W.D))
+    if n_unique is not None:
+        _dev(n_unique, torch.int32, "n_unique", (1,))
+    ws = _workspace(workspace_size(OP_CHUNK_MX, T, K, W), x.device, ws)
+    _check("k3moe_forward_chunk_mx",
+           load().k3moe_forward_chunk_mx(W.ref(), _ptr(x), T, _ptr(idx), _ptr(w), K, int(parts), _ptr(y),
+                                         _ptr(n_unique), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def mx_quant(v: torch.Tensor, parts: int = 1, stream=None):
+    """OCP MXFP8 of a device fp32 or bf16 tensor whose element count is a multiple
+    of 32 (groups of 32 consecutive elements).  Returns ``(codes, scales)`` uint8 of
+    shapes ``[parts, n]`` and ``[parts, n/32]``."""
+    code = {torch.float32: IN_F32, torch.bfloat16: IN_BF16}.get(v.dtype)
+    if code is None:
+        raise TypeError("v must be float32 or bfloat16")
+    _dev(v, v.dtype, "v")
+    n = v.numel()
+    codes = torch.empty((parts, n), dtype=torch.uint8, device=v.device)
+    scales = torch.empty((parts, max(n // 32, 1)), dtype=torch.uint8, device=v.device)
+    _check("k3moe_mx_quant",
+           load().k3moe_mx_quant(_ptr(v), code, n, int(parts), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
 
 
 def dequant_mxfp4(q: torch.Tensor, s: torch.Tensor, out_dtype: torch.dtype = torch.float32,

@@ -293,8 +293,12 @@ def expert(Wg, Wu, Wd, x):
     return instance().expert(Wg, Wu, Wd, x)
 
 
-def forward(weights, x, idx, w, nthreads=None, want_pairs=False):
-    return instance().forward(weights, x, idx, w, nthreads=nthreads, want_pairs=want_pairs)
+def forward(weights, x, idx, w, nthreads=None, want_pairs=False, mx=0):
+    return instance().forward(weights, x, idx, w, nthreads=nthreads, want_pairs=want_pairs, mx=mx)
+
+
+def mx_quant(v, parts=1):
+    return instance().mx_quant(v, parts=parts)
 
 
 def group(idx, E):

@@ -43,6 +43,8 @@ def test_header_constants_match_binding():
     assert int(consts["K3MOE_OP_DECODE"]) == k3.OP_DECODE
     assert int(consts["K3MOE_OP_CHUNK"]) == k3.OP_CHUNK
     assert int(consts["K3MOE_OP_GROUP"]) == k3.OP_GROUP
+    assert int(consts["K3MOE_OP_CHUNK_MX"]) == k3.OP_CHUNK_MX
+    assert int(consts["K3MOE_IN_F32"]) == k3.IN_F32 and int(consts["K3MOE_IN_BF16"]) == k3.IN_BF16
 
 
 def test_status_strings():
@@ -72,6 +74,9 @@ def test_workspace_sizes():
     P = 4096 * 16
     assert ch >= P * 3584 * 4 + P * 3072 * 2
     assert lib.k3moe_workspace_size(k3.OP_GROUP, 4096, 16, ctypes.byref(s)) > 0
+    mx = lib.k3moe_workspace_size(k3.OP_CHUNK_MX, 4096, 16, ctypes.byref(s))
+    assert mx >= P * 3584 * 4 + 2 * P * 3072 + 2 * 4096 * 3584
+    assert lib.k3moe_workspace_size(k3.OP_CHUNK_MX, 4096, 16, ctypes.byref(_struct(D=3584 + 32))) == 0
     assert lib.k3moe_workspace_size(99, 1, 16, ctypes.byref(s)) == 0
     assert lib.k3moe_workspace_size(k3.OP_DECODE, 1, 65, ctypes.byref(s)) == 0
     bad = _struct(D=3583)
@@ -119,6 +124,20 @@ def test_validation_before_any_device_call():
     assert lib.k3moe_dequant_mxfp4(p, p, 4, 64, p, 7, None) == k3.K3MOE_E_DIM
     assert lib.k3moe_dequant_mxfp4(ctypes.c_void_p(257), p, 4, 64, p, 0, None) == k3.K3MOE_E_ALIGN
     assert lib.k3moe_dequant_mxfp4(None, p, 4, 64, p, 0, None) == k3.K3MOE_E_NULL
+    mx = lib.k3moe_forward_chunk_mx
+    assert mx(ctypes.byref(s), p, 32, p, p, 16, 3, p, None, p, ws, None) == k3.K3MOE_E_DIM
+    assert mx(ctypes.byref(s), p, 32, p, p, 16, 0, p, None, p, ws, None) == k3.K3MOE_E_DIM
+    assert mx(ctypes.byref(_struct(D=3584 + 32)), p, 32, p, p, 16, 1, p, None, p, ws, None) == k3.K3MOE_E_DIM
+    assert mx(ctypes.byref(_struct(F=3072 + 64)), p, 32, p, p, 16, 1, p, None, p, ws, None) == k3.K3MOE_E_DIM
+    assert mx(ctypes.byref(s), p, 32, p, p, 16, 1, p, None, p, 100, None) == k3.K3MOE_E_WORKSPACE
+    assert mx(ctypes.byref(s), None, 32, p, p, 16, 1, p, None, p, ws, None) == k3.K3MOE_E_NULL
+    q = lib.k3moe_mx_quant
+    assert q(None, 0, 64, 1, p, p, None) == k3.K3MOE_E_NULL
+    assert q(p, 0, 48, 1, p, p, None) == k3.K3MOE_E_DIM
+    assert q(p, 0, 0, 1, p, p, None) == k3.K3MOE_E_DIM
+    assert q(p, 0, 64, 3, p, p, None) == k3.K3MOE_E_DIM
+    assert q(p, 5, 64, 1, p, p, None) == k3.K3MOE_E_DIM
+    assert q(ctypes.c_void_p(260), 0, 64, 1, p, p, None) == k3.K3MOE_E_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

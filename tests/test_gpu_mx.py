@@ -1,0 +1,212 @@
+"""Chunk path with MXFP8 activations (scaled FP8 x FP4 MFMA) on the GPU vs the oracle.
+
+Quantization (k3moe_mx_quant, the same device code the GEMM epilogue and the
+activation pass use) must match the oracle's codes and scales bit for bit.  The
+forward is compared with the oracle's MXFP8 variant (same quantization, exact
+sums): the GPU accumulates in fp32 inside the MFMA, so an h value within about
+1e-6 of an E4M3 rounding boundary can quantize to the neighbouring code (one
+E4M3 step); the bound 5e-3 (1e-3 with two parts, where the second part absorbs
+such a step) leaves room for a few of those per output.
+
+The distance to the exact (unquantized) oracle is logged and bounded too.  It is
+a property of the format on these weights, not of the kernels: x loses about 3%
+(rel-L2) to one E4M3 part, g and u inherit that as an absolute error of a few
+units (the synthetic gate/up outputs reach |g| ~ 200), and where g sits in the
+SiTU-GLU's transition region (|g| below ~5) that moves h across most of its
+range, so one part lands near 1e-1 on y.  Two parts keep about eight
+significant bits per value (2e-3 to 3e-3, the order of the 3.5e-3 the pages
+report for their per-32 int8 activations)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import assert_close, device_weights, log, oracle_forward_subset, rel_l2, torch_cuda
+
+pytestmark = pytest.mark.gpu
+TOL_MX = {1: 5e-3, 2: 1e-3}       # vs the oracle's MXFP8 variant
+TOL_EXACT = {1: 2e-1, 2: 5e-3}    # vs the exact oracle
+
+
+def _quant_gpu(v: np.ndarray, parts: int, bf16: bool = False):
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).cuda()
+    if bf16:
+        t = t.to(torch.bfloat16)
+    codes, scales = lib.mx_quant(t, parts)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def _quant_inputs():
+    rng = np.random.default_rng(71)
+    blocks = []
+    for b in range(64):
+        v = rng.standard_normal(32) * np.exp2(rng.integers(-24, 24, size=32) * (b % 4 == 0))
+        blocks.append(v * 2.0 ** int(rng.integers(-100, 100)))
+    mags = [(8 + m) * 2.0 ** (e - 10) if e else m * 2.0 ** -9 for e in range(16) for m in range(8)][:127]
+    mids = [(mags[c] + mags[c + 1]) / 2 for c in range(126)]  # exact ties under scale 2^0
+    for i in range(0, len(mids), 31):
+        part = mids[i:i + 31]
+        blocks.append(np.array([448.0] + part + [0.0] * (31 - len(part))))
+        blocks.append(-np.array([448.0] + part + [0.0] * (31 - len(part))))
+    blocks.append(np.array([470.0, -500.0, 463.9, 464.0] + [1.0] * 28) * 2.0 ** 20)  # saturation
+    blocks.append(np.array([1e-39, -3e-40, 2e-45] + [0.0] * 29))  # fp32 subnormals, scale 0
+    blocks.append(np.array([3e38, -3.4e38] + [1e-30] * 30))  # top of the fp32 range
+    blocks.append(np.zeros(32))
+    blocks.append(-np.zeros(32))
+    nanb = rng.standard_normal(32)
+    nanb[7] = np.nan
+    infb = rng.standard_normal(32)
+    infb[30] = -np.inf
+    blocks += [nanb, infb]
+    return np.concatenate(blocks).astype(np.float32)
+
+
+@pytest.mark.parametrize("parts", [1, 2])
+def test_mx_quant_bit_exact(parts):
+    v = _quant_inputs()
+    log(f"mx_quant parts={parts}: {v.size // 32} blocks")
+    codes, scales = _quant_gpu(v, parts)
+    want_c, want_s = oracle.mx_quant(v, parts)
+    want_c, want_s = np.asarray(want_c).reshape(parts, -1), np.asarray(want_s).reshape(parts, -1)
+    assert np.array_equal(scales, want_s), np.argwhere(scales != want_s)[:8]
+    assert np.array_equal(codes, want_c), np.argwhere(codes != want_c)[:8]
+
+
+def test_mx_quant_bf16_input():
+    """bf16 input quantizes as its fp32 value (the activations of the chunk path)."""
+    torch = torch_cuda()
+    v = np.random.default_rng(5).standard_normal(32 * 4096).astype(np.float32)
+    vb = torch.from_numpy(v).to(torch.bfloat16).float().numpy()  # bf16 values, exactly
+    for parts in (1, 2):
+        codes, scales = _quant_gpu(vb, parts, bf16=True)
+        want_c, want_s = oracle.mx_quant(vb, parts)
+        assert np.array_equal(codes, np.asarray(want_c).reshape(parts, -1))
+        assert np.array_equal(scales, np.asarray(want_s).reshape(parts, -1))
+
+
+def _chunk_mx_gpu(W, x, idx, w, parts):
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xb = torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)  # exact: x holds bf16 values
+    assert np.array_equal(xb.float().cpu().numpy(), x)
+    y = lib.forward_chunk_mx(W, xb, torch.from_numpy(np.ascontiguousarray(idx)).cuda(),
+                             torch.from_numpy(np.ascontiguousarray(w)).cuda(), parts=parts, n_unique=nu)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), int(nu.item())
+
+
+def _case(cfg, what, parts, sample=None, exact=True):
+    x, logits, bias = synth.activations(cfg)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    W = device_weights(cfg)
+    log(f"chunk_mx {what} parts={parts}: T={x.shape[0]} E={cfg.E} K={cfg.K} D={cfg.D} F={cfg.F}")
+    got, nu = _chunk_mx_gpu(W, x, idx, w, parts)
+    assert nu == len(np.unique(idx))
+    s = np.arange(x.shape[0]) if sample is None else sample
+    log(f"chunk_mx {what}: running the oracle on {len(s)} tokens")
+    want = oracle_forward_subset(cfg, x[s], idx[s], w[s], mx=parts)
+    e = assert_close(got[s], want, TOL_MX[parts], f"chunk_mx {what} parts={parts} vs MX oracle")
+    if exact:
+        ref = oracle_forward_subset(cfg, x[s], idx[s], w[s])
+        ee = rel_l2(got[s], ref)
+        log(f"chunk_mx {what} parts={parts}: rel-L2 vs exact oracle {ee:.3e} (bound {TOL_EXACT[parts]:g})")
+        assert ee <= TOL_EXACT[parts]
+    return e
+
+
+@pytest.mark.parametrize("parts", [1, 2])
+def test_chunk_mx_tiny_ragged(parts):
+    cfg = synth.scaled(synth.CONFIGS["tiny"], T=5, path="chunk")
+    _case(cfg, "tiny T=5", parts)
+
+
+@pytest.mark.parametrize("parts", [1, 2])
+@pytest.mark.parametrize("E,K,D,F,T", [(8, 4, 512, 384, 600), (16, 4, 384, 256, 100), (6, 6, 256, 128, 131)])
+def test_chunk_mx_tiles_and_tails(E, K, D, F, T, parts):
+    """Several tiles per expert, a ragged last tile, column blocks past the width."""
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name=f"mx{E}_{K}_{D}_{F}", E=E, K=K, D=D, F=F, T=T,
+                       weight_seed=900 + E, act_seed=900 + T, path="chunk")
+    _case(cfg, f"E={E} K={K} D={D} F={F} T={T}", parts)
+
+
+@pytest.mark.parametrize("parts", [1, 2])
+def test_chunk_mx_prefill32(parts):
+    _case(synth.CONFIGS["prefill32"], "prefill32", parts)
+
+
+def test_chunk_mx_prefill256_sampled():
+    cfg = synth.CONFIGS["prefill256"]
+    sample = synth.sample_tokens(cfg, 24, seed=3)
+    for parts in (1, 2):
+        _case(cfg, "prefill256", parts, sample=sample, exact=parts == 2)
+
+
+def test_chunk_mx_batch4096_sampled():
+    """The 4096-token launch.  Its edge experts carry scale bytes over the full
+    0..255 range: in this path a 255 group is NaN, and the NaN pattern of the
+    sampled tokens must match the oracle's MX reading."""
+    cfg = synth.CONFIGS["batch4096"]
+    x, logits, bias = synth.activations(cfg)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    W = device_weights(cfg)
+    log("chunk_mx batch4096: GPU run (parts=1)")
+    got, nu = _chunk_mx_gpu(W, x, idx, w, 1)
+    assert nu == len(np.unique(idx))
+    edge_tok = np.nonzero(np.isin(idx, cfg.edge_experts).any(axis=1))[0]
+    rng = np.random.default_rng(43)
+    pick_edge = rng.choice(edge_tok, size=min(16, len(edge_tok)), replace=False)
+    sample = synth.sample_tokens(cfg, 24, must_include=pick_edge, seed=2)
+    log(f"chunk_mx batch4096: union {nu}; oracle on {len(sample)} tokens")
+    want = oracle_forward_subset(cfg, x[sample], idx[sample], w[sample], mx=1)
+    assert_close(got[sample], want, TOL_MX[1], "chunk_mx batch4096 sample")
+    normal = np.setdiff1d(np.arange(cfg.T), edge_tok)
+    assert np.isfinite(got[normal]).all()
+
+
+def test_chunk_mx_weight_scale_255_is_nan():
+    """A down group with scale byte 255 and zero codes: NaN in the MX path for the
+    output row that reads it, exactly as the oracle's MX reading, while the bf16
+    path (closed form: 0 * 2^128 = 0) is unaffected."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = synth.scaled(synth.CONFIGS["tiny"], T=40, path="chunk", name="mx255", weight_seed=77)
+    Wh = {k: v.copy() for k, v in synth.weights_host(cfg).items()}
+    x, logits, bias = synth.activations(cfg)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    e = int(idx[0, 0])
+    Wh["down_q"][e, 9, 16:32] = 0
+    Wh["down_s"][e, 9, 1] = 255
+    W = lib.ExpertWeights.from_dict({k: torch.from_numpy(v).cuda() for k, v in Wh.items()})
+    for parts in (1, 2):
+        got, _ = _chunk_mx_gpu(W, x, idx, w, parts)
+        want = oracle_forward_subset(cfg, x, idx, w, mx=parts, weights=Wh)
+        uses = (idx == e).any(axis=1)
+        assert np.isnan(got[uses, 9]).all() and np.isnan(want[uses, 9]).all()
+        assert_close(got, want, TOL_MX[parts], f"chunk_mx scale-255 parts={parts}")
+    yb = lib.forward_chunk(W, torch.from_numpy(x).cuda().to(torch.bfloat16), torch.from_numpy(idx).cuda(),
+                           torch.from_numpy(w).cuda()).cpu().numpy()
+    assert np.isfinite(yb).all()
+
+
+def test_chunk_mx_pruned_and_invalid():
+    """Top-p pruned slots contribute nothing; invalid routing gives n_unique -1 and
+    an all-NaN output; repeated runs are bit-identical."""
+    cfg = synth.scaled(synth.CONFIGS["tiny"], T=70, path="chunk")
+    x, logits, bias = synth.activations(cfg)
+    idx, w, _, _ = oracle.route_topp(logits, bias, cfg.K, 0.6)
+    assert (idx == -1).any()
+    W = device_weights(cfg)
+    a, _ = _chunk_mx_gpu(W, x, idx, w, 1)
+    b, _ = _chunk_mx_gpu(W, x, idx, w, 1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    want = oracle_forward_subset(cfg, x, idx, w, mx=1)
+    assert_close(a, want, TOL_MX[1], "chunk_mx top-p 0.6")
+    bad = idx.copy()
+    bad[5, 1] = bad[5, 0] if bad[5, 0] >= 0 else 0
+    bad[5, 0] = bad[5, 1]
+    y, nu = _chunk_mx_gpu(W, x, bad, w, 2)
+    assert nu == -1 and np.all(np.isnan(y))
