@@ -117,14 +117,14 @@ struct MxPieces {
             slds = (pt * MT + r) * 4;
         }
     }
-    __device__ __forceinline__ void load(uint4 (&v)[SLOTS], uint32_t& sv, int step) const {
+    __device__ __forceinline__ void load(u32x4 (&v)[SLOTS], uint32_t& sv, int step) const {
 #pragma unroll
-        for (int i = 0; i < SLOTS; ++i) v[i] = *reinterpret_cast<const uint4*>(src[i] + step * KS);
+        for (int i = 0; i < SLOTS; ++i) v[i] = *reinterpret_cast<const u32x4*>(src[i] + step * KS);
         sv = *reinterpret_cast<const uint32_t*>(ssrc + 4 * step);
     }
-    __device__ __forceinline__ void store(const uint4 (&v)[SLOTS], uint32_t sv, uint8_t* buf, uint8_t* sbuf) const {
+    __device__ __forceinline__ void store(const u32x4 (&v)[SLOTS], uint32_t sv, uint8_t* buf, uint8_t* sbuf) const {
 #pragma unroll
-        for (int i = 0; i < SLOTS; ++i) *reinterpret_cast<uint4*>(buf + lds[i]) = v[i];
+        for (int i = 0; i < SLOTS; ++i) *reinterpret_cast<u32x4*>(buf + lds[i]) = v[i];
         *reinterpret_cast<uint32_t*>(sbuf + slds) = sv;
     }
 };
@@ -134,17 +134,17 @@ struct MxState {
     using AP = MxPieces<MODE, MT, CW * 64, PARTS>;
     static_assert(NBB == 2 || NBB == 4, "ring depth must be a multiple of the two A register sets");
     AP ap;
-    uint4 areg[2][AP::SLOTS];
+    u32x4 areg[2][AP::SLOTS];  // native vectors: a struct type here ends up in scratch
     uint32_t sreg[2];
     const uint8_t* bq[4];  // weight rows in HBM
     const uint8_t* bs[4];  // their scale rows in LDS
-    uint4 bring[NBB][4];
+    u32x4 bring[NBB][4];
 };
 
-__device__ __forceinline__ v8i a_operand(const uint4& lo, const uint4& hi) {
+__device__ __forceinline__ v8i a_operand(const u32x4& lo, const u32x4& hi) {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
-__device__ __forceinline__ v8i b_operand(const uint4& q) {  // FP4: only the first four dwords are read
+__device__ __forceinline__ v8i b_operand(const u32x4& q) {  // FP4: only the first four dwords are read
     return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
 }
 
@@ -203,7 +203,7 @@ __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, 
             const int col = min(step + NBB - 1, nsteps - 1) * KS + 32 * lg;
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns)
-                st.bring[(u + NBB - 1) % NBB][ns] = *reinterpret_cast<const uint4*>(st.bq[ns] + (col >> 1));
+                st.bring[(u + NBB - 1) % NBB][ns] = *reinterpret_cast<const u32x4*>(st.bq[ns] + (col >> 1));
         }
         uint32_t sc[4];
 #pragma unroll
@@ -222,8 +222,8 @@ __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, 
 #pragma unroll
             for (int i = 0; i < MS; ++i) {
                 const uint8_t* arow = abuf + (16 * i + ln) * A_ROW;
-                const uint4 lo = *reinterpret_cast<const uint4*>(arow + 16 * ((pt * 8 + lg) ^ ln));
-                const uint4 hi = *reinterpret_cast<const uint4*>(arow + 16 * ((pt * 8 + 4 + lg) ^ ln));
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + 16 * ((pt * 8 + lg) ^ ln));
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + 16 * ((pt * 8 + 4 + lg) ^ ln));
                 const int sa = sbuf[(pt * MT + 16 * i + ln) * 4 + lg];
                 const v8i aop = a_operand(lo, hi);
 #pragma unroll
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_mx_kernel(MxArgs a) {
         for (int u = 0; u < NBB - 1; ++u) {
             const int col = min(u, nsteps - 1) * KS + 32 * lg;
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns) st.bring[u][ns] = *reinterpret_cast<const uint4*>(st.bq[ns] + (col >> 1));
+            for (int ns = 0; ns < 4; ++ns) st.bring[u][ns] = *reinterpret_cast<const u32x4*>(st.bq[ns] + (col >> 1));
         }
     }
     st.ap.load(st.areg[0], st.sreg[0], 0);
