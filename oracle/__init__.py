@@ -80,6 +80,13 @@ def _bind(path: str):
     lib.k3o_mx_quant.argtypes = [_F32P, ctypes.c_int64, _U8P, _U8P]
     lib.k3o_e4m3_decode.restype = ctypes.c_double
     lib.k3o_e4m3_decode.argtypes = [ctypes.c_uint]
+    lib.k3o_rmsnorm.restype = ctypes.c_double
+    lib.k3o_rmsnorm.argtypes = [_F64P, ctypes.c_int32, _F32P, ctypes.c_double, _F64P]
+    lib.k3o_latent_forward.restype = ctypes.c_int
+    lib.k3o_latent_forward.argtypes = ([ctypes.c_int32] * 3 + [_F32P, _F32P, _F32P, ctypes.c_double, _F32P, _F32P, _F32P]
+                                       + [ctypes.c_int32] * 2 + [_U8P] * 6
+                                       + [_F32P, ctypes.c_int32, _I32P, _F32P, ctypes.c_int32, _F32P,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32])
     lib.k3o_group.restype = ctypes.c_int
     lib.k3o_group.argtypes = [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P, _I32P,
                               _I32P, _I32P, ctypes.POINTER(ctypes.c_int32)]
@@ -230,6 +237,45 @@ class Oracle:
     def e4m3(self, code: int) -> float:
         return float(self.lib.k3o_e4m3_decode(int(code)))
 
+    # ------------------------------------------------------------- LatentMoE wrapper
+    def rmsnorm(self, a: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+        a = _c(a, np.float64)
+        r = np.empty_like(a)
+        self.lib.k3o_rmsnorm(a, a.size, _c(g, np.float32), float(eps), r)
+        return r
+
+    def latent_forward(self, dense: Dict[str, np.ndarray], weights: Dict[str, np.ndarray], h: np.ndarray,
+                       idx: np.ndarray, w: np.ndarray, nthreads: Optional[int] = None, want_parts: bool = False):
+        """The LatentMoE block (k3o_latent_forward): ``dense`` holds ``w_dn [Dl,Dh]``,
+        ``w_up [Dh,Dl]``, ``norm [Dl]``, ``eps``, ``sg/su [Fs,Dh]``, ``sd [Dh,Fs]`` (float
+        values); ``weights`` the routed experts at width Dl.  Returns ``out [T,Dh]`` f32;
+        with ``want_parts`` also ``(x_latent, aggregate)`` [T,Dl] in float64."""
+        names = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
+        arrs = [_c(weights[n], np.uint8) for n in names]
+        E, F, half = arrs[0].shape
+        Dl = 2 * half
+        wdn, wup = _c(dense["w_dn"], np.float32), _c(dense["w_up"], np.float32)
+        sg, su, sd = (_c(dense[k], np.float32) for k in ("sg", "su", "sd"))
+        norm = _c(dense["norm"], np.float32)
+        Dh, Fs = wdn.shape[1], sg.shape[0]
+        if wdn.shape != (Dl, Dh) or wup.shape != (Dh, Dl) or norm.shape != (Dl,) or su.shape != (Fs, Dh) \
+                or sd.shape != (Dh, Fs):
+            raise ValueError("dense weight shapes do not match")
+        h = _c(h, np.float32).reshape(-1, Dh)
+        T = h.shape[0]
+        idx = _c(idx, np.int32).reshape(T, -1)
+        K = idx.shape[1]
+        w = _c(w, np.float32).reshape(T, K)
+        out = np.empty((T, Dh), np.float32)
+        xl = np.empty((T, Dl)) if want_parts else None
+        agg = np.empty((T, Dl)) if want_parts else None
+        rc = self.lib.k3o_latent_forward(Dh, Dl, Fs, wdn, wup, norm, float(dense["eps"]), sg, su, sd, E, F, *arrs,
+                                         h, T, idx, w, K, out, xl.ctypes.data if want_parts else None,
+                                         agg.ctypes.data if want_parts else None, int(nthreads or default_threads()))
+        if rc != 0:
+            raise ValueError("oracle latent forward failed")
+        return (out, xl, agg) if want_parts else out
+
     # -------------------------------------------------------------------------- group
     def group(self, idx: np.ndarray, E: int) -> Dict[str, np.ndarray]:
         """Counting-sort grouping of a chunk's pairs by expert (see ``k3o_group``)."""
@@ -299,6 +345,10 @@ def forward(weights, x, idx, w, nthreads=None, want_pairs=False, mx=0):
 
 def mx_quant(v, parts=1):
     return instance().mx_quant(v, parts=parts)
+
+
+def latent_forward(dense, weights, h, idx, w, nthreads=None, want_parts=False):
+    return instance().latent_forward(dense, weights, h, idx, w, nthreads=nthreads, want_parts=want_parts)
 
 
 def group(idx, E):

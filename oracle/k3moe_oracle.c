@@ -562,3 +562,108 @@ int k3o_group(const int32_t *idx, int32_t T, int32_t K, int32_t E, int32_t *coun
     *n_unique = nu;
     return 0;
 }
+
+/* -------------------------------------------------------------- LatentMoE wrapper */
+
+/* RMSNorm of n values: r_i = g_i * a_i / sqrt(mean(a^2) + eps), in double.
+ * Returns the root mean square sqrt(mean(a^2) + eps). */
+double k3o_rmsnorm(const double *a, int32_t n, const float *g, double eps, double *r)
+{
+    double ss = 0.0;
+    for (int32_t i = 0; i < n; ++i) ss += a[i] * a[i];
+    const double rms = sqrt(ss / n + eps);
+    for (int32_t i = 0; i < n; ++i) r[i] = (double)g[i] * (a[i] / rms);
+    return rms;
+}
+
+/* y[o] = sum_i W[o, i] x[i] for W [O, I] (float values), x double; ascending i. */
+static void dense(const float *W, int32_t O, int32_t I, const double *x, double *y)
+{
+    for (int32_t o = 0; o < O; ++o) {
+        double acc = 0.0;
+        for (int32_t i = 0; i < I; ++i) acc += (double)W[(int64_t)o * I + i] * x[i];
+        y[o] = acc;
+    }
+}
+
+/* The block around the routed experts ([PR684] engine commit, Stable LatentMoE
+ * bullet: latent 7168 <-> 3584 projections around the experts, RMSNorm on the
+ * aggregate, two fused shared experts, SiTU-GLU; [PR676] summary: the routed
+ * experts run in a 3584-dim latent space behind shared down/up projections,
+ * plus two fused full-width shared experts).  The pages give no formulas; the
+ * plainest reading, per token with hidden state h [Dh]:
+ *   x   = Wdn h                           latent input of the routed experts,
+ *                                         held as fp32 like any activation
+ *   a   = sum_k w_k E_k(x)                the routed aggregate (k3o_forward)
+ *   r   = RMSNorm(a) with weight gn, eps  "on the aggregate": in the latent space
+ *   y   = Wup r                           back to the full width
+ *   s   = Sd SiTU(Sg h, Su h)             the two shared experts fused into one
+ *                                         SiTU-GLU MLP of width Fs (both halves)
+ *   out = y + s
+ * Dense weights: Wdn [Dl, Dh], Wup [Dh, Dl], Sg/Su [Fs, Dh], Sd [Dh, Fs] as float
+ * (their bf16 values), gn [Dl]; expert weights and routing as in k3o_forward on
+ * the latent x.  Sums in double; out [T, Dh] fp32; xl (nullable) receives x
+ * [T, Dl] and agg (nullable) a [T, Dl] in double.  Returns 0, or -1 as
+ * k3o_forward does. */
+int k3o_latent_forward(int32_t Dh, int32_t Dl, int32_t Fs,
+                       const float *Wdn, const float *Wup, const float *gn, double eps,
+                       const float *Sg, const float *Su, const float *Sd,
+                       int32_t E, int32_t F,
+                       const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
+                       const uint8_t *dq, const uint8_t *ds,
+                       const float *h, int32_t T, const int32_t *idx, const float *w, int32_t K,
+                       float *out, double *xl, double *agg, int32_t nthreads)
+{
+    float *x32 = (float *)malloc(sizeof(float) * (size_t)T * Dl);
+    float *y32 = (float *)malloc(sizeof(float) * (size_t)T * Dl);
+    double *ytk = (double *)malloc(sizeof(double) * (size_t)T * K * Dl);
+    if (!x32 || !y32 || !ytk) {
+        free(x32);
+        free(y32);
+        free(ytk);
+        return -1;
+    }
+#pragma omp parallel for num_threads(nthreads > 0 ? nthreads : 1) schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        double *hd = (double *)malloc(sizeof(double) * (size_t)Dh);
+        double *xd = (double *)malloc(sizeof(double) * (size_t)Dl);
+        for (int32_t i = 0; i < Dh; ++i) hd[i] = h[(int64_t)t * Dh + i];
+        dense(Wdn, Dl, Dh, hd, xd);
+        for (int32_t i = 0; i < Dl; ++i) {
+            x32[(int64_t)t * Dl + i] = (float)xd[i];
+            if (xl) xl[(int64_t)t * Dl + i] = xd[i];
+        }
+        free(hd);
+        free(xd);
+    }
+    int rc = k3o_forward(E, Dl, F, gq, gs, uq, us, dq, ds, x32, T, idx, w, K, y32, ytk, NULL, nthreads);
+    if (rc == 0) {
+#pragma omp parallel for num_threads(nthreads > 0 ? nthreads : 1) schedule(dynamic, 1)
+        for (int32_t t = 0; t < T; ++t) {
+            double *a = (double *)malloc(sizeof(double) * (size_t)Dl);
+            double *r = (double *)malloc(sizeof(double) * (size_t)Dl);
+            double *y = (double *)malloc(sizeof(double) * (size_t)Dh);
+            double *s = (double *)malloc(sizeof(double) * (size_t)Dh);
+            for (int32_t i = 0; i < Dl; ++i) {
+                double acc = 0.0;
+                for (int32_t k = 0; k < K; ++k)
+                    if (idx[(int64_t)t * K + k] >= 0)
+                        acc += (double)w[(int64_t)t * K + k] * ytk[((int64_t)t * K + k) * Dl + i];
+                a[i] = acc;
+                if (agg) agg[(int64_t)t * Dl + i] = acc;
+            }
+            k3o_rmsnorm(a, Dl, gn, eps, r);
+            dense(Wup, Dh, Dl, r, y);
+            k3o_expert(Sg, Su, Sd, Dh, Fs, h + (int64_t)t * Dh, NULL, NULL, NULL, s);
+            for (int32_t i = 0; i < Dh; ++i) out[(int64_t)t * Dh + i] = (float)(y[i] + s[i]);
+            free(a);
+            free(r);
+            free(y);
+            free(s);
+        }
+    }
+    free(x32);
+    free(y32);
+    free(ytk);
+    return rc;
+}

@@ -16,6 +16,18 @@ colibri PR #676 reports in "It runs the full model"):
   batch4096   4096 tokens, i.i.d. hidden states, logits = h.R, chunk path;
               eight "edge" experts carry scale bytes over the full 0..255 range
 
+LatentMoE block workloads (the routed experts behind 7168 <-> 3584 projections,
+RMSNorm on the aggregate and two fused shared experts; LATENT below):
+
+  latent_tiny   6 tokens, hidden 512 around the tiny experts (latent 256), shared 256
+  latent1       1 token, hidden 7168 around the decode1 experts, shared 2 x 3072
+  latent32      32 tokens, hidden 7168 around the prefill32 experts, shared 2 x 3072
+
+Dense weights are bf16 values: w_down ~ N(0, 1/Dh), w_up ~ N(0, 1/Dl), shared
+gate/up ~ N(0, 1/Dh), shared down ~ N(0, 1/Fs), norm weight 1 + 0.1 N(0, 1), so
+every stage stays O(1); hidden states h ~ N(0, 1) (bf16 values) and the router
+logits are h . R with R ~ N(0, 1/Dh) (the router reads the full hidden state).
+
 Weights: each packed byte is drawn uniform over 0..255, i.e. both e2m1 nibbles
 independent and uniform over the 16 codes.  Scale bytes are uniform integers over
 an inclusive range.  Every (expert, tensor) pair has its own PCG64 sub-stream
@@ -220,3 +232,56 @@ def sample_tokens(cfg: Config, n: int, must_include: Sequence[int] = (), seed: i
     rng = np.random.default_rng([cfg.act_seed, 271828, seed])
     base = rng.choice(cfg.T, size=min(n, cfg.T), replace=False)
     return np.unique(np.concatenate([base, np.asarray(must_include, dtype=np.int64)])).astype(np.int64)
+
+
+# --------------------------------------------------------------------- LatentMoE block
+@dataclasses.dataclass(frozen=True)
+class LatentConfig:
+    name: str
+    experts: Config        # the routed experts (their D is the latent width)
+    Dh: int                # hidden width
+    Fs: int                # width of the two fused shared experts (both halves)
+    seed: int
+    eps: float = 1e-6
+
+
+LATENT: Dict[str, LatentConfig] = {
+    "latent_tiny": LatentConfig("latent_tiny", scaled(CONFIGS["tiny"], T=6, path="chunk"), Dh=512, Fs=256, seed=501),
+    "latent1": LatentConfig("latent1", CONFIGS["decode1"], Dh=7168, Fs=6144, seed=502),
+    "latent32": LatentConfig("latent32", CONFIGS["prefill32"], Dh=7168, Fs=6144, seed=503),
+}
+
+DENSE = ("w_down", "w_up", "norm", "shared_gate", "shared_up", "shared_down")
+
+
+def latent_dense_host(lc: LatentConfig) -> Dict[str, np.ndarray]:
+    """The dense weights of a LatentMoE block as bf16 values held in fp32."""
+    Dh, Dl, Fs = lc.Dh, lc.experts.D, lc.Fs
+    shapes = {"w_down": (Dl, Dh), "w_up": (Dh, Dl), "norm": (Dl,), "shared_gate": (Fs, Dh),
+              "shared_up": (Fs, Dh), "shared_down": (Dh, Fs)}
+    std = {"w_down": Dh ** -0.5, "w_up": Dl ** -0.5, "shared_gate": Dh ** -0.5, "shared_up": Dh ** -0.5,
+           "shared_down": Fs ** -0.5}
+    out = {}
+    for tid, n in enumerate(DENSE):
+        rng = np.random.default_rng([lc.seed, 4242, tid])
+        if n == "norm":
+            v = 1.0 + 0.1 * rng.standard_normal(shapes[n])
+        else:
+            v = std[n] * rng.standard_normal(shapes[n], dtype=np.float32)
+        out[n] = bf16_round(np.asarray(v, dtype=np.float32))
+    return out
+
+
+def latent_activations(lc: LatentConfig, T: Optional[int] = None):
+    """``(h [T,Dh] bf16 values in f32, logits [T,E] f32, bias [E] f32)``."""
+    cfg = lc.experts
+    T = cfg.T if T is None else int(T)
+    rng = np.random.default_rng([lc.seed, 7919])
+    h = bf16_round(rng.standard_normal((T, lc.Dh)).astype(np.float32))
+    R = np.random.default_rng([lc.seed, 104729]).standard_normal((lc.Dh, cfg.E)) * np.sqrt(1.0 / lc.Dh)
+    logits = (h.astype(np.float64) @ R).astype(np.float32)
+    if cfg.bias_std > 0:
+        bias = (cfg.bias_std * np.random.default_rng([lc.seed, 31337]).standard_normal(cfg.E)).astype(np.float32)
+    else:
+        bias = np.zeros(cfg.E, dtype=np.float32)
+    return np.ascontiguousarray(h), np.ascontiguousarray(logits), bias

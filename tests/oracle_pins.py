@@ -701,6 +701,78 @@ def check_forward_mx_weight_nan(o):
     assert np.isfinite(y0).all()
 
 
+# ------------------------------------------------------------- P11 LatentMoE wrapper
+def check_rmsnorm(o):
+    """RMSNorm by hand on a 3-4 vector and the closed form of a constant vector; with
+    eps = 0 scaling the input by a power of two leaves the output bit-identical."""
+    r = o.rmsnorm(np.array([3.0, 4.0]), np.array([1.0, 2.0], np.float32), 0.0)
+    rms = math.sqrt(12.5)
+    assert abs(r[0] - 3 / rms) <= 1e-15 and abs(r[1] - 8 / rms) <= 1e-15
+    c, eps, n = 0.25, 1e-3, 64
+    r = o.rmsnorm(np.full(n, c), np.full(n, 1.5, np.float32), eps)
+    assert np.allclose(r, 1.5 * c / math.sqrt(c * c + eps), rtol=1e-15, atol=0)
+    a = np.random.default_rng(61).standard_normal(100)
+    g = (1 + 0.1 * np.random.default_rng(62).standard_normal(100)).astype(np.float32)
+    assert np.array_equal(o.rmsnorm(a, g, 0.0), o.rmsnorm(a * 2.0 ** 37, g, 0.0))
+
+
+def _latent_tiny():
+    import synth
+    lc = synth.LATENT["latent_tiny"]
+    cfg = lc.experts
+    dense = dict(synth.latent_dense_host(lc))
+    W = synth.weights_host(cfg)
+    h, logits, bias = synth.latent_activations(lc)
+    return lc, cfg, dense, W, h, logits, bias
+
+
+def _ldense(dense, eps):
+    return {"w_dn": dense["w_down"], "w_up": dense["w_up"], "norm": dense["norm"], "eps": eps,
+            "sg": dense["shared_gate"], "su": dense["shared_up"], "sd": dense["shared_down"]}
+
+
+def check_latent_composition(o):
+    """The block is its stages in order: x = Wdn h (fsum of exact products), the
+    routed aggregate of the oracle's own forward on x held in fp32, RMSNorm on that
+    aggregate, Wup, plus the shared experts as one SiTU-GLU expert of width Fs."""
+    lc, cfg, dense, W, h, logits, bias = _latent_tiny()
+    idx, w, _ = o.route(logits, bias, cfg.K)
+    out, xl, agg = o.latent_forward(_ldense(dense, lc.eps), W, h, idx, w, nthreads=2, want_parts=True)
+    Wdn, Wup = dense["w_down"].astype(np.float64), dense["w_up"].astype(np.float64)
+    for t in range(h.shape[0]):
+        for i in range(0, cfg.D, 37):
+            terms = Wdn[i] * h[t].astype(np.float64)
+            assert abs(xl[t, i] - math.fsum(terms)) <= 1e-12 * math.fsum(np.abs(terms)), (t, i)
+    y, ytk, _ = o.forward(W, xl.astype(np.float32), idx, w, want_pairs=True)
+    want_agg = np.zeros_like(agg)
+    for k in range(cfg.K):
+        want_agg += w[:, k:k + 1].astype(np.float64) * ytk[:, k]
+    assert np.array_equal(agg, want_agg)
+    for t in range(h.shape[0]):
+        r = o.rmsnorm(agg[t], dense["norm"], lc.eps)
+        sh = o.expert(dense["shared_gate"], dense["shared_up"], dense["shared_down"], h[t])["y"]
+        for d in range(0, lc.Dh, 29):
+            terms = Wup[d] * r
+            want = math.fsum(terms) + sh[d]
+            assert abs(out[t, d] - want) <= 1e-6 * (math.fsum(np.abs(terms)) + abs(sh[d])) + 1e-30, (t, d)
+
+
+def check_latent_zero_paths(o):
+    """Zero shared down-projection: out is the routed branch alone; zero up-projection:
+    out is the shared experts alone (each path can be switched off on its own)."""
+    lc, cfg, dense, W, h, logits, bias = _latent_tiny()
+    idx, w, _ = o.route(logits, bias, cfg.K)
+    d0 = _ldense(dense, lc.eps)
+    full = o.latent_forward(d0, W, h, idx, w, nthreads=2)
+    no_sh = o.latent_forward(dict(d0, sd=np.zeros_like(d0["sd"])), W, h, idx, w, nthreads=2)
+    no_up = o.latent_forward(dict(d0, w_up=np.zeros_like(d0["w_up"])), W, h, idx, w, nthreads=2)
+    for t in range(h.shape[0]):
+        sh = o.expert(dense["shared_gate"], dense["shared_up"], dense["shared_down"], h[t])["y"]
+        assert np.array_equal(no_up[t], sh.astype(np.float32)), t
+    assert np.allclose(full, no_sh.astype(np.float64) + no_up, rtol=1e-6, atol=1e-6)
+    assert np.abs(no_sh).max() > 0 and np.abs(no_up).max() > 0
+
+
 ALL_CHECKS = [
     check_decode_closed_form, check_decode_conventions, check_layout_fixture, check_scale_groups,
     check_dequant_matches_codes, check_expert_brute_force, check_route_brute_force,
@@ -709,5 +781,6 @@ ALL_CHECKS = [
     check_route_topp_definition, check_route_topp_off_and_monotone, check_forward_pruned, check_group_pruned,
     check_e4m3_decode, check_mx_quant_exact_values, check_mx_quant_brute, check_mx_quant_special,
     check_mx_quant_two_parts, check_forward_mx, check_forward_mx_weight_nan,
+    check_rmsnorm, check_latent_composition, check_latent_zero_paths,
 ]
 # check_gate_moments is run separately (it pins the generator, and is the slowest)

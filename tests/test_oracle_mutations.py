@@ -41,8 +41,9 @@ MUTANTS = [
     ("dropped last input term", "for (int32_t i = 0; i < D; ++i) {", "for (int32_t i = 0; i < D - 1; ++i) {"),
     ("wrong token for a pair", "x + t * D, NULL, NULL", "x + (p % T) * D, NULL, NULL"),
     ("combine ignores weights", "acc += (double)w[(int64_t)t * K + k] * yp[", "acc += yp["),
-    ("combine drops last slot", "for (int32_t k = 0; k < K; ++k)\n                    if (idx[(int64_t)t * K + k] >= 0)",
-     "for (int32_t k = 0; k < K - 1; ++k)\n                    if (idx[(int64_t)t * K + k] >= 0)"),
+    ("combine drops last slot",
+     "for (int32_t k = 0; k < K; ++k)\n                    if (idx[(int64_t)t * K + k] >= 0)\n                        acc += (double)w[(int64_t)t * K + k] * yp[",
+     "for (int32_t k = 0; k < K - 1; ++k)\n                    if (idx[(int64_t)t * K + k] >= 0)\n                        acc += (double)w[(int64_t)t * K + k] * yp["),
     ("group order unstable", "for (int64_t p = 0; p < P; ++p) {\n        int32_t e = idx[p];\n        if (e == -1) continue;",
      "for (int64_t p = P - 1; p >= 0; --p) {\n        int32_t e = idx[p];\n        if (e == -1) continue;"),
     ("union misses singletons", "if (counts[e] > 0) uniq[nu++] = e;", "if (counts[e] > 1) uniq[nu++] = e;"),
@@ -62,6 +63,11 @@ MUTANTS = [
     ("mx second part dropped", "        if (parts > 1) out[i] += mx_value(", "        if (0) out[i] += mx_value("),
     ("mx residual of the input", "    for (int64_t i = 0; i < n; ++i) r[i] = v[i] - mx_value(codes[i], scales[i / 32]);",
      "    for (int64_t i = 0; i < n; ++i) r[i] = v[i];"),
+    ("rmsnorm without the mean", "const double rms = sqrt(ss / n + eps);", "const double rms = sqrt(ss + eps);"),
+    ("rmsnorm weight ignored", "r[i] = (double)g[i] * (a[i] / rms);", "r[i] = a[i] / rms;"),
+    ("shared experts dropped", "(float)(y[i] + s[i]);", "(float)(y[i]);"),
+    ("dense projection transposed", "acc += (double)W[(int64_t)o * I + i] * x[i];", "acc += (double)W[(int64_t)i * O + o] * x[i];"),
+    ("aggregate ignores routing weights", "acc += (double)w[(int64_t)t * K + k] * ytk[", "acc += ytk["),
     ("offsets inclusive", "offsets[e + 1] = offsets[e] + counts[e];", "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
 ]
 
