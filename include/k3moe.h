@@ -215,6 +215,47 @@ int k3moe_forward_chunk_mx(const k3moe_weights_t *W, const uint16_t *x, int32_t 
                            size_t ws_bytes, void *stream);
 
 /*
+ * The LatentMoE block around the routed experts (colibri PR #684 engine commit,
+ * Stable LatentMoE bullet: latent 7168 <-> 3584 projections around the experts,
+ * RMSNorm on the aggregate, two fused shared experts, SiTU-GLU; PR #676 summary:
+ * the routed experts run in the latent space behind shared down/up projections,
+ * plus two fused full-width shared experts).  Dense weights are bf16 (raw 16-bit
+ * patterns), row-major, owned by the caller:
+ *   w_down [d_latent, d_hidden], w_up [d_hidden, d_latent], norm [d_latent],
+ *   shared_gate / shared_up [d_shared, d_hidden], shared_down [d_hidden, d_shared]
+ * (d_shared is the width of the two shared experts fused, both halves), eps the
+ * RMSNorm epsilon.  d_latent is the routed experts' d_model.
+ */
+typedef struct k3moe_latent {
+    int32_t d_hidden, d_shared;
+    float eps;
+    const uint16_t *w_down, *w_up, *norm, *shared_gate, *shared_up, *shared_down;
+} k3moe_latent_t;
+
+/*
+ * One LatentMoE block for T tokens with hidden states h [T, d_hidden] (bf16):
+ *   x = w_down h;  a = sum_k w_k E_k(x) (routing idx/w [T, K] as for the routed
+ *   entry points, e.g. from k3moe_route on the router's logits);
+ *   out = w_up RMSNorm(a) + shared_down SiTU-GLU(shared_gate h, shared_up h)
+ * with RMSNorm(a) = norm * a / sqrt(mean(a^2) + eps).  out [T, d_hidden] fp32.
+ * x is rounded to bf16 (the chunk path's activation format) and the routed
+ * block is k3moe_forward_decode's path for T = 1 and k3moe_forward_chunk's
+ * otherwise; RMSNorm and SiTU-GLU outputs are bf16; the dense products run as
+ * bf16 GEMMs with fp32 accumulation (rocBLAS).
+ * Requires d_hidden and d_shared multiples of 32 in [32, K3MOE_MAX_DIM], eps >= 0,
+ * every pointer 16-byte aligned.  ws: k3moe_latent_workspace_size() bytes.  The
+ * first call on a device creates that device's rocBLAS handle (rocBLAS allocates
+ * its own workspace then); later calls allocate nothing.
+ */
+int k3moe_latent_forward(const k3moe_latent_t *L, const k3moe_weights_t *W, const uint16_t *h, int32_t T,
+                         const int32_t *idx, const float *w, int32_t K, float *out, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* Bytes of device workspace for k3moe_latent_forward; 0 for invalid arguments.
+ * Pure host function. */
+size_t k3moe_latent_workspace_size(const k3moe_latent_t *L, int32_t T, int32_t K, const k3moe_weights_t *W);
+
+/*
  * OCP MXFP8 quantization as the MX chunk path does it, on n values (n a positive
  * multiple of 32) of fp32 (in_dtype K3MOE_IN_F32) or bf16 (K3MOE_IN_BF16, raw
  * 16-bit patterns).  For each group of 32 with largest magnitude amax: scale byte

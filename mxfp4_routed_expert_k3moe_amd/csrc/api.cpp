@@ -222,6 +222,40 @@ int k3moe_forward_chunk_mx(const k3moe_weights_t* W, const uint16_t* x, int32_t 
                                          static_cast<hipStream_t>(stream)));
 }
 
+static bool latent_ok(const k3moe_latent_t* L, const k3moe_weights_t* W) {
+    return L && W && dim_ok(L->d_hidden) && dim_ok(L->d_shared) && L->eps >= 0.0f && dim_ok(W->d_model) &&
+           dim_ok(W->d_ff) && W->n_experts >= 1 && W->n_experts <= K3MOE_MAX_E;
+}
+
+size_t k3moe_latent_workspace_size(const k3moe_latent_t* L, int32_t T, int32_t K, const k3moe_weights_t* W) {
+    if (!latent_ok(L, W) || T < 1 || K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return 0;
+    const k3moe::LatentDims d{L->d_hidden, W->d_model, W->d_ff, L->d_shared};
+    return k3moe::latent_workspace_bytes(d, T, K, W->n_experts);
+}
+
+int k3moe_latent_forward(const k3moe_latent_t* L, const k3moe_weights_t* W, const uint16_t* h, int32_t T,
+                         const int32_t* idx, const float* w, int32_t K, float* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+    if (!L) return K3MOE_E_NULL;
+    int rc = check_weights(W);
+    if (rc != K3MOE_OK) return rc;
+    if (!h || !idx || !w || !out || !ws || !L->w_down || !L->w_up || !L->norm || !L->shared_gate ||
+        !L->shared_up || !L->shared_down)
+        return K3MOE_E_NULL;
+    if (!latent_ok(L, W) || T < 1 || K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return K3MOE_E_DIM;
+    if ((long long)T * K > (1ll << 30)) return K3MOE_E_DIM;
+    if (!aligned16(h) || !aligned16(out) || !aligned16(ws) || !aligned16(L->w_down) || !aligned16(L->w_up) ||
+        !aligned16(L->norm) || !aligned16(L->shared_gate) || !aligned16(L->shared_up) || !aligned16(L->shared_down))
+        return K3MOE_E_ALIGN;
+    if (ws_bytes < k3moe_latent_workspace_size(L, T, K, W)) return K3MOE_E_WORKSPACE;
+    rc = check_device();
+    if (rc != K3MOE_OK) return rc;
+    const k3moe::DevLatent dl{L->d_hidden, L->d_shared, L->eps, L->w_down, L->w_up, L->norm,
+                              L->shared_gate, L->shared_up, L->shared_down};
+    return finish(k3moe::launch_latent(dl, dev_weights(W), h, T, idx, w, K, out, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int k3moe_mx_quant(const void* v, int32_t in_dtype, int64_t n, int32_t parts, uint8_t* codes, uint8_t* scales,
                    void* stream) {
     if (!v || !codes || !scales) return K3MOE_E_NULL;

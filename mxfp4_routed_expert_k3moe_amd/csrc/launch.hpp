@@ -99,6 +99,19 @@ hipError_t launch_chunk_mx(const DevWeights& W, const uint16_t* x, int T, const 
                            int K, int parts, float* y, int32_t* n_unique_out, const ChunkMxWorkspace& ws,
                            hipStream_t stream);
 
+// ------------------------------------------------------------------ LatentMoE block
+struct LatentDims {
+    int Dh, Dl, F, Fs;  // hidden width, latent width (= expert D), expert width, shared width
+};
+struct DevLatent {
+    int Dh, Fs;
+    float eps;
+    const uint16_t *w_down, *w_up, *norm, *shared_gate, *shared_up, *shared_down;  // bf16
+};
+size_t latent_workspace_bytes(const LatentDims& L, int T, int K, int E);
+hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t* h, int T, const int32_t* idx,
+                         const float* w, int K, float* out, void* ws, hipStream_t stream);
+
 // ------------------------------------------------------------------ dequant
 hipError_t launch_dequant(const uint8_t* q, const uint8_t* s, int O, int I, void* out, int out_bf16,
                           hipStream_t stream);

@@ -35,13 +35,18 @@ ENTRY_POINTS = ("k3moe_route", "k3moe_route_topp", "k3moe_group", "k3moe_forward
                 "k3moe_decode_down", "k3moe_forward_chunk", "k3moe_workspace_size", "k3moe_dequant_mxfp4",
                 "k3moe_status_string", "k3moe_slot_layout", "k3moe_pool_create", "k3moe_pool_destroy",
                 "k3moe_pool_plan", "k3moe_pool_weights", "k3moe_pool_stats", "k3moe_forward_decode_pooled",
-                "k3moe_forward_chunk_mx", "k3moe_mx_quant")
+                "k3moe_forward_chunk_mx", "k3moe_mx_quant", "k3moe_latent_forward", "k3moe_latent_workspace_size")
 
 
 class K3moeError(RuntimeError):
     def __init__(self, fn: str, code: int):
         super().__init__(f"{fn} failed: {status_string(code)} (status {code})")
         self.code = code
+
+
+class LatentStruct(ctypes.Structure):
+    _fields_ = ([("d_hidden", ctypes.c_int32), ("d_shared", ctypes.c_int32), ("eps", ctypes.c_float)] +
+                [(n, ctypes.c_void_p) for n in ("w_down", "w_up", "norm", "shared_gate", "shared_up", "shared_down")])
 
 
 class WeightsStruct(ctypes.Structure):
@@ -88,8 +93,13 @@ def load() -> ctypes.CDLL:
     lib.k3moe_forward_decode_pooled.argtypes = [vp, i32, vp, i64, i64, vp, vp, vp, i32, vp, vp, sz, vp, vp]
     lib.k3moe_forward_chunk_mx.argtypes = [wp, vp, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
     lib.k3moe_mx_quant.argtypes = [vp, i32, i64, i32, vp, vp, vp]
+    lp = ctypes.POINTER(LatentStruct)
+    lib.k3moe_latent_forward.argtypes = [lp, wp, vp, i32, vp, vp, i32, vp, vp, sz, vp]
+    lib.k3moe_latent_workspace_size.argtypes = [lp, i32, i32, wp]
+    lib.k3moe_latent_workspace_size.restype = sz
     for name in ENTRY_POINTS:
-        if name not in ("k3moe_workspace_size", "k3moe_status_string", "k3moe_pool_create", "k3moe_pool_destroy"):
+        if name not in ("k3moe_workspace_size", "k3moe_status_string", "k3moe_pool_create", "k3moe_pool_destroy",
+                        "k3moe_latent_workspace_size"):
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -321,6 +331,51 @@ def forward_chunk_mx(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: to
            load().k3moe_forward_chunk_mx(W.ref(), _ptr(x), T, _ptr(idx), _ptr(w), K, int(parts), _ptr(y),
                                          _ptr(n_unique), _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+class LatentWeights:
+    """The dense bf16 weights of a LatentMoE block (device tensors, kept alive here):
+    ``w_down [Dl,Dh]``, ``w_up [Dh,Dl]``, ``norm [Dl]``, ``shared_gate/shared_up [Fs,Dh]``,
+    ``shared_down [Dh,Fs]``, and the RMSNorm ``eps``."""
+
+    NAMES = ("w_down", "w_up", "norm", "shared_gate", "shared_up", "shared_down")
+
+    def __init__(self, tensors: Dict[str, torch.Tensor], eps: float):
+        self.t = {n: tensors[n] for n in self.NAMES}
+        for n, v in self.t.items():
+            _dev(v, torch.bfloat16, n)
+        self.Dl, self.Dh = self.t["w_down"].shape
+        self.Fs = self.t["shared_gate"].shape[0]
+        if (tuple(self.t["w_up"].shape) != (self.Dh, self.Dl) or tuple(self.t["norm"].shape) != (self.Dl,)
+                or tuple(self.t["shared_up"].shape) != (self.Fs, self.Dh)
+                or tuple(self.t["shared_down"].shape) != (self.Dh, self.Fs)):
+            raise ValueError("dense weight shapes do not match")
+        self.s = LatentStruct(self.Dh, self.Fs, float(eps), *[_ptr(self.t[n]) for n in self.NAMES])
+
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+def latent_forward(L: LatentWeights, W: ExpertWeights, h: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                   out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The LatentMoE block: bf16 ``h [T,Dh]``, routing ``idx/w [T,K]`` -> fp32 ``out [T,Dh]``."""
+    T = h.shape[0]
+    _dev(h, torch.bfloat16, "h", (T, L.Dh))
+    if W.D != L.Dl:
+        raise ValueError("the routed experts' d_model must equal the latent width")
+    K = idx.shape[1]
+    _dev(idx, torch.int32, "idx", (T, K))
+    _dev(w, torch.float32, "w", (T, K))
+    out = torch.empty((T, L.Dh), dtype=torch.float32, device=h.device) if out is None else out
+    _dev(out, torch.float32, "out", (T, L.Dh))
+    need = load().k3moe_latent_workspace_size(L.ref(), T, K, W.ref())
+    if need == 0:
+        raise ValueError("invalid LatentMoE arguments")
+    ws = _workspace(need, h.device, ws)
+    _check("k3moe_latent_forward",
+           load().k3moe_latent_forward(L.ref(), W.ref(), _ptr(h), T, _ptr(idx), _ptr(w), K, _ptr(out), _ptr(ws),
+                                       ws.numel(), _stream(stream)))
+    return out
 
 
 def mx_quant(v: torch.Tensor, parts: int = 1, stream=None):

@@ -576,6 +576,17 @@ double k3o_rmsnorm(const double *a, int32_t n, const float *g, double eps, doubl
     return rms;
 }
 
+/* f rounded to the nearest bf16 value (8 significant bits), ties to even; NaN stays NaN. */
+static float bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return f;
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
 /* y[o] = sum_i W[o, i] x[i] for W [O, I] (float values), x double; ascending i. */
 static void dense(const float *W, int32_t O, int32_t I, const double *x, double *y)
 {
@@ -592,8 +603,9 @@ static void dense(const float *W, int32_t O, int32_t I, const double *x, double 
  * experts run in a 3584-dim latent space behind shared down/up projections,
  * plus two fused full-width shared experts).  The pages give no formulas; the
  * plainest reading, per token with hidden state h [Dh]:
- *   x   = Wdn h                           latent input of the routed experts,
- *                                         held as fp32 like any activation
+ *   x   = bf16(fp32(Wdn h))               latent input of the routed experts, in
+ *                                         the bf16 activation format the routed
+ *                                         chunk path takes
  *   a   = sum_k w_k E_k(x)                the routed aggregate (k3o_forward)
  *   r   = RMSNorm(a) with weight gn, eps  "on the aggregate": in the latent space
  *   y   = Wup r                           back to the full width
@@ -602,8 +614,8 @@ static void dense(const float *W, int32_t O, int32_t I, const double *x, double 
  *   out = y + s
  * Dense weights: Wdn [Dl, Dh], Wup [Dh, Dl], Sg/Su [Fs, Dh], Sd [Dh, Fs] as float
  * (their bf16 values), gn [Dl]; expert weights and routing as in k3o_forward on
- * the latent x.  Sums in double; out [T, Dh] fp32; xl (nullable) receives x
- * [T, Dl] and agg (nullable) a [T, Dl] in double.  Returns 0, or -1 as
+ * the latent x.  Sums in double; out [T, Dh] fp32; xl (nullable) receives Wdn h
+ * [T, Dl] before the rounding and agg (nullable) a [T, Dl], in double.  Returns 0, or -1 as
  * k3o_forward does. */
 int k3o_latent_forward(int32_t Dh, int32_t Dl, int32_t Fs,
                        const float *Wdn, const float *Wup, const float *gn, double eps,
@@ -630,7 +642,7 @@ int k3o_latent_forward(int32_t Dh, int32_t Dl, int32_t Fs,
         for (int32_t i = 0; i < Dh; ++i) hd[i] = h[(int64_t)t * Dh + i];
         dense(Wdn, Dl, Dh, hd, xd);
         for (int32_t i = 0; i < Dl; ++i) {
-            x32[(int64_t)t * Dl + i] = (float)xd[i];
+            x32[(int64_t)t * Dl + i] = bf16_round((float)xd[i]);
             if (xl) xl[(int64_t)t * Dl + i] = xd[i];
         }
         free(hd);

@@ -716,6 +716,11 @@ def check_rmsnorm(o):
     assert np.array_equal(o.rmsnorm(a, g, 0.0), o.rmsnorm(a * 2.0 ** 37, g, 0.0))
 
 
+def synth_bf16(x):
+    import synth
+    return synth.bf16_round(x)
+
+
 def _latent_tiny():
     import synth
     lc = synth.LATENT["latent_tiny"]
@@ -733,8 +738,9 @@ def _ldense(dense, eps):
 
 def check_latent_composition(o):
     """The block is its stages in order: x = Wdn h (fsum of exact products), the
-    routed aggregate of the oracle's own forward on x held in fp32, RMSNorm on that
-    aggregate, Wup, plus the shared experts as one SiTU-GLU expert of width Fs."""
+    routed aggregate of the oracle's own forward on x rounded to fp32 and then to
+    bf16 (numpy's rounding), RMSNorm on that aggregate, Wup, plus the shared experts
+    as one SiTU-GLU expert of width Fs."""
     lc, cfg, dense, W, h, logits, bias = _latent_tiny()
     idx, w, _ = o.route(logits, bias, cfg.K)
     out, xl, agg = o.latent_forward(_ldense(dense, lc.eps), W, h, idx, w, nthreads=2, want_parts=True)
@@ -743,7 +749,7 @@ def check_latent_composition(o):
         for i in range(0, cfg.D, 37):
             terms = Wdn[i] * h[t].astype(np.float64)
             assert abs(xl[t, i] - math.fsum(terms)) <= 1e-12 * math.fsum(np.abs(terms)), (t, i)
-    y, ytk, _ = o.forward(W, xl.astype(np.float32), idx, w, want_pairs=True)
+    y, ytk, _ = o.forward(W, synth_bf16(xl.astype(np.float32)), idx, w, want_pairs=True)
     want_agg = np.zeros_like(agg)
     for k in range(cfg.K):
         want_agg += w[:, k:k + 1].astype(np.float64) * ytk[:, k]

@@ -140,6 +140,33 @@ def test_validation_before_any_device_call():
     assert q(ctypes.c_void_p(260), 0, 64, 1, p, p, None) == k3.K3MOE_E_ALIGN
 
 
+def test_latent_validation():
+    """k3moe_latent_forward / k3moe_latent_workspace_size reject bad arguments on the host."""
+    lib = k3.load()
+    s = _struct()
+    p = 256
+    L = k3.LatentStruct(7168, 6144, 1e-6, p, p, p, p, p, p)
+    need = lib.k3moe_latent_workspace_size(ctypes.byref(L), 32, 16, ctypes.byref(s))
+    assert need >= 32 * 6144 * 4 * 2 + 32 * 3584 * 4
+    assert lib.k3moe_latent_workspace_size(ctypes.byref(L), 32, 65, ctypes.byref(s)) == 0
+    for bad in (k3.LatentStruct(7000, 6144, 1e-6, p, p, p, p, p, p), k3.LatentStruct(7168, 6144, -1.0, p, p, p, p, p, p),
+                k3.LatentStruct(7168, 6144, float("nan"), p, p, p, p, p, p)):
+        assert lib.k3moe_latent_workspace_size(ctypes.byref(bad), 32, 16, ctypes.byref(s)) == 0
+        assert lib.k3moe_latent_forward(ctypes.byref(bad), ctypes.byref(s), ctypes.c_void_p(p), 32, ctypes.c_void_p(p),
+                                        ctypes.c_void_p(p), 16, ctypes.c_void_p(p), ctypes.c_void_p(p), need,
+                                        None) == k3.K3MOE_E_DIM
+    vp = ctypes.c_void_p(p)
+    f = lib.k3moe_latent_forward
+    assert f(None, ctypes.byref(s), vp, 32, vp, vp, 16, vp, vp, need, None) == k3.K3MOE_E_NULL
+    assert f(ctypes.byref(L), ctypes.byref(s), None, 32, vp, vp, 16, vp, vp, need, None) == k3.K3MOE_E_NULL
+    nul = k3.LatentStruct(7168, 6144, 1e-6, p, p, None, p, p, p)
+    assert f(ctypes.byref(nul), ctypes.byref(s), vp, 32, vp, vp, 16, vp, vp, need, None) == k3.K3MOE_E_NULL
+    mis = k3.LatentStruct(7168, 6144, 1e-6, p, p + 2, p, p, p, p)
+    assert f(ctypes.byref(mis), ctypes.byref(s), vp, 32, vp, vp, 16, vp, vp, need, None) == k3.K3MOE_E_ALIGN
+    assert f(ctypes.byref(L), ctypes.byref(s), vp, 0, vp, vp, 16, vp, vp, need, None) == k3.K3MOE_E_DIM
+    assert f(ctypes.byref(L), ctypes.byref(s), vp, 32, vp, vp, 16, vp, vp, need - 1, None) == k3.K3MOE_E_WORKSPACE
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(TypeError):

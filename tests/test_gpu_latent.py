@@ -1,0 +1,74 @@
+"""LatentMoE block (projections, routed experts, RMSNorm, shared experts) on the GPU
+vs the oracle: rel-L2 <= 5e-3.
+
+The GPU runs the dense products as bf16 GEMMs with fp32 accumulation and rounds
+the latent input (more than one token: the chunk path takes bf16), the normed
+aggregate and the shared experts' activation to bf16 (2^-9 relative each); the
+routed block adds its own rounding (see the chunk tests).  The oracle keeps
+every sum in double."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import assert_close, device_weights, log, torch_cuda
+
+pytestmark = pytest.mark.gpu
+TOL = 5e-3
+_dense_cache = {}
+
+
+def _dense_device(lc):
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    if lc.name not in _dense_cache:
+        _dense_cache.clear()
+        host = synth.latent_dense_host(lc)
+        dev = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in host.items()}  # exact: bf16 values
+        _dense_cache[lc.name] = (host, lib.LatentWeights(dev, lc.eps))
+    return _dense_cache[lc.name]
+
+
+def _run(lc, T=None, what=""):
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = lc.experts
+    host, L = _dense_device(lc)
+    W = device_weights(cfg)
+    h, logits, bias = synth.latent_activations(lc, T=T)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    log(f"latent {what}: T={h.shape[0]} Dh={lc.Dh} Dl={cfg.D} Fs={lc.Fs} E={cfg.E} K={cfg.K}")
+    out = lib.latent_forward(L, W, torch.from_numpy(h).to(torch.bfloat16).cuda(), torch.from_numpy(idx).cuda(),
+                             torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    used = np.unique(idx)
+    Wh = synth.weights_host(cfg, used)
+    local = np.searchsorted(used, idx).astype(np.int32)
+    dense = {"w_dn": host["w_down"], "w_up": host["w_up"], "norm": host["norm"], "eps": lc.eps,
+             "sg": host["shared_gate"], "su": host["shared_up"], "sd": host["shared_down"]}
+    want = oracle.latent_forward(dense, Wh, h, local, w)
+    assert_close(got, want, TOL, f"latent {what}")
+    return got
+
+
+def test_latent_tiny_chunk():
+    _run(synth.LATENT["latent_tiny"], what="tiny T=6 (chunk path)")
+
+
+def test_latent_tiny_one_token():
+    _run(synth.LATENT["latent_tiny"], T=1, what="tiny T=1 (decode path)")
+
+
+def test_latent_k3_one_token():
+    _run(synth.LATENT["latent1"], what="K3 shape, 1 token")
+
+
+def test_latent_k3_32_tokens():
+    _run(synth.LATENT["latent32"], what="K3 shape, 32 tokens")
+
+
+def test_latent_deterministic():
+    a = _run(synth.LATENT["latent_tiny"], what="tiny repeat a")
+    b = _run(synth.LATENT["latent_tiny"], what="tiny repeat b")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -68,6 +68,7 @@ MUTANTS = [
     ("shared experts dropped", "(float)(y[i] + s[i]);", "(float)(y[i]);"),
     ("dense projection transposed", "acc += (double)W[(int64_t)o * I + i] * x[i];", "acc += (double)W[(int64_t)i * O + o] * x[i];"),
     ("aggregate ignores routing weights", "acc += (double)w[(int64_t)t * K + k] * ytk[", "acc += ytk["),
+    ("latent x kept in fp32", "x32[(int64_t)t * Dl + i] = bf16_round((float)xd[i]);", "x32[(int64_t)t * Dl + i] = (float)xd[i];"),
     ("offsets inclusive", "offsets[e + 1] = offsets[e] + counts[e];", "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
 ]
 
