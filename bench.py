@@ -8,7 +8,8 @@ differ, so each step streams its 16 experts (280.76 MB) from HBM rather than fro
 the 256 MB last-level cache.  The value is routed-expert weight bytes per second
 over the timed steps (inputs resident in HBM).
 
-Also reported: the 4096-token chunk pass (grouped bf16-MFMA path) in TFLOP/s,
+Also reported: the 4096-token chunk pass (grouped bf16-MFMA path, and the
+MXFP8-activation path on the scaled FP8 x FP4 MFMA with one and two parts) in TFLOP/s,
 the roofline of the decode kernels measured with HIP events on their stream, and
 the CPU oracle timed on a bounded sample as a baseline.
 """
@@ -28,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "routed-expert MXFP4 GB/s + µs/layer-token (decode); TFLOP/s (chunk) vs roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0  # dense FP8 (and FP8 x FP4 scaled) MFMA
 
 
 def log(msg):
@@ -137,6 +139,7 @@ def main():
     ap.add_argument("--chunk-iters", type=int, default=5)
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-latent", action="store_true", help="skip the LatentMoE block legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--top-p", type=float, default=0.7, help="also time decode with top-p pruning (0 = skip)")
     ap.add_argument("--pool-slots", type=int, default=128,
@@ -322,6 +325,56 @@ def main():
             f"{el * 1e6 / n_pool:.1f} us/token, host->HBM {copied / el / 1e9:.1f} GB/s")
         pool.close()
         del host, slots_mem, pool
+
+    # the LatentMoE block around the same experts (colibri PR #684 engine commit,
+    # Stable LatentMoE bullet): 7168 -> 3584 projection, the routed experts,
+    # RMSNorm on the aggregate, 3584 -> 7168, plus the two fused shared experts
+    if not args.no_latent:
+        lc = synth.LATENT["latent1"]
+        dense_h = synth.latent_dense_host(lc)
+        Lw = lib.LatentWeights({k: torch.from_numpy(v).to(torch.bfloat16).to(dev) for k, v in dense_h.items()},
+                               lc.eps)
+        dense_bytes = sum(int(v.size) * 2 for v in dense_h.values())
+        hs, lgs, bss = synth.latent_activations(lc, T=n_rot)
+        h_l = torch.from_numpy(hs).to(torch.bfloat16).to(dev)
+        idx_l, w_l = lib.route(torch.from_numpy(lgs).to(dev), torch.from_numpy(bss).to(dev), K)
+        out_l = torch.empty((n_rot, lc.Dh), dtype=torch.float32, device=dev)
+        ws_l = torch.empty(lib.load().k3moe_latent_workspace_size(Lw.ref(), 1, K, W.ref()), dtype=torch.uint8,
+                           device=dev)
+        for j in range(min(args.warmup, n_rot)):
+            lib.latent_forward(Lw, W, h_l[j:j + 1], idx_l[j:j + 1], w_l[j:j + 1], out=out_l[j:j + 1], ws=ws_l)
+        torch.cuda.synchronize()
+        n_lat = min(args.steps, 64)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_lat):
+            j = i % n_rot
+            lib.latent_forward(Lw, W, h_l[j:j + 1], idx_l[j:j + 1], w_l[j:j + 1], out=out_l[j:j + 1], ws=ws_l)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n_lat
+        T_c = 256
+        hc, lgc, bsc = synth.latent_activations(lc, T=T_c)
+        h_c = torch.from_numpy(hc).to(torch.bfloat16).to(dev)
+        idx_cl, w_cl = lib.route(torch.from_numpy(lgc).to(dev), torch.from_numpy(bsc).to(dev), K)
+        out_c = torch.empty((T_c, lc.Dh), dtype=torch.float32, device=dev)
+        ws_c = torch.empty(lib.load().k3moe_latent_workspace_size(Lw.ref(), T_c, K, W.ref()), dtype=torch.uint8,
+                           device=dev)
+        lib.latent_forward(Lw, W, h_c, idx_cl, w_cl, out=out_c, ws=ws_c)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.chunk_iters):
+            lib.latent_forward(Lw, W, h_c, idx_cl, w_cl, out=out_c, ws=ws_c)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_c = e0.elapsed_time(e1) / args.chunk_iters
+        result["latent"] = {"workload": f"LatentMoE block: hidden {lc.Dh}, the decode1 experts in the {cfg.D} latent, "
+                                        f"RMSNorm, shared experts of width {lc.Fs} (bf16 dense weights)",
+                            "decode_us_per_layer_token": round(us, 2),
+                            "decode_weight_gbs": round((bytes_per_token + dense_bytes) / us / 1e3, 1),
+                            "chunk256_ms": round(ms_c, 4), "chunk256_us_per_layer_token": round(ms_c * 1e3 / T_c, 3)}
+        log(f"latent block: {us:.1f} us/token at T=1, {ms_c:.3f} ms for {T_c} tokens")
+        del Lw, ws_l, ws_c
     del W, ws
     torch.cuda.empty_cache()
 
@@ -357,7 +410,32 @@ def main():
                            "tflops_frac_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
                            "weight_gbs": round(wbytes / ms / 1e6, 1), "unique_experts": U}
         log(f"chunk: {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s, union {U}")
-        del Wc, wsc
+        del wsc
+        torch.cuda.empty_cache()
+        # the same pass with MXFP8 activations on the scaled FP8 x FP4 MFMA, one and two parts
+        wsm = torch.empty(lib.workspace_size(lib.OP_CHUNK_MX, ccfg.T, ccfg.K, Wc), dtype=torch.uint8, device=dev)
+        result["chunk_mx"] = {"workload": "batch4096 as above, MXFP8 activations (E4M3 + E8M0 per 32) in one or "
+                                          "two parts, scaled FP8 x FP4 MFMA (route + group + quantize + gate/up + "
+                                          "down + combine); weight groups with scale byte 255 read as NaN"}
+        for parts in (1, 2):
+            lib.forward_chunk_mx(Wc, xc, idx_c, w_c, parts, y=yc, n_unique=nu, ws=wsm)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.chunk_iters):
+                lib.route(lg_c, bs_c, ccfg.K, idx=idx_c, w=w_c)
+                lib.forward_chunk_mx(Wc, xc, idx_c, w_c, parts, y=yc, n_unique=nu, ws=wsm)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            msm = e0.elapsed_time(e1) / args.chunk_iters
+            result["chunk_mx"][f"parts{parts}"] = {
+                "ms": round(msm, 4), "us_per_layer_token": round(msm * 1e3 / ccfg.T, 4),
+                "tflops": round(flops / msm / 1e9, 2),
+                "tflops_frac_fp8_peak": round(flops / msm / 1e9 / FP8_PEAK_TFLOPS, 4),
+                "tflops_frac_bf16_peak": round(flops / msm / 1e9 / BF16_PEAK_TFLOPS, 4),
+                "weight_gbs": round(wbytes / msm / 1e6, 1)}
+            log(f"chunk mx parts={parts}: {msm:.3f} ms, {flops / msm / 1e9:.1f} TFLOP/s")
+        del Wc, wsm
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU baseline
