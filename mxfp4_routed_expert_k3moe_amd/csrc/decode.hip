@@ -346,16 +346,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     float acc = 0.0f;
     for (int k0 = 0; k0 < K; k0 += 16) {
         float v[16], wk[16];
-        bool use[16];
+        int id[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {  // all loads of a group in flight together
-            use[i] = k0 + i < K && idx[k0 + i] != K3MOE_PRUNED;
-            v[i] = use[i] ? ypart[(size_t)(k0 + i) * D + d] : 0.0f;
-            wk[i] = use[i] ? wts[k0 + i] : 0.0f;
+        for (int i = 0; i < 16; ++i) {  // all loads of a group in flight together: the
+            const int kk = min(k0 + i, K - 1);  // partials are read whatever the slot
+            id[i] = idx[kk];                     // holds (a pruned slot's row is
+            wk[i] = wts[kk];                     // workspace memory, never used)
+            v[i] = ypart[(size_t)kk * D + d];
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            if (use[i]) acc = fmaf(wk[i], v[i], acc);
+            if (k0 + i < K && id[i] != K3MOE_PRUNED) acc = fmaf(wk[i], v[i], acc);
     }
     y[d] = acc;
 }

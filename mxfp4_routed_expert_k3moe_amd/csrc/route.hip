@@ -135,6 +135,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
         const unsigned long long c = cand[threadIdx.x];
         if (c != 0ull) {
             int rank = 0;
+            // nc is a multiple of 4; unrolled so the LDS reads overlap instead of
+            // paying one latency each
+#pragma unroll 8
             for (int i = 0; i < nc; ++i) rank += cand[i] > c;
             if (rank < K) {
                 const int e = (int)(~(uint32_t)(c & 0xFFFFFFFFull));
@@ -145,7 +148,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     __syncthreads();
     if (wave != 0) return;
-    double S = 0.0;  // slot order, as in the definition
+    double S = 0.0;  // slot order, as in the definition (reads unrolled, sum in order)
+#pragma unroll 16
     for (int k = 0; k < K; ++k) S += sel_sig[k];
     const double sig = lane < K ? sel_sig[lane] : 0.0;
     int m = K;
