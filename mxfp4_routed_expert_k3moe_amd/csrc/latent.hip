@@ -31,14 +31,27 @@ namespace {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// One workgroup per token row: sum of squares in fp32 (fixed reduction order),
-// then r = g * a * rsqrt(mean + eps) rounded to bf16.
+// One workgroup per token row (n <= 8192, a multiple of 32): every load is issued
+// up front (up to 8 float4 of the row and 4 bf16x8 of the weight per thread), the
+// sum of squares is reduced in a fixed order in fp32, then r = g * a * rsqrt(mean +
+// eps) is rounded to bf16 from the registers.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ a, const uint16_t* __restrict__ g,
                                                       int n, float eps, uint16_t* __restrict__ r) {
     __shared__ float part[256 / kWave];
-    const float* row = a + (size_t)blockIdx.x * n;
+    const float4* row = reinterpret_cast<const float4*>(a + (size_t)blockIdx.x * n);
+    const int n4 = n >> 2;
+    float4 v[8];
+    uint2 gw[8];  // the four bf16 weights of each float4
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        const bool ok = i < n4;
+        v[j] = ok ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        gw[j] = ok ? reinterpret_cast<const uint2*>(g)[i] : make_uint2(0u, 0u);
+    }
     float ss = 0.f;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) ss += row[i] * row[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
     ss = wave_sum(ss);
     if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = ss;
     __syncthreads();
@@ -46,9 +59,16 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 256 / kWave; ++j) tot += part[j];
     const float inv = 1.0f / sqrtf(tot / (float)n + eps);
-    uint16_t* out = r + (size_t)blockIdx.x * n;
-    for (int i = threadIdx.x; i < n; i += blockDim.x)
-        out[i] = (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)g[i] << 16) * (row[i] * inv));
+    uint2* out = reinterpret_cast<uint2*>(r + (size_t)blockIdx.x * n);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        if (i >= n4) break;
+        const float g0 = __uint_as_float(gw[j].x << 16), g1 = __uint_as_float(gw[j].x & 0xFFFF0000u);
+        const float g2 = __uint_as_float(gw[j].y << 16), g3 = __uint_as_float(gw[j].y & 0xFFFF0000u);
+        out[i] = make_uint2(pack_bf16x2(g0 * (v[j].x * inv), g1 * (v[j].y * inv)),
+                            pack_bf16x2(g2 * (v[j].z * inv), g3 * (v[j].w * inv)));
+    }
 }
 
 // bf16 -> fp32 (exact).
