@@ -269,7 +269,7 @@ struct APieces {
 template <int MODE, int MT, int CW, int NBB>
 struct GemmState {
     using AP = APieces<MODE, MT, CW * 64>;
-    static_assert(NBB == 2 || NBB == 4, "ring depth must be a multiple of the two A register sets");
+    static_assert(NBB >= 2 && NBB <= 4, "weight ring depth");
     AP ap;
     uint4 areg[2][AP::SLOTS];
     const uint8_t* bq[4];  // weight rows in HBM
@@ -311,7 +311,8 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) scn[ns] = st.bs[ns][min(lg, sb - 1)];
 
-    for_steps<NBB>(nsteps, [&](auto uc, const int step) {
+    // P steps per loop body: a multiple of the ring depth and of the two A register sets
+    for_steps<(NBB % 2 == 0) ? NBB : 2 * NBB>(nsteps, [&](auto uc, const int step) {
         constexpr int u = decltype(uc)::value;
         st.ap.load(st.areg[u & 1], min(step + 2, nsteps - 1), Kdim);
         {
@@ -339,9 +340,9 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns) {
                 if constexpr (EXACT)
-                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16(valid ? pick(st.bring[u][ns], j) : 0u, sc[ns]));
+                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16(valid ? pick(st.bring[u % NBB][ns], j) : 0u, sc[ns]));
                 else
-                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16_nofix(pick(st.bring[u][ns], j), scf[ns]));
+                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16_nofix(pick(st.bring[u % NBB][ns], j), scf[ns]));
             }
 #pragma unroll
             for (int i = 0; i < MS; ++i) {

@@ -132,7 +132,7 @@ struct MxPieces {
 template <int MODE, int MT, int CW, int NBB, int PARTS>
 struct MxState {
     using AP = MxPieces<MODE, MT, CW * 64, PARTS>;
-    static_assert(NBB == 2 || NBB == 4, "ring depth must be a multiple of the two A register sets");
+    static_assert(NBB >= 2 && NBB <= 4, "weight ring depth");
     AP ap;
     u32x4 areg[2][AP::SLOTS];  // native vectors: a struct type here ends up in scratch
     uint32_t sreg[2];
@@ -196,7 +196,8 @@ __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, 
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) scn[ns] = st.bs[ns][lg];
 
-    for_steps<NBB>(nsteps, [&](auto uc, const int step) {
+    // P steps per loop body: a multiple of the ring depth and of the two A register sets
+    for_steps<(NBB % 2 == 0) ? NBB : 2 * NBB>(nsteps, [&](auto uc, const int step) {
         constexpr int u = decltype(uc)::value;
         st.ap.load(st.areg[u & 1], st.sreg[u & 1], min(step + 2, nsteps - 1));
         {
@@ -229,7 +230,7 @@ __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, 
 #pragma unroll
                 for (int ns = 0; ns < 4; ++ns)
                     acc[i][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        aop, b_operand(st.bring[u][ns]), acc[i][ns], 0, 4, 0, sa, 0, (int)sc[ns]);
+                        aop, b_operand(st.bring[u % NBB][ns]), acc[i][ns], 0, 4, 0, sa, 0, (int)sc[ns]);
             }
         }
         st.ap.store(st.areg[(u + 1) & 1], st.sreg[(u + 1) & 1], alds + (size_t)((step + 1) & 1) * MT * A_ROW,
