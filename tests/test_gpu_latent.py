@@ -72,3 +72,36 @@ def test_latent_deterministic():
     a = _run(synth.LATENT["latent_tiny"], what="tiny repeat a")
     b = _run(synth.LATENT["latent_tiny"], what="tiny repeat b")
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [5, 70])
+def test_latent_ragged_token_counts(T):
+    """Token counts that are not multiples of the 64-token grouping block."""
+    _run(synth.LATENT["latent_tiny"], T=T, what=f"tiny T={T}")
+
+
+def test_latent_single_expert_per_token():
+    import dataclasses
+    lc = synth.LATENT["latent_tiny"]
+    lc1 = dataclasses.replace(lc, name="latent_tiny_k1", experts=synth.scaled(lc.experts, K=1))
+    _run(lc1, what="tiny K=1")
+    _run(lc1, T=1, what="tiny K=1, one token")
+
+
+@pytest.mark.parametrize("T", [1, 6])
+def test_latent_invalid_routing_is_nan(T):
+    """An expert id out of range makes the routed block's output NaN (decode: the
+    token's row; chunk: the whole chunk, n_unique = -1), and the block's output with it."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    lc = synth.LATENT["latent_tiny"]
+    cfg = lc.experts
+    _, L = _dense_device(lc)
+    W = device_weights(cfg)
+    h, logits, bias = synth.latent_activations(lc, T=T)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    idx[0, 0] = cfg.E + 3
+    out = lib.latent_forward(L, W, torch.from_numpy(h).to(torch.bfloat16).cuda(), torch.from_numpy(idx).cuda(),
+                             torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    assert np.isnan(out.cpu().numpy()[0]).all()

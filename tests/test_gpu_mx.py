@@ -210,3 +210,13 @@ def test_chunk_mx_pruned_and_invalid():
     bad[5, 0] = bad[5, 1]
     y, nu = _chunk_mx_gpu(W, x, bad, w, 2)
     assert nu == -1 and np.all(np.isnan(y))
+
+
+@pytest.mark.parametrize("E,K,D,F,T", [(4, 4, 128, 128, 17), (7, 1, 256, 256, 40), (64, 64, 128, 128, 20)])
+def test_chunk_mx_degenerate_shapes(E, K, D, F, T):
+    """Every expert routed by every token (K = E), one expert per token (K = 1), the
+    largest K, and the smallest widths the MX path takes (one 128-column step)."""
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name=f"mxd{E}_{K}_{D}_{F}", E=E, K=K, D=D, F=F, T=T,
+                       weight_seed=950 + E, act_seed=950 + T, path="chunk")
+    for parts in (1, 2):
+        _case(cfg, f"E={E} K={K} D={D} F={F} T={T}", parts, exact=False)
