@@ -5,7 +5,7 @@
 // chunked-prefill commit: the position lists come from a counting sort.  On the
 // GPU the union turns the per-token GEMVs into a grouped matrix product whose
 // weight operand is each routed expert's MXFP4 bytes, streamed once per tile of
-// up to 128 of its pairs.
+// up to 96 of its pairs (16 when the chunk is small).
 //
 // Kernels, in stream order (x arrives as bf16):
 //   group_count    per 64-token block: one 64-bit mask per expert (bit i = token
@@ -19,14 +19,15 @@
 //   combine        y_t = sum_k y_pair[t*K+k] in slot order
 //
 // GEMM structure (gfx950, v_mfma_f32_16x16x32_bf16, wave64):
-//   workgroup = one (tile, column block): 4 waves for 128-row tiles, 8 for
-//   16-row tiles; each wave owns 32 (gate/up) or 64 (down) output columns.  The
-//   reduction runs in 128-column steps through a 4-deep ring: the tile's A rows
-//   (activations, shared by all waves) go global -> LDS directly, 16-byte pieces
-//   XOR-swizzled by row; the weight operand never touches LDS: each lane loads
-//   16 bytes (32 codes = one scale group) of one weight row into a register ring
-//   and converts them with the gfx950 scaled fp4->bf16 converts straight into
-//   four MFMA B operands.  The k order inside a step is permuted (lane group g
+//   workgroup = one (tile, column block): 8 waves (4 when the weight scale rows
+//   of 8 would not fit in LDS); each wave owns 32 (gate/up) or 64 (down) output
+//   columns.  The reduction runs in 128-column steps: the tile's A rows
+//   (activations, shared by all waves) are loaded two steps ahead into registers
+//   and stored into a double-buffered LDS tile, 16-byte pieces XOR-swizzled by
+//   row; the weight operand never touches LDS: each lane loads 16 bytes (32
+//   codes = one scale group) of one weight row into a register ring (2 steps
+//   deep at 96-row tiles, 4 at 16-row tiles) and converts them with the gfx950
+//   scaled fp4->bf16 converts straight into four MFMA B operands.  The k order inside a step is permuted (lane group g
 //   owns columns 32g..32g+31, MFMA j takes 8j..8j+7 of them) identically for A
 //   and B, which leaves the dot products unchanged.  Scale bytes of the
 //   workgroup's weight rows are staged in LDS once.  Workgroup ids are remapped
