@@ -10,8 +10,9 @@ over the timed steps (inputs resident in HBM).
 
 Also reported: the 4096-token chunk pass (grouped bf16-MFMA path, and the
 MXFP8-activation path on the scaled FP8 x FP4 MFMA with one and two parts) in TFLOP/s,
-the roofline of the decode kernels measured with HIP events on their stream, and
-the CPU oracle timed on a bounded sample as a baseline.
+the roofline of the decode gate/up kernel from HIP events that its launch records at
+the kernel's start and end, and the CPU oracle timed on a bounded sample as a
+baseline.
 """
 from __future__ import annotations
 
@@ -192,16 +193,14 @@ def main():
 
     def step(j, ev=None):
         # route, then forward_decode; on a bracketed step forward_decode's two stages
-        # are called one by one so the dominant kernel (gate/up + SiTU) sits between
-        # two events on its own stream (same kernels; the combine then runs as its
-        # own small kernel instead of in the down kernel's last blocks)
+        # are called one by one (the same kernels) and the dominant one (gate/up +
+        # SiTU) is launched with a pair of events that the launch itself records at
+        # the kernel's start and end
         lib.route(l_d[j:j + 1], b_d, K, idx=idx_d[j:j + 1], w=w_d[j:j + 1])
         if ev is None:
             lib.forward_decode(W, x_d[j], idx_d[j], w_d[j], y=y_d[j], ws=ws)
             return
-        ev[0].record(stream)
-        lib.decode_gateup(W, x_d[j], idx_d[j], h=h_d)
-        ev[1].record(stream)
+        lib.decode_gateup_timed(W, x_d[j], idx_d[j], ev[0].cuda_event, ev[1].cuda_event, h=h_d)
         lib.decode_down(W, h_d, idx_d[j], w_d[j], y=y_d[j], ws=ws)
 
     for i in range(args.warmup):
@@ -209,12 +208,15 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps between two synchronizations.  The gate/up
-    # kernel is bracketed by HIP events on every 8th step only: an event
-    # pair between two kernels leaves the queue idle for a few microseconds, which
-    # would otherwise be charged to every step.
+    # kernel is timed on every 8th step with HIP events that its launch records
+    # (hipExtLaunchKernelGGL: kernel start and end, no packets of their own); each
+    # event is recorded once beforehand so that its HIP event exists.
     ev_every = 8
     evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for i in range(0, args.steps, ev_every)}
+    for a, b in evs.values():
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):

@@ -176,6 +176,18 @@ int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t
  */
 int k3moe_decode_gateup(const k3moe_weights_t *W, const float *x, const int32_t *idx, int32_t K,
                         float *h, void *stream);
+
+/*
+ * k3moe_decode_gateup with the kernel's own duration recorded: ev_start and
+ * ev_stop are hipEvent_t handles the caller created (hipEventCreate) and owns;
+ * the kernel is launched through hipExtLaunchKernelGGL, which records ev_start
+ * when the kernel begins and ev_stop when it ends, so hipEventElapsedTime on
+ * the pair is the kernel alone (no launch or queue gap, unlike events recorded
+ * on the stream around the call).  Same arithmetic and errors as
+ * k3moe_decode_gateup; a null event is K3MOE_E_NULL.
+ */
+int k3moe_decode_gateup_timed(const k3moe_weights_t *W, const float *x, const int32_t *idx, int32_t K,
+                              float *h, void *ev_start, void *ev_stop, void *stream);
 int k3moe_decode_down(const k3moe_weights_t *W, const float *h, const int32_t *idx, const float *w,
                       int32_t K, float *y, void *ws, size_t ws_bytes, void *stream);
 

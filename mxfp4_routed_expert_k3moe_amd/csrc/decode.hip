@@ -30,6 +30,8 @@
 // feeds MFMA j = 0..3 with columns 32g + 8j ... + 7 of that group.  The A operand
 // takes the same columns of the activation parts, so each MFMA pairs every
 // product exactly once.
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -380,16 +382,18 @@ DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F) {
 }
 
 hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32_t* idx, int K, float* h,
-                                hipStream_t stream) {
+                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     const dim3 grid((W.F + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, K);
     const size_t lds = decode_lds_bytes(W.D, 2);
     // dword scale copies need every scale row and expert block 4-byte aligned
     const bool dw = (W.D % 128 == 0) && W.gate_s_stride % 4 == 0 && W.up_s_stride % 4 == 0 &&
                     (reinterpret_cast<uintptr_t>(W.gate_s) & 3) == 0 && (reinterpret_cast<uintptr_t>(W.up_s) & 3) == 0;
-    if (dw)
-        hipLaunchKernelGGL(decode_gateup_kernel<true>, grid, dim3(WAVES * 64), lds, stream, W, x, idx, h);
+    const auto kernel = dw ? decode_gateup_kernel<true> : decode_gateup_kernel<false>;
+    if (ev_start != nullptr && ev_stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, dim3(WAVES * 64), (uint32_t)lds, stream, ev_start, ev_stop, 0, W, x, idx,
+                              h);
     else
-        hipLaunchKernelGGL(decode_gateup_kernel<false>, grid, dim3(WAVES * 64), lds, stream, W, x, idx, h);
+        hipLaunchKernelGGL(kernel, grid, dim3(WAVES * 64), lds, stream, W, x, idx, h);
     return hipGetLastError();
 }
 

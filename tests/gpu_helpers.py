@@ -14,6 +14,15 @@ import synth
 _weights_cache: Dict[tuple, object] = {}
 
 
+def timing_event():
+    """A timing-enabled torch event whose HIP event already exists (recorded once),
+    so its raw handle (``.cuda_event``) can be handed to a timed entry point."""
+    torch = torch_cuda()
+    ev = torch.cuda.Event(enable_timing=True)
+    ev.record()
+    return ev
+
+
 def log(msg: str):
     print(f"[gpu-test {time.strftime('%H:%M:%S')}] {msg}", flush=True)
     sys.stdout.flush()

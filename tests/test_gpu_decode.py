@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_helpers import assert_close, device_weights, log, oracle_forward_subset, torch_cuda
+from gpu_helpers import assert_close, device_weights, log, oracle_forward_subset, timing_event, torch_cuda
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -101,3 +101,12 @@ def test_decode_stages_match_oracle():
                         torch.from_numpy(w[0]).cuda()).cpu().numpy()
     want = (w[0].astype(np.float64)[:, None] * ytk[0]).sum(axis=0)
     assert_close(y, want, TOL, "decode stage down (oracle h in)")
+    # the timed launch of the same stage: identical h, a positive kernel duration
+    ev0, ev1 = timing_event(), timing_event()
+    ht = lib.decode_gateup_timed(W, torch.from_numpy(x[0]).cuda(), torch.from_numpy(idx[0]).cuda(),
+                                 ev0.cuda_event, ev1.cuda_event)
+    torch.cuda.synchronize()
+    assert np.array_equal(ht.cpu().numpy().view(np.uint32), h.view(np.uint32))
+    ms = ev0.elapsed_time(ev1)
+    log(f"decode gate/up kernel (own events): {ms * 1e3:.1f} us")
+    assert 0.0 < ms < 100.0
