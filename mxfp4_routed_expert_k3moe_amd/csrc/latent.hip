@@ -5,19 +5,21 @@
 // experts, SiTU-GLU; PR #676 summary: the routed experts run in the latent space
 // behind shared down/up projections, plus two fused full-width shared experts.
 // Per token with hidden state h [Dh] (bf16):
-//   x   = Wdn h                           [Dl]   dense GEMM, bf16 out (the activation format
-//                                                of the routed chunk path; widened to fp32
-//                                                for the one-token decode path)
+//   x   = Wdn h                           [Dl]   bf16 out (the activation format of the
+//                                                routed chunk path; widened to fp32 for
+//                                                the one-token decode path)
 //   a   = sum_k w_k E_k(x)                [Dl]   the routed block: decode GEMVs for one
 //                                                token, the grouped chunk GEMMs otherwise
-//   r   = gn * a / sqrt(mean(a^2) + eps)  [Dl]   rmsnorm kernel, bf16 out
-//   out = Wup r                           [Dh]   dense GEMM, fp32
-//   g   = Sg h, u = Su h                  [Fs]   dense GEMMs, fp32
-//   s   = SiTU(g, u)                      [Fs]   situ kernel, bf16 out
-//   out += Sd s                           [Dh]   dense GEMM accumulating into out
-// The five dense products are plain bf16 GEMMs with fp32 accumulation and go to
-// rocBLAS (Tensile's MFMA kernels for gfx950); the routed block, the norm and
-// the activation are this library's kernels.
+//   r   = gn * a / sqrt(mean(a^2) + eps)  [Dl]   bf16
+//   out = Wup r                           [Dh]   fp32
+//   g   = Sg h, u = Su h                  [Fs]   fp32
+//   s   = SiTU(g, u)                      [Fs]   bf16
+//   out += Sd s                           [Dh]
+// The five dense products are bf16 x bf16 with fp32 accumulation.  For one token
+// they are this file's GEMV kernels (x with its widening in one pass, g, u and s
+// in one pass, the norm folded into the pass that forms out); for a chunk they
+// are rocBLAS GEMMs (Tensile's MFMA kernels for gfx950) around the rmsnorm and
+// situ kernels.
 #include <rocblas/rocblas.h>
 
 #include <mutex>
@@ -71,18 +73,178 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
     }
 }
 
-// bf16 -> fp32 (exact).
-__global__ __launch_bounds__(256) void widen_kernel(const uint16_t* __restrict__ x, int n, float* __restrict__ y) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-        y[i] = __uint_as_float((uint32_t)x[i] << 16);
-}
-
 // s = SiTU-GLU(g, u) elementwise, bf16 out.
 __global__ __launch_bounds__(256) void situ_kernel(const float* __restrict__ g, const float* __restrict__ u,
                                                    size_t n, uint16_t* __restrict__ s) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
         s[i] = (uint16_t)f32_to_bf16_bits(situ_fast(g[i], u[i]));
+}
+
+// ------------------------------------------------ one token: bf16 GEMVs
+// For a single token the five projections are matrix-vector products that stream
+// their bf16 weights once; these kernels do that directly (and fuse what sits
+// between them) instead of going through a GEMM library at n = 1:
+//   GEMV_X    x = Wdn h, written as bf16 and as its exact fp32 widening
+//   GEMV_SITU s = SiTU(Sg h, Su h) in bf16 (both shared projections in one pass)
+//   GEMV_OUT  out = Wup r + Sd s in fp32, r = RMSNorm(a) computed by every
+//             workgroup (same arithmetic as rmsnorm_kernel) while staging
+// Layout: W row-major [O, I] bf16, I a multiple of 32.  A workgroup stages its
+// input vectors in LDS as bf16 (zero-padded to whole 512-column chunks); wave w
+// owns kGemvRows consecutive rows; lane l reads columns 8l + 512c (16 bytes) of
+// each row, eight chunks per batch, and accumulates fp32 products in column
+// order; a wave sum (fixed order) finishes each dot product.
+enum { GEMV_X = 0, GEMV_SITU = 1, GEMV_OUT = 2 };
+constexpr int kGemvRows = 2;     // rows per wave
+constexpr int kGemvBatch = 8;    // 16-byte chunks per row in flight per lane
+constexpr int kGemvRowsPerBlock = 4 * kGemvRows;
+
+struct GemvArgs {
+    const uint16_t* W0;  // X: Wdn; SITU: Sg; OUT: Wup
+    const uint16_t* W1;  // SITU: Su; OUT: Sd
+    int I0, I1;          // widths of the two inputs (SITU: I1 = I0, same input)
+    int O;               // rows
+    const uint16_t* v0;  // X, SITU: h (bf16)
+    const float* a;      // OUT: routed aggregate (fp32 [I0]) ...
+    const uint16_t* gn;  //      ... and the RMSNorm weight (bf16 [I0])
+    float eps;
+    const uint16_t* v1;  // OUT: s (bf16 [I1])
+    uint16_t* yb;        // X: x bf16; SITU: s bf16
+    float* yf;           // X: x widened; OUT: out
+};
+
+__host__ __device__ inline int gemv_pad(int n) { return (n + 511) & ~511; }
+
+// v (bf16, n values) -> LDS, zero past n up to the padded width
+__device__ __forceinline__ void gemv_stage(const uint16_t* __restrict__ v, int n, uint16_t* dst) {
+    const int np = gemv_pad(n);
+    for (int i = 8 * (int)threadIdx.x; i < np; i += 8 * 256) {
+        uint4 q = make_uint4(0u, 0u, 0u, 0u);
+        if (i < n) q = *reinterpret_cast<const uint4*>(v + i);
+        *reinterpret_cast<uint4*>(dst + i) = q;
+    }
+}
+
+__device__ __forceinline__ float dot8_bf16(const u32x4& w, const uint4& v, float acc) {
+    acc = fmaf(__uint_as_float(w.x << 16), __uint_as_float(v.x << 16), acc);
+    acc = fmaf(__uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(v.x & 0xFFFF0000u), acc);
+    acc = fmaf(__uint_as_float(w.y << 16), __uint_as_float(v.y << 16), acc);
+    acc = fmaf(__uint_as_float(w.y & 0xFFFF0000u), __uint_as_float(v.y & 0xFFFF0000u), acc);
+    acc = fmaf(__uint_as_float(w.z << 16), __uint_as_float(v.z << 16), acc);
+    acc = fmaf(__uint_as_float(w.z & 0xFFFF0000u), __uint_as_float(v.z & 0xFFFF0000u), acc);
+    acc = fmaf(__uint_as_float(w.w << 16), __uint_as_float(v.w << 16), acc);
+    acc = fmaf(__uint_as_float(w.w & 0xFFFF0000u), __uint_as_float(v.w & 0xFFFF0000u), acc);
+    return acc;
+}
+
+// acc[r] += W[rows[r], :] . v over the lane's chunks (v in LDS, zero-padded to
+// whole chunks).  Each batch issues all of its loads before any use; chunks past
+// the row (the batch's tail, or a lane past a width that is not a multiple of
+// 512) load an in-range address and are replaced by zeros on both sides, so the
+// body has no branches.
+__device__ __forceinline__ void gemv_rows(const uint16_t* __restrict__ W, int I, const int (&rows)[kGemvRows],
+                                          const uint16_t* v, float (&acc)[kGemvRows]) {
+    const int lane = threadIdx.x & 63;
+    const int nch = gemv_pad(I) / 512;
+    for (int c0 = 0; c0 < nch; c0 += kGemvBatch) {
+        u32x4 w[kGemvRows][kGemvBatch];
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+            for (int b = 0; b < kGemvBatch; ++b) {
+                const int col = 8 * lane + 512 * (c0 + b);
+                const u32x4 q = *reinterpret_cast<const u32x4*>(W + (size_t)rows[r] * I + min(col, I - 8));
+                w[r][b] = col < I ? q : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+        for (int b = 0; b < kGemvBatch; ++b) {
+            const bool in = c0 + b < nch;
+            uint4 vv = *reinterpret_cast<const uint4*>(v + 8 * lane + 512 * min(c0 + b, nch - 1));
+            if (!in) vv = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int r = 0; r < kGemvRows; ++r) acc[r] = dot8_bf16(w[r][b], vv, acc[r]);
+        }
+    }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t vs[];  // v0 (padded), then v1 (padded)
+    __shared__ float part[256 / kWave];
+    uint16_t* vs1 = vs + gemv_pad(g.I0);
+    if (EPI == GEMV_OUT) {
+        // RMSNorm of a, exactly as rmsnorm_kernel: sum of squares in the same order,
+        // r = bf16(gn * (a * inv))
+        const float4* row = reinterpret_cast<const float4*>(g.a);
+        const int n4 = g.I0 >> 2;
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = (int)threadIdx.x + 256 * j;
+            v[j] = i < n4 ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+        ss = wave_sum(ss);
+        if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int j = 0; j < 256 / kWave; ++j) tot += part[j];
+        const float inv = 1.0f / sqrtf(tot / (float)g.I0 + g.eps);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = (int)threadIdx.x + 256 * j;
+            if (i >= n4) break;
+            const uint2 gw = reinterpret_cast<const uint2*>(g.gn)[i];
+            const float g0 = __uint_as_float(gw.x << 16), g1 = __uint_as_float(gw.x & 0xFFFF0000u);
+            const float g2 = __uint_as_float(gw.y << 16), g3 = __uint_as_float(gw.y & 0xFFFF0000u);
+            reinterpret_cast<uint2*>(vs)[i] = make_uint2(pack_bf16x2(g0 * (v[j].x * inv), g1 * (v[j].y * inv)),
+                                                         pack_bf16x2(g2 * (v[j].z * inv), g3 * (v[j].w * inv)));
+        }
+        for (int i = g.I0 + (int)threadIdx.x; i < gemv_pad(g.I0); i += 256) vs[i] = 0;
+        gemv_stage(g.v1, g.I1, vs1);
+    } else {
+        gemv_stage(g.v0, g.I0, vs);
+    }
+    __syncthreads();
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int o0 = blockIdx.x * kGemvRowsPerBlock + wave * kGemvRows;
+    if (o0 >= g.O) return;  // wave-uniform; no barrier follows
+    int rows[kGemvRows];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) rows[r] = min(o0 + r, g.O - 1);
+    float acc0[kGemvRows] = {}, acc1[kGemvRows] = {};
+    gemv_rows(g.W0, g.I0, rows, vs, acc0);
+    if (EPI == GEMV_SITU) gemv_rows(g.W1, g.I0, rows, vs, acc1);
+    if (EPI == GEMV_OUT) gemv_rows(g.W1, g.I1, rows, vs1, acc1);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+        const float d0 = wave_sum(acc0[r]);
+        const float d1 = (EPI == GEMV_X) ? 0.f : wave_sum(acc1[r]);
+        const int o = o0 + r;
+        if (lane != 0 || o >= g.O) continue;
+        if (EPI == GEMV_X) {
+            const uint32_t xb = f32_to_bf16_bits(d0);
+            g.yb[o] = (uint16_t)xb;
+            g.yf[o] = __uint_as_float(xb << 16);
+        } else if (EPI == GEMV_SITU) {
+            g.yb[o] = (uint16_t)f32_to_bf16_bits(situ_fast(d0, d1));
+        } else {
+            g.yf[o] = d0 + d1;
+        }
+    }
+}
+
+template <int EPI>
+hipError_t launch_gemv(const GemvArgs& g, hipStream_t stream) {
+    const size_t lds = (size_t)(gemv_pad(g.I0) + (EPI == GEMV_OUT ? gemv_pad(g.I1) : 0)) * 2;
+    const dim3 grid((g.O + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock);
+    hipLaunchKernelGGL(gemv_kernel<EPI>, grid, dim3(256), lds, stream, g);
+    return hipGetLastError();
 }
 
 int grid_blocks(size_t n, int per_block) {
@@ -131,9 +293,7 @@ size_t latent_workspace_bytes(const LatentDims& L, int T, int K, int E) {
 
 hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t* h, int T, const int32_t* idx,
                          const float* w, int K, float* out, void* ws, hipStream_t stream) {
-    rocblas_handle blas = nullptr;
-    hipError_t err = blas_for(stream, &blas);
-    if (err != hipSuccess) return err;
+    hipError_t err = hipSuccess;
     const int Dh = L.Dh, Dl = W.D, Fs = L.Fs;
     const size_t t = (size_t)T;
     const size_t routed = T == 1 ? decode_workspace_bytes(K, Dl, W.F) : chunk_workspace_bytes(T, K, W.E, Dl, W.F);
@@ -147,15 +307,31 @@ hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t
     float* u = reinterpret_cast<float*>(p); p += align256(t * Fs * 4);
     uint16_t* s = reinterpret_cast<uint16_t*>(p);
 
+    if (T == 1) {
+        // one token: x = Wdn h (bf16 and fp32), s = SiTU(Sg h, Su h), the routed
+        // decode path on x, then out = Wup RMSNorm(a) + Sd s
+        GemvArgs gx{};
+        gx.W0 = L.w_down; gx.I0 = Dh; gx.O = Dl; gx.v0 = h; gx.yb = x; gx.yf = x32;
+        err = launch_gemv<GEMV_X>(gx, stream);
+        if (err != hipSuccess) return err;
+        GemvArgs gs{};
+        gs.W0 = L.shared_gate; gs.W1 = L.shared_up; gs.I0 = Dh; gs.I1 = Dh; gs.O = Fs; gs.v0 = h; gs.yb = s;
+        err = launch_gemv<GEMV_SITU>(gs, stream);
+        if (err != hipSuccess) return err;
+        err = launch_decode(W, x32, idx, w, K, a, decode_workspace_carve(rws, K, Dl, W.F), stream);
+        if (err != hipSuccess) return err;
+        GemvArgs go{};
+        go.W0 = L.w_up; go.W1 = L.shared_down; go.I0 = Dl; go.I1 = Fs; go.O = Dh;
+        go.a = a; go.gn = L.norm; go.eps = L.eps; go.v1 = s; go.yf = out;
+        return launch_gemv<GEMV_OUT>(go, stream);
+    }
+    rocblas_handle blas = nullptr;
+    err = blas_for(stream, &blas);
+    if (err != hipSuccess) return err;
     // x = Wdn h, then the routed block on x
     err = dense(blas, h, T, Dh, L.w_down, Dl, x, false, 0.0f);
     if (err != hipSuccess) return err;
-    if (T == 1) {
-        hipLaunchKernelGGL(widen_kernel, dim3(grid_blocks(Dl, 256)), dim3(256), 0, stream, x, Dl, x32);
-        err = launch_decode(W, x32, idx, w, K, a, decode_workspace_carve(rws, K, Dl, W.F), stream);
-    } else {
-        err = launch_chunk(W, x, T, idx, w, K, a, nullptr, chunk_workspace_carve(rws, T, K, W.E, Dl, W.F), stream);
-    }
+    err = launch_chunk(W, x, T, idx, w, K, a, nullptr, chunk_workspace_carve(rws, T, K, W.E, Dl, W.F), stream);
     if (err != hipSuccess) return err;
     // RMSNorm on the aggregate, then back to the full width
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, stream, a, L.norm, Dl, L.eps, r);
