@@ -78,12 +78,10 @@ def counters_probe(torch, synth, lib, dev):
     used = np.unique(idx.cpu().numpy())
     W = lib.ExpertWeights.from_dict(synth.weights_device(cfg, dev, experts=used))
     x_d = torch.from_numpy(xs).to(dev)
-    h = torch.empty((cfg.K, cfg.F), dtype=torch.float32, device=dev)
     y = torch.empty((PROBE_TOKENS, cfg.D), dtype=torch.float32, device=dev)
     ws = torch.empty(lib.workspace_size(lib.OP_DECODE, 1, cfg.K, W), dtype=torch.uint8, device=dev)
     for j in range(PROBE_TOKENS):
-        lib.decode_gateup(W, x_d[j], idx[j], h=h)
-        lib.decode_down(W, h, idx[j], w[j], y=y[j], ws=ws)
+        lib.forward_decode(W, x_d[j], idx[j], w[j], y=y[j], ws=ws)
     a = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     for _ in range(2):
@@ -189,19 +187,15 @@ def main():
     ws = torch.empty(lib.workspace_size(lib.OP_DECODE, 1, K, W), dtype=torch.uint8, device=dev)
     bytes_per_token = K * cfg.expert_bytes()  # 280 756 224
 
-    h_d = torch.empty((K, cfg.F), dtype=torch.float32, device=dev)
-
     def step(j, ev=None):
-        # route, then forward_decode; on a bracketed step forward_decode's two stages
-        # are called one by one (the same kernels) and the dominant one (gate/up +
-        # SiTU) is launched with a pair of events that the launch itself records at
-        # the kernel's start and end
+        # the router kernel on the token's logits, then forward_decode (gate/up +
+        # SiTU-GLU, down, combine); on a bracketed step the gate/up launch records a
+        # pair of events at the kernel's start and end
         lib.route(l_d[j:j + 1], b_d, K, idx=idx_d[j:j + 1], w=w_d[j:j + 1])
         if ev is None:
             lib.forward_decode(W, x_d[j], idx_d[j], w_d[j], y=y_d[j], ws=ws)
-            return
-        lib.decode_gateup_timed(W, x_d[j], idx_d[j], ev[0].cuda_event, ev[1].cuda_event, h=h_d)
-        lib.decode_down(W, h_d, idx_d[j], w_d[j], y=y_d[j], ws=ws)
+        else:
+            lib.forward_decode_timed(W, x_d[j], idx_d[j], w_d[j], ev[0].cuda_event, ev[1].cuda_event, y=y_d[j], ws=ws)
 
     for i in range(args.warmup):
         step(i % n_rot)
@@ -230,7 +224,7 @@ def main():
     # algorithmic bytes of one gate/up launch: 16 experts' gate and up tensors, x in, h out
     gu_bytes = K * 2 * (cfg.F * cfg.D // 2 + cfg.F * cfg.D // 32) + cfg.D * 4 + K * cfg.F * 4
     achieved = gu_bytes / (gu_avg_us * 1e-6) / 1e9
-    log(f"decode: {ms_per_step * 1e3:.1f} us/step (route + gate/up + down), gate/up kernel {gu_avg_us:.1f} us "
+    log(f"decode: {ms_per_step * 1e3:.1f} us/step (route + gate/up + down + combine), gate/up kernel {gu_avg_us:.1f} us "
         f"(p10 {np.percentile(gu_ms, 10) * 1e3:.1f}, p90 {np.percentile(gu_ms, 90) * 1e3:.1f}) -> "
         f"{achieved:.0f} GB/s")
 
@@ -270,8 +264,7 @@ def main():
 
         def step_topp(j):
             lib.route_topp(l_d[j:j + 1], b_d, K, top_p, idx=idx_d[j:j + 1], w=w_d[j:j + 1], n_kept=n_kept)
-            lib.decode_gateup(W, x_d[j], idx_d[j], h=h_d)
-            lib.decode_down(W, h_d, idx_d[j], w_d[j], y=y_d[j], ws=ws)
+            lib.forward_decode(W, x_d[j], idx_d[j], w_d[j], y=y_d[j], ws=ws)
 
         for i in range(args.warmup):
             step_topp(i % n_rot)

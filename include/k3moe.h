@@ -164,6 +164,20 @@ int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t
                          void *stream);
 
 /*
+ * k3moe_forward_decode with its first kernel's duration recorded: ev_start and
+ * ev_stop are hipEvent_t handles the caller created (hipEventCreate) and owns;
+ * the gate/up + SiTU-GLU kernel (the larger of the two, 2/3 of the expert
+ * bytes) is launched through hipExtLaunchKernelGGL, which records ev_start when
+ * it begins and ev_stop when it ends, so hipEventElapsedTime on the pair is that
+ * kernel alone (no launch or queue gap, unlike events recorded on the stream
+ * around the call).  Same arguments, arithmetic and errors as
+ * k3moe_forward_decode; a null event is K3MOE_E_NULL.
+ */
+int k3moe_forward_decode_timed(const k3moe_weights_t *W, const float *x, const int32_t *idx,
+                               const float *w, int32_t K, float *y, void *ws, size_t ws_bytes,
+                               void *ev_start, void *ev_stop, void *stream);
+
+/*
  * The two stages of k3moe_forward_decode, callable apart (to read the SiTU-GLU
  * activations, or to time the stages).  Same arithmetic as forward_decode.
  * k3moe_decode_gateup (steps 2-3): h[k, f] = SiTU-GLU((W_gate[e_k] x)_f,
@@ -176,18 +190,6 @@ int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t
  */
 int k3moe_decode_gateup(const k3moe_weights_t *W, const float *x, const int32_t *idx, int32_t K,
                         float *h, void *stream);
-
-/*
- * k3moe_decode_gateup with the kernel's own duration recorded: ev_start and
- * ev_stop are hipEvent_t handles the caller created (hipEventCreate) and owns;
- * the kernel is launched through hipExtLaunchKernelGGL, which records ev_start
- * when the kernel begins and ev_stop when it ends, so hipEventElapsedTime on
- * the pair is the kernel alone (no launch or queue gap, unlike events recorded
- * on the stream around the call).  Same arithmetic and errors as
- * k3moe_decode_gateup; a null event is K3MOE_E_NULL.
- */
-int k3moe_decode_gateup_timed(const k3moe_weights_t *W, const float *x, const int32_t *idx, int32_t K,
-                              float *h, void *ev_start, void *ev_stop, void *stream);
 int k3moe_decode_down(const k3moe_weights_t *W, const float *h, const int32_t *idx, const float *w,
                       int32_t K, float *y, void *ws, size_t ws_bytes, void *stream);
 

@@ -156,6 +156,23 @@ int k3moe_forward_decode(const k3moe_weights_t* W, const float* x, const int32_t
     return finish(k3moe::launch_decode(dw, x, idx, w, K, y, dws, static_cast<hipStream_t>(stream)));
 }
 
+int k3moe_forward_decode_timed(const k3moe_weights_t* W, const float* x, const int32_t* idx, const float* w,
+                               int32_t K, float* y, void* ws, size_t ws_bytes, void* ev_start, void* ev_stop,
+                               void* stream) {
+    int rc = check_weights(W);
+    if (rc != K3MOE_OK) return rc;
+    if (!x || !idx || !w || !y || !ws || !ev_start || !ev_stop) return K3MOE_E_NULL;
+    if (K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return K3MOE_E_DIM;
+    if (!aligned16(x) || !aligned16(ws)) return K3MOE_E_ALIGN;
+    if (ws_bytes < k3moe::decode_workspace_bytes(K, W->d_model, W->d_ff)) return K3MOE_E_WORKSPACE;
+    rc = check_device();
+    if (rc != K3MOE_OK) return rc;
+    const DevWeights dw = dev_weights(W);
+    const k3moe::DecodeWorkspace dws = k3moe::decode_workspace_carve(ws, K, dw.D, dw.F);
+    return finish(k3moe::launch_decode(dw, x, idx, w, K, y, dws, static_cast<hipStream_t>(stream),
+                                       static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)));
+}
+
 int k3moe_decode_gateup(const k3moe_weights_t* W, const float* x, const int32_t* idx, int32_t K, float* h,
                         void* stream) {
     int rc = check_weights(W);
@@ -166,19 +183,6 @@ int k3moe_decode_gateup(const k3moe_weights_t* W, const float* x, const int32_t*
     rc = check_device();
     if (rc != K3MOE_OK) return rc;
     return finish(k3moe::launch_decode_gateup(dev_weights(W), x, idx, K, h, static_cast<hipStream_t>(stream)));
-}
-
-int k3moe_decode_gateup_timed(const k3moe_weights_t* W, const float* x, const int32_t* idx, int32_t K, float* h,
-                              void* ev_start, void* ev_stop, void* stream) {
-    int rc = check_weights(W);
-    if (rc != K3MOE_OK) return rc;
-    if (!x || !idx || !h || !ev_start || !ev_stop) return K3MOE_E_NULL;
-    if (K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return K3MOE_E_DIM;
-    if (!aligned16(x)) return K3MOE_E_ALIGN;
-    rc = check_device();
-    if (rc != K3MOE_OK) return rc;
-    return finish(k3moe::launch_decode_gateup(dev_weights(W), x, idx, K, h, static_cast<hipStream_t>(stream),
-                                              static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)));
 }
 
 int k3moe_decode_down(const k3moe_weights_t* W, const float* h, const int32_t* idx, const float* w, int32_t K,

@@ -242,11 +242,12 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DevWeights W, const 
     const int D = W.D, F = W.F, sb = D >> 5;
     const int fblk = blockIdx.x * ROWS_PER_BLOCK;
     const int f0 = fblk + wave * 16;
+    uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(D);
+
     const int e = idx[k];
     if (e == K3MOE_PRUNED) return;  // block-uniform: a pruned slot reads and writes nothing
     const bool valid_e = e >= 0 && e < W.E;
     const int ec = valid_e ? e : 0;
-    uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(D);
 
     // activations and scale rows first: waiting for them later leaves the weights in flight
     Stage st;
@@ -411,8 +412,9 @@ hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t
 }
 
 hipError_t launch_decode(const DevWeights& W, const float* x, const int32_t* idx, const float* w, int K,
-                         float* y, const DecodeWorkspace& ws, hipStream_t stream) {
-    hipError_t err = launch_decode_gateup(W, x, idx, K, ws.h, stream);
+                         float* y, const DecodeWorkspace& ws, hipStream_t stream, hipEvent_t ev_start,
+                         hipEvent_t ev_stop) {
+    hipError_t err = launch_decode_gateup(W, x, idx, K, ws.h, stream, ev_start, ev_stop);
     if (err != hipSuccess) return err;
     return launch_decode_down(W, ws.h, idx, w, K, ws.ypart, y, stream);
 }

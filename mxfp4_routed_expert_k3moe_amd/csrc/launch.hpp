@@ -29,8 +29,11 @@ struct DecodeWorkspace {
 };
 size_t decode_workspace_bytes(int K, int D, int F);
 DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F);
+// With both events given, the gate/up kernel is launched through
+// hipExtLaunchKernelGGL, which records ev_start as it starts and ev_stop as it ends.
 hipError_t launch_decode(const DevWeights& W, const float* x, const int32_t* idx, const float* w, int K,
-                         float* y, const DecodeWorkspace& ws, hipStream_t stream);
+                         float* y, const DecodeWorkspace& ws, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
 // With both events given, the kernel is launched through hipExtLaunchKernelGGL,
 // which records ev_start as the kernel starts and ev_stop as it ends.
 hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32_t* idx, int K, float* h,

@@ -36,7 +36,7 @@ ENTRY_POINTS = ("k3moe_route", "k3moe_route_topp", "k3moe_group", "k3moe_forward
                 "k3moe_status_string", "k3moe_slot_layout", "k3moe_pool_create", "k3moe_pool_destroy",
                 "k3moe_pool_plan", "k3moe_pool_weights", "k3moe_pool_stats", "k3moe_forward_decode_pooled",
                 "k3moe_forward_chunk_mx", "k3moe_mx_quant", "k3moe_latent_forward", "k3moe_latent_workspace_size",
-                "k3moe_decode_gateup_timed")
+                "k3moe_forward_decode_timed")
 
 
 class K3moeError(RuntimeError):
@@ -75,7 +75,7 @@ def load() -> ctypes.CDLL:
     lib.k3moe_forward_decode.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.k3moe_forward_chunk.argtypes = [wp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.k3moe_decode_gateup.argtypes = [wp, vp, vp, i32, vp, vp]
-    lib.k3moe_decode_gateup_timed.argtypes = [wp, vp, vp, i32, vp, vp, vp, vp]
+    lib.k3moe_forward_decode_timed.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp, vp, vp]
     lib.k3moe_decode_down.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.k3moe_workspace_size.argtypes = [i32, i32, i32, wp]
     lib.k3moe_workspace_size.restype = sz
@@ -264,6 +264,26 @@ def forward_decode(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torc
     return y
 
 
+def forward_decode_timed(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor, ev_start: int,
+                         ev_stop: int, y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """forward_decode with the gate/up kernel's own start and end recorded in two
+    caller-owned hipEvent_t handles (raw pointers as ints)."""
+    x = _dev(x.reshape(-1) if x.dim() == 2 and x.shape[0] == 1 else x, torch.float32, "x", (W.D,))
+    idx = idx.reshape(-1)
+    w = w.reshape(-1)
+    K = idx.numel()
+    _dev(idx, torch.int32, "idx", (K,))
+    _dev(w, torch.float32, "w", (K,))
+    y = torch.empty(W.D, dtype=torch.float32, device=x.device) if y is None else y
+    _dev(y, torch.float32, "y", (W.D,))
+    ws = _workspace(workspace_size(OP_DECODE, 1, K, W), x.device, ws)
+    _check("k3moe_forward_decode_timed",
+           load().k3moe_forward_decode_timed(W.ref(), _ptr(x), _ptr(idx), _ptr(w), K, _ptr(y), _ptr(ws), ws.numel(),
+                                             ctypes.c_void_p(ev_start), ctypes.c_void_p(ev_stop), _stream(stream)))
+    return y
+
+
 def decode_gateup(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, h: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """Decode stage 1: ``h [K, F]`` = SiTU-GLU of the K experts' gate/up rows on ``x [D]``."""
@@ -274,22 +294,6 @@ def decode_gateup(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, h: Optio
     h = torch.empty((K, W.F), dtype=torch.float32, device=x.device) if h is None else h
     _dev(h, torch.float32, "h", (K, W.F))
     _check("k3moe_decode_gateup", load().k3moe_decode_gateup(W.ref(), _ptr(x), _ptr(idx), K, _ptr(h), _stream(stream)))
-    return h
-
-
-def decode_gateup_timed(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, ev_start: int, ev_stop: int,
-                        h: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """decode_gateup with the kernel's own start and end recorded in two caller-owned
-    hipEvent_t handles (raw pointers as ints)."""
-    _dev(x, torch.float32, "x", (W.D,))
-    idx = idx.reshape(-1)
-    K = idx.numel()
-    _dev(idx, torch.int32, "idx", (K,))
-    h = torch.empty((K, W.F), dtype=torch.float32, device=x.device) if h is None else h
-    _dev(h, torch.float32, "h", (K, W.F))
-    _check("k3moe_decode_gateup_timed",
-           load().k3moe_decode_gateup_timed(W.ref(), _ptr(x), _ptr(idx), K, _ptr(h), ctypes.c_void_p(ev_start),
-                                            ctypes.c_void_p(ev_stop), _stream(stream)))
     return h
 
 

@@ -114,12 +114,13 @@ def test_validation_before_any_device_call():
         setattr(bad_s, name + "_stride", 3584 * 3072 // 32 + 4)
         assert lib.k3moe_forward_chunk(ctypes.byref(bad_s), p, 32, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_ALIGN
     assert lib.k3moe_forward_decode(ctypes.byref(s), p, p, p, 16, p, p, 100, None) == k3.K3MOE_E_WORKSPACE
-    # the timed gate/up stage: both events are required
-    t = lib.k3moe_decode_gateup_timed
-    assert t(ctypes.byref(s), p, p, 16, p, None, p, None) == k3.K3MOE_E_NULL
-    assert t(ctypes.byref(s), p, p, 16, p, p, None, None) == k3.K3MOE_E_NULL
-    assert t(ctypes.byref(s), p, p, 0, p, p, p, None) == k3.K3MOE_E_DIM
-    assert t(ctypes.byref(s), ctypes.c_void_p(260), p, 16, p, p, p, None) == k3.K3MOE_E_ALIGN
+    # the timed forward: both events are required, the rest as forward_decode
+    t = lib.k3moe_forward_decode_timed
+    assert t(ctypes.byref(s), p, p, p, 16, p, p, ws, None, p, None) == k3.K3MOE_E_NULL
+    assert t(ctypes.byref(s), p, p, p, 16, p, p, ws, p, None, None) == k3.K3MOE_E_NULL
+    assert t(ctypes.byref(s), p, p, p, 0, p, p, ws, p, p, None) == k3.K3MOE_E_DIM
+    assert t(ctypes.byref(s), ctypes.c_void_p(260), p, p, 16, p, p, ws, p, p, None) == k3.K3MOE_E_ALIGN
+    assert t(ctypes.byref(s), p, p, p, 16, p, p, 100, p, p, None) == k3.K3MOE_E_WORKSPACE
     assert lib.k3moe_forward_chunk(ctypes.byref(s), p, 0, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_DIM
     assert lib.k3moe_forward_chunk(ctypes.byref(s), p, 32, p, p, 16, p, None, p, 100, None) == k3.K3MOE_E_WORKSPACE
     assert lib.k3moe_forward_chunk(ctypes.byref(s), p, 32, p, None, 16, p, None, p, ws, None) == k3.K3MOE_E_NULL

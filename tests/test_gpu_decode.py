@@ -101,12 +101,17 @@ def test_decode_stages_match_oracle():
                         torch.from_numpy(w[0]).cuda()).cpu().numpy()
     want = (w[0].astype(np.float64)[:, None] * ytk[0]).sum(axis=0)
     assert_close(y, want, TOL, "decode stage down (oracle h in)")
-    # the timed launch of the same stage: identical h, a positive kernel duration
+    # the stages chained equal the product path bit for bit, and so does the timed
+    # product path (gate/up launched with events its launch records)
+    xd, idd, wd = torch.from_numpy(x[0]).cuda(), torch.from_numpy(idx[0]).cuda(), torch.from_numpy(w[0]).cuda()
+    y_st = lib.decode_down(W, lib.decode_gateup(W, xd, idd), idd, wd)
+    y_fw = lib.forward_decode(W, xd, idd, wd)
     ev0, ev1 = timing_event(), timing_event()
-    ht = lib.decode_gateup_timed(W, torch.from_numpy(x[0]).cuda(), torch.from_numpy(idx[0]).cuda(),
-                                 ev0.cuda_event, ev1.cuda_event)
+    y_t = lib.forward_decode_timed(W, xd, idd, wd, ev0.cuda_event, ev1.cuda_event)
     torch.cuda.synchronize()
-    assert np.array_equal(ht.cpu().numpy().view(np.uint32), h.view(np.uint32))
+    bits = y_fw.cpu().numpy().view(np.uint32)
+    assert np.array_equal(y_st.cpu().numpy().view(np.uint32), bits)
+    assert np.array_equal(y_t.cpu().numpy().view(np.uint32), bits)
     ms = ev0.elapsed_time(ev1)
     log(f"decode gate/up kernel (own events): {ms * 1e3:.1f} us")
     assert 0.0 < ms < 100.0
