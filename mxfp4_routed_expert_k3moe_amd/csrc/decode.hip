@@ -16,7 +16,7 @@
 //
 //   kernel 1  block = (expert slot k, 64 rows of F); wave = 16 rows f: gate and up
 //             tiles for the same f, h = SiTU-GLU(g, u) in the epilogue -> h[k, f]
-//   kernel 2  block = (expert slot k, 64 rows of D); wave = 16 rows d of W_down
+//   kernel 2  block = (expert slot k, 112 rows of D); wave = 16 rows d of W_down
 //             against h[k] -> part[k, d]
 //   kernel 3  y[d] = sum_k w_k * part[k, d] in slot order (no atomics: the same
 //             bits on every run)
@@ -39,7 +39,9 @@ namespace k3moe {
 
 namespace {
 
-constexpr int WAVES = kDecodeWaves;  // 4 waves, 16 rows each
+// 4 waves of 16 rows: F = 3072 gives 48 workgroups per slot, 768 for 16 slots,
+// exactly three per CU (6-wave workgroups, two per CU, measured slower)
+constexpr int WAVES = kDecodeWaves;
 constexpr int ROWS_PER_BLOCK = WAVES * 16;
 constexpr int PD = 4;                // pipeline depth: steps of weights in flight per wave
 
@@ -60,18 +62,19 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
 // Split v (fp32, n a multiple of 32, 16-byte aligned) into three bf16 parts in LDS;
 // columns [n, npad) are zero.  Two phases, so a kernel can issue these loads
 // first, then its weight prefetch, and only then wait for the activations.
-constexpr int kStageMax = 8;  // float4 loads per thread: 256 threads x 8 x 4 = 8192 columns
-
+// NT threads stage the vector; each loads up to kMax float4 (8192 columns in all).
+template <int NT>
 struct Stage {
-    float4 r[kStageMax];
+    static constexpr int kMax = (2048 + NT - 1) / NT;
+    float4 r[kMax];
     int n, nits;
 
     __device__ __forceinline__ void load(const float* __restrict__ v, int n_) {
         n = n_;
-        nits = (((n + 127) & ~127) / 4 + 255) / 256;  // block-uniform
+        nits = (((n + 127) & ~127) / 4 + NT - 1) / NT;  // block-uniform
 #pragma unroll
-        for (int it = 0; it < kStageMax; ++it) {
-            const int i4 = min((int)threadIdx.x + it * 256, n / 4 - 1);  // clamped: no branch around the load
+        for (int it = 0; it < kMax; ++it) {
+            const int i4 = min((int)threadIdx.x + it * NT, n / 4 - 1);  // clamped: no branch around the load
             if (it < nits) r[it] = reinterpret_cast<const float4*>(v)[i4];
         }
     }
@@ -79,8 +82,8 @@ struct Stage {
     __device__ __forceinline__ void store(uint16_t* lds) const {
         const int npad = (n + 127) & ~127, ps = part_stride(n);
 #pragma unroll
-        for (int it = 0; it < kStageMax; ++it) {
-            const int i = 4 * ((int)threadIdx.x + it * 256);
+        for (int it = 0; it < kMax; ++it) {
+            const int i = 4 * ((int)threadIdx.x + it * NT);
             if (it < nits && i < npad) {
                 const bool in = i < n;
                 const float xs[4] = {in ? r[it].x : 0.f, in ? r[it].y : 0.f, in ? r[it].z : 0.f, in ? r[it].w : 0.f};
@@ -106,10 +109,10 @@ __device__ __forceinline__ uint4 load_row_chunk(const uint8_t* __restrict__ qrow
 
 // Copy `rows` consecutive scale rows of `sb` bytes (starting at global row r0,
 // clamped to nrows) into LDS.  Dword loads when every row is 4-byte aligned.
-template <bool DWORD, int ROWS>
+template <bool DWORD, int ROWS, int NT>
 struct ScaleStage {
-    // dwords per thread: 256 threads x 4 B x kMax = ROWS rows x 256 B (the widest scale row)
-    static constexpr int kMax = ROWS / 4;
+    // dwords per thread: NT threads x 4 B x kMax >= ROWS rows x 256 B (the widest scale row)
+    static constexpr int kMax = (ROWS * 64 + NT - 1) / NT;
     uint32_t v[kMax];
     int nbytes;
 
@@ -119,17 +122,17 @@ struct ScaleStage {
         const uint8_t* p = base + (size_t)r0 * sb;
 #pragma unroll
         for (int it = 0; it < kMax; ++it) {
-            const int i = (int)threadIdx.x + it * 256;
+            const int i = (int)threadIdx.x + it * NT;
             if (DWORD) {
                 const int c = min(i, nbytes / 4 - 1);
-                if (it * 1024 < nbytes) v[it] = reinterpret_cast<const uint32_t*>(p)[c];
+                if (it * NT * 4 < nbytes) v[it] = reinterpret_cast<const uint32_t*>(p)[c];
             } else {
                 // byte path: 4 bytes per thread per iteration, assembled in a dword
                 uint32_t w = 0;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int c = min(4 * i + b, nbytes - 1);
-                    if (it * 1024 < nbytes) w |= (uint32_t)p[c] << (8 * b);
+                    if (it * NT * 4 < nbytes) w |= (uint32_t)p[c] << (8 * b);
                 }
                 v[it] = w;
             }
@@ -139,7 +142,7 @@ struct ScaleStage {
     __device__ __forceinline__ void store(uint8_t* lds) const {
 #pragma unroll
         for (int it = 0; it < kMax; ++it) {
-            const int i = (int)threadIdx.x + it * 256;
+            const int i = (int)threadIdx.x + it * NT;
             if (4 * i < nbytes) *reinterpret_cast<uint32_t*>(lds + 4 * i) = v[it];
         }
     }
@@ -232,7 +235,7 @@ __host__ __device__ inline size_t decode_lds_bytes(int kdim, int nt) {
 }
 
 template <bool DS>
-__global__ __launch_bounds__(256) void decode_gateup_kernel(DevWeights W, const float* __restrict__ x,
+__global__ __launch_bounds__(WAVES * 64) void decode_gateup_kernel(DevWeights W, const float* __restrict__ x,
                                                             const int32_t* __restrict__ idx,
                                                             float* __restrict__ h) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -250,9 +253,9 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DevWeights W, const 
     const int ec = valid_e ? e : 0;
 
     // activations and scale rows first: waiting for them later leaves the weights in flight
-    Stage st;
+    Stage<WAVES * 64> st;
     st.load(x, D);
-    ScaleStage<DS, ROWS_PER_BLOCK> sg, su;
+    ScaleStage<DS, ROWS_PER_BLOCK, WAVES * 64> sg, su;
     sg.load(W.gate_s + (size_t)ec * W.gate_s_stride, fblk, ROWS_PER_BLOCK, F, sb);
     su.load(W.up_s + (size_t)ec * W.up_s_stride, fblk, ROWS_PER_BLOCK, F, sb);
     // weights: always prefetched (clamped to real rows), so no load sits behind a branch
@@ -287,10 +290,14 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(DevWeights W, const 
 }
 
 constexpr int DOWN_TILES = 1;  // 16-row tiles of W_down per wave
-constexpr int DOWN_ROWS_PER_BLOCK = WAVES * 16 * DOWN_TILES;
+// 7 waves (112 rows): D = 3584 gives 32 workgroups per slot, 512 for 16 slots,
+// exactly two per CU (64-row workgroups gave 896, 3.5 per CU: 20.9 against
+// 19.6 us; 32-row workgroups, seven per CU: 22.7 us)
+constexpr int DOWN_WAVES = 7;
+constexpr int DOWN_ROWS_PER_BLOCK = DOWN_WAVES * 16 * DOWN_TILES;
 
 template <bool DS>
-__global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const int32_t* __restrict__ idx,
+__global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DevWeights W, const int32_t* __restrict__ idx,
                                                           const float* __restrict__ h,
                                                           float* __restrict__ ypart) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -306,9 +313,9 @@ __global__ __launch_bounds__(256) void decode_down_kernel(DevWeights W, const in
     const int ec = valid_e ? e : 0;
     uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(F);
 
-    Stage st;
+    Stage<DOWN_WAVES * 64> st;
     st.load(h + (size_t)k * F, F);
-    ScaleStage<DS, DOWN_ROWS_PER_BLOCK> sd;
+    ScaleStage<DS, DOWN_ROWS_PER_BLOCK, DOWN_WAVES * 64> sd;
     sd.load(W.down_s + (size_t)ec * W.down_s_stride, dblk, DOWN_ROWS_PER_BLOCK, D, sb);
     const size_t qrow = (size_t)F >> 1;
     RowStream<DOWN_TILES> rs;
@@ -404,9 +411,9 @@ hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t
     const size_t lds = parts_lds_bytes(W.F) + (size_t)DOWN_ROWS_PER_BLOCK * (W.F / 32) + 16;
     const bool dw = (W.F % 128 == 0) && W.down_s_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(W.down_s) & 3) == 0;
     if (dw)
-        hipLaunchKernelGGL(decode_down_kernel<true>, grid, dim3(WAVES * 64), lds, stream, W, idx, h, ypart);
+        hipLaunchKernelGGL(decode_down_kernel<true>, grid, dim3(DOWN_WAVES * 64), lds, stream, W, idx, h, ypart);
     else
-        hipLaunchKernelGGL(decode_down_kernel<false>, grid, dim3(WAVES * 64), lds, stream, W, idx, h, ypart);
+        hipLaunchKernelGGL(decode_down_kernel<false>, grid, dim3(DOWN_WAVES * 64), lds, stream, W, idx, h, ypart);
     hipLaunchKernelGGL(decode_combine_kernel, dim3((W.D + 255) / 256), dim3(256), 0, stream, ypart, w, idx, K, W.D, y);
     return hipGetLastError();
 }

@@ -21,7 +21,7 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
                         float* w, int32_t* n_kept, hipStream_t stream);
 
 // ------------------------------------------------------------------ decode
-constexpr int kDecodeWaves = 4;  // waves per workgroup (16 weight rows each)
+constexpr int kDecodeWaves = 4;  // gate/up waves per workgroup (16 weight rows each)
 
 struct DecodeWorkspace {
     float* h;      // [K, F]  SiTU-GLU outputs per slot
