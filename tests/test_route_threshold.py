@@ -1,0 +1,83 @@
+"""The router's threshold pass, restated on the host: the pool of codes at or above
+T = max over the 4 waves of (the K-th largest lane best in that wave) always holds
+the exact top K, and at least K codes.  Brute force over random, tied, flat and
+adversarial key sets with the kernel's expert-to-lane layout (wave w holds experts
+[w*Q, (w+1)*Q), lane l of it the ones with (e - w*Q) % 64 == l), plus the pool
+sizes the 16-of-896 workloads see (the kernel ranks at most 128 codes and falls
+back to K rounds of wave maxima beyond that)."""
+import numpy as np
+import pytest
+
+
+def codes_of(keys):
+    """Unique 64-bit-like ranking codes: larger key first, then lower id (as the kernel's
+    (key bits << 32) | ~id); returned as a rank order where a larger value ranks higher."""
+    E = len(keys)
+    order = np.lexsort((np.arange(E), -keys))  # descending key, then ascending id
+    code = np.empty(E, np.int64)
+    code[order] = np.arange(E, 0, -1)  # best gets E, worst gets 1 (0 = absent)
+    return code
+
+
+def threshold_pool(code, K):
+    E = len(code)
+    Q = (E + 3) // 4
+    kth = []
+    for w in range(4):
+        best = np.zeros(64, np.int64)
+        for i in range(Q):
+            e = w * Q + i
+            if e < E:
+                best[i % 64] = max(best[i % 64], code[e])
+        nz = np.sort(best[best > 0])[::-1]
+        kth.append(nz[K - 1] if len(nz) >= K else 0)
+    T = max(kth)
+    return np.nonzero((code > 0) & (code >= T))[0]
+
+
+def check(keys, K):
+    code = codes_of(keys)
+    pool = threshold_pool(code, K)
+    top = np.argsort(-code, kind="stable")[:K]
+    assert len(pool) >= K
+    assert set(top.tolist()) <= set(pool.tolist())
+    # ranking the pool by code gives the exact selection in order
+    sel = pool[np.argsort(-code[pool], kind="stable")][:K]
+    assert np.array_equal(sel, top)
+    return len(pool)
+
+
+@pytest.mark.parametrize("E,K", [(8, 2), (20, 1), (64, 64), (100, 33), (300, 1), (896, 16), (896, 1), (2000, 20),
+                                 (4096, 16), (4096, 64)])
+def test_pool_holds_top_k(E, K):
+    rng = np.random.default_rng(E * 131 + K)
+    for trial in range(20):
+        kind = trial % 5
+        if kind == 0:
+            keys = rng.standard_normal(E)
+        elif kind == 1:  # heavy ties: few distinct values
+            keys = rng.integers(0, 3, E).astype(np.float64)
+        elif kind == 2:  # all equal: the order is by id alone
+            keys = np.zeros(E)
+        elif kind == 3:  # the best keys crowded into one wave
+            keys = rng.standard_normal(E)
+            keys[: (E + 3) // 4] += 5.0
+        else:  # the best keys crowded into one lane of each wave
+            keys = rng.standard_normal(E)
+            Q = (E + 3) // 4
+            for w in range(4):
+                keys[w * Q: min(E, (w + 1) * Q): 64] += 10.0
+        check(keys, K)
+
+
+def test_pool_size_at_the_decode_workloads():
+    """16 of 896 with sigmoid keys plus a score bias (the decode workload's routing)
+    and without it: the pool stays far below the 128-code cap."""
+    rng = np.random.default_rng(7)
+    sizes = []
+    for t in range(400):
+        lg = rng.standard_normal(896)
+        keys = 1.0 / (1.0 + np.exp(-lg)) + (0.1 * rng.standard_normal(896) if t % 2 else 0.0)
+        sizes.append(check(keys, 16))
+    assert max(sizes) <= 128, max(sizes)
+    assert 16 <= min(sizes)
