@@ -87,6 +87,7 @@ __global__ __launch_bounds__(256) void situ_kernel(const float* __restrict__ g, 
 // between them) instead of going through a GEMM library at n = 1:
 //   GEMV_X    x = Wdn h, written as bf16 and as its exact fp32 widening
 //   GEMV_SITU s = SiTU(Sg h, Su h) in bf16 (both shared projections in one pass)
+//   (the two above run as one launch, gemv_xs_kernel: both read h)
 //   GEMV_OUT  out = Wup r + Sd s in fp32, r = RMSNorm(a) computed by every
 //             workgroup (same arithmetic as rmsnorm_kernel) while staging
 // Layout: W row-major [O, I] bf16, I a multiple of 32.  A workgroup stages its
@@ -167,6 +168,54 @@ __device__ __forceinline__ void gemv_rows(const uint16_t* __restrict__ W, int I,
     }
 }
 
+// One GEMV workgroup's rows [blk * kGemvRowsPerBlock, ...) once its inputs are in
+// LDS (vs: v0 padded; vs1: v1 padded).
+template <int EPI>
+__device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_t* vs, const uint16_t* vs1, int blk) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int o0 = blk * kGemvRowsPerBlock + wave * kGemvRows;
+    if (o0 >= g.O) return;  // wave-uniform; no barrier follows
+    int rows[kGemvRows];
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) rows[r] = min(o0 + r, g.O - 1);
+    float acc0[kGemvRows] = {}, acc1[kGemvRows] = {};
+    gemv_rows(g.W0, g.I0, rows, vs, acc0);
+    if (EPI == GEMV_SITU) gemv_rows(g.W1, g.I0, rows, vs, acc1);
+    if (EPI == GEMV_OUT) gemv_rows(g.W1, g.I1, rows, vs1, acc1);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+        const float d0 = wave_sum(acc0[r]);
+        const float d1 = (EPI == GEMV_X) ? 0.f : wave_sum(acc1[r]);
+        const int o = o0 + r;
+        if (lane != 0 || o >= g.O) continue;
+        if (EPI == GEMV_X) {
+            const uint32_t xb = f32_to_bf16_bits(d0);
+            g.yb[o] = (uint16_t)xb;
+            g.yf[o] = __uint_as_float(xb << 16);
+        } else if (EPI == GEMV_SITU) {
+            g.yb[o] = (uint16_t)f32_to_bf16_bits(situ_fast(d0, d1));
+        } else {
+            g.yf[o] = d0 + d1;
+        }
+    }
+}
+
+// x = Wdn h and s = SiTU(Sg h, Su h) in one launch: both read h, so one grid
+// stages h once per workgroup and the two projections share one ramp and one
+// tail.  Workgroups [0, nbs) take rows of s (the heavier ones first), the rest
+// rows of x.
+__global__ __launch_bounds__(256) void gemv_xs_kernel(GemvArgs gx, GemvArgs gs, int nbs) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t vs[];
+    gemv_stage(gx.v0, gx.I0, vs);
+    __syncthreads();
+    const int b = blockIdx.x;
+    if (b < nbs)
+        gemv_block_rows<GEMV_SITU>(gs, vs, vs, b);
+    else
+        gemv_block_rows<GEMV_X>(gx, vs, vs, b - nbs);
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint16_t vs[];  // v0 (padded), then v1 (padded)
@@ -209,34 +258,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
         gemv_stage(g.v0, g.I0, vs);
     }
     __syncthreads();
-
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int o0 = blockIdx.x * kGemvRowsPerBlock + wave * kGemvRows;
-    if (o0 >= g.O) return;  // wave-uniform; no barrier follows
-    int rows[kGemvRows];
-#pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) rows[r] = min(o0 + r, g.O - 1);
-    float acc0[kGemvRows] = {}, acc1[kGemvRows] = {};
-    gemv_rows(g.W0, g.I0, rows, vs, acc0);
-    if (EPI == GEMV_SITU) gemv_rows(g.W1, g.I0, rows, vs, acc1);
-    if (EPI == GEMV_OUT) gemv_rows(g.W1, g.I1, rows, vs1, acc1);
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) {
-        const float d0 = wave_sum(acc0[r]);
-        const float d1 = (EPI == GEMV_X) ? 0.f : wave_sum(acc1[r]);
-        const int o = o0 + r;
-        if (lane != 0 || o >= g.O) continue;
-        if (EPI == GEMV_X) {
-            const uint32_t xb = f32_to_bf16_bits(d0);
-            g.yb[o] = (uint16_t)xb;
-            g.yf[o] = __uint_as_float(xb << 16);
-        } else if (EPI == GEMV_SITU) {
-            g.yb[o] = (uint16_t)f32_to_bf16_bits(situ_fast(d0, d1));
-        } else {
-            g.yf[o] = d0 + d1;
-        }
-    }
+    gemv_block_rows<EPI>(g, vs, vs1, blockIdx.x);
 }
 
 template <int EPI>
@@ -244,6 +266,14 @@ hipError_t launch_gemv(const GemvArgs& g, hipStream_t stream) {
     const size_t lds = (size_t)(gemv_pad(g.I0) + (EPI == GEMV_OUT ? gemv_pad(g.I1) : 0)) * 2;
     const dim3 grid((g.O + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock);
     hipLaunchKernelGGL(gemv_kernel<EPI>, grid, dim3(256), lds, stream, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_xs(const GemvArgs& gx, const GemvArgs& gs, hipStream_t stream) {
+    const size_t lds = (size_t)gemv_pad(gx.I0) * 2;
+    const int nbs = (gs.O + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock;
+    const int nbx = (gx.O + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock;
+    hipLaunchKernelGGL(gemv_xs_kernel, dim3(nbs + nbx), dim3(256), lds, stream, gx, gs, nbs);
     return hipGetLastError();
 }
 
@@ -312,11 +342,9 @@ hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t
         // decode path on x, then out = Wup RMSNorm(a) + Sd s
         GemvArgs gx{};
         gx.W0 = L.w_down; gx.I0 = Dh; gx.O = Dl; gx.v0 = h; gx.yb = x; gx.yf = x32;
-        err = launch_gemv<GEMV_X>(gx, stream);
-        if (err != hipSuccess) return err;
         GemvArgs gs{};
         gs.W0 = L.shared_gate; gs.W1 = L.shared_up; gs.I0 = Dh; gs.I1 = Dh; gs.O = Fs; gs.v0 = h; gs.yb = s;
-        err = launch_gemv<GEMV_SITU>(gs, stream);
+        err = launch_gemv_xs(gx, gs, stream);
         if (err != hipSuccess) return err;
         err = launch_decode(W, x32, idx, w, K, a, decode_workspace_carve(rws, K, Dl, W.F), stream);
         if (err != hipSuccess) return err;
