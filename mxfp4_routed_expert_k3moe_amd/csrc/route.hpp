@@ -1,6 +1,5 @@
 // route.hpp -- the sigmoid + score-correction-bias top-K selection of one token
-// by one 256-thread workgroup, shared by the router kernel and the decode kernel
-// that routes its token itself.
+// by one 256-thread workgroup (the body of the router kernel in route.hip).
 //
 // colibri PR #684, engine commit (Stable LatentMoE bullet): sigmoid router plus a
 // score-correction bias, top-16, raw-score renormalization; colibri PR #676
