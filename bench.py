@@ -67,6 +67,35 @@ def traffic_bytes():
     return t.get("bytes_per_launch")
 
 
+def capture_steps(torch, fn, n):
+    """A HIP graph (torch.cuda.CUDAGraph) of the n calls fn(0) .. fn(n-1), captured
+    on a side stream of default priority.  Every call's kernels are replayed with
+    the call's own inputs; only the host-side launch work leaves the timed region."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_replay(torch, g):
+    """One untimed replay (the first one uploads the graph), then one timed replay
+    between two synchronizations; returns seconds."""
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
 def counters_probe(torch, synth, lib, dev):
     """A short run for rocprofv3 --pmc: PROBE_TOKENS decode tokens through route,
     gate/up and down (only the experts they touch are generated), then a plain
@@ -200,26 +229,37 @@ def main():
     for i in range(args.warmup):
         step(i % n_rot)
     torch.cuda.synchronize()
+    y_ref = y_d.clone()  # eager outputs of the 32 tokens (the warm-up covers each at least once)
+    if args.warmup < n_rot:
+        for j in range(n_rot):
+            step(j)
+        torch.cuda.synchronize()
+        y_ref = y_d.clone()
 
-    # timed region: exactly `steps` steps between two synchronizations.  The gate/up
-    # kernel is timed on every 8th step with HIP events that its launch records
-    # (hipExtLaunchKernelGGL: kernel start and end, no packets of their own); each
-    # event is recorded once beforehand so that its HIP event exists.
-    ev_every = 8
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for i in range(0, args.steps, ev_every)}
-    for a, b in evs.values():
+    # timed region: exactly `steps` steps (token i % 32 at step i), captured as one
+    # HIP graph and replayed between two synchronizations after an untimed replay
+    g = capture_steps(torch, lambda i: step(i % n_rot), args.steps)
+    y_d.zero_()
+    elapsed = timed_replay(torch, g)
+    replay_ok = bool(torch.equal(y_d.view(torch.int32), y_ref.view(torch.int32))) if args.steps >= n_rot else None
+    del g
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = bytes_per_token * args.steps / elapsed / 1e9
+    log(f"decode: graph replay of {args.steps} steps, outputs equal to the eager ones: {replay_ok}")
+
+    # the gate/up kernel's own duration: eager steps whose gate/up launch records a
+    # pair of events at the kernel's start and end (hipExtLaunchKernelGGL; each event
+    # is recorded once beforehand so that its HIP event exists)
+    n_ev = min(max(args.steps, 1), 64)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for a, b in evs:
         a.record(stream)
         b.record(stream)
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(i % n_rot, evs.get(i))
+    for i in range(n_ev):
+        step(i % n_rot, evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    gu_ms = np.array([a.elapsed_time(b) for a, b in evs.values()])  # gate/up kernel per bracketed call
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = bytes_per_token * args.steps / elapsed / 1e9
+    gu_ms = np.array([a.elapsed_time(b) for a, b in evs])  # gate/up kernel per bracketed call
     gu_avg_us = float(np.mean(gu_ms) * 1e3)
     # algorithmic bytes of one gate/up launch: 16 experts' gate and up tensors, x in, h out
     gu_bytes = K * 2 * (cfg.F * cfg.D // 2 + cfg.F * cfg.D // 32) + cfg.D * 4 + K * cfg.F * 4
@@ -246,6 +286,8 @@ def main():
                    "tokens_per_step": 1, "experts": cfg.E, "top_k": K, "d_model": cfg.D, "d_ff": cfg.F,
                    "expert_bytes_per_token": bytes_per_token},
         "us_per_layer_token": round(ms_per_step * 1e3, 3),
+        "timing": {"mode": "the K steps captured as one HIP graph, one untimed replay, then one timed replay",
+                   "replay_outputs_equal_eager": replay_ok},
         "roofline": {"bound": "hbm", "kernel": "decode_gateup_kernel (16 experts' gate/up GEMV + SiTU-GLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(),
@@ -269,11 +311,9 @@ def main():
         for i in range(args.warmup):
             step_topp(i % n_rot)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step_topp(i % n_rot)
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
+        g = capture_steps(torch, lambda i: step_topp(i % n_rot), args.steps)
+        el = timed_replay(torch, g)
+        del g
         kept_mean = float(np.mean([kept_all[i % n_rot] for i in range(args.steps)]))
         us = el * 1e6 / args.steps
         result["decode_topp"] = {"top_p": top_p, "mean_experts_kept": round(kept_mean, 3), "of": K,
@@ -348,14 +388,14 @@ def main():
             lib.latent_forward(Lw, W, h_l[j:j + 1], idx_l[j:j + 1], w_l[j:j + 1], out=out_l[j:j + 1], ws=ws_l)
         torch.cuda.synchronize()
         n_lat = min(args.steps, 64)
+        g = capture_steps(torch, lambda i: lib.latent_forward(Lw, W, h_l[i % n_rot:i % n_rot + 1],
+                                                              idx_l[i % n_rot:i % n_rot + 1],
+                                                              w_l[i % n_rot:i % n_rot + 1],
+                                                              out=out_l[i % n_rot:i % n_rot + 1], ws=ws_l), n_lat)
+        el_lat = timed_replay(torch, g)
+        del g
+        us = el_lat * 1e6 / n_lat
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n_lat):
-            j = i % n_rot
-            lib.latent_forward(Lw, W, h_l[j:j + 1], idx_l[j:j + 1], w_l[j:j + 1], out=out_l[j:j + 1], ws=ws_l)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n_lat
         T_c = 256
         hc, lgc, bsc = synth.latent_activations(lc, T=T_c)
         h_c = torch.from_numpy(hc).to(torch.bfloat16).to(dev)
