@@ -418,6 +418,42 @@ def main():
                             "chunk256_ms": round(ms_c, 4), "chunk256_us_per_layer_token": round(ms_c * 1e3 / T_c, 3)}
         log(f"latent block: {us:.1f} us/token at T=1, {ms_c:.3f} ms for {T_c} tokens")
         del Lw, ws_l, ws_c
+    # prefill chunks of 32 and 256 tokens on the same weight set (AR(1) hidden
+    # states, logits = h.R): the grouped path streams each expert of the chunk's
+    # union once, so the expert bytes per token fall by P / U (the pages observe
+    # about 2.7x on real text at 32 tokens)
+    if not args.no_chunk:
+        result["prefill"] = {}
+        for name in ("prefill32", "prefill256"):
+            pc = synth.CONFIGS[name]
+            x, lg, bs = synth.activations(pc)
+            xp = torch.from_numpy(x).to(dev).to(torch.bfloat16)  # x holds bf16 values: exact
+            lg_p, bs_p = torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev)
+            idx_p, w_p = lib.route(lg_p, bs_p, pc.K)
+            yp = torch.empty((pc.T, pc.D), dtype=torch.float32, device=dev)
+            nu = torch.zeros(1, dtype=torch.int32, device=dev)
+            wsp = torch.empty(lib.workspace_size(lib.OP_CHUNK, pc.T, pc.K, W), dtype=torch.uint8, device=dev)
+            lib.forward_chunk(W, xp, idx_p, w_p, y=yp, n_unique=nu, ws=wsp)
+            torch.cuda.synchronize()
+            iters = 20 if pc.T <= 32 else 10
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(iters):
+                lib.route(lg_p, bs_p, pc.K, idx=idx_p, w=w_p)
+                lib.forward_chunk(W, xp, idx_p, w_p, y=yp, n_unique=nu, ws=wsp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / iters
+            U, P = int(nu.item()), pc.T * pc.K
+            result["prefill"][name] = {
+                "tokens": pc.T, "ms": round(ms, 4), "us_per_layer_token": round(ms * 1e3 / pc.T, 3),
+                "unique_experts": U, "pairs": P, "dedup": round(P / U, 3),
+                "expert_bytes_per_token": round(U * cfg.expert_bytes() / pc.T),
+                "weight_gbs": round(U * cfg.expert_bytes() / ms / 1e6, 1),
+                "tflops": round(6.0 * pc.D * pc.F * P / ms / 1e9, 2)}
+            log(f"{name}: {ms:.3f} ms ({ms * 1e3 / pc.T:.1f} us/layer-token), union {U} of {P} pairs "
+                f"(dedup {P / U:.2f}x), {U * cfg.expert_bytes() / ms / 1e6:.0f} GB/s of expert weights")
+            del wsp
     del W, ws
     torch.cuda.empty_cache()
 
