@@ -67,6 +67,14 @@ def traffic_bytes():
     return t.get("bytes_per_launch")
 
 
+def tokens_per_expert(lib, idx, E):
+    """Min / median / max of the tokens routed to each expert of the union, from the
+    library's own grouping (k3moe_group)."""
+    counts = lib.group(idx, E)["counts"].cpu().numpy()
+    used = counts[counts > 0]
+    return {"min": int(used.min()), "median": float(np.median(used)), "max": int(used.max())}
+
+
 def capture_steps(torch, fn, n):
     """A HIP graph (torch.cuda.CUDAGraph) of the n calls fn(0) .. fn(n-1), captured
     on a side stream of default priority.  Every call's kernels are replayed with
@@ -450,7 +458,8 @@ def main():
                 "unique_experts": U, "pairs": P, "dedup": round(P / U, 3),
                 "expert_bytes_per_token": round(U * cfg.expert_bytes() / pc.T),
                 "weight_gbs": round(U * cfg.expert_bytes() / ms / 1e6, 1),
-                "tflops": round(6.0 * pc.D * pc.F * P / ms / 1e9, 2)}
+                "tflops": round(6.0 * pc.D * pc.F * P / ms / 1e9, 2),
+                "tokens_per_expert": tokens_per_expert(lib, idx_p, pc.E)}
             log(f"{name}: {ms:.3f} ms ({ms * 1e3 / pc.T:.1f} us/layer-token), union {U} of {P} pairs "
                 f"(dedup {P / U:.2f}x), {U * cfg.expert_bytes() / ms / 1e6:.0f} GB/s of expert weights")
             del wsp
@@ -487,7 +496,8 @@ def main():
                            "ms": round(ms, 4), "us_per_layer_token": round(ms * 1e3 / ccfg.T, 4),
                            "tflops": round(flops / ms / 1e9, 2),
                            "tflops_frac_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
-                           "weight_gbs": round(wbytes / ms / 1e6, 1), "unique_experts": U}
+                           "weight_gbs": round(wbytes / ms / 1e6, 1), "unique_experts": U,
+                           "tokens_per_expert": tokens_per_expert(lib, idx_c, ccfg.E)}
         log(f"chunk: {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s, union {U}")
         del wsc
         torch.cuda.empty_cache()
