@@ -93,6 +93,25 @@ def capture_steps(torch, fn, n):
     return g
 
 
+def timed_steps(torch, fn, n):
+    """Seconds for the n calls fn(0) .. fn(n-1): one HIP graph replay (after an
+    untimed one), or, if capture fails on this machine, the n calls issued eagerly
+    between two synchronizations.  Returns (seconds, mode)."""
+    try:
+        g = capture_steps(torch, fn, n)
+    except RuntimeError as exc:
+        torch.cuda.synchronize()
+        log(f"graph capture failed ({exc}); timing eagerly")
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, "eager"
+    el = timed_replay(torch, g)
+    del g
+    return el, "graph"
+
+
 def timed_replay(torch, g):
     """One untimed replay (the first one uploads the graph), then one timed replay
     between two synchronizations; returns seconds."""
@@ -246,14 +265,12 @@ def main():
 
     # timed region: exactly `steps` steps (token i % 32 at step i), captured as one
     # HIP graph and replayed between two synchronizations after an untimed replay
-    g = capture_steps(torch, lambda i: step(i % n_rot), args.steps)
     y_d.zero_()
-    elapsed = timed_replay(torch, g)
+    elapsed, mode = timed_steps(torch, lambda i: step(i % n_rot), args.steps)
     replay_ok = bool(torch.equal(y_d.view(torch.int32), y_ref.view(torch.int32))) if args.steps >= n_rot else None
-    del g
     ms_per_step = elapsed * 1e3 / args.steps
     value = bytes_per_token * args.steps / elapsed / 1e9
-    log(f"decode: graph replay of {args.steps} steps, outputs equal to the eager ones: {replay_ok}")
+    log(f"decode: {mode} timing of {args.steps} steps, outputs equal to the eager ones: {replay_ok}")
 
     # the gate/up kernel's own duration: eager steps whose gate/up launch records a
     # pair of events at the kernel's start and end (hipExtLaunchKernelGGL; each event
@@ -294,7 +311,8 @@ def main():
                    "tokens_per_step": 1, "experts": cfg.E, "top_k": K, "d_model": cfg.D, "d_ff": cfg.F,
                    "expert_bytes_per_token": bytes_per_token},
         "us_per_layer_token": round(ms_per_step * 1e3, 3),
-        "timing": {"mode": "the K steps captured as one HIP graph, one untimed replay, then one timed replay",
+        "timing": {"mode": ("the K steps captured as one HIP graph, one untimed replay, then one timed replay"
+                            if mode == "graph" else "the K steps issued eagerly (graph capture failed)"),
                    "replay_outputs_equal_eager": replay_ok},
         "roofline": {"bound": "hbm", "kernel": "decode_gateup_kernel (16 experts' gate/up GEMV + SiTU-GLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -319,9 +337,7 @@ def main():
         for i in range(args.warmup):
             step_topp(i % n_rot)
         torch.cuda.synchronize()
-        g = capture_steps(torch, lambda i: step_topp(i % n_rot), args.steps)
-        el = timed_replay(torch, g)
-        del g
+        el, _ = timed_steps(torch, lambda i: step_topp(i % n_rot), args.steps)
         kept_mean = float(np.mean([kept_all[i % n_rot] for i in range(args.steps)]))
         us = el * 1e6 / args.steps
         result["decode_topp"] = {"top_p": top_p, "mean_experts_kept": round(kept_mean, 3), "of": K,
@@ -396,12 +412,11 @@ def main():
             lib.latent_forward(Lw, W, h_l[j:j + 1], idx_l[j:j + 1], w_l[j:j + 1], out=out_l[j:j + 1], ws=ws_l)
         torch.cuda.synchronize()
         n_lat = min(args.steps, 64)
-        g = capture_steps(torch, lambda i: lib.latent_forward(Lw, W, h_l[i % n_rot:i % n_rot + 1],
-                                                              idx_l[i % n_rot:i % n_rot + 1],
-                                                              w_l[i % n_rot:i % n_rot + 1],
-                                                              out=out_l[i % n_rot:i % n_rot + 1], ws=ws_l), n_lat)
-        el_lat = timed_replay(torch, g)
-        del g
+        el_lat, _ = timed_steps(torch, lambda i: lib.latent_forward(Lw, W, h_l[i % n_rot:i % n_rot + 1],
+                                                                    idx_l[i % n_rot:i % n_rot + 1],
+                                                                    w_l[i % n_rot:i % n_rot + 1],
+                                                                    out=out_l[i % n_rot:i % n_rot + 1], ws=ws_l),
+                                n_lat)
         us = el_lat * 1e6 / n_lat
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         T_c = 256
