@@ -224,7 +224,7 @@ inline size_t gemm_lds_bytes(int mt, int nb, int srows, int kdim) {
 
 // A pieces of one loading thread (index lt of NT loading threads): piece
 // c = (lt + i*NT) mod PIECES is tile row c/16, 16-byte segment c%16 of a step; it
-// is stored at LDS slot seg ^ (row % 16) of the row, so the 16 lanes that read
+// is stored at LDS slot seg ^ a_key(row) of the row, so the 16 lanes that read
 // one MFMA fragment (16 rows, same segment) hit 16 different bank groups.
 // Threads past the pieces repeat earlier ones (same bytes to the same place).
 // Rows past the tile re-read its last row; columns past Kdim are clamped on load
@@ -245,7 +245,7 @@ struct APieces {
             const size_t row = (MODE == GATEUP) ? (size_t)(a.perm[row0 + rc] / a.K) : (size_t)(row0 + rc);
             src[i] = a.A + row * (size_t)a.Kdim;
             col[i] = 8 * seg;
-            lds[i] = r * A_ROW + 16 * (seg ^ (r & 15));
+            lds[i] = r * A_ROW + 16 * (seg ^ a_key(r));
         }
     }
     __device__ __forceinline__ void load(uint4 (&v)[SLOTS], int step, int Kdim) const {
@@ -298,6 +298,7 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lg = lane >> 4;
+    const int akey = a_key(ln);  // swizzle key of this lane's fragment row (16 * i + ln)
     const int Kdim = a.Kdim, N = a.N, sb = Kdim >> 5;
     const int n0 = nb0 + wave * WN;
     const int nsteps = (Kdim + KS - 1) / KS;
@@ -348,7 +349,7 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
 #pragma unroll
             for (int i = 0; i < MS; ++i) {
                 const bf16x8 aop =
-                    *reinterpret_cast<const bf16x8*>(abuf + (16 * i + ln) * A_ROW + 16 * ((4 * lg + j) ^ ln));
+                    *reinterpret_cast<const bf16x8*>(abuf + (16 * i + ln) * A_ROW + 16 * ((4 * lg + j) ^ akey));
 #pragma unroll
                 for (int ns = 0; ns < 4; ++ns)
                     acc[i][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[ns], acc[i][ns], 0, 0, 0);

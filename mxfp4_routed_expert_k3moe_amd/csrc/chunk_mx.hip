@@ -106,7 +106,7 @@ struct MxPieces {
             const int rc = min(r, mrows - 1);
             const size_t row = (MODE == MX_GATEUP) ? (size_t)(a.perm[row0 + rc] / a.K) : (size_t)(row0 + rc);
             src[i] = a.aq + pt * a.aq_plane + row * (size_t)a.Kdim + 16 * j;
-            lds[i] = r * A_ROW + 16 * ((pt * 8 + j) ^ (r & 15));
+            lds[i] = r * A_ROW + 16 * ((pt * 8 + j) ^ a_key(r));
         }
         {
             const int c = lt % (MT * PARTS);
@@ -182,6 +182,7 @@ __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lg = lane >> 4;
+    const int akey = a_key(ln);  // swizzle key of this lane's fragment row (16 * i + ln)
     const int Kdim = a.Kdim, N = a.N;
     const int n0 = nb0 + wave * WN;
     const int nsteps = Kdim / KS;
@@ -223,8 +224,8 @@ __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, 
 #pragma unroll
             for (int i = 0; i < MS; ++i) {
                 const uint8_t* arow = abuf + (16 * i + ln) * A_ROW;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + 16 * ((pt * 8 + lg) ^ ln));
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + 16 * ((pt * 8 + 4 + lg) ^ ln));
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + 16 * ((pt * 8 + lg) ^ akey));
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + 16 * ((pt * 8 + 4 + lg) ^ akey));
                 const int sa = sbuf[(pt * MT + 16 * i + ln) * 4 + lg];
                 const v8i aop = a_operand(lo, hi);
 #pragma unroll

@@ -11,13 +11,24 @@ namespace k3moe {
 namespace gemm {
 
 constexpr int KS = 128;       // reduction columns per pipeline step
-constexpr int A_ROW = 256;    // bytes per staged A row and step: 16 pieces of 16 bytes, XOR-swizzled
+constexpr int A_ROW = 256;    // bytes per staged A row and step: 16 pieces of 16 bytes, XOR-swizzled (a_key)
 constexpr int N_XCD = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* glb_ptr_t;
 
 constexpr size_t kLdsLimit = 160 * 1024;
+
+// Swizzle key of staged A row r: a bit permutation of r % 16 (row bits 3,2,1,0 go
+// to key bits 3,0,2,1).  Piece `seg` of row r sits at LDS slot seg ^ a_key(r).
+// One LDS pass of a 16-byte read serves 16 consecutive lanes; the lanes of an MFMA
+// A fragment read 16 rows at one segment, so the key must map those 16 rows to
+// 16 distinct slots that also fall in distinct banks.  Keyed by the row itself,
+// row pairs still share banks (a read rate of about two thirds of a conflict-free
+// one was measured on gfx950); the permuted key reads at the conflict-free rate.
+__device__ __forceinline__ int a_key(int r) {
+    return ((r >> 1) & 3) | ((r & 1) << 2) | (r & 8);
+}
 
 __device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
     return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
