@@ -188,14 +188,16 @@ struct RowStream {
     }
 
     // acc[t] += A(parts) x B(tile t) over all steps; each buffer slot is refilled
-    // with the step PD ahead as soon as it is consumed.
-    __device__ __forceinline__ void run(const uint16_t* lds, f32x4 (&acc)[NT]) {
+    // with the step PD ahead as soon as it is consumed.  A range of columns
+    // [col0, col0 + kdim) of a vector staged with part stride ps: qrow and srow
+    // then point at the range's first column.
+    __device__ __forceinline__ void run(const uint16_t* lds, f32x4 (&acc)[NT], int ps = -1, int col0 = 0) {
         const int lane = threadIdx.x & 63;
         const int ln = lane & 15, lg = lane >> 4;
         const int nsteps = (kdim + 127) >> 7;
-        const int ps = part_stride(kdim);
+        if (ps < 0) ps = part_stride(kdim);
         // A operand: part ln (< 3) at this lane group's columns, or the zero block
-        const uint16_t* abase = (ln < 3) ? lds + ln * ps + 32 * lg : lds + 3 * ps;
+        const uint16_t* abase = (ln < 3) ? lds + ln * ps + col0 + 32 * lg : lds + 3 * ps;
         const int astep = (ln < 3) ? 128 : 0;
         const int jstep = (ln < 3) ? 8 : 0;
         int s0 = 0;
@@ -234,20 +236,30 @@ __host__ __device__ inline size_t decode_lds_bytes(int kdim, int nt) {
     return parts_lds_bytes(kdim) + (size_t)nt * ROWS_PER_BLOCK * (kdim / 32) + 16;
 }
 
-template <bool DS>
-__global__ __launch_bounds__(WAVES * 64) void decode_gateup_kernel(DevWeights W, const float* __restrict__ x,
-                                                            const int32_t* __restrict__ idx,
-                                                            float* __restrict__ h) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    const int k = blockIdx.y;
+// Gate/up with pruned slots: the kept slots' rows are served by twice as many
+// workgroups of 32 rows, each 16-row tile by two waves that reduce one half of
+// the columns each (the second half's sums are added to the first's through
+// LDS).  All slots kept: the 64-row workgroups and their summation order.
+constexpr int SPLIT_ROWS = ROWS_PER_BLOCK / 2;
+constexpr int SPLIT_MERGE_BYTES = 2 * 16 * 8 * 4;  // 2 waves x 16 lanes x 2 tiles x 4 floats
+__host__ __device__ inline bool decode_split_ok(int D) { return D % 256 == 0; }
+
+// Rows of one workgroup for slot k and expert e (full: 64 rows [blk*64, +64), four
+// waves of 16; SPLIT: 32 rows [blk*32, +32), waves w and w+2 on tile w&1, columns
+// [0, D/2) and [D/2, D)).
+template <bool DS, bool SPLIT>
+__device__ __forceinline__ void gateup_block(const DevWeights& W, const float* __restrict__ x, int e, int k, int blk,
+                                             float* __restrict__ h, uint16_t* lds) {
+    constexpr int ROWS = SPLIT ? SPLIT_ROWS : ROWS_PER_BLOCK;
     const int lane = threadIdx.x & 63, ln = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int D = W.D, F = W.F, sb = D >> 5;
-    const int fblk = blockIdx.x * ROWS_PER_BLOCK;
-    const int f0 = fblk + wave * 16;
+    const int fblk = blk * ROWS;
+    const int f0 = fblk + (SPLIT ? (wave & 1) : wave) * 16;
+    const int half = SPLIT ? (wave >> 1) : 0;
+    const int col0 = half * (D / 2);  // first column of this wave's range
     uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(D);
 
-    const int e = idx[k];
     if (e == K3MOE_PRUNED) return;  // block-uniform: a pruned slot reads and writes nothing
     const bool valid_e = e >= 0 && e < W.E;
     const int ec = valid_e ? e : 0;
@@ -255,31 +267,56 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gateup_kernel(DevWeights W,
     // activations and scale rows first: waiting for them later leaves the weights in flight
     Stage<WAVES * 64> st;
     st.load(x, D);
-    ScaleStage<DS, ROWS_PER_BLOCK, WAVES * 64> sg, su;
-    sg.load(W.gate_s + (size_t)ec * W.gate_s_stride, fblk, ROWS_PER_BLOCK, F, sb);
-    su.load(W.up_s + (size_t)ec * W.up_s_stride, fblk, ROWS_PER_BLOCK, F, sb);
+    ScaleStage<DS, ROWS, WAVES * 64> sg, su;
+    sg.load(W.gate_s + (size_t)ec * W.gate_s_stride, fblk, ROWS, F, sb);
+    su.load(W.up_s + (size_t)ec * W.up_s_stride, fblk, ROWS, F, sb);
     // weights: always prefetched (clamped to real rows), so no load sits behind a branch
     const int fc = min(f0, F - 16);
     const size_t qrow = (size_t)D >> 1;
     RowStream<2> rs;
-    rs.kdim = D;
-    rs.qrow[0] = W.gate_q + (size_t)ec * W.gate_q_stride + (size_t)(fc + ln) * qrow;
-    rs.qrow[1] = W.up_q + (size_t)ec * W.up_q_stride + (size_t)(fc + ln) * qrow;
-    rs.srow[0] = slds + (size_t)(fc - fblk + ln) * sb;
-    rs.srow[1] = slds + (size_t)(ROWS_PER_BLOCK + fc - fblk + ln) * sb;
+    rs.kdim = SPLIT ? D / 2 : D;
+    rs.qrow[0] = W.gate_q + (size_t)ec * W.gate_q_stride + (size_t)(fc + ln) * qrow + (col0 >> 1);
+    rs.qrow[1] = W.up_q + (size_t)ec * W.up_q_stride + (size_t)(fc + ln) * qrow + (col0 >> 1);
+    rs.srow[0] = slds + (size_t)(fc - fblk + ln) * sb + (col0 >> 5);
+    rs.srow[1] = slds + (size_t)(ROWS + fc - fblk + ln) * sb + (col0 >> 5);
     rs.prefetch();
     st.store(lds);
     sg.store(slds);
-    su.store(slds + ROWS_PER_BLOCK * sb);
+    su.store(slds + ROWS * sb);
     __syncthreads();
-    if (f0 >= F) return;  // no barrier follows
     float* hk = h + (size_t)k * F;
     if (!valid_e) {
-        if (lane < 16) hk[f0 + lane] = __builtin_nanf("");
-        return;
+        if (f0 < F && lane < 16 && half == 0) hk[f0 + lane] = __builtin_nanf("");
+        return;  // block-uniform
     }
+    if (!SPLIT && f0 >= F) return;  // no barrier follows
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    rs.run(lds, acc);
+    if constexpr (SPLIT) {
+        rs.run(lds, acc, part_stride(D), col0);
+        // the second half's sums to LDS (after the sweep: the merge region follows
+        // the scales), then added to the first half's
+        float* mrg = reinterpret_cast<float*>(slds + 2 * ROWS * sb + 16);
+        if (half == 1 && lane < 16) {
+            float* m = mrg + ((wave & 1) * 16 + lane) * 8;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                m[c] = acc[0][c];
+                m[4 + c] = acc[1][c];
+            }
+        }
+        __syncthreads();
+        if (half == 1 || f0 >= F) return;
+        if (lane < 16) {
+            const float* m = mrg + ((wave & 1) * 16 + lane) * 8;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                acc[0][c] += m[c];
+                acc[1][c] += m[4 + c];
+            }
+        }
+    } else {
+        rs.run(lds, acc);
+    }
     // C layout: lane l, register r -> row 4*(l/16)+r, column l%16; rows 0..2 are the
     // hi/mid/lo sums of column (= weight row) l for lanes 0..15
     if (lane < 16) {
@@ -287,6 +324,37 @@ __global__ __launch_bounds__(WAVES * 64) void decode_gateup_kernel(DevWeights W,
         const float u = (acc[1][0] + acc[1][1]) + acc[1][2];
         hk[f0 + lane] = situ_accurate(g, u);
     }
+}
+
+// One-dimensional grid of 2*K*nblk workgroups (nblk = 64-row blocks of F).  With
+// every slot kept, workgroup g < K*nblk serves slot g / nblk, block g % nblk (the
+// rest exit); with some slot pruned (and D a multiple of 256), g < m*2*nblk serves
+// the (g / (2*nblk))-th of the m kept slots, 32-row block g % (2*nblk).  split >= 0
+// fixes the choice instead (0: 64-row blocks, 1: split when D allows).
+template <bool DS>
+__global__ __launch_bounds__(WAVES * 64) void decode_gateup_kernel(DevWeights W, const float* __restrict__ x,
+                                                            const int32_t* __restrict__ idx, int K, int split,
+                                                            float* __restrict__ h) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int g = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int nblk = (W.F + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    const int kf = min(g / nblk, K - 1);
+    const int ef = idx[kf];  // the full-mode expert, loaded beside the kept mask
+    const uint64_t keptm = __ballot(lane < K && idx[min(lane, K - 1)] != K3MOE_PRUNED);
+    const int m = __popcll(keptm);
+    if ((split < 0 ? m == K : split == 0) || !decode_split_ok(W.D)) {
+        if (g >= K * nblk) return;
+        gateup_block<DS, false>(W, x, ef, kf, g % nblk, h, lds);
+        return;
+    }
+    const int nblk2 = 2 * nblk;
+    if (g >= m * nblk2) return;
+    // slot of the j-th kept entry
+    uint64_t rest = keptm;
+    for (int j = g / nblk2; j > 0; --j) rest &= rest - 1;
+    const int k = __ffsll((long long)rest) - 1;
+    gateup_block<DS, true>(W, x, idx[k], k, g % nblk2, h, lds);
 }
 
 constexpr int DOWN_TILES = 1;  // 16-row tiles of W_down per wave
@@ -390,18 +458,18 @@ DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F) {
 }
 
 hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32_t* idx, int K, float* h,
-                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
-    const dim3 grid((W.F + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, K);
-    const size_t lds = decode_lds_bytes(W.D, 2);
+                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop, int split) {
+    const dim3 grid(2 * K * ((W.F + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK));
+    const size_t lds = decode_lds_bytes(W.D, 2) + SPLIT_MERGE_BYTES;
     // dword scale copies need every scale row and expert block 4-byte aligned
     const bool dw = (W.D % 128 == 0) && W.gate_s_stride % 4 == 0 && W.up_s_stride % 4 == 0 &&
                     (reinterpret_cast<uintptr_t>(W.gate_s) & 3) == 0 && (reinterpret_cast<uintptr_t>(W.up_s) & 3) == 0;
     const auto kernel = dw ? decode_gateup_kernel<true> : decode_gateup_kernel<false>;
     if (ev_start != nullptr && ev_stop != nullptr)
         hipExtLaunchKernelGGL(kernel, grid, dim3(WAVES * 64), (uint32_t)lds, stream, ev_start, ev_stop, 0, W, x, idx,
-                              h);
+                              K, split, h);
     else
-        hipLaunchKernelGGL(kernel, grid, dim3(WAVES * 64), lds, stream, W, x, idx, h);
+        hipLaunchKernelGGL(kernel, grid, dim3(WAVES * 64), lds, stream, W, x, idx, K, split, h);
     return hipGetLastError();
 }
 

@@ -35,9 +35,13 @@ hipError_t launch_decode(const DevWeights& W, const float* x, const int32_t* idx
                          float* y, const DecodeWorkspace& ws, hipStream_t stream, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);
 // With both events given, the kernel is launched through hipExtLaunchKernelGGL,
-// which records ev_start as the kernel starts and ev_stop as it ends.
+// which records ev_start as the kernel starts and ev_stop as it ends.  split: -1
+// serves the kept slots with 32-row split workgroups when idx holds a pruned slot,
+// 0 never, 1 always (a caller that launches a token's slots in parts passes the
+// token's own choice, so every part sums in the token's order).
 hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32_t* idx, int K, float* h,
-                                hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                                hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                                int split = -1);
 hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t* idx, const float* w, int K,
                               float* ypart, float* y, hipStream_t stream);
 

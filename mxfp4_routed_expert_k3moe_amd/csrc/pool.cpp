@@ -214,7 +214,12 @@ int k3moe_forward_decode_pooled(k3moe_pool_t* pool, int32_t layer, const uint8_t
         ++nmiss;
     }
     if ((e = hipEventRecord(pool->copies_done, copy_stream)) != hipSuccess) return status_of(e);
-    // 4. slot ids: all slots, resident ones only, missing ones only (pruned elsewhere)
+    // 4. slot ids: all slots, resident ones only, missing ones only (pruned elsewhere);
+    //    both gate/up parts take the workgroup shape the whole token would take
+    //    (split rows iff the token itself has a pruned slot), so the sums match
+    //    k3moe_forward_decode's bit for bit
+    int split = 0;
+    for (int32_t k = 0; k < K; ++k) split |= experts[k] == K3MOE_PRUNED;
     int32_t* ids = pool->staging + K3MOE_MAX_K;  // [2 * K]: hits-only, misses-only
     for (int32_t k = 0; k < K; ++k) {
         ids[k] = missed[k] ? K3MOE_PRUNED : slots[k];
@@ -243,10 +248,12 @@ int k3moe_forward_decode_pooled(k3moe_pool_t* pool, int32_t layer, const uint8_t
     dw.gate_q_stride = dw.gate_s_stride = dw.up_q_stride = dw.up_s_stride = dw.down_q_stride = dw.down_s_stride =
         Wp.gate_q_stride;
     const k3moe::DecodeWorkspace dws = k3moe::decode_workspace_carve(ws, K, dw.D, dw.F);
-    if (nmiss < K && (e = k3moe::launch_decode_gateup(dw, x, d_hit, K, dws.h, stream)) != hipSuccess)
+    if (nmiss < K &&
+        (e = k3moe::launch_decode_gateup(dw, x, d_hit, K, dws.h, stream, nullptr, nullptr, split)) != hipSuccess)
         return status_of(e);
     if ((e = hipStreamWaitEvent(stream, pool->copies_done, 0)) != hipSuccess) return status_of(e);
-    if (nmiss > 0 && (e = k3moe::launch_decode_gateup(dw, x, d_miss, K, dws.h, stream)) != hipSuccess)
+    if (nmiss > 0 &&
+        (e = k3moe::launch_decode_gateup(dw, x, d_miss, K, dws.h, stream, nullptr, nullptr, split)) != hipSuccess)
         return status_of(e);
     if ((e = k3moe::launch_decode_down(dw, dws.h, d_all, w, K, dws.ypart, y, stream)) != hipSuccess)
         return status_of(e);

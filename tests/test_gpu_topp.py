@@ -98,3 +98,42 @@ def test_chunk_topp():
     assert np.array_equal(g["counts"].cpu().numpy(), go["counts"])
     assert np.array_equal(g["offsets"].cpu().numpy(), go["offsets"])
     assert np.array_equal(g["perm"].cpu().numpy()[:len(go["perm"])], go["perm"])
+
+
+@pytest.mark.parametrize("E,K,D,F", [(896, 16, 3584, 3072), (40, 8, 512, 192), (12, 5, 352, 160)])
+def test_decode_pruned_anywhere(E, K, D, F):
+    """Pruned slots at arbitrary positions (not only the tail): the kept slots are
+    served by the 32-row split workgroups when D is a multiple of 256 (first two
+    shapes), by the 64-row ones otherwise; both within the decode tolerance.  An
+    out-of-range expert beside a pruned slot gives an all-NaN output."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    if D == 3584:
+        cfg = synth.CONFIGS["decode1"]
+    else:
+        cfg = synth.scaled(synth.CONFIGS["tiny"], name=f"prune{E}_{K}_{D}_{F}", E=E, K=K, D=D, F=F,
+                           weight_seed=1100 + E, act_seed=1100 + K)
+    x, logits, bias = synth.activations(cfg, T=1, stream=31)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    W = device_weights(cfg)
+    rng = np.random.default_rng(E + K)
+    for trial in range(3):
+        keep = rng.random(cfg.K) < 0.6
+        keep[rng.integers(cfg.K)] = True  # at least one kept
+        if keep.all():
+            keep[rng.integers(cfg.K)] = False
+        idx_t = np.where(keep, idx[0], -1).astype(np.int32)
+        w_t = np.where(keep, w[0], 0.0).astype(np.float32)
+        log(f"decode pruned {E}x{K} D={D}: kept slots {np.nonzero(keep)[0].tolist()}")
+        y = lib.forward_decode(W, torch.from_numpy(x[0]).cuda(), torch.from_numpy(idx_t).cuda(),
+                               torch.from_numpy(w_t).cuda())
+        torch.cuda.synchronize()
+        want = oracle_forward_subset(cfg, x, idx_t[None], w_t[None])[0]
+        assert_close(y.cpu().numpy(), want, 1e-5, f"decode pruned {E}x{K} D={D} trial {trial}")
+    # an out-of-range expert id in a kept slot, another slot pruned
+    bad = idx[0].copy()
+    bad[0], bad[cfg.K - 1] = cfg.E + 3, -1
+    y = lib.forward_decode(W, torch.from_numpy(x[0]).cuda(), torch.from_numpy(bad).cuda(),
+                           torch.from_numpy(w[0]).cuda())
+    torch.cuda.synchronize()
+    assert np.isnan(y.cpu().numpy()).all()
