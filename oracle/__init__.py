@@ -87,6 +87,8 @@ def _bind(path: str):
                                        + [ctypes.c_int32] * 2 + [_U8P] * 6
                                        + [_F32P, ctypes.c_int32, _I32P, _F32P, ctypes.c_int32, _F32P,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32])
+    lib.k3o_set_progress.restype = None
+    lib.k3o_set_progress.argtypes = [ctypes.c_int32]
     lib.k3o_group.restype = ctypes.c_int
     lib.k3o_group.argtypes = [_I32P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P, _I32P,
                               _I32P, _I32P, ctypes.POINTER(ctypes.c_int32)]
@@ -186,13 +188,14 @@ class Oracle:
 
     # ------------------------------------------------------------------------ forward
     def forward(self, weights: Dict[str, np.ndarray], x: np.ndarray, idx: np.ndarray, w: np.ndarray,
-                nthreads: Optional[int] = None, want_pairs: bool = False, mx: int = 0):
+                nthreads: Optional[int] = None, want_pairs: bool = False, mx: int = 0, progress: int = 0):
         """Routed-expert block on host weights ``{name: [E, rows, cols]}``.
 
         Returns ``y [T, D] f32``; with ``want_pairs`` also ``(ytk [T,K,D], hk [T,K,F])``
         in float64.  ``mx=1`` or ``mx=2`` runs the MXFP8-activation variant in that many
-        parts (``k3o_forward_mx``: x and h quantized per 32 to E4M3 with an E8M0 scale,
-        weight scale byte 255 read as NaN).
+        parts (``k3o_forward_mx``: x and h quantized per 32 to E4M3 with an E8M0 scale;
+        the weights keep the closed form for every scale byte).  ``progress=n`` reports
+        every n-th finished expert on stderr.
         """
         names = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
         arrs = [_c(weights[n], np.uint8) for n in names]
@@ -213,7 +216,11 @@ class Oracle:
         hk = np.empty((T, K, F)) if want_pairs else None
         args = [E, D, F, *arrs, x, T, idx, w, K, y, ytk.ctypes.data if want_pairs else None,
                 hk.ctypes.data if want_pairs else None, int(nthreads or default_threads())]
-        rc = self.lib.k3o_forward_mx(*args, int(mx)) if mx else self.lib.k3o_forward(*args)
+        self.lib.k3o_set_progress(int(progress))
+        try:
+            rc = self.lib.k3o_forward_mx(*args, int(mx)) if mx else self.lib.k3o_forward(*args)
+        finally:
+            self.lib.k3o_set_progress(0)
         if rc != 0:
             raise ValueError("oracle forward failed (expert index out of range or out of memory)")
         return (y, ytk, hk) if want_pairs else y
@@ -339,8 +346,9 @@ def expert(Wg, Wu, Wd, x):
     return instance().expert(Wg, Wu, Wd, x)
 
 
-def forward(weights, x, idx, w, nthreads=None, want_pairs=False, mx=0):
-    return instance().forward(weights, x, idx, w, nthreads=nthreads, want_pairs=want_pairs, mx=mx)
+def forward(weights, x, idx, w, nthreads=None, want_pairs=False, mx=0, progress=0):
+    return instance().forward(weights, x, idx, w, nthreads=nthreads, want_pairs=want_pairs, mx=mx,
+                              progress=progress)
 
 
 def mx_quant(v, parts=1):

@@ -22,6 +22,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -66,12 +67,14 @@ void k3o_decode_table(float *table)
  * per 32 consecutive inputs of a row ([PR684] MXFP4 commit).  out is [O, I] fp32. */
 void k3o_dequant(const uint8_t *q, const uint8_t *s, int64_t O, int64_t I, float *out)
 {
+    float table[16 * 256]; /* every (code, scale) pair, each entry from k3o_decode */
+    k3o_decode_table(table);
     for (int64_t o = 0; o < O; ++o) {
         for (int64_t i = 0; i < I; ++i) {
             uint8_t byte = q[o * (I / 2) + i / 2];
             unsigned code = (i % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4);
             unsigned scale = s[o * (I / 32) + i / 32];
-            out[o * I + i] = k3o_decode(code, scale);
+            out[o * I + i] = table[code * 256 + scale];
         }
     }
 }
@@ -381,17 +384,6 @@ static void mx_roundtrip(const float *v, int64_t n, int32_t parts, double *out)
     free(sc);
 }
 
-/* In the MXFP8 variant the weights are OCP MXFP4: the same e2m1 codes and scale
- * bytes, but scale byte 255 is the E8M0 NaN, so every weight of such a group is
- * NaN (the exact path reads it as 2^128 instead). */
-static void mx_weight_nan(const uint8_t *s, int64_t O, int64_t I, float *W)
-{
-    for (int64_t o = 0; o < O; ++o)
-        for (int64_t b = 0; b < I / 32; ++b)
-            if (s[o * (I / 32) + b] == 255)
-                for (int64_t i = 0; i < 32; ++i) W[o * I + 32 * b + i] = NAN;
-}
-
 /* k3o_expert with MXFP8 activations in `parts` parts: x is quantized as above,
  * g and u are sums over the quantized x, h = SiTU(g, u) is rounded to fp32 and
  * quantized the same way (in groups of 32 consecutive f), and y is the sum over
@@ -415,6 +407,11 @@ void k3o_expert_mx(const float *Wg, const float *Wu, const float *Wd, int32_t D,
 }
 
 /* ----------------------------------------------------------------- block forward */
+
+/* Progress of k3o_forward: every n-th expert finished is reported on stderr (n = 0:
+ * silent), so a long run shows that it advances. */
+static int32_t g_progress = 0;
+void k3o_set_progress(int32_t every) { g_progress = every; }
 
 /* The routed-expert block for T tokens given their routing (idx [T,K], w [T,K]):
  *   y_t = sum_{k=0}^{K-1} w_{t,k} * expert_{idx[t,k]}(x_t)     (double, k order)
@@ -451,6 +448,7 @@ static int forward_impl(int32_t E, int32_t D, int32_t F,
     const int64_t gq_n = (int64_t)F * D / 2, gs_n = (int64_t)F * D / 32;
     const int64_t dq_n = (int64_t)D * F / 2, ds_n = (int64_t)D * F / 32;
     int failed = 0;
+    int32_t done = 0;
 
 #pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
     {
@@ -468,11 +466,6 @@ static int forward_impl(int32_t E, int32_t D, int32_t F,
             k3o_dequant(gq + e * gq_n, gs + e * gs_n, F, D, Wg);
             k3o_dequant(uq + e * gq_n, us + e * gs_n, F, D, Wu);
             k3o_dequant(dq + e * dq_n, ds + e * ds_n, D, F, Wd);
-            if (mx_parts) {
-                mx_weight_nan(gs + e * gs_n, F, D, Wg);
-                mx_weight_nan(us + e * gs_n, F, D, Wu);
-                mx_weight_nan(ds + e * ds_n, D, F, Wd);
-            }
             for (int64_t p = 0; p < P; ++p) {
                 if (idx[p] != e) continue;
                 int64_t t = p / K;
@@ -481,6 +474,15 @@ static int forward_impl(int32_t E, int32_t D, int32_t F,
                 else
                     k3o_expert(Wg, Wu, Wd, D, F, x + t * D, NULL, NULL,
                                hk ? hk + p * F : NULL, yp + p * D);
+            }
+            if (g_progress > 0) {
+                int32_t n;
+#pragma omp atomic capture
+                n = ++done;
+                if (n % g_progress == 0 || n == nu) {
+                    fprintf(stderr, "[oracle] %d / %d experts\n", n, nu);
+                    fflush(stderr);
+                }
             }
         }
         free(Wg);
@@ -513,8 +515,11 @@ int k3o_forward(int32_t E, int32_t D, int32_t F,
     return forward_impl(E, D, F, gq, gs, uq, us, dq, ds, x, T, idx, w, K, y, ytk, hk, nthreads, 0);
 }
 
-/* k3o_forward with MXFP8 activations in `parts` (1 or 2) parts and MXFP4 weights
- * read as OCP MX (k3o_expert_mx for every pair); hk receives the dequantized h. */
+/* k3o_forward with MXFP8 activations in `parts` (1 or 2) parts (k3o_expert_mx for
+ * every pair); the weights are the same closed-form values as in k3o_forward for
+ * every scale byte, 255 included ([PR684] MXFP4-kernel commit: w = v * 2^(s-127),
+ * and the engine's kernels agree on the s = 0 and s = 255 edge cases); hk receives
+ * the dequantized h. */
 int k3o_forward_mx(int32_t E, int32_t D, int32_t F,
                    const uint8_t *gq, const uint8_t *gs, const uint8_t *uq, const uint8_t *us,
                    const uint8_t *dq, const uint8_t *ds,
@@ -576,17 +581,6 @@ double k3o_rmsnorm(const double *a, int32_t n, const float *g, double eps, doubl
     return rms;
 }
 
-/* f rounded to the nearest bf16 value (8 significant bits), ties to even; NaN stays NaN. */
-static float bf16_round(float f)
-{
-    uint32_t u;
-    memcpy(&u, &f, 4);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return f;
-    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
-    memcpy(&f, &u, 4);
-    return f;
-}
-
 /* y[o] = sum_i W[o, i] x[i] for W [O, I] (float values), x double; ascending i. */
 static void dense(const float *W, int32_t O, int32_t I, const double *x, double *y)
 {
@@ -603,9 +597,11 @@ static void dense(const float *W, int32_t O, int32_t I, const double *x, double 
  * experts run in a 3584-dim latent space behind shared down/up projections,
  * plus two fused full-width shared experts).  The pages give no formulas; the
  * plainest reading, per token with hidden state h [Dh]:
- *   x   = bf16(fp32(Wdn h))               latent input of the routed experts, in
- *                                         the bf16 activation format the routed
- *                                         chunk path takes
+ *   x   = fp32(Wdn h)                     latent input of the routed experts: the
+ *                                         projection rounded once to fp32 (the
+ *                                         engine's activations are fp32; the pages
+ *                                         round nothing between the projection
+ *                                         and the experts)
  *   a   = sum_k w_k E_k(x)                the routed aggregate (k3o_forward)
  *   r   = RMSNorm(a) with weight gn, eps  "on the aggregate": in the latent space
  *   y   = Wup r                           back to the full width
@@ -615,7 +611,7 @@ static void dense(const float *W, int32_t O, int32_t I, const double *x, double 
  * Dense weights: Wdn [Dl, Dh], Wup [Dh, Dl], Sg/Su [Fs, Dh], Sd [Dh, Fs] as float
  * (their bf16 values), gn [Dl]; expert weights and routing as in k3o_forward on
  * the latent x.  Sums in double; out [T, Dh] fp32; xl (nullable) receives Wdn h
- * [T, Dl] before the rounding and agg (nullable) a [T, Dl], in double.  Returns 0, or -1 as
+ * [T, Dl] before the fp32 rounding and agg (nullable) a [T, Dl], in double.  Returns 0, or -1 as
  * k3o_forward does. */
 int k3o_latent_forward(int32_t Dh, int32_t Dl, int32_t Fs,
                        const float *Wdn, const float *Wup, const float *gn, double eps,
@@ -642,7 +638,7 @@ int k3o_latent_forward(int32_t Dh, int32_t Dl, int32_t Fs,
         for (int32_t i = 0; i < Dh; ++i) hd[i] = h[(int64_t)t * Dh + i];
         dense(Wdn, Dl, Dh, hd, xd);
         for (int32_t i = 0; i < Dl; ++i) {
-            x32[(int64_t)t * Dl + i] = bf16_round((float)xd[i]);
+            x32[(int64_t)t * Dl + i] = (float)xd[i];
             if (xl) xl[(int64_t)t * Dl + i] = xd[i];
         }
         free(hd);

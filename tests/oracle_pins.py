@@ -674,31 +674,40 @@ def check_forward_mx(o):
             assert np.array_equal(y[t], acc.astype(np.float32)), (parts, t)
 
 
-def check_forward_mx_weight_nan(o):
-    """In the MX variant a weight group with scale byte 255 is NaN (OCP E8M0), where
-    the exact path reads it as 2^128: with all-zero codes in such a down group the
-    exact output is unchanged and the MX output of the pairs using it is NaN."""
+def check_forward_mx_weight_scale_255(o):
+    """The MX variant keeps the weights' closed form at scale byte 255 (w = v * 2^128,
+    colibri PR #684, MXFP4-kernel commit): a down group of zero codes at s = 255 is
+    +-0, so every output equals the one with that group's scale byte set to 127; and
+    codes 1 / 9 (+-0.5) at s = 255 are the weights +-2^127, which codes 2 / 10
+    (+-1.0) at s = 254 also denote, so those two encodings give identical outputs.
+    Both hold for the exact path too."""
     import synth
     cfg = synth.scaled(synth.CONFIGS["tiny"], T=2, E=4, K=2, D=64, F=64)
     W = {k: v.copy() for k, v in synth.weights_host(cfg).items()}
     x, logits, bias = synth.activations(cfg)
     idx, w, _ = o.route(logits, bias, cfg.K)
     e = int(idx[0, 0])
-    y0 = o.forward(W, x, idx, w, nthreads=1)
-    W["down_q"][e, 5, 0:16] = 0
+    W["down_q"][e, 5, 0:16] = 0x80  # codes 0 and 8: +0 and -0
     W["down_s"][e, 5, 0] = 255
     W_ref = {k: v.copy() for k, v in W.items()}
     W_ref["down_s"][e, 5, 0] = 127
-    assert np.array_equal(o.forward(W, x, idx, w, nthreads=1), o.forward(W_ref, x, idx, w, nthreads=1))
-    ym = o.forward(W, x, idx, w, nthreads=1, mx=1)
-    ym_ref = o.forward(W_ref, x, idx, w, nthreads=1, mx=1)
+    # tiny weights beside a 2^127 group would vanish in h; the one-part MX h of
+    # this block is O(1), so down products stay far below the fp32 range
+    W_big = {k: v.copy() for k, v in W.items()}
+    W_big["down_q"][e, 7, 16:32] = np.uint8(0x91)  # codes 1 and 9: +0.5, -0.5
+    W_big["down_s"][e, 7, 1] = 255
+    W_big2 = {k: v.copy() for k, v in W.items()}
+    W_big2["down_q"][e, 7, 16:32] = np.uint8(0xA2)  # codes 2 and 10: +1.0, -1.0
+    W_big2["down_s"][e, 7, 1] = 254
     uses = (idx == e).any(axis=1)
-    for t in range(cfg.T):
-        if uses[t]:
-            assert np.isnan(ym[t, 5]) and np.array_equal(np.delete(ym[t], 5), np.delete(ym_ref[t], 5)), t
-        else:
-            assert np.array_equal(ym[t], ym_ref[t]), t
-    assert np.isfinite(y0).all()
+    assert uses.any()
+    for mx in (0, 1, 2):
+        y = o.forward(W, x, idx, w, nthreads=1, mx=mx)
+        assert np.isfinite(y).all(), mx
+        assert np.array_equal(y, o.forward(W_ref, x, idx, w, nthreads=1, mx=mx)), mx
+        yb = o.forward(W_big, x, idx, w, nthreads=1, mx=mx)
+        assert np.array_equal(yb, o.forward(W_big2, x, idx, w, nthreads=1, mx=mx)), mx
+        assert np.all(np.abs(yb[uses, 7]) > 1e30), mx
 
 
 # ------------------------------------------------------------- P11 LatentMoE wrapper
@@ -714,11 +723,6 @@ def check_rmsnorm(o):
     a = np.random.default_rng(61).standard_normal(100)
     g = (1 + 0.1 * np.random.default_rng(62).standard_normal(100)).astype(np.float32)
     assert np.array_equal(o.rmsnorm(a, g, 0.0), o.rmsnorm(a * 2.0 ** 37, g, 0.0))
-
-
-def synth_bf16(x):
-    import synth
-    return synth.bf16_round(x)
 
 
 def _latent_tiny():
@@ -738,9 +742,9 @@ def _ldense(dense, eps):
 
 def check_latent_composition(o):
     """The block is its stages in order: x = Wdn h (fsum of exact products), the
-    routed aggregate of the oracle's own forward on x rounded to fp32 and then to
-    bf16 (numpy's rounding), RMSNorm on that aggregate, Wup, plus the shared experts
-    as one SiTU-GLU expert of width Fs."""
+    routed aggregate of the oracle's own forward on x rounded once to fp32 (no other
+    rounding between the projection and the experts), RMSNorm on that aggregate,
+    Wup, plus the shared experts as one SiTU-GLU expert of width Fs."""
     lc, cfg, dense, W, h, logits, bias = _latent_tiny()
     idx, w, _ = o.route(logits, bias, cfg.K)
     out, xl, agg = o.latent_forward(_ldense(dense, lc.eps), W, h, idx, w, nthreads=2, want_parts=True)
@@ -749,7 +753,7 @@ def check_latent_composition(o):
         for i in range(0, cfg.D, 37):
             terms = Wdn[i] * h[t].astype(np.float64)
             assert abs(xl[t, i] - math.fsum(terms)) <= 1e-12 * math.fsum(np.abs(terms)), (t, i)
-    y, ytk, _ = o.forward(W, synth_bf16(xl.astype(np.float32)), idx, w, want_pairs=True)
+    y, ytk, _ = o.forward(W, xl.astype(np.float32), idx, w, want_pairs=True)
     want_agg = np.zeros_like(agg)
     for k in range(cfg.K):
         want_agg += w[:, k:k + 1].astype(np.float64) * ytk[:, k]
@@ -786,7 +790,7 @@ ALL_CHECKS = [
     check_forward_pairs, check_forward_combine, check_chunk_equals_tokens, check_group,
     check_route_topp_definition, check_route_topp_off_and_monotone, check_forward_pruned, check_group_pruned,
     check_e4m3_decode, check_mx_quant_exact_values, check_mx_quant_brute, check_mx_quant_special,
-    check_mx_quant_two_parts, check_forward_mx, check_forward_mx_weight_nan,
+    check_mx_quant_two_parts, check_forward_mx, check_forward_mx_weight_scale_255,
     check_rmsnorm, check_latent_composition, check_latent_zero_paths,
 ]
 # check_gate_moments is run separately (it pins the generator, and is the slowest)

@@ -59,7 +59,11 @@ MUTANTS = [
     ("mx zero block scale", "            scales[b] = 0;\n", "            scales[b] = 127;\n"),
     ("mx h kept in fp32", "    mx_roundtrip(hf, F, parts, hd);", "    for (int32_t f = 0; f < F; ++f) hd[f] = hf[f];"),
     ("mx x kept in fp32", "    mx_roundtrip(x, D, parts, xq);", "    for (int32_t i = 0; i < D; ++i) xq[i] = x[i];"),
-    ("mx weights keep scale 255", "            if (mx_parts) {\n                mx_weight_nan(", "            if (0) {\n                mx_weight_nan("),
+    ("mx weights read 255 as NaN", "            k3o_dequant(dq + e * dq_n, ds + e * ds_n, D, F, Wd);\n",
+     "            k3o_dequant(dq + e * dq_n, ds + e * ds_n, D, F, Wd);\n            if (mx_parts)\n"
+     "                for (int64_t z = 0; z < (int64_t)D * F; ++z)\n"
+     "                    if (ds[e * ds_n + z / 32] == 255) Wd[z] = NAN;\n"),
+    ("dequant table transposed", "out[o * I + i] = table[code * 256 + scale];", "out[o * I + i] = table[(scale & 15u) * 256 + (scale >> 4) * 16 + code];"),
     ("mx second part dropped", "        if (parts > 1) out[i] += mx_value(", "        if (0) out[i] += mx_value("),
     ("mx residual of the input", "    for (int64_t i = 0; i < n; ++i) r[i] = v[i] - mx_value(codes[i], scales[i / 32]);",
      "    for (int64_t i = 0; i < n; ++i) r[i] = v[i];"),
@@ -68,7 +72,10 @@ MUTANTS = [
     ("shared experts dropped", "(float)(y[i] + s[i]);", "(float)(y[i]);"),
     ("dense projection transposed", "acc += (double)W[(int64_t)o * I + i] * x[i];", "acc += (double)W[(int64_t)i * O + o] * x[i];"),
     ("aggregate ignores routing weights", "acc += (double)w[(int64_t)t * K + k] * ytk[", "acc += ytk["),
-    ("latent x kept in fp32", "x32[(int64_t)t * Dl + i] = bf16_round((float)xd[i]);", "x32[(int64_t)t * Dl + i] = (float)xd[i];"),
+    ("latent x rounded to bf16", "x32[(int64_t)t * Dl + i] = (float)xd[i];",
+     "float xf = (float)xd[i];\n            uint32_t xu;\n            memcpy(&xu, &xf, 4);\n"
+     "            xu = (xu + 0x7FFFu + ((xu >> 16) & 1u)) & 0xFFFF0000u;\n            memcpy(&xf, &xu, 4);\n"
+     "            x32[(int64_t)t * Dl + i] = xf;"),
     ("offsets inclusive", "offsets[e + 1] = offsets[e] + counts[e];", "offsets[e + 1] = offsets[e] + counts[e] + (e == 0);"),
 ]
 
