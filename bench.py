@@ -20,6 +20,7 @@ import argparse
 import json
 import os
 import sys
+import statistics
 import time
 
 import numpy as np
@@ -186,6 +187,63 @@ def summarize_counters(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+def achievable_peaks(torch, lib, dev):
+    """Rates the library's probe kernels reach on this GPU, beside the published
+    peaks: a streaming read of a 2 GiB buffer (best over loads in flight per thread
+    and plain or non-temporal loads), the same over 281 MB (one decode token's
+    expert bytes, so ramp-up and drain count as they do for the decode kernels),
+    and MFMA issue loops (bf16 16x16x32; scaled 16x16x128 FP8 x FP4, FP4 x FP4)."""
+    stream = torch.cuda.current_stream()
+    out = {}
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(8192, dtype=torch.int32, device=dev)
+
+    def rate(nbytes, unroll, nt, blocks, reps):
+        view = buf[:nbytes]
+        lib.probe_stream_read(view, unroll, nt, blocks, sink=sink)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            lib.probe_stream_read(view, unroll, nt, blocks, sink=sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return nbytes / (statistics.median(ts) * 1e-3) / 1e9
+
+    best = (0.0, None)
+    for unroll in (4, 8, 16):
+        for nt in (False, True):
+            for blocks in (2048, 4096, 8192):
+                g = rate(2 << 30, unroll, nt, blocks, 5)
+                if g > best[0]:
+                    best = (g, {"unroll": unroll, "nontemporal": nt, "blocks": blocks})
+    out["hbm_read_gbs"] = round(best[0], 1)
+    out["hbm_read_config"] = best[1]
+    small = 280756224 // 16 * 16
+    out["hbm_read_281MB_gbs"] = round(max(rate(small, best[1]["unroll"], best[1]["nontemporal"], b, 20)
+                                          for b in (1024, 2048, 4096)), 1)
+    del buf
+    flops = {0: 16384, 1: 65536, 2: 65536, 4: 32768, 5: 131072, 6: 131072}
+    names = {0: "bf16_16x16x32", 1: "fp8_fp4_16x16x128", 2: "fp4_fp4_16x16x128", 4: "bf16_32x32x16",
+             5: "fp4_fp4_32x32x64", 6: "fp8_fp4_32x32x64"}
+    blocks, iters = 2048, 2000
+    o = torch.empty(4 * blocks, dtype=torch.float32, device=dev)
+    for kind in (0, 4, 1, 6, 2, 5):
+        lib.probe_mfma(kind, 10, blocks, out=o)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        lib.probe_mfma(kind, iters, blocks, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        out[f"mfma_{names[kind]}_tflops"] = round(blocks * 4 * iters * 8 * flops[kind] / (ms * 1e-3) / 1e12, 1)
+    log(f"achievable: read {out['hbm_read_gbs']:.0f} GB/s ({best[1]}), 281 MB {out['hbm_read_281MB_gbs']:.0f} GB/s; "
+        "MFMA TFLOP/s " + ", ".join(f"{k[5:-7]} {v:.0f}" for k, v in out.items() if k.startswith("mfma_")))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,6 +282,7 @@ def main():
     if args.counters_probe:
         counters_probe(torch, synth, lib, dev)
         return
+    peaks = achievable_peaks(torch, lib, dev)
 
     # ------------------------------------------------------------- decode workload
     cfg = synth.CONFIGS["decode1"]
@@ -317,7 +376,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_gateup_kernel (16 experts' gate/up GEMV + SiTU-GLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(),
-                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_us, 3)},
+                     "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_us, 3),
+                     "frac_of_achievable_read": round(achieved / peaks["hbm_read_gbs"], 4)},
+        "achievable_peaks": peaks,
     }
 
     # top-p pruning (colibri PR #676, K3_TOPP paragraph) on the same tokens: the
@@ -450,7 +511,9 @@ def main():
         for name in ("prefill32", "prefill256"):
             pc = synth.CONFIGS[name]
             x, lg, bs = synth.activations(pc)
-            xp = torch.from_numpy(x).to(dev).to(torch.bfloat16)  # x holds bf16 values: exact
+            xp = torch.from_numpy(x).to(dev)
+            if pc.x_bf16:  # the 256-token workload's bf16 activations (x holds bf16 values: exact)
+                xp = xp.to(torch.bfloat16)
             lg_p, bs_p = torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev)
             idx_p, w_p = lib.route(lg_p, bs_p, pc.K)
             yp = torch.empty((pc.T, pc.D), dtype=torch.float32, device=dev)
@@ -487,7 +550,7 @@ def main():
         log(f"generating {ccfg.name} weights")
         Wc = lib.ExpertWeights.from_dict(synth.weights_device(ccfg, dev))
         x, lg, bs = synth.activations(ccfg)
-        xc = torch.from_numpy(x).to(dev).to(torch.bfloat16)  # x holds bf16 values: exact
+        xc = torch.from_numpy(x).to(dev)  # fp32 hidden states
         lg_c, bs_c = torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev)
         idx_c, w_c = lib.route(lg_c, bs_c, ccfg.K)
         yc = torch.empty((ccfg.T, ccfg.D), dtype=torch.float32, device=dev)
@@ -506,8 +569,9 @@ def main():
         U = int(nu.item())
         flops = 6.0 * ccfg.D * ccfg.F * ccfg.T * ccfg.K
         wbytes = U * ccfg.expert_bytes()
-        result["chunk"] = {"workload": "batch4096: 4096 tokens, i.i.d. hidden states, logits = h.R, same shape, "
-                                       "bf16 MFMA grouped GEMM (route + group + gate/up + down + combine)",
+        result["chunk"] = {"workload": "batch4096: 4096 tokens, i.i.d. fp32 hidden states, logits = h.R, same "
+                                       "shape, bf16 MFMA grouped GEMM with the MXFP4 low part of x (route + group "
+                                       "+ split + gate/up + down + combine)",
                            "ms": round(ms, 4), "us_per_layer_token": round(ms * 1e3 / ccfg.T, 4),
                            "tflops": round(flops / ms / 1e9, 2),
                            "tflops_frac_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
@@ -520,7 +584,7 @@ def main():
         wsm = torch.empty(lib.workspace_size(lib.OP_CHUNK_MX, ccfg.T, ccfg.K, Wc), dtype=torch.uint8, device=dev)
         result["chunk_mx"] = {"workload": "batch4096 as above, MXFP8 activations (E4M3 + E8M0 per 32) in one or "
                                           "two parts, scaled FP8 x FP4 MFMA (route + group + quantize + gate/up + "
-                                          "down + combine); weight groups with scale byte 255 read as NaN"}
+                                          "down + combine)"}
         for parts in (1, 2):
             lib.forward_chunk_mx(Wc, xc, idx_c, w_c, parts, y=yc, n_unique=nu, ws=wsm)
             torch.cuda.synchronize()

@@ -195,21 +195,35 @@ int k3moe_decode_down(const k3moe_weights_t *W, const float *h, const int32_t *i
 
 /*
  * A chunk of T tokens through the routed experts (steps 2-5) with the chunk's
- * expert union deduplicated: the pairs are grouped by expert (k3moe_group), each
- * routed expert's weights are streamed once per group of up to 96 of its
- * tokens, and gate/up and down run as bf16 MFMA matrix products with fp32
- * accumulation.  The activations x are bf16; the decoded weights are exact in
- * bf16; h is rounded to bf16 (round-to-nearest-even) between the two products.
- * The combine sums w_{t,k} * y_{t,k} in slot order in fp32.
- * x [T, D] bf16 (raw 16-bit patterns), idx [T, K] int32 (K3MOE_PRUNED slots
- * skipped), w [T, K] fp32, y [T, D] fp32; n_unique (device int32, nullable)
- * receives the union size, or
- * -1 for invalid routing, in which case every element of y is NaN.
+ * expert union deduplicated (colibri PR #676, chunked-prefill paragraph: each
+ * unique expert of a chunk is loaded once and run for every position routed to
+ * it): the pairs are grouped by expert (k3moe_group), each routed expert's
+ * weights are streamed once per group of up to 96 of its tokens, and gate/up and
+ * down run as bf16 MFMA matrix products with fp32 accumulation.  The decoded
+ * weights are exact in bf16.  x [T, D] is fp32: it is split exactly into
+ * hi = bf16(x) and lo = x - hi; hi enters the bf16 product, lo (below 2^-9 |x|)
+ * a second product in MXFP4 (e2m1 codes, one power-of-two scale per 32 columns)
+ * against the weights' own FP4 codes, summed into the same fp32 accumulators.
+ * h is rounded to bf16 (round to nearest even) between the two products.  The
+ * combine sums w_{t,k} * y_{t,k} in slot order in fp32.  The result is within
+ * about 2e-3 (relative L2) of the exact block at the K3 shape.
+ * x [T, D] fp32 (16-byte aligned), idx [T, K] int32 (K3MOE_PRUNED slots skipped),
+ * w [T, K] fp32, y [T, D] fp32; n_unique (device int32, nullable) receives the
+ * union size, or -1 for invalid routing, in which case every element of y is NaN.
  * ws: k3moe_workspace_size(K3MOE_OP_CHUNK, T, K, W) bytes.
  */
-int k3moe_forward_chunk(const k3moe_weights_t *W, const uint16_t *x, int32_t T, const int32_t *idx,
+int k3moe_forward_chunk(const k3moe_weights_t *W, const float *x, int32_t T, const int32_t *idx,
                         const float *w, int32_t K, float *y, int32_t *n_unique, void *ws,
                         size_t ws_bytes, void *stream);
+
+/*
+ * k3moe_forward_chunk for activations that are already bf16 (raw 16-bit
+ * patterns, [T, D], 16-byte aligned): the same path without the low part.  Same
+ * arguments, workspace (K3MOE_OP_CHUNK), outputs and errors.
+ */
+int k3moe_forward_chunk_bf16(const k3moe_weights_t *W, const uint16_t *x, int32_t T, const int32_t *idx,
+                             const float *w, int32_t K, float *y, int32_t *n_unique, void *ws,
+                             size_t ws_bytes, void *stream);
 
 /*
  * The chunk path with MXFP8 activations (the GPU form of the pages' per-32
@@ -218,13 +232,13 @@ int k3moe_forward_chunk(const k3moe_weights_t *W, const uint16_t *x, int32_t T, 
  * E8M0 scale byte per group; see k3moe_mx_quant) in `parts` parts (1, or 2 where
  * the second part quantizes the first's fp32 residual), and the products run on
  * the scaled FP8 x FP4 MFMA with the MXFP4 weights as stored, fp32 accumulation.
- * In this path a weight scale byte of 255 is the E8M0 NaN (OCP MX), so every
- * output that reads such a group is NaN; the other entry points read it as
- * 2^128.  Arguments, outputs and the combine as in k3moe_forward_chunk, plus
- * parts.  Requires d_model and d_ff multiples of 128.
+ * The weights keep the closed form for every scale byte, 255 included (2^128;
+ * colibri PR #684, MXFP4-kernel commit).  x [T, D] fp32; arguments, outputs and
+ * the combine as in k3moe_forward_chunk, plus parts.  Requires d_model and d_ff
+ * multiples of 128.
  * ws: k3moe_workspace_size(K3MOE_OP_CHUNK_MX, T, K, W) bytes (for either parts).
  */
-int k3moe_forward_chunk_mx(const k3moe_weights_t *W, const uint16_t *x, int32_t T, const int32_t *idx,
+int k3moe_forward_chunk_mx(const k3moe_weights_t *W, const float *x, int32_t T, const int32_t *idx,
                            const float *w, int32_t K, int32_t parts, float *y, int32_t *n_unique, void *ws,
                            size_t ws_bytes, void *stream);
 
@@ -252,10 +266,11 @@ typedef struct k3moe_latent {
  *   entry points, e.g. from k3moe_route on the router's logits);
  *   out = w_up RMSNorm(a) + shared_down SiTU-GLU(shared_gate h, shared_up h)
  * with RMSNorm(a) = norm * a / sqrt(mean(a^2) + eps).  out [T, d_hidden] fp32.
- * x is rounded to bf16 (the chunk path's activation format) and the routed
- * block is k3moe_forward_decode's path for T = 1 and k3moe_forward_chunk's
- * otherwise; RMSNorm and SiTU-GLU outputs are bf16; the dense products run as
- * bf16 GEMMs with fp32 accumulation (rocBLAS).
+ * x stays fp32 (the projection's fp32 accumulation) and the routed block is
+ * k3moe_forward_decode's path for T = 1 and k3moe_forward_chunk's (fp32 x)
+ * otherwise; RMSNorm and SiTU-GLU outputs are bf16; the dense products are bf16
+ * x bf16 with fp32 accumulation (this library's GEMV kernels for T = 1, rocBLAS
+ * GEMMs otherwise).
  * Requires d_hidden and d_shared multiples of 32 in [32, K3MOE_MAX_DIM], eps >= 0,
  * every pointer 16-byte aligned.  ws: k3moe_latent_workspace_size() bytes.  The
  * first call on a device creates that device's rocBLAS handle (rocBLAS allocates
@@ -343,6 +358,24 @@ size_t k3moe_workspace_size(int32_t op, int32_t T, int32_t K, const k3moe_weight
  */
 int k3moe_dequant_mxfp4(const uint8_t *q, const uint8_t *s, int32_t O, int32_t I, void *out,
                         int32_t out_dtype, void *stream);
+
+/*
+ * Measurement probes (not part of the block; the benchmark reports their rates as
+ * the achievable peaks beside MI355X's published ones).
+ * k3moe_probe_stream_read: reads `bytes` (a multiple of 16, buf 16-byte aligned)
+ *   with `blocks` workgroups of 256 threads, each thread keeping `unroll` (4, 8
+ *   or 16) 16-byte loads in flight, as ordinary or (nontemporal != 0)
+ *   non-temporal loads; writes one dword per workgroup to sink[blocks] (device).
+ * k3moe_probe_mfma: `blocks` workgroups of four waves, each issuing `iters`
+ *   rounds of eight independent MFMAs of one kind (0: v_mfma_f32_16x16x32_bf16,
+ *   16384 flops each; 1: v_mfma_scale_f32_16x16x128_f8f6f4 with FP8 E4M3 x FP4,
+ *   2: FP4 x FP4, 3: FP8 x FP8, 65536 flops each; 4: v_mfma_f32_32x32x16_bf16,
+ *   32768 flops; 5: v_mfma_scale_f32_32x32x64_f8f6f4 FP4 x FP4, 6: FP8 x FP4,
+ *   131072 flops each); writes one float per wave to out[4 * blocks] (device).
+ */
+int k3moe_probe_stream_read(const void *buf, size_t bytes, int32_t unroll, int32_t nontemporal, int32_t blocks,
+                            uint32_t *sink, void *stream);
+int k3moe_probe_mfma(int32_t kind, int32_t iters, int32_t blocks, float *out, void *stream);
 
 /* Text for a status code (static storage; for K3MOE_E_HIP it includes the HIP
  * runtime's message for the calling thread's last failure). */

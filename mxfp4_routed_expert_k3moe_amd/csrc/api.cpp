@@ -200,9 +200,10 @@ int k3moe_decode_down(const k3moe_weights_t* W, const float* h, const int32_t* i
     return finish(k3moe::launch_decode_down(dw, h, idx, w, K, dws.ypart, y, static_cast<hipStream_t>(stream)));
 }
 
-int k3moe_forward_chunk(const k3moe_weights_t* W, const uint16_t* x, int32_t T, const int32_t* idx,
-                        const float* w, int32_t K, float* y, int32_t* n_unique, void* ws, size_t ws_bytes,
-                        void* stream) {
+static int forward_chunk_any(const k3moe_weights_t* W, const float* x32, const uint16_t* xb16, int32_t T,
+                             const int32_t* idx, const float* w, int32_t K, float* y, int32_t* n_unique, void* ws,
+                             size_t ws_bytes, void* stream) {
+    const void* x = x32 ? static_cast<const void*>(x32) : static_cast<const void*>(xb16);
     int rc = check_weights(W);
     if (rc != K3MOE_OK) return rc;
     if (!x || !idx || !w || !y || !ws) return K3MOE_E_NULL;
@@ -215,10 +216,24 @@ int k3moe_forward_chunk(const k3moe_weights_t* W, const uint16_t* x, int32_t T, 
     if (rc != K3MOE_OK) return rc;
     const DevWeights dw = dev_weights(W);
     const k3moe::ChunkWorkspace cws = k3moe::chunk_workspace_carve(ws, T, K, dw.E, dw.D, dw.F);
-    return finish(k3moe::launch_chunk(dw, x, T, idx, w, K, y, n_unique, cws, static_cast<hipStream_t>(stream)));
+    return finish(
+        k3moe::launch_chunk(dw, x32, xb16, T, idx, w, K, y, n_unique, cws, static_cast<hipStream_t>(stream)));
 }
 
-int k3moe_forward_chunk_mx(const k3moe_weights_t* W, const uint16_t* x, int32_t T, const int32_t* idx,
+int k3moe_forward_chunk(const k3moe_weights_t* W, const float* x, int32_t T, const int32_t* idx, const float* w,
+                        int32_t K, float* y, int32_t* n_unique, void* ws, size_t ws_bytes, void* stream) {
+    if (!x) return K3MOE_E_NULL;
+    return forward_chunk_any(W, x, nullptr, T, idx, w, K, y, n_unique, ws, ws_bytes, stream);
+}
+
+int k3moe_forward_chunk_bf16(const k3moe_weights_t* W, const uint16_t* x, int32_t T, const int32_t* idx,
+                             const float* w, int32_t K, float* y, int32_t* n_unique, void* ws, size_t ws_bytes,
+                             void* stream) {
+    if (!x) return K3MOE_E_NULL;
+    return forward_chunk_any(W, nullptr, x, T, idx, w, K, y, n_unique, ws, ws_bytes, stream);
+}
+
+int k3moe_forward_chunk_mx(const k3moe_weights_t* W, const float* x, int32_t T, const int32_t* idx,
                            const float* w, int32_t K, int32_t parts, float* y, int32_t* n_unique, void* ws,
                            size_t ws_bytes, void* stream) {
     int rc = check_weights(W);

@@ -7,13 +7,15 @@
 // weight operand is each routed expert's MXFP4 bytes, streamed once per tile of
 // up to 96 of its pairs (16 when the chunk is small).
 //
-// Kernels, in stream order (x arrives as bf16):
+// Kernels, in stream order (x arrives as fp32, or as bf16 through the bf16 entry):
 //   group_count    per 64-token block: one 64-bit mask per expert (bit i = token
 //                  t0+i chose it); popcounts are the block's per-expert counts
 //   group_scan     one workgroup: per-expert totals, offsets, the union list,
 //                  and the GEMM tile list (expert, first row, rows)
 //   group_scatter  pair p = t*K+k goes to offsets[e] + (pairs of e in earlier
 //                  blocks) + popcount(mask & bits below t): a stable counting sort
+//   xsplit         (fp32 x) x = hi + lo: hi = bf16(x), and the exact residual lo
+//                  as MXFP4 codes with one E8M0 scale per 32 (see below)
 //   gemm<GATEUP>   h = SiTU(x W_gate^T, x W_up^T) per tile, bf16 MFMA, h in bf16
 //   gemm<DOWN>     y_pair = w_pair * (h W_down^T), fp32, at row p = t*K+k
 //   combine        y_t = sum_k y_pair[t*K+k] in slot order
@@ -33,6 +35,20 @@
 //   workgroup's weight rows are staged in LDS once.  Workgroup ids are remapped
 //   so each XCD walks a contiguous run of (tile, column block) items: the column
 //   blocks of one tile share that XCD's L2 copy of the tile's activations.
+//
+// fp32 activations.  Rounding x to bf16 alone would move the block's output by
+// about 7e-3 (rel-L2) on the K3-shape weights: where g = W_gate x sits in the
+// SiTU-GLU's transition region, an error of 2^-9 |x| in every input shifts h by a
+// large share of its range.  So x is split exactly, x = hi + lo with hi = bf16(x),
+// and lo (|lo| <= 2^-9 |x|) enters as a second product: its codes are MXFP4 (e2m1
+// with one E8M0 scale per 32 columns, chosen so the block's largest |lo| is at
+// most 6 * 2^e, rounded to nearest even), multiplied with the weights' own FP4
+// codes and scales by v_mfma_scale_f32_16x16x128_f8f6f4 into the same
+// accumulators -- one MFMA per 128 columns against four bf16 MFMAs for hi.  The
+// residual's own rounding is below 2^-11 of its block's largest value, i.e. about
+// 2^-20 of x: the block output then sits about 1.5e-3 from the exact one, most of
+// it the bf16 rounding of h.  The weights' scale byte 255 (which the scaled MFMA
+// would read as NaN) is passed as 254 and the group's product added twice.
 #include <type_traits>
 
 #include "device.hpp"
@@ -189,6 +205,8 @@ enum { GATEUP = 0, DOWN = 1 };
 
 struct GemmArgs {
     const uint16_t* A;      // GATEUP: x bf16 [T, Kdim] by token; DOWN: h bf16 [P, Kdim] by grouped row
+    const uint8_t* alo;     // GATEUP with a low part: x - bf16(x) as FP4 codes [T, nsteps * 64]
+    const uint8_t* alos;    //   and their E8M0 scales [T, nsteps * 4] (rows padded with zero codes)
     const int32_t* perm;    // grouped row -> pair id
     int K;                  // slots per token
     const uint8_t *q0, *s0, *q1, *s1;  // GATEUP: gate, up; DOWN: down (q1/s1 unused)
@@ -214,9 +232,13 @@ struct GemmShape {
 };
 
 
-// A buffers, the row table, and the scale rows rounded up to whole 1 KiB copies.
-inline size_t gemm_lds_bytes(int mt, int nb, int srows, int kdim) {
-    return (size_t)nb * mt * A_ROW + (size_t)mt * 8 + (((size_t)srows * (kdim / 32) + 1023) & ~(size_t)1023);
+constexpr int LO_ROW = 64;  // bytes per staged low-part row and step: 128 FP4 codes
+
+// A buffers, the row table, the low-part buffers and their per-step scale tables
+// (with a low part), and the scale rows rounded up to whole 1 KiB copies.
+inline size_t gemm_lds_bytes(int mt, int nb, int srows, int kdim, bool lo = false) {
+    return (size_t)nb * mt * A_ROW + (size_t)mt * 8 + (lo ? (size_t)nb * mt * (LO_ROW + 4) : 0) +
+           (((size_t)srows * (kdim / 32) + 1023) & ~(size_t)1023);
 }
 
 
@@ -228,55 +250,118 @@ inline size_t gemm_lds_bytes(int mt, int nb, int srows, int kdim) {
 // one MFMA fragment (16 rows, same segment) hit 16 different bank groups.
 // Threads past the pieces repeat earlier ones (same bytes to the same place).
 // Rows past the tile re-read its last row; columns past Kdim are clamped on load
-// and stored as zeros.
+// and stored as zeros.  NT is a multiple of 256, so a thread's segment and the
+// row bits its swizzle key reads are the same for every i: per piece only the
+// row's byte offset in A is kept (32 bits, added to the uniform base).
 template <int MODE, int MT, int NT>
 struct APieces {
+    static_assert(NT % 256 == 0, "segment and key invariant over a thread's pieces");
     static constexpr int PIECES = MT * 16;
     static constexpr int SLOTS = (PIECES + NT - 1) / NT;
-    const uint16_t* src[SLOTS];  // row start
-    int col[SLOTS];              // element offset of the piece within a step
-    int lds[SLOTS];              // byte offset in one LDS buffer
+    uint32_t roff[SLOTS];  // byte offset of the piece's row in A
+    int seg, key;          // the thread's segment, the key of its rows
+    __device__ __forceinline__ static int row_of(int i) { return (((int)threadIdx.x + i * NT) % PIECES) >> 4; }
     __device__ __forceinline__ void init(const GemmArgs& a, int lt, int row0, int mrows) {
+        seg = lt & 15;
+        key = a_key(row_of(0));
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
-            const int c = (lt + i * NT) % PIECES;
-            const int r = c >> 4, seg = c & 15;
-            const int rc = min(r, mrows - 1);
-            const size_t row = (MODE == GATEUP) ? (size_t)(a.perm[row0 + rc] / a.K) : (size_t)(row0 + rc);
-            src[i] = a.A + row * (size_t)a.Kdim;
-            col[i] = 8 * seg;
-            lds[i] = r * A_ROW + 16 * (seg ^ a_key(r));
+            const int rc = min(row_of(i), mrows - 1);
+            const uint32_t row = (MODE == GATEUP) ? (uint32_t)(a.perm[row0 + rc] / a.K) : (uint32_t)(row0 + rc);
+            roff[i] = row * (uint32_t)a.Kdim * 2u;
         }
     }
-    __device__ __forceinline__ void load(uint4 (&v)[SLOTS], int step, int Kdim) const {
+    __device__ __forceinline__ void load(const GemmArgs& a, uint4 (&v)[SLOTS], int step, int Kdim) const {
+        const uint32_t c = 2u * (uint32_t)min(step * KS + 8 * seg, Kdim - 8);
+        const char* base = reinterpret_cast<const char*>(a.A);
 #pragma unroll
-        for (int i = 0; i < SLOTS; ++i)
-            v[i] = *reinterpret_cast<const uint4*>(src[i] + min(step * KS + col[i], Kdim - 8));
+        for (int i = 0; i < SLOTS; ++i) v[i] = *reinterpret_cast<const uint4*>(base + (roff[i] + c));
     }
     __device__ __forceinline__ void store(const uint4 (&v)[SLOTS], uint8_t* buf, int step, int Kdim) const {
+        // mask word by word: a select between two uint4 objects would keep the
+        // register arrays in memory
+        const uint32_t m = step * KS + 8 * seg < Kdim ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int i = 0; i < SLOTS; ++i) {
-            // mask word by word: a select between two uint4 objects would keep the
-            // register arrays in memory
-            const uint32_t m = step * KS + col[i] < Kdim ? 0xFFFFFFFFu : 0u;
-            *reinterpret_cast<uint4*>(buf + lds[i]) = make_uint4(v[i].x & m, v[i].y & m, v[i].z & m, v[i].w & m);
-        }
+        for (int i = 0; i < SLOTS; ++i)
+            *reinterpret_cast<uint4*>(buf + row_of(i) * A_ROW + 16 * (seg ^ key)) =
+                make_uint4(v[i].x & m, v[i].y & m, v[i].z & m, v[i].w & m);
     }
 };
 
 
+// Low-part pieces of one loading thread (index lt of NT): piece c = (lt + i*NT) mod
+// PIECES is tile row c/4, 16-byte segment c%4 (32 codes = one scale group) of a
+// step, stored at slot seg ^ ((row >> 2) & 3) of the row's 64 LDS bytes, so the 16
+// lanes reading one fragment (16 rows, one segment) hit 16 distinct 16-byte slots
+// of a 256-byte bank row.  Thread lt also carries the step's scale dword (four
+// groups) of row lt % MT.  The low-part rows are padded to whole steps with zero
+// codes, so no load is clamped or masked.
+template <int MT, int NT>
+struct LoPieces {
+    static_assert(NT % 64 == 0, "segment and key invariant over a thread's pieces");
+    static constexpr int PIECES = MT * 4;
+    static constexpr int SLOTS = (PIECES + NT - 1) / NT;
+    uint32_t roff[SLOTS];  // byte offset of the piece's row in the codes (plus its segment)
+    uint32_t soff;         // byte offset of row lt % MT in the scales
+    __device__ __forceinline__ static int row_of(int i) { return (((int)threadIdx.x + i * NT) % PIECES) >> 2; }
+    __device__ __forceinline__ void init(const GemmArgs& a, int row0, int mrows, int nsteps) {
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i)
+            roff[i] = (uint32_t)(a.perm[row0 + min(row_of(i), mrows - 1)] / a.K) * (uint32_t)(nsteps * LO_ROW) +
+                      16u * (threadIdx.x & 3);
+        const int r = (int)threadIdx.x % MT;
+        soff = (uint32_t)(a.perm[row0 + min(r, mrows - 1)] / a.K) * (uint32_t)(nsteps * 4);
+    }
+    __device__ __forceinline__ void load(const GemmArgs& a, u32x4 (&v)[SLOTS], uint32_t& sv, int step) const {
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i)
+            v[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.alo) + (roff[i] + step * LO_ROW));
+        sv = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(a.alos) + (soff + 4 * step));
+    }
+    __device__ __forceinline__ void store(const u32x4 (&v)[SLOTS], uint32_t sv, uint8_t* buf, uint8_t* sbuf) const {
+        const int seg = threadIdx.x & 3;
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int r = row_of(i);
+            *reinterpret_cast<u32x4*>(buf + r * LO_ROW + 16 * (seg ^ ((r >> 2) & 3))) = v[i];
+        }
+        *reinterpret_cast<uint32_t*>(sbuf + 4 * ((int)threadIdx.x % MT)) = sv;
+    }
+};
+
 // Per-lane state of one work item that outlives the prologue: the activation
-// pieces this thread stages, the weight rows this lane streams, and both rings.
-template <int MODE, int MT, int CW, int NBB>
+// pieces this thread stages (and with a low part, its pieces), the weight rows this
+// lane streams, and the rings.
+template <int MODE, int MT, int CW, int NBB, bool LO>
 struct GemmState {
     using AP = APieces<MODE, MT, CW * 64>;
+    using LP = LoPieces<MT, CW * 64>;
     static_assert(NBB >= 2 && NBB <= 4, "weight ring depth");
+    // activation register sets: two (loads two steps ahead) for bf16 x; one (loads
+    // one step ahead) with a low part, whose extra staging would not fit beside two
+    static constexpr int AS = LO ? 1 : 2;
     AP ap;
-    uint4 areg[2][AP::SLOTS];
-    const uint8_t* bq[4];  // weight rows in HBM
-    const uint8_t* bs[4];  // their scale rows in LDS
+    uint4 areg[AS][AP::SLOTS];
+    LP lp;
+    u32x4 lreg[AS][LO ? LP::SLOTS : 1];
+    uint32_t lsreg[AS];
+    uint32_t qoff[4];      // byte offset of this lane's weight row of subtile ns in its tensor
+    uint32_t soff[4];      // byte offset of that row's scale bytes in the LDS scale region
     uint4 bring[NBB][4];
 };
+
+// Tensor of subtile ns (GATEUP: 0, 1 gate, 2, 3 up).
+template <int MODE>
+__device__ __forceinline__ constexpr int tensor_of(int ns) { return MODE == GATEUP ? (ns >> 1) : 0; }
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i fp4_operand(const uint4& q) {  // FP4: only the first four dwords are read
+    return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+}
+__device__ __forceinline__ v8i fp4_operand(const u32x4& q) {
+    return v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+}
 
 // The reduction of one work item after the prologue, with the number of 16-row
 // subtiles (MS) fixed at compile time so the step body is straight-line code.
@@ -290,8 +375,9 @@ struct GemmState {
 // A(t + 1) into buffer (t + 1) % 2 (read last in step t - 1); barrier.  All loads
 // are ordinary vector loads, so the compiler's per-register waits stay exact
 // across the loop.
-template <int MODE, int MT, int CW, int NBB, int MS, bool EXACT>
-__device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT, CW, NBB>& st, uint8_t* alds,
+template <int MODE, int MT, int CW, int NBB, bool LO, int MS, bool EXACT>
+__device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT, CW, NBB, LO>& st, uint8_t* alds,
+                                           uint8_t* llds, const uint8_t* slds, const char* qb0, const char* qb1,
                                            const int32_t* rperm, const float* rw, int row0, int mrows, int nb0) {
     using SH = GemmShape<MODE, CW>;
     constexpr int WN = SH::WN;
@@ -311,17 +397,19 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
 
     uint32_t scn[4];  // scale bytes of the next step
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) scn[ns] = st.bs[ns][min(lg, sb - 1)];
+    for (int ns = 0; ns < 4; ++ns) scn[ns] = slds[st.soff[ns] + min(lg, sb - 1)];
 
     // P steps per loop body: a multiple of the ring depth and of the two A register sets
     for_steps<(NBB % 2 == 0) ? NBB : 2 * NBB>(nsteps, [&](auto uc, const int step) {
         constexpr int u = decltype(uc)::value;
-        st.ap.load(st.areg[u & 1], min(step + 2, nsteps - 1), Kdim);
+        constexpr int AS = GemmState<MODE, MT, CW, NBB, LO>::AS;
+        if constexpr (AS == 2) st.ap.load(a, st.areg[u & 1], min(step + 2, nsteps - 1), Kdim);
         {
             const int col = min((step + NBB - 1) * KS + 32 * lg, Kdim - 32);
 #pragma unroll
             for (int ns = 0; ns < 4; ++ns)
-                st.bring[(u + NBB - 1) % NBB][ns] = *reinterpret_cast<const uint4*>(st.bq[ns] + (col >> 1));
+                st.bring[(u + NBB - 1) % NBB][ns] = *reinterpret_cast<const uint4*>(
+                    (tensor_of<MODE>(ns) ? qb1 : qb0) + (st.qoff[ns] + (uint32_t)(col >> 1)));
         }
         uint32_t sc[4];
 #pragma unroll
@@ -329,13 +417,49 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
         {
             const int nidx = min(4 * (step + 1) + lg, sb - 1);
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns) scn[ns] = st.bs[ns][nidx];
+            for (int ns = 0; ns < 4; ++ns) scn[ns] = slds[st.soff[ns] + nidx];
         }
         const uint8_t* abuf = alds + (size_t)(u & 1) * MT * A_ROW;
         const bool valid = step * KS + 32 * lg < Kdim;
         float scf[4];
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) scf[ns] = scale_operand(sc[ns]);
+        if constexpr (LO) {
+            // the low part of x: FP4 x FP4 with both E8M0 scales, into the same
+            // accumulators; the weight chunk is the B operand as loaded
+            const uint8_t* lbuf = llds + (size_t)(u & 1) * MT * (LO_ROW + 4);
+            const uint8_t* lsb = lbuf + MT * LO_ROW;
+            const int lkey = (ln >> 2) & 3;
+            int bsc[4];
+            bool b255[4];
+#pragma unroll
+            for (int ns = 0; ns < 4; ++ns) {
+                b255[ns] = EXACT && sc[ns] == 255u;
+                bsc[ns] = b255[ns] ? 254 : (int)sc[ns];
+            }
+#pragma unroll
+            for (int i = 0; i < MS; ++i) {
+                const int r = 16 * i + ln;
+                const u32x4 alo = *reinterpret_cast<const u32x4*>(lbuf + r * LO_ROW + 16 * (lg ^ lkey));
+                const int sa = lsb[4 * r + lg];
+                const v8i aop = fp4_operand(alo);
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns) {
+                    const v8i bop = fp4_operand(st.bring[u % NBB][ns]);
+                    acc[i][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[i][ns], 4, 4, 0, sa,
+                                                                                   0, bsc[ns]);
+                    if constexpr (EXACT) {
+                        // scale byte 255 = 2^128: the group at 2^127 once more
+                        if (__any(b255[ns])) {
+                            const v8i b2 = b255[ns] ? bop : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                            acc[i][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, b2, acc[i][ns], 4, 4,
+                                                                                           0, sa, 0, bsc[ns]);
+                        }
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);  // the low part's fragments die before the converts
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             bf16x8 bop[4];
@@ -358,7 +482,15 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
             // (registers for them would push the weight ring out of VGPRs)
             __builtin_amdgcn_sched_barrier(0);
         }
-        st.ap.store(st.areg[(u + 1) & 1], alds + (size_t)((step + 1) & 1) * MT * A_ROW, step + 1, Kdim);
+        st.ap.store(st.areg[(u + 1) % AS], alds + (size_t)((step + 1) & 1) * MT * A_ROW, step + 1, Kdim);
+        if constexpr (LO) {
+            uint8_t* lb = llds + (size_t)((step + 1) & 1) * MT * (LO_ROW + 4);
+            st.lp.store(st.lreg[0], st.lsreg[0], lb, lb + MT * LO_ROW);
+        }
+        if constexpr (AS == 1) {  // the next step's activations, one step ahead
+            st.ap.load(a, st.areg[0], min(step + 2, nsteps - 1), Kdim);
+            if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(step + 2, nsteps - 1));
+        }
         lds_barrier();
     });
 
@@ -398,17 +530,18 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
 //   - one barrier per step; the scale bytes of the workgroup's weight rows are
 //     copied to LDS up front, while the first activation and weight loads are
 //     already in flight.
-template <int MODE, int MT, int CW, int NBB>
+template <int MODE, int MT, int CW, int NBB, bool LO>
 __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
     using SH = GemmShape<MODE, CW>;
-    using ST = GemmState<MODE, MT, CW, NBB>;
+    using ST = GemmState<MODE, MT, CW, NBB, LO>;
     constexpr int WN = SH::WN, BN = SH::BN;
     constexpr int THREADS = CW * 64;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* alds = smem;                   // [2][MT][A_ROW]
     int32_t* rperm = reinterpret_cast<int32_t*>(smem + 2 * MT * A_ROW);  // [MT] pair of each tile row
     float* rw = reinterpret_cast<float*>(rperm + MT);                      // [MT] its routing weight
-    uint8_t* slds = reinterpret_cast<uint8_t*>(rw + MT);                   // [TENSORS][rows][Kdim/32]
+    uint8_t* llds = reinterpret_cast<uint8_t*>(rw + MT);                   // LO: [2][MT * LO_ROW + MT * 4]
+    uint8_t* slds = llds + (LO ? 2 * MT * (LO_ROW + 4) : 0);               // [TENSORS][rows][Kdim/32]
 
     // ---- work item (XCD-aware): XCD x walks items [x*per, (x+1)*per)
     const int item = xcd_item(a.scalars[1] * a.nblk_n);
@@ -426,6 +559,7 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
 
     ST st;
     st.ap.init(a, tid, row0, mrows);  // pair ids of the staged rows (first loads)
+    if constexpr (LO) st.lp.init(a, row0, mrows, nsteps);
 
     // ---- scale bytes of the workgroup's rows: srows_real * sb contiguous bytes per
     // tensor (a multiple of 32, 16-byte aligned), copied global -> LDS directly
@@ -448,15 +582,16 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
 
     // ---- weight rows of this lane (clamped to real rows; columns past N are
     // computed from a repeated row and never stored), and the first ring steps
-    const size_t qrow = (size_t)Kdim >> 1;
+    const uint32_t qrow = (uint32_t)Kdim >> 1;
+    // the expert's weight tensors: wave-uniform bases, per-lane 32-bit row offsets
+    const char* qb0 = reinterpret_cast<const char*>(a.q0 + (size_t)e * a.q0_stride);
+    const char* qb1 = (MODE == GATEUP) ? reinterpret_cast<const char*>(a.q1 + (size_t)e * a.q1_stride) : qb0;
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
-        const int tsel = (MODE == GATEUP) ? (ns >> 1) : 0;
         const int r = (MODE == GATEUP) ? n0 + 16 * (ns & 1) + ln : n0 + 16 * ns + ln;
         const int row = min(r, N - 1);
-        const uint8_t* q = (tsel == 0) ? a.q0 + (size_t)e * a.q0_stride : a.q1 + (size_t)e * a.q1_stride;
-        st.bq[ns] = q + (size_t)row * qrow;
-        st.bs[ns] = slds + (size_t)tsel * srows_real * sb + (size_t)(row - nb0) * sb;
+        st.qoff[ns] = (uint32_t)row * qrow;
+        st.soff[ns] = (uint32_t)(tensor_of<MODE>(ns) * srows_real * sb + (row - nb0) * sb);
     }
     {
         const int lg = lane >> 4;
@@ -464,17 +599,25 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
         for (int u = 0; u < NBB - 1; ++u) {
             const int col = min(min(u, nsteps - 1) * KS + 32 * lg, Kdim - 32);
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns) st.bring[u][ns] = *reinterpret_cast<const uint4*>(st.bq[ns] + (col >> 1));
+            for (int ns = 0; ns < 4; ++ns)
+                st.bring[u][ns] = *reinterpret_cast<const uint4*>((tensor_of<MODE>(ns) ? qb1 : qb0) +
+                                                                  (st.qoff[ns] + (uint32_t)(col >> 1)));
         }
     }
-    st.ap.load(st.areg[0], 0, Kdim);
-    st.ap.load(st.areg[1], min(1, nsteps - 1), Kdim);
+    st.ap.load(a, st.areg[0], 0, Kdim);
+    if constexpr (ST::AS == 2) st.ap.load(a, st.areg[1], min(1, nsteps - 1), Kdim);
+    if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], 0);
     if (MODE == DOWN && tid < mrows) {  // pair id and routing weight of each tile row
         const int p = a.perm[row0 + tid];
         rperm[tid] = p;
         rw[tid] = a.wts[p];
     }
     st.ap.store(st.areg[0], alds, 0, Kdim);
+    if constexpr (LO) st.lp.store(st.lreg[0], st.lsreg[0], llds, llds + MT * LO_ROW);
+    if constexpr (ST::AS == 1) {  // step 1's activations into the one register set
+        st.ap.load(a, st.areg[0], min(1, nsteps - 1), Kdim);
+        if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(1, nsteps - 1));
+    }
     __syncthreads();  // scales, the first A buffer and the row table are in LDS
 
     // ---- any scale byte equal to 255 in the staged rows?
@@ -488,7 +631,8 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
     const bool exact = __syncthreads_or(has255) != 0 || (Kdim % KS) != 0;
 
     if (exact) {
-        gemm_steps<MODE, MT, CW, NBB, MT / 16, true>(a, st, alds, rperm, rw, row0, mrows, nb0);
+        gemm_steps<MODE, MT, CW, NBB, LO, MT / 16, true>(a, st, alds, llds, slds, qb0, qb1, rperm, rw, row0, mrows,
+                                                         nb0);
         return;
     }
     // tiles hold at most MT rows; the clamp keeps every wave on a path with the
@@ -497,7 +641,8 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
 #define K3_TILE_CASE(MSV)                                                                       \
     case MSV:                                                                                   \
         if constexpr (MSV <= MT / 16)                                                           \
-            gemm_steps<MODE, MT, CW, NBB, MSV, false>(a, st, alds, rperm, rw, row0, mrows, nb0); \
+            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false>(a, st, alds, llds, slds, qb0, qb1, rperm, rw, row0, \
+                                                          mrows, nb0);                                      \
         break;
     switch (msub) {
         K3_TILE_CASE(1)
@@ -513,17 +658,17 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
 #undef K3_TILE_CASE
 }
 
-template <int MODE, int MT, int CW, int NBB>
+template <int MODE, int MT, int CW, int NBB, bool LO>
 hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
     using SH = GemmShape<MODE, CW>;
     a.nblk_n = (a.N + SH::BN - 1) / SH::BN;
-    const size_t lds = gemm_lds_bytes(MT, 2, SH::SROWS, a.Kdim);
+    const size_t lds = gemm_lds_bytes(MT, 2, SH::SROWS, a.Kdim, LO);
     const long max_items = (long)max_tiles * a.nblk_n;
     const dim3 grid(xcd_grid(max_items));
-    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, NBB>);
+    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, NBB, LO>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, NBB>), grid, dim3(CW * 64), lds, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, NBB, LO>), grid, dim3(CW * 64), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -532,12 +677,74 @@ hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
 // waves per SIMD beside two sets of activation registers.  LDS: two A buffers plus
 // the staged scales; when the scales of eight waves' rows do not fit (long rows,
 // e.g. a gate/up reduction of 8192), four waves with half the rows.
-template <int MODE>
+template <int MODE, bool LO>
 hipError_t launch_gemm(const GemmArgs& a, int mt, int max_tiles, hipStream_t stream) {
-    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 4>(a, max_tiles, stream);
-    if (gemm_lds_bytes(kTileRowsLarge, 2, GemmShape<MODE, 8>::SROWS, a.Kdim) <= kLdsLimit)
-        return launch_gemm_t<MODE, kTileRowsLarge, 8, 2>(a, max_tiles, stream);
-    return launch_gemm_t<MODE, kTileRowsLarge, 4, 2>(a, max_tiles, stream);
+    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 4, LO>(a, max_tiles, stream);
+    if (gemm_lds_bytes(kTileRowsLarge, 2, GemmShape<MODE, 8>::SROWS, a.Kdim, LO) <= kLdsLimit)
+        return launch_gemm_t<MODE, kTileRowsLarge, 8, 2, LO>(a, max_tiles, stream);
+    return launch_gemm_t<MODE, kTileRowsLarge, 4, 2, LO>(a, max_tiles, stream);
+}
+
+// ------------------------------------------------------------------ x = hi + lo
+// Eight lanes per 32-column group, four columns per lane: hi = bf16(x) (RNE); lo =
+// x - hi exactly (0 where x or hi is not finite); the group's scale exponent e is
+// the smallest with max|lo| <= 6 * 2^e (clamped to the E8M0 range), and each lo /
+// 2^e is rounded to the nearest e2m1 value, ties to the even code.  Output rows of
+// lo are padded to whole 128-column steps with zero codes (scale byte 127).
+__device__ __forceinline__ uint32_t e2m1_rne(float v, float inv) {
+    const float y = fabsf(v) * inv;  // <= 6 by the choice of the scale
+    const uint32_t m = (uint32_t)(y > 0.25f) + (uint32_t)(y >= 0.75f) + (uint32_t)(y > 1.25f) +
+                       (uint32_t)(y >= 1.75f) + (uint32_t)(y > 2.5f) + (uint32_t)(y >= 3.5f) + (uint32_t)(y > 5.0f);
+    return m | (v < 0.0f ? 8u : 0u);
+}
+
+__global__ __launch_bounds__(256) void xsplit_kernel(const float* __restrict__ x, int T, int D,
+                                                     uint16_t* __restrict__ xh, uint8_t* __restrict__ xl,
+                                                     uint8_t* __restrict__ xls) {
+    const int nsteps = (D + KS - 1) / KS, gpr = nsteps * 4;  // groups per padded row
+    const size_t ngroups = (size_t)T * gpr;
+    const int sub = threadIdx.x & 7;  // lane within the group
+    const size_t stride = (size_t)gridDim.x * (blockDim.x / 8);
+    // every lane of a group takes the same trip count (the loop bound is per group)
+    for (size_t gi = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) / 8; gi < ngroups; gi += stride) {
+        const size_t t = gi / gpr;
+        const int g = (int)(gi % gpr);
+        const bool real = 32 * g < D;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (real) {
+            const float4 q = reinterpret_cast<const float4*>(x + t * D + 32 * g)[sub];
+            v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        }
+        uint32_t hb[4];
+        float lo[4];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            hb[j] = f32_to_bf16_bits(v[j]);
+            const float h = __uint_as_float(hb[j] << 16);
+            lo[j] = (__builtin_isfinite(v[j]) && __builtin_isfinite(h)) ? v[j] - h : 0.0f;
+            amax = max(amax, __float_as_uint(lo[j]) & 0x7FFFFFFFu);
+        }
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 8));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 8));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4, 8));
+        int e = 0;
+        if (amax >= 0x00800000u) {
+            e = (int)(amax >> 23) - 127 - 2 + ((amax & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+            e = max(min(e, 127), -127);
+        } else if (amax != 0u) {
+            e = -127;
+        }
+        const float inv = __builtin_ldexpf(1.0f, -e);
+        uint32_t codes = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) codes |= e2m1_rne(lo[j], inv) << (4 * j);
+        if (real)
+            reinterpret_cast<uint2*>(xh + t * D + 32 * g)[sub] =
+                make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        reinterpret_cast<uint16_t*>(xl + t * (size_t)nsteps * LO_ROW + 16 * g)[sub] = (uint16_t)codes;
+        if (sub == 0) xls[t * (size_t)gpr + g] = (uint8_t)(e + 127);
+    }
 }
 
 // -------------------------------------------------------------------------- combine
@@ -612,18 +819,24 @@ GroupBuffers group_workspace_carve(void* ws, int T, int K, int E, bool with_outp
     return g;
 }
 
+// group buffers, h [P, F] bf16, the pair rows [P, D] fp32, then (fp32 x) hi [T, D]
+// bf16, the low part's codes [T, nsteps * 64] and scales [T, nsteps * 4].
 size_t chunk_workspace_bytes(int T, int K, int E, int D, int F) {
-    const size_t P = (size_t)T * K;
-    return group_workspace_bytes(T, K, E, true) + align256(P * F * 2) + align256(P * D * 4);
+    const size_t P = (size_t)T * K, t = (size_t)T, ns = (size_t)(D + KS - 1) / KS;
+    return group_workspace_bytes(T, K, E, true) + align256(P * F * 2) + align256(P * D * 4) +
+           align256(t * D * 2) + align256(t * ns * LO_ROW) + align256(t * ns * 4);
 }
 
 ChunkWorkspace chunk_workspace_carve(void* ws, int T, int K, int E, int D, int F) {
     ChunkWorkspace c;
     c.g = group_workspace_carve(ws, T, K, E, true);
-    const size_t P = (size_t)T * K;
+    const size_t P = (size_t)T * K, t = (size_t)T, ns = (size_t)(D + KS - 1) / KS;
     char* p = static_cast<char*>(ws) + group_workspace_bytes(T, K, E, true);
     c.h_bf16 = reinterpret_cast<uint16_t*>(p); p += align256(P * F * 2);
-    c.ytk = reinterpret_cast<float*>(p);
+    c.ytk = reinterpret_cast<float*>(p); p += align256(P * D * 4);
+    c.x_hi = reinterpret_cast<uint16_t*>(p); p += align256(t * D * 2);
+    c.x_lo = reinterpret_cast<uint8_t*>(p); p += align256(t * ns * LO_ROW);
+    c.x_los = reinterpret_cast<uint8_t*>(p);
     return c;
 }
 
@@ -641,14 +854,24 @@ hipError_t launch_group(const int32_t* idx, int T, int K, int E, const GroupBuff
     return hipGetLastError();
 }
 
-hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int32_t* idx, const float* w,
-                        int K, float* y, int32_t* n_unique_out, const ChunkWorkspace& ws,
+hipError_t launch_chunk(const DevWeights& W, const float* x32, const uint16_t* xb16, int T, const int32_t* idx,
+                        const float* w, int K, float* y, int32_t* n_unique_out, const ChunkWorkspace& ws,
                         hipStream_t stream) {
     hipError_t err = launch_group(idx, T, K, W.E, ws.g, n_unique_out, stream);
     if (err != hipSuccess) return err;
+    const bool lo = x32 != nullptr;
+    if (lo) {
+        const size_t groups = (size_t)T * ((W.D + KS - 1) / KS) * 4;
+        hipLaunchKernelGGL(xsplit_kernel, dim3(grid_for(groups, 256 / 8)), dim3(256), 0, stream, x32, T, W.D,
+                           ws.x_hi, ws.x_lo, ws.x_los);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
 
     GemmArgs gu{};
-    gu.A = x;
+    gu.A = lo ? ws.x_hi : xb16;
+    gu.alo = ws.x_lo;
+    gu.alos = ws.x_los;
     gu.perm = ws.g.perm;
     gu.K = K;
     gu.q0 = W.gate_q; gu.s0 = W.gate_s; gu.q1 = W.up_q; gu.s1 = W.up_s;
@@ -659,7 +882,8 @@ hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int
     gu.tiles = ws.g.tiles;
     gu.scalars = ws.g.scalars;
     gu.h_out = ws.h_bf16;
-    err = launch_gemm<GATEUP>(gu, ws.g.mt, ws.g.max_tiles, stream);
+    err = lo ? launch_gemm<GATEUP, true>(gu, ws.g.mt, ws.g.max_tiles, stream)
+             : launch_gemm<GATEUP, false>(gu, ws.g.mt, ws.g.max_tiles, stream);
     if (err != hipSuccess) return err;
 
     GemmArgs dn{};
@@ -674,7 +898,7 @@ hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int
     dn.scalars = ws.g.scalars;
     dn.y_out = ws.ytk;
     dn.wts = w;
-    err = launch_gemm<DOWN>(dn, ws.g.mt, ws.g.max_tiles, stream);
+    err = launch_gemm<DOWN, false>(dn, ws.g.mt, ws.g.max_tiles, stream);
     if (err != hipSuccess) return err;
 
     return launch_combine(ws.ytk, idx, T, K, W.D, ws.g.scalars, y, stream);

@@ -6,11 +6,13 @@
 // group of 32 stays, the activations become OCP MXFP8 (mx.hpp) in one or two
 // parts, and the weights' e2m1 nibbles and ue8m0 bytes go straight into
 // v_mfma_scale_f32_16x16x128_f8f6f4 as FP4 codes with their E8M0 block scales:
-// no weight conversion at all, and one MFMA covers 128 reduction columns.  In
-// this path a weight scale byte of 255 is the E8M0 NaN (OCP MX) rather than the
-// closed form's 2^128.
+// no weight conversion at all, and one MFMA covers 128 reduction columns.  The
+// weights keep their closed form for every scale byte: the MFMA would read E8M0
+// 255 as NaN, so a work item whose staged scale rows hold a 255 runs a step body
+// that passes 254 instead and adds those groups' products a second time
+// (2^128 = 2 * 2^127, exact).
 //
-// Kernels, in stream order (x arrives as bf16):
+// Kernels, in stream order (x arrives as fp32):
 //   group_*        as in the bf16 chunk path (chunk.hip)
 //   mx_quant       x -> codes [parts][T][D], scales [parts][T][D/32]
 //   gemm_mx<GATEUP> g, u over the quantized x, h = SiTU(g, u) in fp32, quantized
@@ -173,7 +175,7 @@ __device__ __forceinline__ void mx_store_pair(float v0, float v1, int ln, uint8_
 // used and the weights of step t + NBB - 1 into the ring slot step t - 1 used;
 // read the weight scale bytes of step t + 1; compute step t from LDS buffer t % 2
 // and ring slot t % NBB; store A(t + 1) into buffer (t + 1) % 2; barrier.
-template <int MODE, int MT, int CW, int NBB, int PARTS, int MS>
+template <int MODE, int MT, int CW, int NBB, int PARTS, int MS, bool EXACT>
 __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, NBB, PARTS>& st, uint8_t* alds,
                                          uint8_t* sl, const int32_t* rperm, const float* rw, int row0, int mrows,
                                          int nb0) {
@@ -217,6 +219,13 @@ __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, 
         }
         const uint8_t* abuf = alds + (size_t)(u & 1) * MT * A_ROW;
         const uint8_t* sbuf = sl + (size_t)(u & 1) * PARTS * MT * 4;
+        int bsc[4];
+        bool b255[4];
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) {
+            b255[ns] = EXACT && sc[ns] == 255u;
+            bsc[ns] = b255[ns] ? 254 : (int)sc[ns];
+        }
         // A fragments in (part, subtile) order; the compiler interleaves the LDS
         // reads with the MFMAs (a scheduling barrier per fragment costs spills)
 #pragma unroll
@@ -229,9 +238,19 @@ __device__ __forceinline__ void mx_steps(const MxArgs& a, MxState<MODE, MT, CW, 
                 const int sa = sbuf[(pt * MT + 16 * i + ln) * 4 + lg];
                 const v8i aop = a_operand(lo, hi);
 #pragma unroll
-                for (int ns = 0; ns < 4; ++ns)
-                    acc[i][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        aop, b_operand(st.bring[u % NBB][ns]), acc[i][ns], 0, 4, 0, sa, 0, (int)sc[ns]);
+                for (int ns = 0; ns < 4; ++ns) {
+                    const v8i bop = b_operand(st.bring[u % NBB][ns]);
+                    acc[i][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[i][ns], 0, 4, 0, sa,
+                                                                                   0, bsc[ns]);
+                    if constexpr (EXACT) {
+                        // scale byte 255 = 2^128: the group at 2^127 once more
+                        if (__any(b255[ns])) {
+                            const v8i b2 = b255[ns] ? bop : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+                            acc[i][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, b2, acc[i][ns], 0, 4,
+                                                                                           0, sa, 0, bsc[ns]);
+                        }
+                    }
+                }
             }
         }
         st.ap.store(st.areg[(u + 1) & 1], st.sreg[(u + 1) & 1], alds + (size_t)((step + 1) & 1) * MT * A_ROW,
@@ -346,11 +365,24 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_mx_kernel(MxArgs a) {
     st.ap.store(st.areg[0], st.sreg[0], alds, sl);
     __syncthreads();  // weight scales, the first A buffer and the row table are in LDS
 
+    // any weight scale byte equal to 255 in the staged rows?
+    int has255 = 0;
+    for (int c = tid; c < stotal; c += THREADS) {
+        const uint4 v = *reinterpret_cast<const uint4*>(slds + 16 * c);
+        const uint32_t w4[4] = {~v.x, ~v.y, ~v.z, ~v.w};  // 255 -> zero byte
+#pragma unroll
+        for (int d = 0; d < 4; ++d) has255 |= ((w4[d] - 0x01010101u) & ~w4[d] & 0x80808080u) != 0u;
+    }
+    if (__syncthreads_or(has255) != 0) {
+        mx_steps<MODE, MT, CW, NBB, PARTS, MT / 16, true>(a, st, alds, sl, rperm, rw, row0, mrows, nb0);
+        return;
+    }
+
     const int msub = min((mrows + 15) >> 4, MT / 16);
 #define K3_MX_CASE(MSV)                                                                          \
     case MSV:                                                                                    \
         if constexpr (MSV <= MT / 16)                                                            \
-            mx_steps<MODE, MT, CW, NBB, PARTS, MSV>(a, st, alds, sl, rperm, rw, row0, mrows, nb0); \
+            mx_steps<MODE, MT, CW, NBB, PARTS, MSV, false>(a, st, alds, sl, rperm, rw, row0, mrows, nb0); \
         break;
     switch (msub) {
         K3_MX_CASE(1)
@@ -511,14 +543,14 @@ ChunkMxWorkspace chunk_mx_workspace_carve(void* ws, int T, int K, int E, int D, 
     return c;
 }
 
-hipError_t launch_chunk_mx(const DevWeights& W, const uint16_t* x, int T, const int32_t* idx, const float* w,
+hipError_t launch_chunk_mx(const DevWeights& W, const float* x, int T, const int32_t* idx, const float* w,
                            int K, int parts, float* y, int32_t* n_unique_out, const ChunkMxWorkspace& ws,
                            hipStream_t stream) {
     hipError_t err = launch_group(idx, T, K, W.E, ws.g, n_unique_out, stream);
     if (err != hipSuccess) return err;
     const size_t P = (size_t)T * K;
     const size_t xplane = (size_t)T * W.D, xsplane = xplane / 32;
-    err = launch_mx_quant(x, true, (size_t)T * W.D, parts, ws.xq, ws.xs, xplane, xsplane, stream);
+    err = launch_mx_quant(x, false, (size_t)T * W.D, parts, ws.xq, ws.xs, xplane, xsplane, stream);
     if (err != hipSuccess) return err;
 
     MxArgs gu{};

@@ -5,9 +5,8 @@
 // experts, SiTU-GLU; PR #676 summary: the routed experts run in the latent space
 // behind shared down/up projections, plus two fused full-width shared experts.
 // Per token with hidden state h [Dh] (bf16):
-//   x   = Wdn h                           [Dl]   bf16 out (the activation format of the
-//                                                routed chunk path; widened to fp32 for
-//                                                the one-token decode path)
+//   x   = Wdn h                           [Dl]   fp32 (the products' fp32 accumulation;
+//                                                nothing is rounded before the experts)
 //   a   = sum_k w_k E_k(x)                [Dl]   the routed block: decode GEMVs for one
 //                                                token, the grouped chunk GEMMs otherwise
 //   r   = gn * a / sqrt(mean(a^2) + eps)  [Dl]   bf16
@@ -16,7 +15,7 @@
 //   s   = SiTU(g, u)                      [Fs]   bf16
 //   out += Sd s                           [Dh]
 // The five dense products are bf16 x bf16 with fp32 accumulation.  For one token
-// they are this file's GEMV kernels (x with its widening in one pass, g, u and s
+// they are this file's GEMV kernels (x in one pass with g, u and s
 // in one pass, the norm folded into the pass that forms out); for a chunk they
 // are rocBLAS GEMMs (Tensile's MFMA kernels for gfx950) around the rmsnorm and
 // situ kernels.
@@ -85,7 +84,7 @@ __global__ __launch_bounds__(256) void situ_kernel(const float* __restrict__ g, 
 // For a single token the five projections are matrix-vector products that stream
 // their bf16 weights once; these kernels do that directly (and fuse what sits
 // between them) instead of going through a GEMM library at n = 1:
-//   GEMV_X    x = Wdn h, written as bf16 and as its exact fp32 widening
+//   GEMV_X    x = Wdn h in fp32
 //   GEMV_SITU s = SiTU(Sg h, Su h) in bf16 (both shared projections in one pass)
 //   (the two above run as one launch, gemv_xs_kernel: both read h)
 //   GEMV_OUT  out = Wup r + Sd s in fp32, r = RMSNorm(a) computed by every
@@ -110,8 +109,8 @@ struct GemvArgs {
     const uint16_t* gn;  //      ... and the RMSNorm weight (bf16 [I0])
     float eps;
     const uint16_t* v1;  // OUT: s (bf16 [I1])
-    uint16_t* yb;        // X: x bf16; SITU: s bf16
-    float* yf;           // X: x widened; OUT: out
+    uint16_t* yb;        // SITU: s bf16
+    float* yf;           // X: x fp32; OUT: out
 };
 
 __host__ __device__ inline int gemv_pad(int n) { return (n + 511) & ~511; }
@@ -190,9 +189,7 @@ __device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_
         const int o = o0 + r;
         if (lane != 0 || o >= g.O) continue;
         if (EPI == GEMV_X) {
-            const uint32_t xb = f32_to_bf16_bits(d0);
-            g.yb[o] = (uint16_t)xb;
-            g.yf[o] = __uint_as_float(xb << 16);
+            g.yf[o] = d0;
         } else if (EPI == GEMV_SITU) {
             g.yb[o] = (uint16_t)f32_to_bf16_bits(situ_fast(d0, d1));
         } else {
@@ -313,12 +310,12 @@ hipError_t dense(rocblas_handle h, const uint16_t* in, int T, int Kd, const uint
 
 }  // namespace
 
-// x (bf16, and fp32 for one token), the routed block's workspace, a, r, g, u, s.
+// x (fp32), the routed block's workspace, a, r, g, u, s.
 size_t latent_workspace_bytes(const LatentDims& L, int T, int K, int E) {
     const size_t t = (size_t)T;
     const size_t routed = T == 1 ? decode_workspace_bytes(K, L.Dl, L.F) : chunk_workspace_bytes(T, K, E, L.Dl, L.F);
-    return align256(t * L.Dl * 2) + align256(t * L.Dl * 4) + align256(routed) + align256(t * L.Dl * 4) +
-           align256(t * L.Dl * 2) + 2 * align256(t * L.Fs * 4) + align256(t * L.Fs * 2);
+    return align256(t * L.Dl * 4) + align256(routed) + align256(t * L.Dl * 4) + align256(t * L.Dl * 2) +
+           2 * align256(t * L.Fs * 4) + align256(t * L.Fs * 2);
 }
 
 hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t* h, int T, const int32_t* idx,
@@ -328,7 +325,6 @@ hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t
     const size_t t = (size_t)T;
     const size_t routed = T == 1 ? decode_workspace_bytes(K, Dl, W.F) : chunk_workspace_bytes(T, K, W.E, Dl, W.F);
     char* p = static_cast<char*>(ws);
-    uint16_t* x = reinterpret_cast<uint16_t*>(p); p += align256(t * Dl * 2);
     float* x32 = reinterpret_cast<float*>(p); p += align256(t * Dl * 4);
     void* rws = p; p += align256(routed);
     float* a = reinterpret_cast<float*>(p); p += align256(t * Dl * 4);
@@ -338,10 +334,10 @@ hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t
     uint16_t* s = reinterpret_cast<uint16_t*>(p);
 
     if (T == 1) {
-        // one token: x = Wdn h (bf16 and fp32), s = SiTU(Sg h, Su h), the routed
-        // decode path on x, then out = Wup RMSNorm(a) + Sd s
+        // one token: x = Wdn h (fp32), s = SiTU(Sg h, Su h), the routed decode path
+        // on x, then out = Wup RMSNorm(a) + Sd s
         GemvArgs gx{};
-        gx.W0 = L.w_down; gx.I0 = Dh; gx.O = Dl; gx.v0 = h; gx.yb = x; gx.yf = x32;
+        gx.W0 = L.w_down; gx.I0 = Dh; gx.O = Dl; gx.v0 = h; gx.yf = x32;
         GemvArgs gs{};
         gs.W0 = L.shared_gate; gs.W1 = L.shared_up; gs.I0 = Dh; gs.I1 = Dh; gs.O = Fs; gs.v0 = h; gs.yb = s;
         err = launch_gemv_xs(gx, gs, stream);
@@ -356,10 +352,11 @@ hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t
     rocblas_handle blas = nullptr;
     err = blas_for(stream, &blas);
     if (err != hipSuccess) return err;
-    // x = Wdn h, then the routed block on x
-    err = dense(blas, h, T, Dh, L.w_down, Dl, x, false, 0.0f);
+    // x = Wdn h in fp32, then the routed block on x
+    err = dense(blas, h, T, Dh, L.w_down, Dl, x32, true, 0.0f);
     if (err != hipSuccess) return err;
-    err = launch_chunk(W, x, T, idx, w, K, a, nullptr, chunk_workspace_carve(rws, T, K, W.E, Dl, W.F), stream);
+    err = launch_chunk(W, x32, nullptr, T, idx, w, K, a, nullptr, chunk_workspace_carve(rws, T, K, W.E, Dl, W.F),
+                       stream);
     if (err != hipSuccess) return err;
     // RMSNorm on the aggregate, then back to the full width
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, stream, a, L.norm, Dl, L.eps, r);

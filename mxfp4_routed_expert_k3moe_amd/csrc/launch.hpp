@@ -74,6 +74,9 @@ struct ChunkWorkspace {
     GroupBuffers g;
     uint16_t* h_bf16;       // [T*K, F]  (grouped pair order)
     float* ytk;             // [T*K, D]  (pair order t*K + k)
+    uint16_t* x_hi;         // [T, D]    fp32 x: bf16(x)
+    uint8_t* x_lo;          // [T, ceil(D/128) * 64]  x - bf16(x) as FP4 codes, rows padded to whole steps
+    uint8_t* x_los;         // [T, ceil(D/128) * 4]   their E8M0 scales
 };
 
 int group_max_tiles(int T, int K, int E);
@@ -84,8 +87,9 @@ ChunkWorkspace chunk_workspace_carve(void* ws, int T, int K, int E, int D, int F
 
 hipError_t launch_group(const int32_t* idx, int T, int K, int E, const GroupBuffers& g,
                         int32_t* n_unique_out, hipStream_t stream);
-hipError_t launch_chunk(const DevWeights& W, const uint16_t* x, int T, const int32_t* idx, const float* w,
-                        int K, float* y, int32_t* n_unique_out, const ChunkWorkspace& ws,
+// x32 (fp32 [T, D]) or xb16 (bf16 [T, D]): exactly one is non-null.
+hipError_t launch_chunk(const DevWeights& W, const float* x32, const uint16_t* xb16, int T, const int32_t* idx,
+                        const float* w, int K, float* y, int32_t* n_unique_out, const ChunkWorkspace& ws,
                         hipStream_t stream);
 
 hipError_t launch_combine(const float* ytk, const int32_t* idx, int T, int K, int D, const int32_t* scalars,
@@ -104,7 +108,7 @@ size_t chunk_mx_workspace_bytes(int T, int K, int E, int D, int F);
 ChunkMxWorkspace chunk_mx_workspace_carve(void* ws, int T, int K, int E, int D, int F);
 hipError_t launch_mx_quant(const void* v, bool bf16, size_t n, int parts, uint8_t* codes, uint8_t* scales,
                            size_t code_plane, size_t scale_plane, hipStream_t stream);
-hipError_t launch_chunk_mx(const DevWeights& W, const uint16_t* x, int T, const int32_t* idx, const float* w,
+hipError_t launch_chunk_mx(const DevWeights& W, const float* x, int T, const int32_t* idx, const float* w,
                            int K, int parts, float* y, int32_t* n_unique_out, const ChunkMxWorkspace& ws,
                            hipStream_t stream);
 

@@ -32,11 +32,11 @@ IN_F32, IN_BF16 = 0, 1
 PRUNED = -1  # K3MOE_PRUNED: a routing slot dropped by top-p
 
 ENTRY_POINTS = ("k3moe_route", "k3moe_route_topp", "k3moe_group", "k3moe_forward_decode", "k3moe_decode_gateup",
-                "k3moe_decode_down", "k3moe_forward_chunk", "k3moe_workspace_size", "k3moe_dequant_mxfp4",
+                "k3moe_decode_down", "k3moe_forward_chunk", "k3moe_forward_chunk_bf16", "k3moe_workspace_size", "k3moe_dequant_mxfp4",
                 "k3moe_status_string", "k3moe_slot_layout", "k3moe_pool_create", "k3moe_pool_destroy",
                 "k3moe_pool_plan", "k3moe_pool_weights", "k3moe_pool_stats", "k3moe_forward_decode_pooled",
                 "k3moe_forward_chunk_mx", "k3moe_mx_quant", "k3moe_latent_forward", "k3moe_latent_workspace_size",
-                "k3moe_forward_decode_timed")
+                "k3moe_forward_decode_timed", "k3moe_probe_stream_read", "k3moe_probe_mfma")
 
 
 class K3moeError(RuntimeError):
@@ -74,6 +74,7 @@ def load() -> ctypes.CDLL:
     lib.k3moe_group.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.k3moe_forward_decode.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.k3moe_forward_chunk.argtypes = [wp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.k3moe_forward_chunk_bf16.argtypes = [wp, vp, i32, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.k3moe_decode_gateup.argtypes = [wp, vp, vp, i32, vp, vp]
     lib.k3moe_forward_decode_timed.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp, vp, vp]
     lib.k3moe_decode_down.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp]
@@ -99,6 +100,8 @@ def load() -> ctypes.CDLL:
     lib.k3moe_latent_forward.argtypes = [lp, wp, vp, i32, vp, vp, i32, vp, vp, sz, vp]
     lib.k3moe_latent_workspace_size.argtypes = [lp, i32, i32, wp]
     lib.k3moe_latent_workspace_size.restype = sz
+    lib.k3moe_probe_stream_read.argtypes = [vp, sz, i32, i32, i32, vp, vp]
+    lib.k3moe_probe_mfma.argtypes = [i32, i32, i32, vp, vp]
     for name in ENTRY_POINTS:
         if name not in ("k3moe_workspace_size", "k3moe_status_string", "k3moe_pool_create", "k3moe_pool_destroy",
                         "k3moe_latent_workspace_size"):
@@ -317,9 +320,12 @@ def decode_down(W: ExpertWeights, h: torch.Tensor, idx: torch.Tensor, w: torch.T
 def forward_chunk(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
                   y: Optional[torch.Tensor] = None, n_unique: Optional[torch.Tensor] = None,
                   ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """A chunk: bf16 ``x [T,D]``, ``idx/w [T,K]`` -> fp32 ``y [T,D]`` (bf16 MFMA path)."""
+    """A chunk: ``x [T,D]``, ``idx/w [T,K]`` -> fp32 ``y [T,D]`` (bf16 MFMA path).  An
+    fp32 ``x`` goes to ``k3moe_forward_chunk`` (x = bf16 high part + MXFP4 low
+    part), a bf16 ``x`` to ``k3moe_forward_chunk_bf16``."""
     T = x.shape[0]
-    _dev(x, torch.bfloat16, "x", (T, W.D))
+    fn = "k3moe_forward_chunk_bf16" if x.dtype == torch.bfloat16 else "k3moe_forward_chunk"
+    _dev(x, torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float32, "x", (T, W.D))
     K = idx.shape[1]
     _dev(idx, torch.int32, "idx", (T, K))
     _dev(w, torch.float32, "w", (T, K))
@@ -328,19 +334,18 @@ def forward_chunk(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch
     if n_unique is not None:
         _dev(n_unique, torch.int32, "n_unique", (1,))
     ws = _workspace(workspace_size(OP_CHUNK, T, K, W), x.device, ws)
-    _check("k3moe_forward_chunk",
-           load().k3moe_forward_chunk(W.ref(), _ptr(x), T, _ptr(idx), _ptr(w), K, _ptr(y), _ptr(n_unique),
-                                      _ptr(ws), ws.numel(), _stream(stream)))
+    _check(fn, getattr(load(), fn)(W.ref(), _ptr(x), T, _ptr(idx), _ptr(w), K, _ptr(y), _ptr(n_unique),
+                                   _ptr(ws), ws.numel(), _stream(stream)))
     return y
 
 
 def forward_chunk_mx(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor, parts: int = 1,
                      y: Optional[torch.Tensor] = None, n_unique: Optional[torch.Tensor] = None,
                      ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """A chunk with MXFP8 activations in ``parts`` parts: bf16 ``x [T,D]``,
+    """A chunk with MXFP8 activations in ``parts`` parts: fp32 ``x [T,D]``,
     ``idx/w [T,K]`` -> fp32 ``y [T,D]`` (scaled FP8 x FP4 MFMA path)."""
     T = x.shape[0]
-    _dev(x, torch.bfloat16, "x", (T, W.D))
+    _dev(x, torch.float32, "x", (T, W.D))
     K = idx.shape[1]
     _dev(idx, torch.int32, "idx", (T, K))
     _dev(w, torch.float32, "w", (T, K))
@@ -509,3 +514,24 @@ def forward_decode_pooled(pool: Pool, layer: int, host: torch.Tensor, layer_stri
                                               int(layer_stride), int(expert_stride), _ptr(x), _ptr(idx), _ptr(w),
                                               K, _ptr(y), _ptr(ws), ws.numel(), _stream(stream), cs))
     return y
+
+
+def probe_stream_read(buf: torch.Tensor, unroll: int = 8, nontemporal: bool = False, blocks: int = 2048,
+                      sink: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Launch the streaming-read probe over the bytes of ``buf`` (measurement only)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous CUDA tensor")
+    sink = torch.empty(blocks, dtype=torch.int32, device=buf.device) if sink is None else sink
+    _check("k3moe_probe_stream_read",
+           load().k3moe_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(unroll),
+                                          int(bool(nontemporal)), int(blocks), _ptr(sink), _stream(stream)))
+    return sink
+
+
+def probe_mfma(kind: int, iters: int, blocks: int, out: Optional[torch.Tensor] = None, stream=None,
+               device="cuda") -> torch.Tensor:
+    """Launch the MFMA issue-rate probe (measurement only)."""
+    out = torch.empty(4 * blocks, dtype=torch.float32, device=device) if out is None else out
+    _check("k3moe_probe_mfma", load().k3moe_probe_mfma(int(kind), int(iters), int(blocks), _ptr(out),
+                                                       _stream(stream)))
+    return out

@@ -16,6 +16,20 @@ colibri PR #676 reports in "It runs the full model"):
   batch4096   4096 tokens, i.i.d. hidden states, logits = h.R, chunk path;
               eight "edge" experts carry scale bytes over the full 0..255 range
 
+Hidden states are fp32 except for prefill256, whose workload names bf16
+activations (those values are rounded to bf16 here, so both sides see them).
+
+Edge experts (batch4096): in each scale tensor a quarter of the groups, drawn
+independently, take a scale byte uniform over 0..255 (every byte value occurs a
+few hundred times per tensor); the rest keep the workload's range.  In an edge
+group whose scale byte exceeds 128 the codes are +-0 (nibbles 0 and 8 only), so
+its weights are +-0 * 2^(s-127) = +-0 by the closed form, s = 255 included; edge
+groups at or below 128 keep uniform codes (s = 0 gives fp32 subnormal weights).
+All 16 codes and all 256 scale bytes appear, and a token routed to an edge
+expert keeps a finite output that the parity tests measure.  edge_mode
+"literal" instead draws every scale byte of an edge expert uniform over 0..255
+(weights up to +-inf; most outputs NaN), for the non-finite mask check.
+
 LatentMoE block workloads (the routed experts behind 7168 <-> 3584 projections,
 RMSNorm on the aggregate and two fused shared experts; LATENT below):
 
@@ -64,6 +78,8 @@ class Config:
     bias_std: float        # score-correction bias ~ N(0, bias_std^2); 0 -> zeros
     path: str              # "decode" or "chunk"
     edge_experts: Tuple[int, ...] = ()
+    x_bf16: bool = False   # hidden states rounded to bf16 (a workload with bf16 activations)
+    edge_mode: str = "finite"  # "finite" or "literal" (see the module docstring)
 
     @property
     def pairs(self) -> int:
@@ -97,7 +113,7 @@ CONFIGS: Dict[str, Config] = {
                         logit_kind="hR", bias_std=0.0, path="chunk"),
     "prefill256": Config("prefill256", T=256, E=896, K=16, D=3584, F=3072, weight_seed=102,
                          act_seed=104, scale_lo=118, scale_hi=128, x_kind="ar1",
-                         logit_kind="hR", bias_std=0.0, path="chunk"),
+                         logit_kind="hR", bias_std=0.0, path="chunk", x_bf16=True),
     "batch4096": Config("batch4096", T=4096, E=896, K=16, D=3584, F=3072, weight_seed=105,
                         act_seed=105, scale_lo=118, scale_hi=128, x_kind="normal",
                         logit_kind="hR", bias_std=0.0, path="chunk", edge_experts=_EDGE),
@@ -110,14 +126,29 @@ def scaled(cfg: Config, **changes) -> Config:
 
 
 # ----------------------------------------------------------------------------- weights
+EDGE_FRACTION = 0.25   # share of an edge expert's groups with a full-range scale byte
+EDGE_ZERO_ABOVE = 128  # edge groups with a larger scale byte hold +-0 codes only
+
+
 def _tensor(cfg: Config, e: int, tid: int) -> np.ndarray:
     name = TENSORS[tid]
     shape = cfg.shapes()[name]
     rng = np.random.default_rng([cfg.weight_seed, e, tid])
+    edge = e in cfg.edge_experts
     if name.endswith("_q"):
+        q = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        if edge and cfg.edge_mode == "finite":
+            s = _tensor(cfg, e, tid + 1)  # the scale bytes of the same rows
+            zero = np.repeat(s > EDGE_ZERO_ABOVE, 16, axis=1)  # 16 packed bytes per group
+            q = np.where(zero, q & 0x88, q).astype(np.uint8)
+        return q
+    if edge and cfg.edge_mode == "literal":
         return rng.integers(0, 256, size=shape, dtype=np.uint8)
-    lo, hi = (0, 255) if e in cfg.edge_experts else (cfg.scale_lo, cfg.scale_hi)
-    return rng.integers(lo, hi + 1, size=shape, dtype=np.uint8)
+    s = rng.integers(cfg.scale_lo, cfg.scale_hi + 1, size=shape, dtype=np.uint8)
+    if edge:
+        pick = rng.random(shape) < EDGE_FRACTION
+        s = np.where(pick, rng.integers(0, 256, size=shape, dtype=np.uint8), s).astype(np.uint8)
+    return s
 
 
 def expert_tensors(cfg: Config, e: int) -> Dict[str, np.ndarray]:
@@ -176,8 +207,8 @@ def weights_device(cfg: Config, device, batch: int = 32, experts: Optional[Itera
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """fp32 values rounded to the nearest bf16 (ties to even), returned as fp32.
 
-    Chunk workloads carry bf16 hidden states (the grouped GEMM takes bf16
-    activations); both the oracle and the device receive exactly these values."""
+    The bf16-activation workload's hidden states are these values; both the
+    oracle and the device receive exactly them."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
     return r.view(np.float32).reshape(np.shape(x))
@@ -187,11 +218,12 @@ def activations(cfg: Config, T: Optional[int] = None, stream: int = 0, bf16: Opt
     """``(x [T,D] f32, logits [T,E] f32, bias [E] f32)`` for the workload.
 
     ``stream`` selects an independent draw of the same distribution (used to
-    build several different decode tokens for cache-cold timing).  For chunk
-    workloads (or ``bf16=True``) the hidden states are bf16 values held in fp32,
-    and the logits are computed from those values.
+    build several different decode tokens for cache-cold timing).  For a
+    workload with bf16 activations (``cfg.x_bf16``, or ``bf16=True``) the hidden
+    states are bf16 values held in fp32, and the logits are computed from those
+    values.
     """
-    bf16 = (cfg.path == "chunk") if bf16 is None else bf16
+    bf16 = cfg.x_bf16 if bf16 is None else bf16
     T = cfg.T if T is None else int(T)
     rng = np.random.default_rng([cfg.act_seed, 7919, stream])
     if cfg.x_kind == "normal":

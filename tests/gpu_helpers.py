@@ -55,14 +55,23 @@ def device_weights(cfg: synth.Config):
 
 
 def oracle_forward_subset(cfg: synth.Config, x: np.ndarray, idx: np.ndarray, w: np.ndarray,
-                          want_pairs: bool = False, mx: int = 0, weights=None):
+                          want_pairs: bool = False, mx: int = 0, weights=None, progress: int = 0):
     """The oracle on ``x [T,D]`` with routing ``idx/w [T,K]``, given host weights of
     only the experts the routing touches (regenerated from the seeded generator,
-    or taken from ``weights`` when given).  ``mx`` selects the MXFP8 variant."""
+    or taken from ``weights`` when given).  ``mx`` selects the MXFP8 variant;
+    ``progress=n`` has the oracle report every n-th finished expert."""
     used = np.unique(idx[idx >= 0])  # pruned slots (id -1) touch no expert
-    W = synth.weights_host(cfg, used) if weights is None else {k: v[used] for k, v in weights.items()}
+    if weights is None:
+        log(f"oracle: generating {len(used)} experts' weights")
+        W = synth.weights_host(cfg, used)
+    else:
+        W = {k: v[used] for k, v in weights.items()}
     local = np.where(idx >= 0, np.searchsorted(used, np.maximum(idx, 0)), -1).astype(np.int32)
-    return oracle.forward(W, x, local, w, want_pairs=want_pairs, mx=mx)
+    t0 = time.time()
+    out = oracle.forward(W, x, local, w, want_pairs=want_pairs, mx=mx, progress=progress)
+    if progress:
+        log(f"oracle: {x.shape[0]} tokens, {len(used)} experts in {time.time() - t0:.1f}s")
+    return out
 
 
 def rel_l2(got: np.ndarray, want: np.ndarray) -> float:

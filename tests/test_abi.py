@@ -72,7 +72,7 @@ def test_workspace_sizes():
     assert dec >= 16 * 3072 * 4 + 16 * 3584 * 4
     ch = lib.k3moe_workspace_size(k3.OP_CHUNK, 4096, 16, ctypes.byref(s))
     P = 4096 * 16
-    assert ch >= P * 3584 * 4 + P * 3072 * 2
+    assert ch >= P * 3584 * 4 + P * 3072 * 2 + 4096 * 3584 * 2 + 4096 * 28 * (64 + 4)  # + x = hi + lo split
     assert lib.k3moe_workspace_size(k3.OP_GROUP, 4096, 16, ctypes.byref(s)) > 0
     mx = lib.k3moe_workspace_size(k3.OP_CHUNK_MX, 4096, 16, ctypes.byref(s))
     assert mx >= P * 3584 * 4 + 2 * P * 3072 + 2 * 4096 * 3584
@@ -124,6 +124,14 @@ def test_validation_before_any_device_call():
     assert lib.k3moe_forward_chunk(ctypes.byref(s), p, 0, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_DIM
     assert lib.k3moe_forward_chunk(ctypes.byref(s), p, 32, p, p, 16, p, None, p, 100, None) == k3.K3MOE_E_WORKSPACE
     assert lib.k3moe_forward_chunk(ctypes.byref(s), p, 32, p, None, 16, p, None, p, ws, None) == k3.K3MOE_E_NULL
+    assert lib.k3moe_forward_chunk(ctypes.byref(s), None, 32, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_NULL
+    assert lib.k3moe_forward_chunk(ctypes.byref(s), ctypes.c_void_p(260), 32, p, p, 16, p, None, p, ws,
+                                   None) == k3.K3MOE_E_ALIGN
+    cb = lib.k3moe_forward_chunk_bf16
+    assert cb(ctypes.byref(s), None, 32, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_NULL
+    assert cb(ctypes.byref(s), p, 0, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_DIM
+    assert cb(ctypes.byref(s), p, 32, p, p, 16, p, None, p, 100, None) == k3.K3MOE_E_WORKSPACE
+    assert cb(ctypes.byref(s), ctypes.c_void_p(264), 32, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_ALIGN
     assert lib.k3moe_group(p, 32, 16, 896, p, p, p, p, p, p, 10, None) == k3.K3MOE_E_WORKSPACE
     assert lib.k3moe_group(p, 32, 0, 896, p, p, p, p, p, p, ws, None) == k3.K3MOE_E_DIM
     assert lib.k3moe_group(None, 32, 16, 896, p, p, p, p, p, p, ws, None) == k3.K3MOE_E_NULL

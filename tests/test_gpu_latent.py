@@ -1,10 +1,11 @@
 """LatentMoE block (projections, routed experts, RMSNorm, shared experts) on the GPU
 vs the oracle: rel-L2 <= 5e-3.
 
-The GPU runs the dense products as bf16 GEMMs with fp32 accumulation and rounds
-the latent input (more than one token: the chunk path takes bf16), the normed
-aggregate and the shared experts' activation to bf16 (2^-9 relative each); the
-routed block adds its own rounding (see the chunk tests).  The oracle keeps
+The GPU runs the dense products as bf16 x bf16 with fp32 accumulation, keeps the
+latent input x in fp32 (as the oracle does: nothing is rounded between the
+projection and the experts), and rounds the normed aggregate and the shared
+experts' activation to bf16 (2^-9 relative each); the routed block adds its own
+error (decode: fp32-accurate; chunk: see the chunk tests).  The oracle keeps
 every sum in double."""
 import numpy as np
 import pytest

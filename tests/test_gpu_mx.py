@@ -13,9 +13,10 @@ a property of the format on these weights, not of the kernels: x loses about 3%
 (rel-L2) to one E4M3 part, g and u inherit that as an absolute error of a few
 units (the synthetic gate/up outputs reach |g| ~ 200), and where g sits in the
 SiTU-GLU's transition region (|g| below ~5) that moves h across most of its
-range, so one part lands near 1e-1 on y.  Two parts keep about eight
-significant bits per value (2e-3 to 3e-3, the order of the 3.5e-3 the pages
-report for their per-32 int8 activations)."""
+range, so one part lands near 1e-1 on y.  Two parts keep about eight bits
+relative to each block's largest value; on fp32 activations that is 5.7e-3 to
+6.3e-3 at these shapes (bf16 rounding of x alone costs 7.3e-3 at the K3 shape),
+the order of the 3.5e-3 the pages report for their per-32 int8 activations."""
 import numpy as np
 import pytest
 
@@ -25,7 +26,7 @@ from gpu_helpers import assert_close, device_weights, log, oracle_forward_subset
 
 pytestmark = pytest.mark.gpu
 TOL_MX = {1: 5e-3, 2: 1e-3}       # vs the oracle's MXFP8 variant
-TOL_EXACT = {1: 2e-1, 2: 5e-3}    # vs the exact oracle
+TOL_EXACT = {1: 2e-1, 2: 1e-2}    # vs the exact oracle (a property of the format, see above)
 
 
 def _quant_gpu(v: np.ndarray, parts: int, bf16: bool = False):
@@ -76,7 +77,7 @@ def test_mx_quant_bit_exact(parts):
 
 
 def test_mx_quant_bf16_input():
-    """bf16 input quantizes as its fp32 value (the activations of the chunk path)."""
+    """bf16 input quantizes as its fp32 value."""
     torch = torch_cuda()
     v = np.random.default_rng(5).standard_normal(32 * 4096).astype(np.float32)
     vb = torch.from_numpy(v).to(torch.bfloat16).float().numpy()  # bf16 values, exactly
@@ -91,9 +92,8 @@ def _chunk_mx_gpu(W, x, idx, w, parts):
     torch = torch_cuda()
     from mxfp4_routed_expert_k3moe_amd import lib
     nu = torch.zeros(1, dtype=torch.int32, device="cuda")
-    xb = torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)  # exact: x holds bf16 values
-    assert np.array_equal(xb.float().cpu().numpy(), x)
-    y = lib.forward_chunk_mx(W, xb, torch.from_numpy(np.ascontiguousarray(idx)).cuda(),
+    xd = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    y = lib.forward_chunk_mx(W, xd, torch.from_numpy(np.ascontiguousarray(idx)).cuda(),
                              torch.from_numpy(np.ascontiguousarray(w)).cuda(), parts=parts, n_unique=nu)
     torch.cuda.synchronize()
     return y.cpu().numpy(), int(nu.item())
@@ -147,30 +147,36 @@ def test_chunk_mx_prefill256_sampled():
 
 def test_chunk_mx_batch4096_sampled():
     """The 4096-token launch.  Its edge experts carry scale bytes over the full
-    0..255 range: in this path a 255 group is NaN, and the NaN pattern of the
-    sampled tokens must match the oracle's MX reading."""
+    0..255 range, s = 255 included (closed form: those groups' zero codes are +-0,
+    which the scaled MFMA would read as NaN without the exact step body).  The MX
+    oracle computes 256 seeded tokens plus 64 edge-expert tokens."""
     cfg = synth.CONFIGS["batch4096"]
     x, logits, bias = synth.activations(cfg)
     idx, w, _ = oracle.route(logits, bias, cfg.K)
     W = device_weights(cfg)
-    log("chunk_mx batch4096: GPU run (parts=1)")
-    got, nu = _chunk_mx_gpu(W, x, idx, w, 1)
-    assert nu == len(np.unique(idx))
-    edge_tok = np.nonzero(np.isin(idx, cfg.edge_experts).any(axis=1))[0]
-    rng = np.random.default_rng(43)
-    pick_edge = rng.choice(edge_tok, size=min(16, len(edge_tok)), replace=False)
-    sample = synth.sample_tokens(cfg, 24, must_include=pick_edge, seed=2)
-    log(f"chunk_mx batch4096: union {nu}; oracle on {len(sample)} tokens")
-    want = oracle_forward_subset(cfg, x[sample], idx[sample], w[sample], mx=1)
-    assert_close(got[sample], want, TOL_MX[1], "chunk_mx batch4096 sample")
-    normal = np.setdiff1d(np.arange(cfg.T), edge_tok)
-    assert np.isfinite(got[normal]).all()
+    for parts in (1, 2):
+        log(f"chunk_mx batch4096: GPU run (parts={parts})")
+        got, nu = _chunk_mx_gpu(W, x, idx, w, parts)
+        assert nu == len(np.unique(idx))
+        assert np.isfinite(got).all()
+        edge_tok = np.nonzero(np.isin(idx, cfg.edge_experts).any(axis=1))[0]
+        pick_edge = np.random.default_rng(43).choice(edge_tok, size=min(64, len(edge_tok)), replace=False)
+        sample = synth.sample_tokens(cfg, 256, must_include=pick_edge, seed=2)
+        log(f"chunk_mx batch4096: union {nu}; MX oracle on {len(sample)} tokens")
+        want = oracle_forward_subset(cfg, x[sample], idx[sample], w[sample], mx=parts, progress=128)
+        assert_close(got[sample], want, TOL_MX[parts], f"chunk_mx batch4096 sample parts={parts}")
+        if parts == 2:
+            ref = oracle_forward_subset(cfg, x[sample], idx[sample], w[sample], progress=128)
+            ee = rel_l2(got[sample], ref)
+            log(f"chunk_mx batch4096 parts=2: rel-L2 vs exact oracle {ee:.3e}")
+            assert ee <= TOL_EXACT[2]
 
 
-def test_chunk_mx_weight_scale_255_is_nan():
-    """A down group with scale byte 255 and zero codes: NaN in the MX path for the
-    output row that reads it, exactly as the oracle's MX reading, while the bf16
-    path (closed form: 0 * 2^128 = 0) is unaffected."""
+def test_chunk_mx_weight_scale_255_closed_form():
+    """Weight groups with scale byte 255 follow the closed form (2^128 * v): zero
+    codes there give +-0, not the E8M0 NaN the scaled MFMA would produce, and codes
+    +-0.5 give +-2^127 (a gate group, so g saturates the activation instead of
+    overflowing a sum).  Both compared with the oracle's MX variant."""
     torch = torch_cuda()
     from mxfp4_routed_expert_k3moe_amd import lib
     cfg = synth.scaled(synth.CONFIGS["tiny"], T=40, path="chunk", name="mx255", weight_seed=77)
@@ -178,18 +184,27 @@ def test_chunk_mx_weight_scale_255_is_nan():
     x, logits, bias = synth.activations(cfg)
     idx, w, _ = oracle.route(logits, bias, cfg.K)
     e = int(idx[0, 0])
-    Wh["down_q"][e, 9, 16:32] = 0
+    Wh["down_q"][e, 9, 16:32] = 0x80  # codes 0 and 8
     Wh["down_s"][e, 9, 1] = 255
+    Wh["gate_q"][e, 3, 0:16] = 0x90   # codes 0 and 9: +0, -0.5
+    Wh["gate_s"][e, 3, 0] = 255
+    Wh["up_q"][e, 5, 32:48] = 0x08    # +0 and -0
+    Wh["up_s"][e, 5, 2] = 255
     W = lib.ExpertWeights.from_dict({k: torch.from_numpy(v).cuda() for k, v in Wh.items()})
     for parts in (1, 2):
         got, _ = _chunk_mx_gpu(W, x, idx, w, parts)
         want = oracle_forward_subset(cfg, x, idx, w, mx=parts, weights=Wh)
-        uses = (idx == e).any(axis=1)
-        assert np.isnan(got[uses, 9]).all() and np.isnan(want[uses, 9]).all()
+        assert np.isfinite(want).all()
         assert_close(got, want, TOL_MX[parts], f"chunk_mx scale-255 parts={parts}")
-    yb = lib.forward_chunk(W, torch.from_numpy(x).cuda().to(torch.bfloat16), torch.from_numpy(idx).cuda(),
+    # the bf16-MFMA path on the zero-code groups only: +-2^127 weights times N(0, 1)
+    # activations overflow its fp32 partial sums, whose infinity then takes the sign
+    # of whichever partial overflowed first (the oracle sums in double)
+    Wz = {k: v.copy() for k, v in Wh.items()}
+    Wz["gate_q"][e, 3, 0:16] = 0x80
+    Wzd = lib.ExpertWeights.from_dict({k: torch.from_numpy(v).cuda() for k, v in Wz.items()})
+    yb = lib.forward_chunk(Wzd, torch.from_numpy(x).cuda(), torch.from_numpy(idx).cuda(),
                            torch.from_numpy(w).cuda()).cpu().numpy()
-    assert np.isfinite(yb).all()
+    assert_close(yb, oracle_forward_subset(cfg, x, idx, w, weights=Wz), 5e-3, "chunk scale-255 (fp32 x)")
 
 
 def test_chunk_mx_pruned_and_invalid():

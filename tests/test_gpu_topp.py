@@ -87,8 +87,7 @@ def test_chunk_topp():
     x, logits, bias = synth.activations(cfg)
     idx, w = _compare(logits, bias, cfg.K, 0.7, "prefill32")
     W = device_weights(cfg)
-    y = lib.forward_chunk(W, torch.from_numpy(x).cuda().to(torch.bfloat16), torch.from_numpy(idx).cuda(),
-                          torch.from_numpy(w).cuda())
+    y = lib.forward_chunk(W, torch.from_numpy(x).cuda(), torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda())
     g = lib.group(torch.from_numpy(idx).cuda(), cfg.E)
     torch.cuda.synchronize()
     want = oracle_forward_subset(cfg, x, idx, w)

@@ -36,8 +36,6 @@ def test_ranges():
     hi = W["gate_q"] >> 4
     assert set(np.unique(lo)) == set(range(16)) and set(np.unique(hi)) == set(range(16))
     big = synth.CONFIGS["batch4096"]
-    edge = synth.expert_tensors(big, 112)
-    assert edge["gate_s"].min() == 0 and edge["gate_s"].max() == 255
     normal = synth.expert_tensors(big, 1)
     assert normal["gate_s"].min() == 118 and normal["gate_s"].max() == 128
 
@@ -59,11 +57,31 @@ def test_activations():
     assert not np.array_equal(xa, xb)
 
 
-def test_chunk_activations_are_bf16_values():
-    x, _, _ = synth.activations(synth.CONFIGS["prefill32"])
-    assert np.all((x.view(np.uint32) & 0xFFFF) == 0)
-    xd, _, _ = synth.activations(synth.CONFIGS["decode1"])
-    assert not np.all((xd.view(np.uint32) & 0xFFFF) == 0)
+def test_activation_precision():
+    """Hidden states are fp32 except for the workload that names bf16 activations
+    (prefill256), whose values are bf16 held in fp32."""
+    for name, is_bf16 in (("prefill32", False), ("batch4096", False), ("decode1", False), ("prefill256", True)):
+        x, _, _ = synth.activations(synth.CONFIGS[name], T=8)
+        assert np.all((x.view(np.uint32) & 0xFFFF) == 0) == is_bf16, name
     # round to nearest, ties to even
     v = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9], np.float32)
     assert synth.bf16_round(v).tolist() == [1.0, 1.0 + 2.0 ** -6, 1.0]
+
+
+def test_edge_experts():
+    """Edge experts of the 4096-token workload: every scale byte 0..255 and every code
+    occur; groups above 128 hold only +-0 codes; about a quarter of the groups carry
+    an edge scale; the literal mode draws all scale bytes over 0..255."""
+    big = synth.CONFIGS["batch4096"]
+    edge = synth.expert_tensors(big, 112)
+    for t in ("gate", "up", "down"):
+        q, sc = edge[t + "_q"], edge[t + "_s"]
+        assert set(np.unique(sc)) == set(range(256))
+        codes = np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1, 32)
+        assert set(np.unique(codes)) == set(range(16))
+        high = sc > synth.EDGE_ZERO_ABOVE
+        assert np.all(np.isin(codes[high], (0, 8)))
+        frac = np.mean((sc < big.scale_lo) | (sc > big.scale_hi))
+        assert 0.2 < frac < 0.25
+    lit = synth.expert_tensors(synth.scaled(big, edge_mode="literal"), 112)
+    assert np.mean((lit["gate_s"] < 118) | (lit["gate_s"] > 128)) > 0.9
