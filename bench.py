@@ -38,34 +38,42 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join("profiles", "decode_gateup_traffic.json")
-# sources whose change invalidates the counter figures
-TRAFFIC_SOURCES = ("mxfp4_routed_expert_k3moe_amd/csrc/decode.hip", "mxfp4_routed_expert_k3moe_amd/csrc/device.hpp",
-                   "mxfp4_routed_expert_k3moe_amd/csrc/launch.hpp")
+# counter summaries per kind, and the sources whose change invalidates them
+TRAFFIC_FILES = {"decode": os.path.join("profiles", "decode_gateup_traffic.json"),
+                 "chunk": os.path.join("profiles", "chunk_gemm_traffic.json")}
+TRAFFIC_SOURCES = {
+    "decode": ("mxfp4_routed_expert_k3moe_amd/csrc/decode.hip", "mxfp4_routed_expert_k3moe_amd/csrc/device.hpp",
+               "mxfp4_routed_expert_k3moe_amd/csrc/launch.hpp"),
+    "chunk": ("mxfp4_routed_expert_k3moe_amd/csrc/chunk.hip", "mxfp4_routed_expert_k3moe_amd/csrc/gemm.hpp",
+              "mxfp4_routed_expert_k3moe_amd/csrc/device.hpp", "mxfp4_routed_expert_k3moe_amd/csrc/launch.hpp")}
 PROBE_TOKENS = 8
 COPY_BYTES = 1 << 30
 
 
-def sources_digest() -> str:
+def sources_digest(kind: str = "decode") -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in TRAFFIC_SOURCES[kind]:
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def traffic_bytes():
-    """HBM bytes per decode gate/up launch from the committed counter runs, or None
-    when they are missing or were taken on other kernel sources."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+def traffic_record(kind: str = "decode"):
+    """The committed counter summary of `kind`, or None when it is missing or was
+    taken on other kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_FILES[kind])
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("sources_sha256") != sources_digest():
-        return None
-    return t.get("bytes_per_launch")
+    return t if t.get("sources_sha256") == sources_digest(kind) else None
+
+
+def traffic_bytes():
+    """HBM bytes per decode gate/up launch from the committed counter runs, or None."""
+    t = traffic_record("decode")
+    return None if t is None else t.get("bytes_per_launch")
 
 
 def tokens_per_expert(lib, idx, E):
@@ -94,23 +102,34 @@ def capture_steps(torch, fn, n):
     return g
 
 
-def timed_steps(torch, fn, n):
+def timed_steps(torch, fn, n, extra=0):
     """Seconds for the n calls fn(0) .. fn(n-1): one HIP graph replay (after an
     untimed one), or, if capture fails on this machine, the n calls issued eagerly
-    between two synchronizations.  Returns (seconds, mode)."""
+    between two synchronizations.  `extra` more timed repetitions follow the first
+    (replays, or eager passes) for the spread.  Returns (seconds, mode, [seconds of
+    each extra repetition])."""
     try:
         g = capture_steps(torch, fn, n)
     except RuntimeError as exc:
         torch.cuda.synchronize()
         log(f"graph capture failed ({exc}); timing eagerly")
-        t0 = time.perf_counter()
-        for i in range(n):
-            fn(i)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, "eager"
+        times = []
+        for _ in range(1 + extra):
+            t0 = time.perf_counter()
+            for i in range(n):
+                fn(i)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        return times[0], "eager", times[1:]
     el = timed_replay(torch, g)
+    more = []
+    for _ in range(extra):
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        more.append(time.perf_counter() - t0)
     del g
-    return el, "graph"
+    return el, "graph", more
 
 
 def timed_replay(torch, g):
@@ -122,6 +141,39 @@ def timed_replay(torch, g):
     g.replay()
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def chunk_algorithmic_bytes(cfg, U, T):
+    """Algorithmic HBM bytes of the two grouped GEMM launches of one fp32 chunk pass:
+    gate/up reads the union's gate and up tensors, x's bf16 high part, its MXFP4 low
+    part (codes and scales, rows padded to whole 128-column steps) and writes h (bf16,
+    one row per pair); down reads the down tensors and h and writes the per-pair fp32
+    rows."""
+    P = T * cfg.K
+    tensor = cfg.F * cfg.D // 2 + cfg.F * cfg.D // 32
+    steps = -(-cfg.D // 128)
+    gate_up = U * 2 * tensor + T * cfg.D * 2 + T * steps * (64 + 4) + P * cfg.F * 2
+    down = U * tensor + P * cfg.F * 2 + P * cfg.D * 4
+    return {"gemm_gateup": gate_up, "gemm_down": down}
+
+
+def counters_probe_chunk(torch, synth, lib, dev):
+    """A short run for rocprofv3 --pmc: the 4096-token fp32 chunk pass twice, then a
+    plain device copy of COPY_BYTES twice (the calibration)."""
+    cfg = synth.CONFIGS["batch4096"]
+    W = lib.ExpertWeights.from_dict(synth.weights_device(cfg, dev))
+    x, lg, bs = synth.activations(cfg)
+    xc = torch.from_numpy(x).to(dev)
+    idx, w = lib.route(torch.from_numpy(lg).to(dev), torch.from_numpy(bs).to(dev), cfg.K)
+    ws = torch.empty(lib.workspace_size(lib.OP_CHUNK, cfg.T, cfg.K, W), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        lib.forward_chunk(W, xc, idx, w, ws=ws)
+    a = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"chunk counters probe: 2 passes of {cfg.T} tokens, copy {COPY_BYTES} B x 2")
 
 
 def counters_probe(torch, synth, lib, dev):
@@ -163,25 +215,41 @@ def _pmc_rows(folder, counter):
     return rows
 
 
-def summarize_counters(fetch_dir, write_dir):
-    cfg_k, cfg_f, cfg_d = 16, 3072, 3584
-    algo = cfg_k * 2 * (cfg_f * cfg_d // 2 + cfg_f * cfg_d // 32) + cfg_d * 4 + cfg_k * cfg_f * 4
-    out = {"kernel": "decode_gateup_kernel", "algorithmic_bytes_per_launch": algo,
-           "sources_sha256": sources_digest(), "copy_bytes": COPY_BYTES}
-    per = {}
-    for key, folder, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
-        rows = _pmc_rows(folder, counter)
-        copy = [v for n, v in rows if "copy" in n.lower() and v > COPY_BYTES / 4]
-        gu = [v for n, v in rows if "decode_gateup_kernel" in n]
-        if not copy or not gu:
-            raise SystemExit(f"{counter}: copy dispatches {len(copy)}, gate/up dispatches {len(gu)}")
-        factor = COPY_BYTES / float(np.median(copy))
-        per[key] = {"counter": counter, "raw_bytes_per_launch": float(np.mean(gu)), "copy_raw_bytes": float(np.median(copy)),
-                    "calibration_factor": factor, "bytes_per_launch": float(np.mean(gu)) * factor, "launches": len(gu)}
-    out.update(per)
-    out["bytes_per_launch"] = round(per["fetch"]["bytes_per_launch"] + per["write"]["bytes_per_launch"])
-    out["traffic_over_algorithmic"] = round(out["bytes_per_launch"] / algo, 4)
-    with open(os.path.join(ROOT, TRAFFIC_FILE), "w") as fh:
+def _calibrated(rows, match, counter):
+    """Mean calibrated bytes per dispatch of the kernels whose name contains `match`."""
+    copy = [v for n, v in rows if "copy" in n.lower() and v > COPY_BYTES / 4]
+    ks = [v for n, v in rows if match in n]
+    if not copy or not ks:
+        raise SystemExit(f"{counter}: copy dispatches {len(copy)}, {match} dispatches {len(ks)}")
+    factor = COPY_BYTES / float(np.median(copy))
+    return {"counter": counter, "raw_bytes_per_launch": float(np.mean(ks)), "copy_raw_bytes": float(np.median(copy)),
+            "calibration_factor": factor, "bytes_per_launch": float(np.mean(ks)) * factor, "launches": len(ks)}
+
+
+def summarize_counters(fetch_dir, write_dir, kind="decode"):
+    if kind == "decode":
+        cfg_k, cfg_f, cfg_d = 16, 3072, 3584
+        algo = cfg_k * 2 * (cfg_f * cfg_d // 2 + cfg_f * cfg_d // 32) + cfg_d * 4 + cfg_k * cfg_f * 4
+        kernels = {"decode_gateup_kernel": ("decode_gateup_kernel", algo)}
+    else:
+        import synth
+        cfg = synth.CONFIGS["batch4096"]
+        algos = chunk_algorithmic_bytes(cfg, cfg.E, cfg.T)  # the 4096-token union is all 896 experts
+        kernels = {"gemm_gateup": ("gemm_kernel<0,", algos["gemm_gateup"]), "gemm_down": ("gemm_kernel<1,", algos["gemm_down"])}
+    out = {"kind": kind, "sources_sha256": sources_digest(kind), "copy_bytes": COPY_BYTES, "kernels": {}}
+    rows = {"fetch": _pmc_rows(fetch_dir, "FETCH_SIZE"), "write": _pmc_rows(write_dir, "WRITE_SIZE")}
+    for name, (match, algo) in kernels.items():
+        rows_n = {k: [(n.replace(" ", ""), v) for n, v in r] for k, r in rows.items()}
+        per = {key: _calibrated(rows_n[key], match.replace(" ", ""), cnt)
+               for key, cnt in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"))}
+        tot = round(per["fetch"]["bytes_per_launch"] + per["write"]["bytes_per_launch"])
+        out["kernels"][name] = dict(per, algorithmic_bytes_per_launch=algo, bytes_per_launch=tot,
+                                    traffic_over_algorithmic=round(tot / algo, 4))
+    if kind == "decode":  # flat fields read by the bench line
+        k = out["kernels"]["decode_gateup_kernel"]
+        out.update(kernel="decode_gateup_kernel", algorithmic_bytes_per_launch=k["algorithmic_bytes_per_launch"],
+                   bytes_per_launch=k["bytes_per_launch"], traffic_over_algorithmic=k["traffic_over_algorithmic"])
+    with open(os.path.join(ROOT, TRAFFIC_FILES[kind]), "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print(json.dumps(out, indent=1))
@@ -249,7 +317,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--chunk-iters", type=int, default=5)
+    ap.add_argument("--chunk-iters", type=int, default=10)
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-latent", action="store_true", help="skip the LatentMoE block legs")
@@ -257,13 +325,17 @@ def main():
     ap.add_argument("--top-p", type=float, default=0.7, help="also time decode with top-p pruning (0 = skip)")
     ap.add_argument("--pool-slots", type=int, default=128,
                     help="also time decode with experts in pinned host memory behind an HBM pool (0 = skip)")
-    ap.add_argument("--counters-probe", action="store_true",
-                    help="run only a few decode steps and the copy calibration (for rocprofv3 --pmc)")
+    ap.add_argument("--counters-probe", nargs="?", const="decode", choices=("decode", "chunk"),
+                    help="run only a few decode steps (or two 4096-token chunk passes) and the copy calibration "
+                         "(for rocprofv3 --pmc)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 --pmc output folders into " + TRAFFIC_FILE)
+                    help="turn two rocprofv3 --pmc output folders into the counter summary of --kind")
+    ap.add_argument("--kind", default="decode", choices=("decode", "chunk"))
+    ap.add_argument("--replays", type=int, default=0,
+                    help="extra timed replays of the K-step graph for the spread (default: enough for >= 50 steps)")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, kind=args.kind)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this block's kernels run on a single MI355X "
@@ -279,8 +351,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    if args.counters_probe:
+    if args.counters_probe == "decode":
         counters_probe(torch, synth, lib, dev)
+        return
+    if args.counters_probe == "chunk":
+        counters_probe_chunk(torch, synth, lib, dev)
         return
     peaks = achievable_peaks(torch, lib, dev)
 
@@ -325,11 +400,17 @@ def main():
     # timed region: exactly `steps` steps (token i % 32 at step i), captured as one
     # HIP graph and replayed between two synchronizations after an untimed replay
     y_d.zero_()
-    elapsed, mode = timed_steps(torch, lambda i: step(i % n_rot), args.steps)
-    replay_ok = bool(torch.equal(y_d.view(torch.int32), y_ref.view(torch.int32))) if args.steps >= n_rot else None
+    extra = args.replays if args.replays > 0 else max(4, -(-50 // args.steps))
+    elapsed, mode, more = timed_steps(torch, lambda i: step(i % n_rot), args.steps, extra)
+    # the tokens the timed steps ran (all 32 once K >= 32) against their eager outputs
+    n_chk = min(args.steps, n_rot)
+    replay_ok = bool(torch.equal(y_d[:n_chk].view(torch.int32), y_ref[:n_chk].view(torch.int32)))
     ms_per_step = elapsed * 1e3 / args.steps
     value = bytes_per_token * args.steps / elapsed / 1e9
-    log(f"decode: {mode} timing of {args.steps} steps, outputs equal to the eager ones: {replay_ok}")
+    spread = np.array([elapsed] + more) * 1e3 / args.steps  # ms per step of every timed repetition
+    log(f"decode: {mode} timing of {args.steps} steps, outputs of {n_chk} tokens equal to the eager ones: {replay_ok}; "
+        f"{len(spread)} repetitions: median {np.median(spread) * 1e3:.1f} us/step "
+        f"(p10 {np.percentile(spread, 10) * 1e3:.1f}, p90 {np.percentile(spread, 90) * 1e3:.1f})")
 
     # the gate/up kernel's own duration: eager steps whose gate/up launch records a
     # pair of events at the kernel's start and end (hipExtLaunchKernelGGL; each event
@@ -372,7 +453,13 @@ def main():
         "us_per_layer_token": round(ms_per_step * 1e3, 3),
         "timing": {"mode": ("the K steps captured as one HIP graph, one untimed replay, then one timed replay"
                             if mode == "graph" else "the K steps issued eagerly (graph capture failed)"),
-                   "replay_outputs_equal_eager": replay_ok},
+                   "replay_outputs_equal_eager": replay_ok, "replay_tokens_checked": n_chk,
+                   "repetitions": len(spread), "steps_timed_in_all": len(spread) * args.steps,
+                   "us_per_step_median": round(float(np.median(spread)) * 1e3, 3),
+                   "us_per_step_p10": round(float(np.percentile(spread, 10)) * 1e3, 3),
+                   "us_per_step_p90": round(float(np.percentile(spread, 90)) * 1e3, 3),
+                   "gateup_kernel_us_p10": round(float(np.percentile(gu_ms, 10)) * 1e3, 3),
+                   "gateup_kernel_us_p90": round(float(np.percentile(gu_ms, 90)) * 1e3, 3)},
         "roofline": {"bound": "hbm", "kernel": "decode_gateup_kernel (16 experts' gate/up GEMV + SiTU-GLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_bytes(),
@@ -398,7 +485,7 @@ def main():
         for i in range(args.warmup):
             step_topp(i % n_rot)
         torch.cuda.synchronize()
-        el, _ = timed_steps(torch, lambda i: step_topp(i % n_rot), args.steps)
+        el, _, _ = timed_steps(torch, lambda i: step_topp(i % n_rot), args.steps)
         kept_mean = float(np.mean([kept_all[i % n_rot] for i in range(args.steps)]))
         us = el * 1e6 / args.steps
         result["decode_topp"] = {"top_p": top_p, "mean_experts_kept": round(kept_mean, 3), "of": K,
@@ -473,7 +560,7 @@ def main():
             lib.latent_forward(Lw, W, h_l[j:j + 1], idx_l[j:j + 1], w_l[j:j + 1], out=out_l[j:j + 1], ws=ws_l)
         torch.cuda.synchronize()
         n_lat = min(args.steps, 64)
-        el_lat, _ = timed_steps(torch, lambda i: lib.latent_forward(Lw, W, h_l[i % n_rot:i % n_rot + 1],
+        el_lat, _, _ = timed_steps(torch, lambda i: lib.latent_forward(Lw, W, h_l[i % n_rot:i % n_rot + 1],
                                                                     idx_l[i % n_rot:i % n_rot + 1],
                                                                     w_l[i % n_rot:i % n_rot + 1],
                                                                     out=out_l[i % n_rot:i % n_rot + 1], ws=ws_l),
@@ -545,6 +632,7 @@ def main():
     torch.cuda.empty_cache()
 
     # -------------------------------------------------------------- chunk workload
+    chunk_outputs, chunk_sample = {}, None
     if not args.no_chunk:
         ccfg = synth.CONFIGS["batch4096"]
         log(f"generating {ccfg.name} weights")
@@ -555,78 +643,140 @@ def main():
         idx_c, w_c = lib.route(lg_c, bs_c, ccfg.K)
         yc = torch.empty((ccfg.T, ccfg.D), dtype=torch.float32, device=dev)
         nu = torch.zeros(1, dtype=torch.int32, device=dev)
-        wsc = torch.empty(lib.workspace_size(lib.OP_CHUNK, ccfg.T, ccfg.K, Wc), dtype=torch.uint8, device=dev)
-        lib.forward_chunk(Wc, xc, idx_c, w_c, y=yc, n_unique=nu, ws=wsc)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.chunk_iters):
-            lib.route(lg_c, bs_c, ccfg.K, idx=idx_c, w=w_c)
-            lib.forward_chunk(Wc, xc, idx_c, w_c, y=yc, n_unique=nu, ws=wsc)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.chunk_iters
-        U = int(nu.item())
         flops = 6.0 * ccfg.D * ccfg.F * ccfg.T * ccfg.K
-        wbytes = U * ccfg.expert_bytes()
-        result["chunk"] = {"workload": "batch4096: 4096 tokens, i.i.d. fp32 hidden states, logits = h.R, same "
-                                       "shape, bf16 MFMA grouped GEMM with the MXFP4 low part of x (route + group "
-                                       "+ split + gate/up + down + combine)",
-                           "ms": round(ms, 4), "us_per_layer_token": round(ms * 1e3 / ccfg.T, 4),
-                           "tflops": round(flops / ms / 1e9, 2),
-                           "tflops_frac_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
-                           "weight_gbs": round(wbytes / ms / 1e6, 1), "unique_experts": U,
-                           "tokens_per_expert": tokens_per_expert(lib, idx_c, ccfg.E)}
-        log(f"chunk: {ms:.3f} ms, {flops / ms / 1e9:.1f} TFLOP/s, union {U}")
+        # 16 seeded tokens whose outputs the CPU leg checks against the oracle
+        chunk_sample = np.sort(np.random.default_rng(4096).choice(ccfg.T, 16, replace=False))
+        chunk_outputs = {}
+
+        def time_passes(fn):
+            """Per-pass milliseconds of `chunk_iters` passes (route + fn), each
+            between its own pair of events, after one untimed pass."""
+            lib.route(lg_c, bs_c, ccfg.K, idx=idx_c, w=w_c)
+            fn()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.chunk_iters)]
+            for a, b in evs:
+                a.record(stream)
+                lib.route(lg_c, bs_c, ccfg.K, idx=idx_c, w=w_c)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) for a, b in evs])
+
+        def leg(ms_all, U, extra=None):
+            ms = float(np.median(ms_all))
+            wbytes = U * ccfg.expert_bytes()
+            d = {"ms": round(ms, 4), "ms_p10": round(float(np.percentile(ms_all, 10)), 4),
+                 "ms_p90": round(float(np.percentile(ms_all, 90)), 4), "passes": len(ms_all),
+                 "us_per_layer_token": round(ms * 1e3 / ccfg.T, 4), "tflops": round(flops / ms / 1e9, 2),
+                 "tflops_frac_bf16_peak": round(flops / ms / 1e9 / BF16_PEAK_TFLOPS, 4),
+                 "weight_gbs": round(wbytes / ms / 1e6, 1)}
+            d.update(extra or {})
+            return d
+
+        wsc = torch.empty(lib.workspace_size(lib.OP_CHUNK, ccfg.T, ccfg.K, Wc), dtype=torch.uint8, device=dev)
+        ms_all = time_passes(lambda: lib.forward_chunk(Wc, xc, idx_c, w_c, y=yc, n_unique=nu, ws=wsc))
+        U = int(nu.item())
+        chunk_outputs["chunk"] = yc[torch.from_numpy(chunk_sample).to(dev)].cpu().numpy()
+        tr = traffic_record("chunk")
+        result["chunk"] = leg(ms_all, U, {
+            "workload": "batch4096: 4096 tokens, i.i.d. fp32 hidden states, logits = h.R, same shape, bf16 MFMA "
+                        "grouped GEMM with the MXFP4 low part of x (route + group + split + gate/up + down + combine)",
+            "unique_experts": U, "tokens_per_expert": tokens_per_expert(lib, idx_c, ccfg.E),
+            "traffic": None if tr is None else {k: {"bytes_per_launch": v["bytes_per_launch"],
+                                                    "algorithmic_bytes_per_launch": v["algorithmic_bytes_per_launch"],
+                                                    "traffic_over_algorithmic": v["traffic_over_algorithmic"]}
+                                                for k, v in tr["kernels"].items()}})
+        log(f"chunk: {result['chunk']['ms']:.3f} ms (p10 {result['chunk']['ms_p10']:.3f}, p90 "
+            f"{result['chunk']['ms_p90']:.3f}), {result['chunk']['tflops']:.1f} TFLOP/s, union {U}")
         del wsc
         torch.cuda.empty_cache()
         # the same pass with MXFP8 activations on the scaled FP8 x FP4 MFMA, one and two parts
         wsm = torch.empty(lib.workspace_size(lib.OP_CHUNK_MX, ccfg.T, ccfg.K, Wc), dtype=torch.uint8, device=dev)
         result["chunk_mx"] = {"workload": "batch4096 as above, MXFP8 activations (E4M3 + E8M0 per 32) in one or "
                                           "two parts, scaled FP8 x FP4 MFMA (route + group + quantize + gate/up + "
-                                          "down + combine)"}
+                                          "down + combine); a lower-precision variant, its distance to the exact "
+                                          "block is in cpu_baseline.accuracy"}
         for parts in (1, 2):
-            lib.forward_chunk_mx(Wc, xc, idx_c, w_c, parts, y=yc, n_unique=nu, ws=wsm)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(args.chunk_iters):
-                lib.route(lg_c, bs_c, ccfg.K, idx=idx_c, w=w_c)
-                lib.forward_chunk_mx(Wc, xc, idx_c, w_c, parts, y=yc, n_unique=nu, ws=wsm)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            msm = e0.elapsed_time(e1) / args.chunk_iters
-            result["chunk_mx"][f"parts{parts}"] = {
-                "ms": round(msm, 4), "us_per_layer_token": round(msm * 1e3 / ccfg.T, 4),
-                "tflops": round(flops / msm / 1e9, 2),
-                "tflops_frac_fp8_peak": round(flops / msm / 1e9 / FP8_PEAK_TFLOPS, 4),
-                "tflops_frac_bf16_peak": round(flops / msm / 1e9 / BF16_PEAK_TFLOPS, 4),
-                "weight_gbs": round(wbytes / msm / 1e6, 1)}
-            log(f"chunk mx parts={parts}: {msm:.3f} ms, {flops / msm / 1e9:.1f} TFLOP/s")
+            ms_all = time_passes(lambda: lib.forward_chunk_mx(Wc, xc, idx_c, w_c, parts, y=yc, n_unique=nu, ws=wsm))
+            chunk_outputs[f"chunk_mx_parts{parts}"] = yc[torch.from_numpy(chunk_sample).to(dev)].cpu().numpy()
+            d = leg(ms_all, U)
+            d["tflops_frac_fp8_peak"] = round(d["tflops"] / FP8_PEAK_TFLOPS, 4)
+            result["chunk_mx"][f"parts{parts}"] = d
+            log(f"chunk mx parts={parts}: {d['ms']:.3f} ms, {d['tflops']:.1f} TFLOP/s")
         del Wc, wsm
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU baseline
+    # the oracle (plain C, double sums) on this host: the decode workload on the
+    # box's CPU share (16 threads for one GPU), one thread for the tiny and decode
+    # workloads, the near-tie count of each workload's routing, and the chunk legs'
+    # sampled outputs against the exact block
     if not args.no_cpu:
+        import platform
         import oracle
-        n_thr = oracle.default_threads()
+        n_thr = 16
+        try:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name"))
+        except (OSError, StopIteration):
+            cpu_model = platform.processor()
         xs_h, lg_h, bs_h = synth.activations(cfg, T=64, stream=9)
         idx_h, w_h, _ = oracle.route(lg_h, bs_h, K)
-        done, t_cpu = 0, 0.0
-        while done < 64 and t_cpu < args.cpu_seconds:
-            used = np.unique(idx_h[done])
-            Wh = synth.weights_host(cfg, used)
-            local = np.searchsorted(used, idx_h[done:done + 1]).astype(np.int32)
-            t0 = time.perf_counter()
-            oracle.forward(Wh, xs_h[done:done + 1], local, w_h[done:done + 1], nthreads=n_thr)
-            t_cpu += time.perf_counter() - t0
-            done += 1
+
+        def decode_tokens(nthreads, budget_s, max_tokens):
+            done, t_cpu = 0, 0.0
+            while done < max_tokens and t_cpu < budget_s:
+                used = np.unique(idx_h[done])
+                Wh = synth.weights_host(cfg, used)
+                local = np.searchsorted(used, idx_h[done:done + 1]).astype(np.int32)
+                t0 = time.perf_counter()
+                oracle.forward(Wh, xs_h[done:done + 1], local, w_h[done:done + 1], nthreads=nthreads)
+                t_cpu += time.perf_counter() - t0
+                done += 1
+            return done, t_cpu
+
+        done, t_cpu = decode_tokens(n_thr, args.cpu_seconds, 64)
         cpu_gbs = done * bytes_per_token / t_cpu / 1e9
-        result["cpu_baseline"] = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": n_thr, "kind": "oracle",
-                                  "sample": f"{done} decode1 tokens (16 experts each, route excluded), "
-                                            f"{t_cpu:.1f} s on {n_thr} threads",
-                                  "us_per_layer_token": round(t_cpu / done * 1e6, 1)}
-        log(f"cpu oracle: {cpu_gbs:.3f} GB/s over {done} tokens")
+        done1, t1 = decode_tokens(1, 6.0, 4)
+        tiny = synth.CONFIGS["tiny"]
+        Wt = synth.weights_host(tiny)
+        xt, lgt, bst = synth.activations(tiny, T=256, stream=3)
+        it, wt, _ = oracle.route(lgt, bst, tiny.K)
+        t0 = time.perf_counter()
+        oracle.forward(Wt, xt, it, wt, nthreads=1)
+        t_tiny = (time.perf_counter() - t0) / xt.shape[0]
+        near = {}
+        for name in ("decode1", "prefill32", "prefill256", "batch4096"):
+            c = synth.CONFIGS[name]
+            _, lgn, bsn = synth.activations(c, T=32 if name == "decode1" else None, stream=5 if name == "decode1" else 0)
+            _, _, gap = oracle.route(lgn, bsn, c.K)
+            near[name] = {"tokens": int(gap.size), "gap_below_1e-6": int(np.count_nonzero(gap < 1e-6))}
+        accuracy = {}
+        if chunk_outputs:
+            ccfg = synth.CONFIGS["batch4096"]
+            x_s, lg_s, bs_s = synth.activations(ccfg)
+            i_s, w_s, _ = oracle.route(lg_s[chunk_sample], bs_s, ccfg.K)
+            used = np.unique(i_s)
+            Ws = synth.weights_host(ccfg, used)
+            loc = np.searchsorted(used, i_s).astype(np.int32)
+            exact = oracle.forward(Ws, x_s[chunk_sample], loc, w_s, nthreads=n_thr).astype(np.float64)
+            for k, got in chunk_outputs.items():
+                accuracy[k] = float(np.linalg.norm(got - exact) / np.linalg.norm(exact))
+        result["cpu_baseline"] = {
+            "value": round(cpu_gbs, 4), "unit": "GB/s", "cores": n_thr, "kind": "oracle",
+            "sample": f"{done} decode1 tokens (16 experts each, route excluded), {t_cpu:.1f} s on {n_thr} threads "
+                      f"(the box's CPU share for one GPU)",
+            "us_per_layer_token": round(t_cpu / done * 1e6, 1),
+            "host": {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": cpu_model},
+            "one_thread": {"decode1_us_per_layer_token": round(t1 / done1 * 1e6, 1), "decode1_tokens": done1,
+                           "decode1_gbs": round(done1 * bytes_per_token / t1 / 1e9, 4),
+                           "tiny_us_per_token": round(t_tiny * 1e6, 2)},
+            "near_ties": near,
+            "accuracy": {"what": "rel-L2 of 16 seeded tokens of each 4096-token leg against the exact block "
+                                 "(the oracle on the fp32 hidden states)", **{k: round(v, 6) for k, v in accuracy.items()}}}
+        log(f"cpu oracle: {cpu_gbs:.3f} GB/s over {done} tokens on {n_thr} threads; one thread "
+            f"{t1 / done1 * 1e3:.0f} ms/token; near ties {near}; accuracy {accuracy}")
 
     print(json.dumps(result), flush=True)
 

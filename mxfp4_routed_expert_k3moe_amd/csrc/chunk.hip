@@ -586,6 +586,8 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
     // the expert's weight tensors: wave-uniform bases, per-lane 32-bit row offsets
     const char* qb0 = reinterpret_cast<const char*>(a.q0 + (size_t)e * a.q0_stride);
     const char* qb1 = (MODE == GATEUP) ? reinterpret_cast<const char*>(a.q1 + (size_t)e * a.q1_stride) : qb0;
+    // ring entry ns: 16-row subtile ns (GATEUP: gate 0, 1, up 2, 3), lane row ln,
+    // columns 32 * (lane / 16) of each step
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
         const int r = (MODE == GATEUP) ? n0 + 16 * (ns & 1) + ln : n0 + 16 * ns + ln;
@@ -593,15 +595,14 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
         st.qoff[ns] = (uint32_t)row * qrow;
         st.soff[ns] = (uint32_t)(tensor_of<MODE>(ns) * srows_real * sb + (row - nb0) * sb);
     }
-    {
-        const int lg = lane >> 4;
 #pragma unroll
-        for (int u = 0; u < NBB - 1; ++u) {
-            const int col = min(min(u, nsteps - 1) * KS + 32 * lg, Kdim - 32);
+    for (int u = 0; u < NBB - 1; ++u) {
 #pragma unroll
-            for (int ns = 0; ns < 4; ++ns)
-                st.bring[u][ns] = *reinterpret_cast<const uint4*>((tensor_of<MODE>(ns) ? qb1 : qb0) +
-                                                                  (st.qoff[ns] + (uint32_t)(col >> 1)));
+        for (int ns = 0; ns < 4; ++ns) {
+            const int c0 = 32 * (lane >> 4);
+            const int col = min(min(u, nsteps - 1) * KS + c0, Kdim - 32);
+            st.bring[u][ns] = *reinterpret_cast<const uint4*>((tensor_of<MODE>(ns) ? qb1 : qb0) +
+                                                              (st.qoff[ns] + (uint32_t)(col >> 1)));
         }
     }
     st.ap.load(a, st.areg[0], 0, Kdim);
