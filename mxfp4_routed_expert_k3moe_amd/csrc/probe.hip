@@ -55,7 +55,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // 2: scaled 16x16x128 FP4 x FP4; 3: scaled 16x16x128 FP8 x FP8;
 // 4: v_mfma_f32_32x32x16_bf16; 5: scaled 32x32x64 FP4 x FP4; 6: scaled 32x32x64 FP8 x FP4.
 template <int KIND>
-__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __restrict__ out) {
+__global__ __launch_bounds__(256, 2) void mfma_loop_kernel(int iters, float* __restrict__ out) {
     const int lane = threadIdx.x & 63;
     constexpr bool BIG = KIND >= 4;
     using acc_t = typename std::conditional<BIG, f32x16, f32x4>::type;
