@@ -52,12 +52,14 @@ extern "C" {
 #define K3MOE_E_WORKSPACE (-4)  /* workspace smaller than k3moe_workspace_size()      */
 #define K3MOE_E_DEVICE (-5)     /* current device is not gfx950                       */
 #define K3MOE_E_HIP (-6)        /* the HIP runtime reported an error at launch        */
+#define K3MOE_E_SCRATCH (-7)    /* the call needs more than the fixed scratch array   */
 
 /* Limits shared by the entry points. */
 #define K3MOE_MAX_K 64          /* experts per token                                  */
 #define K3MOE_PRUNED (-1)       /* routing slot dropped by top-p (k3moe_route_topp)   */
 #define K3MOE_MAX_E 4096        /* experts per layer                                  */
 #define K3MOE_MAX_DIM 8192      /* latent width D and expert width F                  */
+#define K3MOE_NOALLOC_SCRATCH_BYTES (2u << 20) /* per device, k3moe_forward_decode_noalloc */
 
 /* Workspace kinds for k3moe_workspace_size(). */
 #define K3MOE_OP_DECODE 1
@@ -162,6 +164,28 @@ int k3moe_group(const int32_t *idx, int32_t T, int32_t K, int32_t E, int32_t *co
 int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t *idx,
                          const float *w, int32_t K, float *y, void *ws, size_t ws_bytes,
                          void *stream);
+
+/*
+ * k3moe_forward_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid hipMalloc):
+ * the same kernels, arithmetic, results and errors, but the workspace is the
+ * library's own fixed scratch array of K3MOE_NOALLOC_SCRATCH_BYTES per device
+ * (a static device array, held by each device the library runs on until the
+ * process ends) instead of a caller buffer.  Nothing is allocated: no hipMalloc,
+ * no hipFree, no allocating library call.  The caller passes x, idx, w and y as
+ * for k3moe_forward_decode.
+ * K3MOE_E_SCRATCH if k3moe_workspace_size(K3MOE_OP_DECODE, 1, K, W) exceeds
+ * K3MOE_NOALLOC_SCRATCH_BYTES (2 MiB: up to K = 32 at D = F = 8192, K = 64 at the K3
+ * shape D = 3584, F = 3072), checked on the host before anything is launched.
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress, no allocation); make that first call outside stream
+ * capture.  Nothing in the scratch has to start at zero, so no call clears it.  Every call
+ * on one device shares that device's array: calls that overlap on one device
+ * (different streams, or different host threads without ordering) race and
+ * their outputs are undefined; calls ordered on one stream are safe.
+ */
+int k3moe_forward_decode_noalloc(const k3moe_weights_t *W, const float *x, const int32_t *idx,
+                                 const float *w, int32_t K, float *y, void *stream);
 
 /*
  * k3moe_forward_decode with its first kernel's duration recorded: ev_start and

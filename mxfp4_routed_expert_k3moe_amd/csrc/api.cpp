@@ -156,6 +156,24 @@ int k3moe_forward_decode(const k3moe_weights_t* W, const float* x, const int32_t
     return finish(k3moe::launch_decode(dw, x, idx, w, K, y, dws, static_cast<hipStream_t>(stream)));
 }
 
+int k3moe_forward_decode_noalloc(const k3moe_weights_t* W, const float* x, const int32_t* idx, const float* w,
+                                 int32_t K, float* y, void* stream) {
+    int rc = check_weights(W);
+    if (rc != K3MOE_OK) return rc;
+    if (!x || !idx || !w || !y) return K3MOE_E_NULL;
+    if (K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return K3MOE_E_DIM;
+    if (!aligned16(x)) return K3MOE_E_ALIGN;
+    if (k3moe::decode_workspace_bytes(K, W->d_model, W->d_ff) > K3MOE_NOALLOC_SCRATCH_BYTES) return K3MOE_E_SCRATCH;
+    rc = check_device();
+    if (rc != K3MOE_OK) return rc;
+    void* ws = nullptr;
+    hipError_t err = k3moe::noalloc_scratch(&ws);
+    if (err != hipSuccess) return hip_fail(err);
+    const DevWeights dw = dev_weights(W);
+    const k3moe::DecodeWorkspace dws = k3moe::decode_workspace_carve(ws, K, dw.D, dw.F);
+    return finish(k3moe::launch_decode(dw, x, idx, w, K, y, dws, static_cast<hipStream_t>(stream)));
+}
+
 int k3moe_forward_decode_timed(const k3moe_weights_t* W, const float* x, const int32_t* idx, const float* w,
                                int32_t K, float* y, void* ws, size_t ws_bytes, void* ev_start, void* ev_stop,
                                void* stream) {
@@ -321,6 +339,9 @@ const char* k3moe_status_string(int status) {
         case K3MOE_E_WORKSPACE: return "workspace smaller than k3moe_workspace_size()";
         case K3MOE_E_DEVICE: return "the current device is not gfx950";
         case K3MOE_E_HIP: return g_hip_msg[0] ? g_hip_msg : "HIP error";
+        case K3MOE_E_SCRATCH:
+            return "the call needs more device scratch than K3MOE_NOALLOC_SCRATCH_BYTES (use the entry point that takes "
+                   "a workspace)";
         default: return "unknown status";
     }
 }

@@ -28,6 +28,9 @@ struct DecodeWorkspace {
     float* ypart;  // [K, D]  down-projection outputs per slot
 };
 size_t decode_workspace_bytes(int K, int D, int F);
+// Address of the current device's fixed scratch array (K3MOE_NOALLOC_SCRATCH_BYTES),
+// looked up once per device; allocates nothing.
+hipError_t noalloc_scratch(void** out);
 DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F);
 // With both events given, the gate/up kernel is launched through
 // hipExtLaunchKernelGGL, which records ev_start as it starts and ev_stop as it ends.

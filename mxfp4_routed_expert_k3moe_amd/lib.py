@@ -22,6 +22,8 @@ K3MOE_E_ALIGN = -3
 K3MOE_E_WORKSPACE = -4
 K3MOE_E_DEVICE = -5
 K3MOE_E_HIP = -6
+K3MOE_E_SCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 2 << 20  # K3MOE_NOALLOC_SCRATCH_BYTES
 K3MOE_MAX_K = 64
 K3MOE_MAX_E = 4096
 K3MOE_MAX_DIM = 8192
@@ -36,7 +38,8 @@ ENTRY_POINTS = ("k3moe_route", "k3moe_route_topp", "k3moe_group", "k3moe_forward
                 "k3moe_status_string", "k3moe_slot_layout", "k3moe_pool_create", "k3moe_pool_destroy",
                 "k3moe_pool_plan", "k3moe_pool_weights", "k3moe_pool_stats", "k3moe_forward_decode_pooled",
                 "k3moe_forward_chunk_mx", "k3moe_mx_quant", "k3moe_latent_forward", "k3moe_latent_workspace_size",
-                "k3moe_forward_decode_timed", "k3moe_probe_stream_read", "k3moe_probe_mfma")
+                "k3moe_forward_decode_timed", "k3moe_probe_stream_read", "k3moe_probe_mfma",
+                "k3moe_forward_decode_noalloc")
 
 
 class K3moeError(RuntimeError):
@@ -78,6 +81,7 @@ def load() -> ctypes.CDLL:
     lib.k3moe_decode_gateup.argtypes = [wp, vp, vp, i32, vp, vp]
     lib.k3moe_forward_decode_timed.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp, vp, vp]
     lib.k3moe_decode_down.argtypes = [wp, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.k3moe_forward_decode_noalloc.argtypes = [wp, vp, vp, vp, i32, vp, vp]
     lib.k3moe_workspace_size.argtypes = [i32, i32, i32, wp]
     lib.k3moe_workspace_size.restype = sz
     lib.k3moe_dequant_mxfp4.argtypes = [vp, vp, i32, i32, vp, i32, vp]
@@ -264,6 +268,24 @@ def forward_decode(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torc
     _check("k3moe_forward_decode",
            load().k3moe_forward_decode(W.ref(), _ptr(x), _ptr(idx), _ptr(w), K, _ptr(y), _ptr(ws), ws.numel(),
                                        _stream(stream)))
+    return y
+
+
+def forward_decode_noalloc(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                           y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """forward_decode on the library's fixed per-device scratch (no workspace
+    argument; the C entry point allocates nothing -- pass ``y`` to allocate nothing
+    here either).  Calls that overlap on one device race."""
+    x = _dev(x.reshape(-1) if x.dim() == 2 and x.shape[0] == 1 else x, torch.float32, "x", (W.D,))
+    idx = idx.reshape(-1)
+    w = w.reshape(-1)
+    K = idx.numel()
+    _dev(idx, torch.int32, "idx", (K,))
+    _dev(w, torch.float32, "w", (K,))
+    y = torch.empty(W.D, dtype=torch.float32, device=x.device) if y is None else y
+    _dev(y, torch.float32, "y", (W.D,))
+    _check("k3moe_forward_decode_noalloc",
+           load().k3moe_forward_decode_noalloc(W.ref(), _ptr(x), _ptr(idx), _ptr(w), K, _ptr(y), _stream(stream)))
     return y
 
 

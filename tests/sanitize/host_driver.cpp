@@ -113,6 +113,18 @@ int main() {
           K3MOE_E_WORKSPACE);
     CHECK(k3moe_forward_decode(&w, (float*)260, (int32_t*)p, (float*)p, 16, (float*)p, p, ws, nullptr) == K3MOE_E_ALIGN);
     CHECK(k3moe_forward_decode(&bad_d, (float*)p, (int32_t*)p, (float*)p, 16, (float*)p, p, ws, nullptr) == K3MOE_E_DIM);
+    CHECK(k3moe_forward_decode_noalloc(nullptr, (float*)p, (int32_t*)p, (float*)p, 16, (float*)p, nullptr) ==
+          K3MOE_E_NULL);
+    CHECK(k3moe_forward_decode_noalloc(&w, (float*)p, (int32_t*)p, (float*)p, 0, (float*)p, nullptr) == K3MOE_E_DIM);
+    CHECK(k3moe_forward_decode_noalloc(&w, (float*)260, (int32_t*)p, (float*)p, 16, (float*)p, nullptr) ==
+          K3MOE_E_ALIGN);
+    {
+        k3moe_weights_t big = weights(8192, 8192, 896);
+        CHECK(k3moe_workspace_size(K3MOE_OP_DECODE, 1, 32, &big) <= K3MOE_NOALLOC_SCRATCH_BYTES);
+        CHECK(k3moe_forward_decode_noalloc(&big, (float*)p, (int32_t*)p, (float*)p, 33, (float*)p, nullptr) ==
+              K3MOE_E_SCRATCH);
+        CHECK(std::strlen(k3moe_status_string(K3MOE_E_SCRATCH)) > 20);
+    }
     CHECK(k3moe_forward_decode_timed(&w, (float*)p, (int32_t*)p, (float*)p, 16, (float*)p, p, ws, nullptr, p,
                                      nullptr) == K3MOE_E_NULL);
     CHECK(k3moe_decode_gateup(&w, nullptr, (int32_t*)p, 16, (float*)p, nullptr) == K3MOE_E_NULL);

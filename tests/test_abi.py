@@ -38,6 +38,9 @@ def test_header_constants_match_binding():
     assert int(consts["K3MOE_E_WORKSPACE"]) == k3.K3MOE_E_WORKSPACE
     assert int(consts["K3MOE_E_DEVICE"]) == k3.K3MOE_E_DEVICE
     assert int(consts["K3MOE_E_HIP"]) == k3.K3MOE_E_HIP
+    assert int(consts["K3MOE_E_SCRATCH"]) == k3.K3MOE_E_SCRATCH
+    assert re.search(r"#define K3MOE_NOALLOC_SCRATCH_BYTES \(2u << 20\)", text)
+    assert k3.NOALLOC_SCRATCH_BYTES == 2 << 20
     assert int(consts["K3MOE_MAX_K"]) == k3.K3MOE_MAX_K
     assert int(consts["K3MOE_PRUNED"]) == k3.PRUNED
     assert int(consts["K3MOE_OP_DECODE"]) == k3.OP_DECODE
@@ -48,7 +51,7 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert isinstance(k3.status_string(code), str)
     assert k3.status_string(0) == "ok"
 
@@ -114,6 +117,19 @@ def test_validation_before_any_device_call():
         setattr(bad_s, name + "_stride", 3584 * 3072 // 32 + 4)
         assert lib.k3moe_forward_chunk(ctypes.byref(bad_s), p, 32, p, p, 16, p, None, p, ws, None) == k3.K3MOE_E_ALIGN
     assert lib.k3moe_forward_decode(ctypes.byref(s), p, p, p, 16, p, p, 100, None) == k3.K3MOE_E_WORKSPACE
+    # the allocation-free forward: validation as forward_decode; a call whose
+    # workspace would exceed the fixed scratch array is refused on the host
+    na = lib.k3moe_forward_decode_noalloc
+    assert na(None, p, p, p, 16, p, None) == k3.K3MOE_E_NULL
+    assert na(ctypes.byref(s), p, p, None, 16, p, None) == k3.K3MOE_E_NULL
+    assert na(ctypes.byref(s), p, p, p, 0, p, None) == k3.K3MOE_E_DIM
+    assert na(ctypes.byref(s), p, p, p, 65, p, None) == k3.K3MOE_E_DIM
+    assert na(ctypes.byref(s), ctypes.c_void_p(260), p, p, 16, p, None) == k3.K3MOE_E_ALIGN
+    big = _struct(E=896, D=8192, F=8192)
+    assert lib.k3moe_workspace_size(k3.OP_DECODE, 1, 33, ctypes.byref(big)) > k3.NOALLOC_SCRATCH_BYTES
+    assert na(ctypes.byref(big), p, p, p, 33, p, None) == k3.K3MOE_E_SCRATCH
+    assert na(ctypes.byref(s), p, p, p, 64, p, None) != k3.K3MOE_E_SCRATCH  # K = 64 at the K3 shape fits
+    assert "K3MOE_NOALLOC_SCRATCH_BYTES" in k3.status_string(k3.K3MOE_E_SCRATCH)
     # the timed forward: both events are required, the rest as forward_decode
     t = lib.k3moe_forward_decode_timed
     assert t(ctypes.byref(s), p, p, p, 16, p, p, ws, None, p, None) == k3.K3MOE_E_NULL
