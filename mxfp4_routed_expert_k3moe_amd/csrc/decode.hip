@@ -44,6 +44,9 @@ namespace {
 constexpr int WAVES = kDecodeWaves;
 constexpr int ROWS_PER_BLOCK = WAVES * 16;
 constexpr int PD = 4;                // pipeline depth: steps of weights in flight per wave
+// Counters of the down kernel's folded combine: one per block of D rows, 64 words
+// apart (one per cache line: device-scope atomics on one line serialize).
+constexpr int CNT_STRIDE = 64;
 
 // LDS layout (uint16 elements): [part 0 | part 1 | part 2] each `pstride` long, then
 // an 8-element zero block.  pstride = padded columns + 8, so the three parts start
@@ -334,9 +337,12 @@ __device__ __forceinline__ void gateup_block(const DevWeights& W, const float* _
 template <bool DS>
 __global__ __launch_bounds__(WAVES * 64) void decode_gateup_kernel(DevWeights W, const float* __restrict__ x,
                                                             const int32_t* __restrict__ idx, int K, int split,
-                                                            float* __restrict__ h) {
+                                                            float* __restrict__ h, int32_t* __restrict__ cnt,
+                                                            int ncnt) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int g = blockIdx.x;
+    // the down kernel's combine counters (when folded) start this call at zero
+    if (cnt != nullptr && g == 0 && (int)threadIdx.x < ncnt) cnt[threadIdx.x * CNT_STRIDE] = 0;
     const int lane = threadIdx.x & 63;
     const int nblk = (W.F + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
     const int kf = min(g / nblk, K - 1);
@@ -364,11 +370,31 @@ constexpr int DOWN_TILES = 1;  // 16-row tiles of W_down per wave
 constexpr int DOWN_WAVES = 7;
 constexpr int DOWN_ROWS_PER_BLOCK = DOWN_WAVES * 16 * DOWN_TILES;
 
-template <bool DS>
+__host__ __device__ inline int down_blocks(int D) { return (D + DOWN_ROWS_PER_BLOCK - 1) / DOWN_ROWS_PER_BLOCK; }
+
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every memory operation this wave issued so far has completed (stores included)
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// FOLD: the combine is folded in.  Each workgroup writes its partial rows with
+// agent-scope stores, waits until they have completed, and counts itself in its
+// block's counter (device-scope atomic); the workgroup that brings the count to
+// the number of kept slots has seen every partial of the block completed, and
+// forms y there in slot order with agent-scope loads (the same fmaf chain as
+// decode_combine_kernel, so the same bits).  The counters start at zero: the
+// gate/up kernel of the same call clears them.
+template <bool DS, bool FOLD>
 __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DevWeights W, const int32_t* __restrict__ idx,
                                                           const float* __restrict__ h,
-                                                          float* __restrict__ ypart) {
+                                                          float* __restrict__ ypart, const float* __restrict__ wts,
+                                                          int K, float* __restrict__ y, int32_t* __restrict__ cnt) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    __shared__ int s_last;
     const int k = blockIdx.y;
     const int lane = threadIdx.x & 63, ln = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -376,7 +402,17 @@ __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DevWeights
     const int dblk = blockIdx.x * DOWN_ROWS_PER_BLOCK;
     const int d0 = dblk + wave * 16 * DOWN_TILES;
     const int e = idx[k];
-    if (e == K3MOE_PRUNED) return;  // block-uniform
+    if (e == K3MOE_PRUNED) {  // block-uniform; a pruned slot is not counted
+        if (FOLD && k == 0 && threadIdx.x < 64) {
+            // every slot pruned: no workgroup counts, so slot 0's write y = 0 (the
+            // combine of no slots)
+            const int v = (int)threadIdx.x < K ? idx[threadIdx.x] : K3MOE_PRUNED;
+            if (__ballot(v != K3MOE_PRUNED) == 0ull) {
+                for (int d = dblk + (int)threadIdx.x; d < min(dblk + DOWN_ROWS_PER_BLOCK, D); d += 64) y[d] = 0.0f;
+            }
+        }
+        return;
+    }
     const bool valid_e = e >= 0 && e < W.E;
     const int ec = valid_e ? e : 0;
     uint8_t* slds = reinterpret_cast<uint8_t*>(lds) + parts_lds_bytes(F);
@@ -398,20 +434,67 @@ __global__ __launch_bounds__(DOWN_WAVES * 64) void decode_down_kernel(DevWeights
     st.store(lds);
     sd.store(slds);
     __syncthreads();
-    if (d0 >= D) return;
     float* yk = ypart + (size_t)k * D;
-    if (!valid_e) {
-        for (int t = 0; t < DOWN_TILES; ++t)
-            if (lane < 16 && d0 + 16 * t < D) yk[d0 + 16 * t + lane] = __builtin_nanf("");
-        return;
+    if constexpr (!FOLD) {
+        if (d0 >= D) return;
+        if (!valid_e) {
+            for (int t = 0; t < DOWN_TILES; ++t)
+                if (lane < 16 && d0 + 16 * t < D) yk[d0 + 16 * t + lane] = __builtin_nanf("");
+            return;
+        }
     }
-    f32x4 acc[DOWN_TILES];
+    float pv[DOWN_TILES];
 #pragma unroll
-    for (int t = 0; t < DOWN_TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    rs.run(lds, acc);
+    for (int t = 0; t < DOWN_TILES; ++t) pv[t] = __builtin_nanf("");  // an id out of range: NaN rows
+    if (valid_e && d0 < D) {  // wave-uniform
+        f32x4 acc[DOWN_TILES];
 #pragma unroll
-    for (int t = 0; t < DOWN_TILES; ++t)
-        if (lane < 16 && d0 + 16 * t < D) yk[d0 + 16 * t + lane] = (acc[t][0] + acc[t][1]) + acc[t][2];
+        for (int t = 0; t < DOWN_TILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        rs.run(lds, acc);
+#pragma unroll
+        for (int t = 0; t < DOWN_TILES; ++t) pv[t] = (acc[t][0] + acc[t][1]) + acc[t][2];
+    }
+#pragma unroll
+    for (int t = 0; t < DOWN_TILES; ++t) {
+        if (lane < 16 && d0 + 16 * t < D) {
+            if constexpr (FOLD) st_agent(yk + d0 + 16 * t + lane, pv[t]);
+            else yk[d0 + 16 * t + lane] = pv[t];
+        }
+    }
+    if constexpr (FOLD) {
+        wait_memory();
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            // kept slots of the token (the workgroups that count themselves)
+            const int v = (int)threadIdx.x < K ? idx[threadIdx.x] : K3MOE_PRUNED;
+            const int m = __popcll(__ballot(v != K3MOE_PRUNED));
+            if (threadIdx.x == 0)
+                s_last = __hip_atomic_fetch_add(cnt + (size_t)blockIdx.x * CNT_STRIDE, 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) == m - 1;
+        }
+        __syncthreads();
+        if (s_last && threadIdx.x < DOWN_ROWS_PER_BLOCK) {
+            const int d = dblk + (int)threadIdx.x;
+            if (d < D) {
+                float acc = 0.0f;
+                for (int k0 = 0; k0 < K; k0 += 16) {
+                    float v[16], wk[16];
+                    int id[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {  // the group's loads in flight together
+                        const int kk = min(k0 + i, K - 1);
+                        id[i] = idx[kk];
+                        wk[i] = wts[kk];
+                        v[i] = ld_agent(ypart + (size_t)kk * D + d);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (k0 + i < K && id[i] != K3MOE_PRUNED) acc = fmaf(wk[i], v[i], acc);
+                }
+                y[d] = acc;
+            }
+        }
+    }
 }
 
 // y[d] = sum over slots in order of w_k * part[k, d]; pruned slots are skipped.
@@ -444,7 +527,7 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t decode_workspace_bytes(int K, int D, int F) {
-    return align256((size_t)K * F * 4) + align256((size_t)K * D * 4);
+    return align256((size_t)K * F * 4) + align256((size_t)K * D * 4) + align256((size_t)down_blocks(D) * CNT_STRIDE * 4);
 }
 
 DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F) {
@@ -453,12 +536,14 @@ DecodeWorkspace decode_workspace_carve(void* ws, int K, int D, int F) {
     r.h = reinterpret_cast<float*>(p);
     p += align256((size_t)K * F * 4);
     r.ypart = reinterpret_cast<float*>(p);
-    (void)D;
+    p += align256((size_t)K * D * 4);
+    r.cnt = reinterpret_cast<int32_t*>(p);
     return r;
 }
 
 hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32_t* idx, int K, float* h,
-                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop, int split) {
+                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop, int split,
+                                int32_t* cnt) {
     const dim3 grid(2 * K * ((W.F + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK));
     const size_t lds = decode_lds_bytes(W.D, 2) + SPLIT_MERGE_BYTES;
     // dword scale copies need every scale row and expert block 4-byte aligned
@@ -467,21 +552,24 @@ hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32
     const auto kernel = dw ? decode_gateup_kernel<true> : decode_gateup_kernel<false>;
     if (ev_start != nullptr && ev_stop != nullptr)
         hipExtLaunchKernelGGL(kernel, grid, dim3(WAVES * 64), (uint32_t)lds, stream, ev_start, ev_stop, 0, W, x, idx,
-                              K, split, h);
+                              K, split, h, cnt, down_blocks(W.D));
     else
-        hipLaunchKernelGGL(kernel, grid, dim3(WAVES * 64), lds, stream, W, x, idx, K, split, h);
+        hipLaunchKernelGGL(kernel, grid, dim3(WAVES * 64), lds, stream, W, x, idx, K, split, h, cnt, down_blocks(W.D));
     return hipGetLastError();
 }
 
 hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t* idx, const float* w, int K,
-                              float* ypart, float* y, hipStream_t stream) {
-    const dim3 grid((W.D + DOWN_ROWS_PER_BLOCK - 1) / DOWN_ROWS_PER_BLOCK, K);
+                              float* ypart, float* y, hipStream_t stream, int32_t* cnt) {
+    const dim3 grid(down_blocks(W.D), K);
     const size_t lds = parts_lds_bytes(W.F) + (size_t)DOWN_ROWS_PER_BLOCK * (W.F / 32) + 16;
     const bool dw = (W.F % 128 == 0) && W.down_s_stride % 4 == 0 && (reinterpret_cast<uintptr_t>(W.down_s) & 3) == 0;
-    if (dw)
-        hipLaunchKernelGGL(decode_down_kernel<true>, grid, dim3(DOWN_WAVES * 64), lds, stream, W, idx, h, ypart);
-    else
-        hipLaunchKernelGGL(decode_down_kernel<false>, grid, dim3(DOWN_WAVES * 64), lds, stream, W, idx, h, ypart);
+    if (cnt != nullptr) {  // combine folded in (the counters were cleared by this call's gate/up kernel)
+        const auto kernel = dw ? decode_down_kernel<true, true> : decode_down_kernel<false, true>;
+        hipLaunchKernelGGL(kernel, grid, dim3(DOWN_WAVES * 64), lds, stream, W, idx, h, ypart, w, K, y, cnt);
+        return hipGetLastError();
+    }
+    const auto kernel = dw ? decode_down_kernel<true, false> : decode_down_kernel<false, false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(DOWN_WAVES * 64), lds, stream, W, idx, h, ypart, w, K, y, cnt);
     hipLaunchKernelGGL(decode_combine_kernel, dim3((W.D + 255) / 256), dim3(256), 0, stream, ypart, w, idx, K, W.D, y);
     return hipGetLastError();
 }
@@ -489,9 +577,9 @@ hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t
 hipError_t launch_decode(const DevWeights& W, const float* x, const int32_t* idx, const float* w, int K,
                          float* y, const DecodeWorkspace& ws, hipStream_t stream, hipEvent_t ev_start,
                          hipEvent_t ev_stop) {
-    hipError_t err = launch_decode_gateup(W, x, idx, K, ws.h, stream, ev_start, ev_stop);
+    hipError_t err = launch_decode_gateup(W, x, idx, K, ws.h, stream, ev_start, ev_stop, -1, ws.cnt);
     if (err != hipSuccess) return err;
-    return launch_decode_down(W, ws.h, idx, w, K, ws.ypart, y, stream);
+    return launch_decode_down(W, ws.h, idx, w, K, ws.ypart, y, stream, ws.cnt);
 }
 
 }  // namespace k3moe

@@ -26,6 +26,7 @@ constexpr int kDecodeWaves = 4;  // gate/up waves per workgroup (16 weight rows 
 struct DecodeWorkspace {
     float* h;      // [K, F]  SiTU-GLU outputs per slot
     float* ypart;  // [K, D]  down-projection outputs per slot
+    int32_t* cnt;  // counters of the down kernel's folded combine (cleared by gate/up)
 };
 size_t decode_workspace_bytes(int K, int D, int F);
 // Address of the current device's fixed scratch array (K3MOE_NOALLOC_SCRATCH_BYTES),
@@ -44,9 +45,11 @@ hipError_t launch_decode(const DevWeights& W, const float* x, const int32_t* idx
 // token's own choice, so every part sums in the token's order).
 hipError_t launch_decode_gateup(const DevWeights& W, const float* x, const int32_t* idx, int K, float* h,
                                 hipStream_t stream, hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
-                                int split = -1);
+                                int split = -1, int32_t* cnt = nullptr);
+// cnt (from the same call's gate/up launch, which cleared it): the combine is folded
+// into the down kernel; nullptr: a separate combine kernel.
 hipError_t launch_decode_down(const DevWeights& W, const float* h, const int32_t* idx, const float* w, int K,
-                              float* ypart, float* y, hipStream_t stream);
+                              float* ypart, float* y, hipStream_t stream, int32_t* cnt = nullptr);
 
 // ------------------------------------------------------------------ chunk
 constexpr int kGroupTokens = 64;   // tokens per grouping block (one u64 mask bit each)

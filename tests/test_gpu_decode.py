@@ -81,7 +81,34 @@ def test_decode_deterministic_and_invalid_index():
     bad[1] = cfg.E + 3
     y = _decode_gpu(W, x[0], bad, w[0])
     assert np.all(np.isnan(y))
+    # every slot pruned: y = 0 (the combine of no slot)
+    y = _decode_gpu(W, x[0], np.full_like(idx[0], -1), w[0])
+    assert np.all(y == 0.0)
     del torch
+
+
+def test_decode_workspace_garbage_and_reuse():
+    """The down kernel's combine counters live in the workspace: a workspace full of
+    garbage, and one reused by consecutive calls (tokens with different kept-slot
+    counts), give the same bits as fresh workspaces."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = synth.CONFIGS["decode1"]
+    W = device_weights(cfg)
+    x, logits, bias = synth.activations(cfg, T=3, stream=22)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    idx[1, 3] = -1  # a token with a pruned slot between two full ones
+    w[1, 3] = 0.0
+    ws = torch.empty(lib.workspace_size(lib.OP_DECODE, 1, cfg.K, W), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)
+    for t in range(3):
+        xd, idd, wd = (torch.from_numpy(np.ascontiguousarray(a[t])).cuda() for a in (x, idx, w))
+        got = lib.forward_decode(W, xd, idd, wd, ws=ws)
+        fresh = lib.forward_decode(W, xd, idd, wd)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), fresh.cpu().numpy().view(np.uint32)), t
+        want = oracle_forward_subset(cfg, x[t:t + 1], idx[t:t + 1], w[t:t + 1])[0]
+        assert_close(got.cpu().numpy(), want, TOL, f"decode reused workspace token {t}")
 
 
 def test_decode_stages_match_oracle():
