@@ -124,23 +124,37 @@ def timed_steps(torch, fn, n, extra=0):
     el = timed_replay(torch, g)
     more = []
     for _ in range(extra):
-        t0 = time.perf_counter()
-        g.replay()
         torch.cuda.synchronize()
-        more.append(time.perf_counter() - t0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        WALL.append(time.perf_counter() - t0)
+        more.append(e0.elapsed_time(e1) * 1e-3)
     del g
     return el, "graph", more
 
 
 def timed_replay(torch, g):
     """One untimed replay (the first one uploads the graph), then one timed replay
-    between two synchronizations; returns seconds."""
+    between two synchronizations; returns seconds of GPU time (events recorded on
+    the stream around the replay) and records the host clock's reading of the same
+    bracket in WALL."""
     g.replay()
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    WALL.append(time.perf_counter() - t0)
+    return e0.elapsed_time(e1) * 1e-3
+
+
+WALL = []  # host-clock seconds of each timed replay, in order
 
 
 def chunk_algorithmic_bytes(cfg, U, T):
@@ -400,7 +414,9 @@ def main():
     # HIP graph and replayed between two synchronizations after an untimed replay
     y_d.zero_()
     extra = args.replays if args.replays > 0 else max(4, -(-50 // args.steps))
+    n_wall = len(WALL)
     elapsed, mode, more = timed_steps(torch, lambda i: step(i % n_rot), args.steps, extra)
+    wall = np.array(WALL[n_wall:]) * 1e3 / args.steps  # host-clock ms per step of the same replays
     # the tokens the timed steps ran (all 32 once K >= 32) against their eager outputs
     n_chk = min(args.steps, n_rot)
     replay_ok = bool(torch.equal(y_d[:n_chk].view(torch.int32), y_ref[:n_chk].view(torch.int32)))
@@ -452,6 +468,10 @@ def main():
         "us_per_layer_token": round(ms_per_step * 1e3, 3),
         "timing": {"mode": ("the K steps captured as one HIP graph, one untimed replay, then one timed replay"
                             if mode == "graph" else "the K steps issued eagerly (graph capture failed)"),
+                   "clock": ("GPU time between events recorded on the stream around each replay, with a "
+                             "device synchronization before and after" if mode == "graph" else "host clock"),
+                   "wall_us_per_step_first": round(float(wall[0]) * 1e3, 3) if len(wall) else None,
+                   "wall_us_per_step_median": round(float(np.median(wall)) * 1e3, 3) if len(wall) else None,
                    "replay_outputs_equal_eager": replay_ok, "replay_tokens_checked": n_chk,
                    "repetitions": len(spread), "steps_timed_in_all": len(spread) * args.steps,
                    "us_per_step_median": round(float(np.median(spread)) * 1e3, 3),
