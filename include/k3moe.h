@@ -59,7 +59,7 @@ extern "C" {
 #define K3MOE_PRUNED (-1)       /* routing slot dropped by top-p (k3moe_route_topp)   */
 #define K3MOE_MAX_E 4096        /* experts per layer                                  */
 #define K3MOE_MAX_DIM 8192      /* latent width D and expert width F                  */
-#define K3MOE_NOALLOC_SCRATCH_BYTES (2u << 20) /* per device, k3moe_forward_decode_noalloc */
+#define K3MOE_NOALLOC_SCRATCH_BYTES ((2u << 20) + (64u << 10)) /* per device, k3moe_forward_decode_noalloc */
 
 /* Workspace kinds for k3moe_workspace_size(). */
 #define K3MOE_OP_DECODE 1
@@ -175,11 +175,14 @@ int k3moe_forward_decode(const k3moe_weights_t *W, const float *x, const int32_t
  * no hipFree, no allocating library call.  The caller passes x, idx, w and y as
  * for k3moe_forward_decode.
  * K3MOE_E_SCRATCH if k3moe_workspace_size(K3MOE_OP_DECODE, 1, K, W) exceeds
- * K3MOE_NOALLOC_SCRATCH_BYTES (2 MiB: up to K = 32 at D = F = 8192, K = 64 at the K3
- * shape D = 3584, F = 3072), checked on the host before anything is launched.
+ * K3MOE_NOALLOC_SCRATCH_BYTES (2 MiB + 64 KiB: h, the per-slot partials and the
+ * combine counters of up to K = 32 at D = F = 8192, or K = 64 at the K3 shape
+ * D = 3584, F = 3072), checked on the host before anything is launched.
  * The first call on a device looks up that device's copy of the array
  * (hipGetSymbolAddress, no allocation); make that first call outside stream
- * capture.  Nothing in the scratch has to start at zero, so no call clears it.  Every call
+ * capture.  Nothing in the scratch has to be zero before a call: the counters
+ * the down kernel uses are cleared by the same call's gate/up kernel (a kernel
+ * store, not a memset), the rest is written before it is read.  Every call
  * on one device shares that device's array: calls that overlap on one device
  * (different streams, or different host threads without ordering) race and
  * their outputs are undefined; calls ordered on one stream are safe.

@@ -23,7 +23,7 @@ K3MOE_E_WORKSPACE = -4
 K3MOE_E_DEVICE = -5
 K3MOE_E_HIP = -6
 K3MOE_E_SCRATCH = -7
-NOALLOC_SCRATCH_BYTES = 2 << 20  # K3MOE_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = (2 << 20) + (64 << 10)  # K3MOE_NOALLOC_SCRATCH_BYTES
 K3MOE_MAX_K = 64
 K3MOE_MAX_E = 4096
 K3MOE_MAX_DIM = 8192

@@ -39,8 +39,8 @@ def test_header_constants_match_binding():
     assert int(consts["K3MOE_E_DEVICE"]) == k3.K3MOE_E_DEVICE
     assert int(consts["K3MOE_E_HIP"]) == k3.K3MOE_E_HIP
     assert int(consts["K3MOE_E_SCRATCH"]) == k3.K3MOE_E_SCRATCH
-    assert re.search(r"#define K3MOE_NOALLOC_SCRATCH_BYTES \(2u << 20\)", text)
-    assert k3.NOALLOC_SCRATCH_BYTES == 2 << 20
+    assert re.search(r"#define K3MOE_NOALLOC_SCRATCH_BYTES \(\(2u << 20\) \+ \(64u << 10\)\)", text)
+    assert k3.NOALLOC_SCRATCH_BYTES == (2 << 20) + (64 << 10)
     assert int(consts["K3MOE_MAX_K"]) == k3.K3MOE_MAX_K
     assert int(consts["K3MOE_PRUNED"]) == k3.PRUNED
     assert int(consts["K3MOE_OP_DECODE"]) == k3.OP_DECODE
