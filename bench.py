@@ -159,14 +159,13 @@ WALL = []  # host-clock seconds of each timed replay, in order
 
 def chunk_algorithmic_bytes(cfg, U, T):
     """Algorithmic HBM bytes of the two grouped GEMM launches of one fp32 chunk pass:
-    gate/up reads the union's gate and up tensors, x's bf16 high part, its MXFP4 low
-    part (codes and scales, rows padded to whole 128-column steps) and writes h (bf16,
-    one row per pair); down reads the down tensors and h and writes the per-pair fp32
-    rows."""
+    gate/up reads the union's gate and up tensors and x once as 16-bit values (the
+    fp16 items read x in fp16; the few items on the bf16 path read its high part and
+    low part instead) and writes h (16-bit, one row per pair); down reads the down
+    tensors and h and writes the per-pair fp32 rows."""
     P = T * cfg.K
     tensor = cfg.F * cfg.D // 2 + cfg.F * cfg.D // 32
-    steps = -(-cfg.D // 128)
-    gate_up = U * 2 * tensor + T * cfg.D * 2 + T * steps * (64 + 4) + P * cfg.F * 2
+    gate_up = U * 2 * tensor + T * cfg.D * 2 + P * cfg.F * 2
     down = U * tensor + P * cfg.F * 2 + P * cfg.D * 4
     return {"gemm_gateup": gate_up, "gemm_down": down}
 
@@ -698,8 +697,9 @@ def main():
         chunk_outputs["chunk"] = yc[torch.from_numpy(chunk_sample).to(dev)].cpu().numpy()
         tr = traffic_record("chunk")
         result["chunk"] = leg(ms_all, U, {
-            "workload": "batch4096: 4096 tokens, i.i.d. fp32 hidden states, logits = h.R, same shape, bf16 MFMA "
-                        "grouped GEMM with the MXFP4 low part of x (route + group + split + gate/up + down + combine)",
+            "workload": "batch4096: 4096 tokens, i.i.d. fp32 hidden states, logits = h.R, same shape, grouped MFMA "
+                        "GEMMs: fp16 (x and h in fp16) on items whose weights are fp16 normals, bf16 with the MXFP4 "
+                        "low part of x elsewhere (route + group + split + gate/up + down + combine)",
             "unique_experts": U, "tokens_per_expert": tokens_per_expert(lib, idx_c, ccfg.E),
             "traffic": None if tr is None else {k: {"bytes_per_launch": v["bytes_per_launch"],
                                                     "algorithmic_bytes_per_launch": v["algorithmic_bytes_per_launch"],

@@ -226,14 +226,18 @@ int k3moe_decode_down(const k3moe_weights_t *W, const float *h, const int32_t *i
  * unique expert of a chunk is loaded once and run for every position routed to
  * it): the pairs are grouped by expert (k3moe_group), each routed expert's
  * weights are streamed once per group of up to 96 of its tokens, and gate/up and
- * down run as bf16 MFMA matrix products with fp32 accumulation.  The decoded
- * weights are exact in bf16.  x [T, D] is fp32: it is split exactly into
- * hi = bf16(x) and lo = x - hi; hi enters the bf16 product, lo (below 2^-9 |x|)
- * a second product in MXFP4 (e2m1 codes, one power-of-two scale per 32 columns)
- * against the weights' own FP4 codes, summed into the same fp32 accumulators.
- * h is rounded to bf16 (round to nearest even) between the two products.  The
- * combine sums w_{t,k} * y_{t,k} in slot order in fp32.  The result is within
- * about 2e-3 (relative L2) of the exact block at the K3 shape.
+ * down run as MFMA matrix products with fp32 accumulation.  x [T, D] is fp32.  A
+ * work item (a tile of one expert's pairs and a block of output columns) whose
+ * weights all decode to fp16 normals (scale bytes 114..140) multiplies on the fp16
+ * MFMA: x rounded to fp16 (RNE) and h rounded to fp16 between the two products,
+ * the weights exact.  Any other item (other scale bytes, or some |x| beyond the
+ * fp16 range) multiplies on the bf16 MFMA: x split exactly into hi = bf16(x) and
+ * lo = x - hi, hi in the bf16 product, lo (below 2^-9 |x|) in a second product in
+ * MXFP4 (e2m1 codes, one power-of-two scale per 32 columns) against the weights'
+ * own FP4 codes, summed into the same fp32 accumulators; its down product takes h
+ * rounded to bf16.  The combine sums w_{t,k} * y_{t,k} in slot order in fp32.  The
+ * result is within about 1e-3 (relative L2) of the exact block at the K3 shape
+ * (1.5e-3 on the bf16 items).
  * x [T, D] fp32 (16-byte aligned), idx [T, K] int32 (K3MOE_PRUNED slots skipped),
  * w [T, K] fp32, y [T, D] fp32; n_unique (device int32, nullable) receives the
  * union size, or -1 for invalid routing, in which case every element of y is NaN.
@@ -245,7 +249,8 @@ int k3moe_forward_chunk(const k3moe_weights_t *W, const float *x, int32_t T, con
 
 /*
  * k3moe_forward_chunk for activations that are already bf16 (raw 16-bit
- * patterns, [T, D], 16-byte aligned): the same path without the low part.  Same
+ * patterns, [T, D], 16-byte aligned): every item on the bf16 MFMA without a low
+ * part, h rounded to bf16.  Same
  * arguments, workspace (K3MOE_OP_CHUNK), outputs and errors.
  */
 int k3moe_forward_chunk_bf16(const k3moe_weights_t *W, const uint16_t *x, int32_t T, const int32_t *idx,

@@ -14,9 +14,9 @@
 //                  and the GEMM tile list (expert, first row, rows)
 //   group_scatter  pair p = t*K+k goes to offsets[e] + (pairs of e in earlier
 //                  blocks) + popcount(mask & bits below t): a stable counting sort
-//   xsplit         (fp32 x) x = hi + lo: hi = bf16(x), and the exact residual lo
-//                  as MXFP4 codes with one E8M0 scale per 32 (see below)
-//   gemm<GATEUP>   h = SiTU(x W_gate^T, x W_up^T) per tile, bf16 MFMA, h in bf16
+//   xsplit         (fp32 x) fp16(x); and x = hi + lo: hi = bf16(x), the exact
+//                  residual lo as MXFP4 codes with one E8M0 scale per 32 (below)
+//   gemm<GATEUP>   h = SiTU(x W_gate^T, x W_up^T) per tile (fp32 x: h in fp16)
 //   gemm<DOWN>     y_pair = w_pair * (h W_down^T), fp32, at row p = t*K+k
 //   combine        y_t = sum_k y_pair[t*K+k] in slot order
 //
@@ -36,7 +36,16 @@
 //   so each XCD walks a contiguous run of (tile, column block) items: the column
 //   blocks of one tile share that XCD's L2 copy of the tile's activations.
 //
-// fp32 activations.  Rounding x to bf16 alone would move the block's output by
+// fp32 activations.  A work item whose weights all decode to fp16 normals (every
+// staged scale byte in 114..140: 0.5 * 2^(s-127) >= 2^-14, 6 * 2^(s-127) <= 65504)
+// runs on v_mfma_f32_16x16x32_f16 with x and h rounded to fp16 (11 significant
+// bits): the weights are exact in fp16, and the block output sits about 9e-4 from
+// the exact one at the K3 shape (CPU emulation).  The test is per item, over the
+// scale rows it stages anyway; an item that fails it (other scale bytes, byte 255,
+// a ragged step, or some |x| past the fp16 range, flagged by the split) takes the
+// bf16 path below, with h converted from fp16 to bf16 as its down item stages it.
+//
+// Rounding x to bf16 alone would move the block's output by
 // about 7e-3 (rel-L2) on the K3-shape weights: where g = W_gate x sits in the
 // SiTU-GLU's transition region, an error of 2^-9 |x| in every input shifts h by a
 // large share of its range.  So x is split exactly, x = hi + lo with hi = bf16(x),
@@ -176,6 +185,7 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(int T, int K, int E, i
         const int nu = s_err ? -1 : ui;
         scalars[0] = nu;
         scalars[1] = s_err ? 0 : min(nti, max_tiles);
+        scalars[2] = 0;  // raised by the x split when some |x| overflows fp16
         if (n_unique_out) *n_unique_out = nu;
     }
 }
@@ -204,7 +214,9 @@ __global__ __launch_bounds__(256) void group_scatter_kernel(const int32_t* __res
 enum { GATEUP = 0, DOWN = 1 };
 
 struct GemmArgs {
-    const uint16_t* A;      // GATEUP: x bf16 [T, Kdim] by token; DOWN: h bf16 [P, Kdim] by grouped row
+    const uint16_t* A;      // GATEUP: x bf16 [T, Kdim] by token (the high part for fp32 x);
+                            // DOWN: h [P, Kdim] by grouped row (fp16 after an fp32-x gate/up, else bf16)
+    const uint16_t* A16;    // GATEUP of fp32 x: x rounded to fp16 [T, Kdim]
     const uint8_t* alo;     // GATEUP with a low part: x - bf16(x) as FP4 codes [T, nsteps * 64]
     const uint8_t* alos;    //   and their E8M0 scales [T, nsteps * 4] (rows padded with zero codes)
     const int32_t* perm;    // grouped row -> pair id
@@ -214,9 +226,9 @@ struct GemmArgs {
     int Kdim;               // reduction length (multiple of 32, <= 8192)
     int N;                  // output columns per expert (multiple of 32)
     const int4* tiles;
-    const int32_t* scalars;  // [1] = number of tiles
+    const int32_t* scalars;  // [1] = number of tiles, [2] = some |x| overflows fp16
     int nblk_n;             // column blocks
-    uint16_t* h_out;        // GATEUP output [P, N] bf16, grouped rows
+    uint16_t* h_out;        // GATEUP output [P, N] (fp16 in the fp32-x kernels, else bf16), grouped rows
     float* y_out;           // DOWN output [P, N] fp32, pair rows
     const float* wts;       // DOWN: [P] routing weight of each pair
 };
@@ -271,20 +283,32 @@ struct APieces {
             roff[i] = row * (uint32_t)a.Kdim * 2u;
         }
     }
-    __device__ __forceinline__ void load(const GemmArgs& a, uint4 (&v)[SLOTS], int step, int Kdim) const {
+    // rows of A (16-bit elements, [rows, Kdim]) at the offsets computed by init
+    __device__ __forceinline__ void load(const uint16_t* A, uint4 (&v)[SLOTS], int step, int Kdim) const {
         const uint32_t c = 2u * (uint32_t)min(step * KS + 8 * seg, Kdim - 8);
-        const char* base = reinterpret_cast<const char*>(a.A);
+        const char* base = reinterpret_cast<const char*>(A);
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) v[i] = *reinterpret_cast<const uint4*>(base + (roff[i] + c));
     }
+    // CVT: the loaded elements are fp16 and are stored as bf16 (round to nearest even)
+    template <bool CVT = false>
     __device__ __forceinline__ void store(const uint4 (&v)[SLOTS], uint8_t* buf, int step, int Kdim) const {
         // mask word by word: a select between two uint4 objects would keep the
         // register arrays in memory
         const uint32_t m = step * KS + 8 * seg < Kdim ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int i = 0; i < SLOTS; ++i)
+        for (int i = 0; i < SLOTS; ++i) {
+            uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            if constexpr (CVT) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const f16x2 hv = __builtin_bit_cast(f16x2, w[d]);
+                    w[d] = f32_to_bf16_bits((float)hv[0]) | (f32_to_bf16_bits((float)hv[1]) << 16);
+                }
+            }
             *reinterpret_cast<uint4*>(buf + row_of(i) * A_ROW + 16 * (seg ^ key)) =
-                make_uint4(v[i].x & m, v[i].y & m, v[i].z & m, v[i].w & m);
+                make_uint4(w[0] & m, w[1] & m, w[2] & m, w[3] & m);
+        }
     }
 };
 
@@ -375,10 +399,20 @@ __device__ __forceinline__ v8i fp4_operand(const u32x4& q) {
 // A(t + 1) into buffer (t + 1) % 2 (read last in step t - 1); barrier.  All loads
 // are ordinary vector loads, so the compiler's per-register waits stay exact
 // across the loop.
-template <int MODE, int MT, int CW, int NBB, bool LO, int MS, bool EXACT>
+//
+// BODY: B_BF16 -- bf16 A and weights on v_mfma_f32_16x16x32_bf16 (plus the low
+// part of x when the state has one); B_F16 -- fp16 A and weights on
+// v_mfma_f32_16x16x32_f16 (every weight of the item an fp16 normal, no low part);
+// B_CVT -- as B_BF16 with A loaded as fp16 and stored as bf16.  H16: the gate/up
+// output h is stored as fp16 (else bf16).  asrc: the rows A is loaded from.
+enum { B_BF16 = 0, B_F16 = 1, B_CVT = 2 };
+template <int MODE, int MT, int CW, int NBB, bool LO, int MS, bool EXACT, int BODY, bool H16>
 __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT, CW, NBB, LO>& st, uint8_t* alds,
                                            uint8_t* llds, const uint8_t* slds, const char* qb0, const char* qb1,
-                                           const int32_t* rperm, const float* rw, int row0, int mrows, int nb0) {
+                                           const int32_t* rperm, const float* rw, int row0, int mrows, int nb0,
+                                           const uint16_t* asrc) {
+    static_assert(!(EXACT && BODY == B_F16), "fp16 items are never exact");
+    constexpr bool DO_LO = LO && BODY == B_BF16;  // the low part of x enters with the bf16 high part
     using SH = GemmShape<MODE, CW>;
     constexpr int WN = SH::WN;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -403,7 +437,7 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
     for_steps<(NBB % 2 == 0) ? NBB : 2 * NBB>(nsteps, [&](auto uc, const int step) {
         constexpr int u = decltype(uc)::value;
         constexpr int AS = GemmState<MODE, MT, CW, NBB, LO>::AS;
-        if constexpr (AS == 2) st.ap.load(a, st.areg[u & 1], min(step + 2, nsteps - 1), Kdim);
+        if constexpr (AS == 2) st.ap.load(asrc, st.areg[u & 1], min(step + 2, nsteps - 1), Kdim);
         {
             const int col = min((step + NBB - 1) * KS + 32 * lg, Kdim - 32);
 #pragma unroll
@@ -424,7 +458,7 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
         float scf[4];
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns) scf[ns] = scale_operand(sc[ns]);
-        if constexpr (LO) {
+        if constexpr (DO_LO) {
             // the low part of x: FP4 x FP4 with both E8M0 scales, into the same
             // accumulators; the weight chunk is the B operand as loaded
             const uint8_t* lbuf = llds + (size_t)(u & 1) * MT * (LO_ROW + 4);
@@ -462,34 +496,51 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            bf16x8 bop[4];
-#pragma unroll
-            for (int ns = 0; ns < 4; ++ns) {
-                if constexpr (EXACT)
-                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16(valid ? pick(st.bring[u % NBB][ns], j) : 0u, sc[ns]));
-                else
-                    bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16_nofix(pick(st.bring[u % NBB][ns], j), scf[ns]));
-            }
-#pragma unroll
-            for (int i = 0; i < MS; ++i) {
-                const bf16x8 aop =
-                    *reinterpret_cast<const bf16x8*>(abuf + (16 * i + ln) * A_ROW + 16 * ((4 * lg + j) ^ akey));
+            if constexpr (BODY == B_F16) {
+                f16x8 bop[4];
 #pragma unroll
                 for (int ns = 0; ns < 4; ++ns)
-                    acc[i][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[ns], acc[i][ns], 0, 0, 0);
+                    bop[ns] = __builtin_bit_cast(f16x8, fp4x8_to_f16_nofix(pick(st.bring[u % NBB][ns], j), scf[ns]));
+#pragma unroll
+                for (int i = 0; i < MS; ++i) {
+                    const f16x8 aop =
+                        *reinterpret_cast<const f16x8*>(abuf + (16 * i + ln) * A_ROW + 16 * ((4 * lg + j) ^ akey));
+#pragma unroll
+                    for (int ns = 0; ns < 4; ++ns)
+                        acc[i][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[ns], acc[i][ns], 0, 0, 0);
+                }
+            } else {
+                bf16x8 bop[4];
+#pragma unroll
+                for (int ns = 0; ns < 4; ++ns) {
+                    if constexpr (EXACT)
+                        bop[ns] = __builtin_bit_cast(bf16x8,
+                                                     fp4x8_to_bf16(valid ? pick(st.bring[u % NBB][ns], j) : 0u, sc[ns]));
+                    else
+                        bop[ns] = __builtin_bit_cast(bf16x8, fp4x8_to_bf16_nofix(pick(st.bring[u % NBB][ns], j), scf[ns]));
+                }
+#pragma unroll
+                for (int i = 0; i < MS; ++i) {
+                    const bf16x8 aop =
+                        *reinterpret_cast<const bf16x8*>(abuf + (16 * i + ln) * A_ROW + 16 * ((4 * lg + j) ^ akey));
+#pragma unroll
+                    for (int ns = 0; ns < 4; ++ns)
+                        acc[i][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[ns], acc[i][ns], 0, 0, 0);
+                }
             }
             // keep the scheduler from hoisting the next sub-step's operand reads
             // (registers for them would push the weight ring out of VGPRs)
             __builtin_amdgcn_sched_barrier(0);
         }
-        st.ap.store(st.areg[(u + 1) % AS], alds + (size_t)((step + 1) & 1) * MT * A_ROW, step + 1, Kdim);
-        if constexpr (LO) {
+        st.ap.template store<BODY == B_CVT>(st.areg[(u + 1) % AS], alds + (size_t)((step + 1) & 1) * MT * A_ROW,
+                                            step + 1, Kdim);
+        if constexpr (DO_LO) {
             uint8_t* lb = llds + (size_t)((step + 1) & 1) * MT * (LO_ROW + 4);
             st.lp.store(st.lreg[0], st.lsreg[0], lb, lb + MT * LO_ROW);
         }
         if constexpr (AS == 1) {  // the next step's activations, one step ahead
-            st.ap.load(a, st.areg[0], min(step + 2, nsteps - 1), Kdim);
-            if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(step + 2, nsteps - 1));
+            st.ap.load(asrc, st.areg[0], min(step + 2, nsteps - 1), Kdim);
+            if constexpr (DO_LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(step + 2, nsteps - 1));
         }
         lds_barrier();
     });
@@ -505,8 +556,11 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
             if (MODE == GATEUP) {
                 uint16_t* hrow = a.h_out + (size_t)(row0 + m) * N;
 #pragma unroll
-                for (int ns = 0; ns < 2; ++ns)
-                    hrow[n0 + 16 * ns + ln] = (uint16_t)f32_to_bf16_bits(situ_fast(acc[i][ns][r], acc[i][ns + 2][r]));
+                for (int ns = 0; ns < 2; ++ns) {
+                    const float hv = situ_fast(acc[i][ns][r], acc[i][ns + 2][r]);
+                    hrow[n0 + 16 * ns + ln] = H16 ? __builtin_bit_cast(uint16_t, (_Float16)hv)
+                                                  : (uint16_t)f32_to_bf16_bits(hv);
+                }
             } else {
                 const int p = rperm[m];
                 const float wp = rw[m];
@@ -517,6 +571,37 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
             }
         }
     }
+}
+
+// Scale bytes whose e2m1 values are all fp16 normals: 0.5 * 2^(s-127) >= 2^-14 and
+// 6 * 2^(s-127) <= 65504.
+constexpr uint32_t kF16ScaleLo = 114, kF16ScaleHi = 140;
+
+// Any staged scale byte equal to 255 among this thread's 16-byte pieces.
+__device__ __forceinline__ int scales_have_255(const uint8_t* slds, int stotal, int nthreads) {
+    int has = 0;
+    for (int c = threadIdx.x; c < stotal; c += nthreads) {
+        const uint4 v = *reinterpret_cast<const uint4*>(slds + 16 * c);
+        const uint32_t w4[4] = {~v.x, ~v.y, ~v.z, ~v.w};  // 255 -> zero byte
+#pragma unroll
+        for (int d = 0; d < 4; ++d) has |= ((w4[d] - 0x01010101u) & ~w4[d] & 0x80808080u) != 0u;
+    }
+    return has;
+}
+
+// Any staged scale byte outside [lo, hi] among this thread's 16-byte pieces.
+__device__ __forceinline__ int scales_outside(const uint8_t* slds, int stotal, int nthreads, uint32_t lo,
+                                              uint32_t hi) {
+    uint32_t bad = 0;
+    for (int c = threadIdx.x; c < stotal; c += nthreads) {
+        const uint4 v = *reinterpret_cast<const uint4*>(slds + 16 * c);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bad |= (uint32_t)(((w4[d] >> (8 * b)) & 0xFFu) - lo > hi - lo);
+    }
+    return (int)bad;
 }
 
 // One workgroup = one (tile of <= MT pair rows of one expert, block of BN output
@@ -530,7 +615,7 @@ __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT
 //   - one barrier per step; the scale bytes of the workgroup's weight rows are
 //     copied to LDS up front, while the first activation and weight loads are
 //     already in flight.
-template <int MODE, int MT, int CW, int NBB, bool LO>
+template <int MODE, int MT, int CW, int NBB, bool LO, bool F16K>
 __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
     using SH = GemmShape<MODE, CW>;
     using ST = GemmState<MODE, MT, CW, NBB, LO>;
@@ -605,71 +690,133 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
                                                               (st.qoff[ns] + (uint32_t)(col >> 1)));
         }
     }
-    st.ap.load(a, st.areg[0], 0, Kdim);
-    if constexpr (ST::AS == 2) st.ap.load(a, st.areg[1], min(1, nsteps - 1), Kdim);
-    if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], 0);
     if (MODE == DOWN && tid < mrows) {  // pair id and routing weight of each tile row
         const int p = a.perm[row0 + tid];
         rperm[tid] = p;
         rw[tid] = a.wts[p];
     }
-    st.ap.store(st.areg[0], alds, 0, Kdim);
-    if constexpr (LO) st.lp.store(st.lreg[0], st.lsreg[0], llds, llds + MT * LO_ROW);
-    if constexpr (ST::AS == 1) {  // step 1's activations into the one register set
-        st.ap.load(a, st.areg[0], min(1, nsteps - 1), Kdim);
-        if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(1, nsteps - 1));
-    }
-    __syncthreads();  // scales, the first A buffer and the row table are in LDS
-
-    // ---- any scale byte equal to 255 in the staged rows?
-    int has255 = 0;
-    for (int c = tid; c < stotal; c += THREADS) {
-        const uint4 v = *reinterpret_cast<const uint4*>(slds + 16 * c);
-        const uint32_t w4[4] = {~v.x, ~v.y, ~v.z, ~v.w};  // 255 -> zero byte
-#pragma unroll
-        for (int d = 0; d < 4; ++d) has255 |= ((w4[d] - 0x01010101u) & ~w4[d] & 0x80808080u) != 0u;
-    }
-    const bool exact = __syncthreads_or(has255) != 0 || (Kdim % KS) != 0;
-
-    if (exact) {
-        gemm_steps<MODE, MT, CW, NBB, LO, MT / 16, true>(a, st, alds, llds, slds, qb0, qb1, rperm, rw, row0, mrows,
-                                                         nb0);
-        return;
-    }
-    // tiles hold at most MT rows; the clamp keeps every wave on a path with the
-    // same barrier count even if that were ever violated
     const int msub = min((mrows + 15) >> 4, MT / 16);
-#define K3_TILE_CASE(MSV)                                                                       \
-    case MSV:                                                                                   \
-        if constexpr (MSV <= MT / 16)                                                           \
-            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false>(a, st, alds, llds, slds, qb0, qb1, rperm, rw, row0, \
-                                                          mrows, nb0);                                      \
+
+    if constexpr (!F16K) {
+        // bf16 activations: their first steps go out before the scale check
+        st.ap.load(a.A, st.areg[0], 0, Kdim);
+        if constexpr (ST::AS == 2) st.ap.load(a.A, st.areg[1], min(1, nsteps - 1), Kdim);
+        if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], 0);
+        st.ap.store(st.areg[0], alds, 0, Kdim);
+        if constexpr (LO) st.lp.store(st.lreg[0], st.lsreg[0], llds, llds + MT * LO_ROW);
+        if constexpr (ST::AS == 1) {  // step 1's activations into the one register set
+            st.ap.load(a.A, st.areg[0], min(1, nsteps - 1), Kdim);
+            if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(1, nsteps - 1));
+        }
+        __syncthreads();  // scales, the first A buffer and the row table are in LDS
+        const bool exact = __syncthreads_or(scales_have_255(slds, stotal, THREADS)) != 0 || (Kdim % KS) != 0;
+        if (exact) {
+            gemm_steps<MODE, MT, CW, NBB, LO, MT / 16, true, B_BF16, false>(a, st, alds, llds, slds, qb0, qb1, rperm,
+                                                                           rw, row0, mrows, nb0, a.A);
+            return;
+        }
+#define K3_TILE_CASE(MSV)                                                                                        \
+    case MSV:                                                                                                    \
+        if constexpr (MSV <= MT / 16)                                                                            \
+            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, B_BF16, false>(a, st, alds, llds, slds, qb0, qb1, rperm, \
+                                                                         rw, row0, mrows, nb0, a.A);             \
         break;
-    switch (msub) {
-        K3_TILE_CASE(1)
-        K3_TILE_CASE(2)
-        K3_TILE_CASE(3)
-        K3_TILE_CASE(4)
-        K3_TILE_CASE(5)
-        K3_TILE_CASE(6)
-        K3_TILE_CASE(7)
-        K3_TILE_CASE(8)
-        default: break;
-    }
+        switch (msub) {
+            K3_TILE_CASE(1)
+            K3_TILE_CASE(2)
+            K3_TILE_CASE(3)
+            K3_TILE_CASE(4)
+            K3_TILE_CASE(5)
+            K3_TILE_CASE(6)
+            K3_TILE_CASE(7)
+            K3_TILE_CASE(8)
+            default: break;
+        }
 #undef K3_TILE_CASE
+    } else {
+        // fp32 x (gate/up) or the fp16 h it produced (down): the item runs on the
+        // fp16 MFMA when every weight it reads is an fp16 normal (scale bytes 114..140),
+        // no |x| overflows fp16 and the steps are whole; else on bf16 (x: the bf16
+        // high part plus the MXFP4 low part; h: converted to bf16 as it is staged)
+        __syncthreads();  // the scales and the row table are in LDS
+        const bool f16 = __syncthreads_or(scales_outside(slds, stotal, THREADS, kF16ScaleLo, kF16ScaleHi)) == 0 &&
+                         (Kdim % KS) == 0 && (MODE == DOWN || a.scalars[2] == 0);
+        if (f16) {
+            const uint16_t* src = MODE == GATEUP ? a.A16 : a.A;
+            st.ap.load(src, st.areg[0], 0, Kdim);
+            if constexpr (ST::AS == 2) st.ap.load(src, st.areg[1], min(1, nsteps - 1), Kdim);
+            st.ap.store(st.areg[0], alds, 0, Kdim);
+            if constexpr (ST::AS == 1) st.ap.load(src, st.areg[0], min(1, nsteps - 1), Kdim);
+            __syncthreads();
+#define K3_TILE_CASE(MSV)                                                                                      \
+    case MSV:                                                                                                  \
+        if constexpr (MSV <= MT / 16)                                                                          \
+            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, B_F16, true>(a, st, alds, llds, slds, qb0, qb1, rperm, \
+                                                                       rw, row0, mrows, nb0, src);             \
+        break;
+            switch (msub) {
+                K3_TILE_CASE(1)
+                K3_TILE_CASE(2)
+                K3_TILE_CASE(3)
+                K3_TILE_CASE(4)
+                K3_TILE_CASE(5)
+                K3_TILE_CASE(6)
+                K3_TILE_CASE(7)
+                K3_TILE_CASE(8)
+                default: break;
+            }
+#undef K3_TILE_CASE
+            return;
+        }
+        constexpr int BODY = MODE == GATEUP ? B_BF16 : B_CVT;
+        st.ap.load(a.A, st.areg[0], 0, Kdim);
+        if constexpr (ST::AS == 2) st.ap.load(a.A, st.areg[1], min(1, nsteps - 1), Kdim);
+        if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], 0);
+        st.ap.template store<BODY == B_CVT>(st.areg[0], alds, 0, Kdim);
+        if constexpr (LO) st.lp.store(st.lreg[0], st.lsreg[0], llds, llds + MT * LO_ROW);
+        if constexpr (ST::AS == 1) {
+            st.ap.load(a.A, st.areg[0], min(1, nsteps - 1), Kdim);
+            if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(1, nsteps - 1));
+        }
+        __syncthreads();  // the first A buffer is in LDS
+        const bool exact = __syncthreads_or(scales_have_255(slds, stotal, THREADS)) != 0 || (Kdim % KS) != 0;
+        if (exact) {
+            gemm_steps<MODE, MT, CW, NBB, LO, MT / 16, true, BODY, true>(a, st, alds, llds, slds, qb0, qb1, rperm, rw,
+                                                                        row0, mrows, nb0, a.A);
+            return;
+        }
+#define K3_TILE_CASE(MSV)                                                                                    \
+    case MSV:                                                                                                \
+        if constexpr (MSV <= MT / 16)                                                                        \
+            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, BODY, true>(a, st, alds, llds, slds, qb0, qb1, rperm, \
+                                                                      rw, row0, mrows, nb0, a.A);            \
+        break;
+        switch (msub) {
+            K3_TILE_CASE(1)
+            K3_TILE_CASE(2)
+            K3_TILE_CASE(3)
+            K3_TILE_CASE(4)
+            K3_TILE_CASE(5)
+            K3_TILE_CASE(6)
+            K3_TILE_CASE(7)
+            K3_TILE_CASE(8)
+            default: break;
+        }
+#undef K3_TILE_CASE
+    }
 }
 
-template <int MODE, int MT, int CW, int NBB, bool LO>
+template <int MODE, int MT, int CW, int NBB, bool LO, bool F16K>
 hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
     using SH = GemmShape<MODE, CW>;
     a.nblk_n = (a.N + SH::BN - 1) / SH::BN;
     const size_t lds = gemm_lds_bytes(MT, 2, SH::SROWS, a.Kdim, LO);
     const long max_items = (long)max_tiles * a.nblk_n;
     const dim3 grid(xcd_grid(max_items));
-    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, NBB, LO>);
+    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, NBB, LO, F16K>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, NBB, LO>), grid, dim3(CW * 64), lds, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, NBB, LO, F16K>), grid, dim3(CW * 64), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -678,12 +825,13 @@ hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
 // waves per SIMD beside two sets of activation registers.  LDS: two A buffers plus
 // the staged scales; when the scales of eight waves' rows do not fit (long rows,
 // e.g. a gate/up reduction of 8192), four waves with half the rows.
-template <int MODE, bool LO>
+// F16K: the fp32-x kernels (fp16 items where the weights allow, h in fp16).
+template <int MODE, bool LO, bool F16K>
 hipError_t launch_gemm(const GemmArgs& a, int mt, int max_tiles, hipStream_t stream) {
-    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 4, LO>(a, max_tiles, stream);
+    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 4, LO, F16K>(a, max_tiles, stream);
     if (gemm_lds_bytes(kTileRowsLarge, 2, GemmShape<MODE, 8>::SROWS, a.Kdim, LO) <= kLdsLimit)
-        return launch_gemm_t<MODE, kTileRowsLarge, 8, 2, LO>(a, max_tiles, stream);
-    return launch_gemm_t<MODE, kTileRowsLarge, 4, 2, LO>(a, max_tiles, stream);
+        return launch_gemm_t<MODE, kTileRowsLarge, 8, 2, LO, F16K>(a, max_tiles, stream);
+    return launch_gemm_t<MODE, kTileRowsLarge, 4, 2, LO, F16K>(a, max_tiles, stream);
 }
 
 // ------------------------------------------------------------------ x = hi + lo
@@ -699,9 +847,12 @@ __device__ __forceinline__ uint32_t e2m1_rne(float v, float inv) {
     return m | (v < 0.0f ? 8u : 0u);
 }
 
+// The same pass also writes x rounded to fp16 (RNE) for the fp16 items, and raises
+// flag[0] when some finite |x| rounds past the fp16 range (>= 65520).
 __global__ __launch_bounds__(256) void xsplit_kernel(const float* __restrict__ x, int T, int D,
                                                      uint16_t* __restrict__ xh, uint8_t* __restrict__ xl,
-                                                     uint8_t* __restrict__ xls) {
+                                                     uint8_t* __restrict__ xls, uint16_t* __restrict__ x16,
+                                                     int32_t* __restrict__ flag) {
     const int nsteps = (D + KS - 1) / KS, gpr = nsteps * 4;  // groups per padded row
     const size_t ngroups = (size_t)T * gpr;
     const int sub = threadIdx.x & 7;  // lane within the group
@@ -740,9 +891,19 @@ __global__ __launch_bounds__(256) void xsplit_kernel(const float* __restrict__ x
         uint32_t codes = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) codes |= e2m1_rne(lo[j], inv) << (4 * j);
-        if (real)
+        if (real) {
             reinterpret_cast<uint2*>(xh + t * D + 32 * g)[sub] =
                 make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+            uint32_t f[4];
+            bool over = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f[j] = __builtin_bit_cast(uint16_t, (_Float16)v[j]);
+                over |= __builtin_isfinite(v[j]) && fabsf(v[j]) >= 65520.0f;
+            }
+            reinterpret_cast<uint2*>(x16 + t * D + 32 * g)[sub] = make_uint2(f[0] | (f[1] << 16), f[2] | (f[3] << 16));
+            if (over) flag[0] = 1;  // every writer stores the same value
+        }
         reinterpret_cast<uint16_t*>(xl + t * (size_t)nsteps * LO_ROW + 16 * g)[sub] = (uint16_t)codes;
         if (sub == 0) xls[t * (size_t)gpr + g] = (uint8_t)(e + 127);
     }
@@ -820,12 +981,12 @@ GroupBuffers group_workspace_carve(void* ws, int T, int K, int E, bool with_outp
     return g;
 }
 
-// group buffers, h [P, F] bf16, the pair rows [P, D] fp32, then (fp32 x) hi [T, D]
-// bf16, the low part's codes [T, nsteps * 64] and scales [T, nsteps * 4].
+// group buffers, h [P, F] (16-bit), the pair rows [P, D] fp32, then (fp32 x) hi [T, D]
+// bf16, the low part's codes [T, nsteps * 64] and scales [T, nsteps * 4], x in fp16 [T, D].
 size_t chunk_workspace_bytes(int T, int K, int E, int D, int F) {
     const size_t P = (size_t)T * K, t = (size_t)T, ns = (size_t)(D + KS - 1) / KS;
     return group_workspace_bytes(T, K, E, true) + align256(P * F * 2) + align256(P * D * 4) +
-           align256(t * D * 2) + align256(t * ns * LO_ROW) + align256(t * ns * 4);
+           align256(t * D * 2) + align256(t * ns * LO_ROW) + align256(t * ns * 4) + align256(t * D * 2);
 }
 
 ChunkWorkspace chunk_workspace_carve(void* ws, int T, int K, int E, int D, int F) {
@@ -837,7 +998,8 @@ ChunkWorkspace chunk_workspace_carve(void* ws, int T, int K, int E, int D, int F
     c.ytk = reinterpret_cast<float*>(p); p += align256(P * D * 4);
     c.x_hi = reinterpret_cast<uint16_t*>(p); p += align256(t * D * 2);
     c.x_lo = reinterpret_cast<uint8_t*>(p); p += align256(t * ns * LO_ROW);
-    c.x_los = reinterpret_cast<uint8_t*>(p);
+    c.x_los = reinterpret_cast<uint8_t*>(p); p += align256(t * ns * 4);
+    c.x16 = reinterpret_cast<uint16_t*>(p);
     return c;
 }
 
@@ -864,13 +1026,14 @@ hipError_t launch_chunk(const DevWeights& W, const float* x32, const uint16_t* x
     if (lo) {
         const size_t groups = (size_t)T * ((W.D + KS - 1) / KS) * 4;
         hipLaunchKernelGGL(xsplit_kernel, dim3(grid_for(groups, 256 / 8)), dim3(256), 0, stream, x32, T, W.D,
-                           ws.x_hi, ws.x_lo, ws.x_los);
+                           ws.x_hi, ws.x_lo, ws.x_los, ws.x16, ws.g.scalars + 2);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
 
     GemmArgs gu{};
     gu.A = lo ? ws.x_hi : xb16;
+    gu.A16 = ws.x16;
     gu.alo = ws.x_lo;
     gu.alos = ws.x_los;
     gu.perm = ws.g.perm;
@@ -883,8 +1046,8 @@ hipError_t launch_chunk(const DevWeights& W, const float* x32, const uint16_t* x
     gu.tiles = ws.g.tiles;
     gu.scalars = ws.g.scalars;
     gu.h_out = ws.h_bf16;
-    err = lo ? launch_gemm<GATEUP, true>(gu, ws.g.mt, ws.g.max_tiles, stream)
-             : launch_gemm<GATEUP, false>(gu, ws.g.mt, ws.g.max_tiles, stream);
+    err = lo ? launch_gemm<GATEUP, true, true>(gu, ws.g.mt, ws.g.max_tiles, stream)
+             : launch_gemm<GATEUP, false, false>(gu, ws.g.mt, ws.g.max_tiles, stream);
     if (err != hipSuccess) return err;
 
     GemmArgs dn{};
@@ -899,7 +1062,8 @@ hipError_t launch_chunk(const DevWeights& W, const float* x32, const uint16_t* x
     dn.scalars = ws.g.scalars;
     dn.y_out = ws.ytk;
     dn.wts = w;
-    err = launch_gemm<DOWN, false>(dn, ws.g.mt, ws.g.max_tiles, stream);
+    err = lo ? launch_gemm<DOWN, false, true>(dn, ws.g.mt, ws.g.max_tiles, stream)   // h in fp16
+             : launch_gemm<DOWN, false, false>(dn, ws.g.mt, ws.g.max_tiles, stream);
     if (err != hipSuccess) return err;
 
     return launch_combine(ws.ytk, idx, T, K, W.D, ws.g.scalars, y, stream);

@@ -22,6 +22,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -75,6 +77,19 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16_nofix(uint32_t q, float sc) {
     r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
     r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
     r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
+    return r;
+}
+
+// 8 codes -> 8 fp16 (as four packed dwords, column order), scale 2^(s-127) given as
+// an fp32; exact when every decoded value is an fp16 normal (callers check the
+// scale bytes: 114 <= s <= 140 keeps 0.5 * 2^(s-127) >= 2^-14 and 6 * 2^(s-127) <=
+// 65504).
+__device__ __forceinline__ u32x4 fp4x8_to_f16_nofix(uint32_t q, float sc) {
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc, 3));
     return r;
 }
 

@@ -83,6 +83,7 @@ struct ChunkWorkspace {
     uint16_t* x_hi;         // [T, D]    fp32 x: bf16(x)
     uint8_t* x_lo;          // [T, ceil(D/128) * 64]  x - bf16(x) as FP4 codes, rows padded to whole steps
     uint8_t* x_los;         // [T, ceil(D/128) * 4]   their E8M0 scales
+    uint16_t* x16;          // [T, D]    fp32 x: x rounded to fp16 (the fp16 items' activations)
 };
 
 int group_max_tiles(int T, int K, int E);

@@ -342,8 +342,8 @@ def decode_down(W: ExpertWeights, h: torch.Tensor, idx: torch.Tensor, w: torch.T
 def forward_chunk(W: ExpertWeights, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
                   y: Optional[torch.Tensor] = None, n_unique: Optional[torch.Tensor] = None,
                   ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """A chunk: ``x [T,D]``, ``idx/w [T,K]`` -> fp32 ``y [T,D]`` (bf16 MFMA path).  An
-    fp32 ``x`` goes to ``k3moe_forward_chunk`` (x = bf16 high part + MXFP4 low
+    """A chunk: ``x [T,D]``, ``idx/w [T,K]`` -> fp32 ``y [T,D]`` (grouped MFMA path).  An
+    fp32 ``x`` goes to ``k3moe_forward_chunk`` (fp16 items, or bf16 high part + MXFP4 low
     part), a bf16 ``x`` to ``k3moe_forward_chunk_bf16``."""
     T = x.shape[0]
     fn = "k3moe_forward_chunk_bf16" if x.dtype == torch.bfloat16 else "k3moe_forward_chunk"

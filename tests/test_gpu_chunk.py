@@ -1,11 +1,13 @@
-"""Chunk path (grouped bf16-MFMA GEMMs) on the GPU vs the oracle: rel-L2 <= 5e-3.
+"""Chunk path (grouped MFMA GEMMs) on the GPU vs the oracle: rel-L2 <= 5e-3.
 
 fp32 activations (the 32- and 4096-token workloads) go through
-k3moe_forward_chunk: x = bf16(x) + lo, the low part as MXFP4 in a second product
-into the same accumulators; h is rounded to bf16 between the two products.  On
-the K3-shape weights that lands near 1.5e-3 from the exact block, most of it the
-bf16 rounding of h (a CPU emulation puts bf16 rounding of x alone at 7.3e-3, over
-the budget: test_chunk_prefill32 checks that the low part removes it).  The
+k3moe_forward_chunk: a work item whose weights are all fp16 normals runs on the
+fp16 MFMA with x and h rounded to fp16 (CPU emulation at the K3 shape: 9.4e-4 from
+the exact block); other items (scale bytes outside 114..140, byte 255, ragged
+steps, or some |x| past the fp16 range) take x = bf16(x) + lo, the low part as
+MXFP4 in a second product into the same accumulators (1.5e-3), with h converted
+to bf16 for their down products.  Rounding x to bf16 alone would cost 7.3e-3, over
+the budget: test_chunk_prefill32 checks the fp32 path against that.  The
 256-token workload has bf16 activations and goes through k3moe_forward_chunk_bf16
 with both sides seeing the same bf16 values.
 
@@ -122,6 +124,22 @@ def test_chunk_batch4096_sampled():
     e_edge = rel_l2(got[sample[is_edge]], want[is_edge])
     log(f"chunk batch4096: largest per-token rel-L2 {pt:.3e}; edge tokens alone {e_edge:.3e}")
     assert pt <= TOL and e_edge <= TOL
+
+
+def test_chunk_x_beyond_fp16():
+    """fp32 x with entries past the fp16 range (|x| >= 65520): the launch takes the
+    bf16 high part plus MXFP4 low part for every item, and still meets the oracle."""
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name="x_big", T=40, path="chunk", weight_seed=91, act_seed=91)
+    x, logits, bias = synth.activations(cfg)
+    x = x.copy()
+    x[3, 7] = 7.0e4
+    x[17, 100] = -1.0e5
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    W = device_weights(cfg)
+    got, _ = _chunk_gpu(W, x, idx, w)
+    want = oracle_forward_subset(cfg, x, idx, w)
+    assert_close(got, want, TOL, "chunk x beyond fp16")
+    assert per_token_max(got, want) <= TOL
 
 
 def test_chunk_literal_edge_masks():
