@@ -58,6 +58,7 @@
 // 2^-20 of x: the block output then sits about 1.5e-3 from the exact one, most of
 // it the bf16 rounding of h.  The weights' scale byte 255 (which the scaled MFMA
 // would read as NaN) is passed as 254 and the group's product added twice.
+#include <algorithm>
 #include <type_traits>
 
 #include "device.hpp"
@@ -406,6 +407,8 @@ __device__ __forceinline__ v8i fp4_operand(const u32x4& q) {
 // B_CVT -- as B_BF16 with A loaded as fp16 and stored as bf16.  H16: the gate/up
 // output h is stored as fp16 (else bf16).  asrc: the rows A is loaded from.
 enum { B_BF16 = 0, B_F16 = 1, B_CVT = 2 };
+// Launch kinds of the GEMM kernel (see launch_gemm).
+enum { K_BF16 = 0, K_F16 = 1 };
 template <int MODE, int MT, int CW, int NBB, bool LO, int MS, bool EXACT, int BODY, bool H16>
 __device__ __forceinline__ void gemm_steps(const GemmArgs& a, GemmState<MODE, MT, CW, NBB, LO>& st, uint8_t* alds,
                                            uint8_t* llds, const uint8_t* slds, const char* qb0, const char* qb1,
@@ -615,64 +618,29 @@ __device__ __forceinline__ int scales_outside(const uint8_t* slds, int stotal, i
 //   - one barrier per step; the scale bytes of the workgroup's weight rows are
 //     copied to LDS up front, while the first activation and weight loads are
 //     already in flight.
-template <int MODE, int MT, int CW, int NBB, bool LO, bool F16K>
-__global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
+// Per-item setup shared by the kernel and the bf16 fallback of the fp32-x kernels:
+// the staged rows' pair ids (item_init), the lane's weight rows and scale offsets
+// and the first ring steps (item_ring).
+template <int MODE, int MT, int CW, int NBB, bool LO>
+__device__ __forceinline__ void item_init(const GemmArgs& a, GemmState<MODE, MT, CW, NBB, LO>& st, int row0,
+                                          int mrows) {
+    st.ap.init(a, threadIdx.x, row0, mrows);  // pair ids of the staged rows (first loads)
+    if constexpr (LO) st.lp.init(a, row0, mrows, (a.Kdim + KS - 1) / KS);
+}
+
+template <int MODE, int MT, int CW, int NBB, bool LO>
+__device__ __forceinline__ void item_ring(const GemmArgs& a, GemmState<MODE, MT, CW, NBB, LO>& st, int nb0,
+                                          int srows_real, const char* qb0, const char* qb1) {
     using SH = GemmShape<MODE, CW>;
-    using ST = GemmState<MODE, MT, CW, NBB, LO>;
-    constexpr int WN = SH::WN, BN = SH::BN;
-    constexpr int THREADS = CW * 64;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* alds = smem;                   // [2][MT][A_ROW]
-    int32_t* rperm = reinterpret_cast<int32_t*>(smem + 2 * MT * A_ROW);  // [MT] pair of each tile row
-    float* rw = reinterpret_cast<float*>(rperm + MT);                      // [MT] its routing weight
-    uint8_t* llds = reinterpret_cast<uint8_t*>(rw + MT);                   // LO: [2][MT * LO_ROW + MT * 4]
-    uint8_t* slds = llds + (LO ? 2 * MT * (LO_ROW + 4) : 0);               // [TENSORS][rows][Kdim/32]
-
-    // ---- work item (XCD-aware): XCD x walks items [x*per, (x+1)*per)
-    const int item = xcd_item(a.scalars[1] * a.nblk_n);
-    if (item < 0) return;  // block-uniform
-    const int tile = item / a.nblk_n, nblk = item % a.nblk_n;
-    const int4 td = a.tiles[tile];
-    const int e = td.x, row0 = td.y, mrows = td.z;  // 1 <= mrows <= MT
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ln = lane & 15;
+    const int lane = threadIdx.x & 63, ln = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int Kdim = a.Kdim, N = a.N, sb = Kdim >> 5;
-    const int nb0 = nblk * BN;
-    const int n0 = nb0 + wave * WN;
+    const int n0 = nb0 + wave * SH::WN;
     const int nsteps = (Kdim + KS - 1) / KS;
-
-    ST st;
-    st.ap.init(a, tid, row0, mrows);  // pair ids of the staged rows (first loads)
-    if constexpr (LO) st.lp.init(a, row0, mrows, nsteps);
-
-    // ---- scale bytes of the workgroup's rows: srows_real * sb contiguous bytes per
-    // tensor (a multiple of 32, 16-byte aligned), copied global -> LDS directly
-    // (global_load_lds) with tensor 1 right after tensor 0, so 16-byte piece c lands
-    // at byte 16*c.  A wave whose 64 pieces all lie past the end skips the copy;
-    // the lanes of the last wave that run past it re-copy the last piece into the
-    // rounded-up tail of the region.
-    const int srows_real = min(BN, N - nb0);
-    const int spieces = (srows_real * sb) >> 4;
-    const int stotal = SH::TENSORS * spieces;
-    for (int c0 = 0; c0 < stotal; c0 += THREADS) {
-        if (c0 + wave * 64 < stotal) {  // wave-uniform
-            const int cc = min(c0 + tid, stotal - 1);
-            const int tsel = cc >= spieces ? 1 : 0, pc = cc - tsel * spieces;
-            const uint8_t* sbase = tsel == 0 ? a.s0 + (size_t)e * a.s0_stride : a.s1 + (size_t)e * a.s1_stride;
-            __builtin_amdgcn_global_load_lds((glb_ptr_t)(sbase + (size_t)nb0 * sb + 16 * pc),
-                                             (lds_ptr_t)(slds + 16 * (c0 + wave * 64)), 16, 0, 0);
-        }
-    }
-
-    // ---- weight rows of this lane (clamped to real rows; columns past N are
-    // computed from a repeated row and never stored), and the first ring steps
     const uint32_t qrow = (uint32_t)Kdim >> 1;
-    // the expert's weight tensors: wave-uniform bases, per-lane 32-bit row offsets
-    const char* qb0 = reinterpret_cast<const char*>(a.q0 + (size_t)e * a.q0_stride);
-    const char* qb1 = (MODE == GATEUP) ? reinterpret_cast<const char*>(a.q1 + (size_t)e * a.q1_stride) : qb0;
     // ring entry ns: 16-row subtile ns (GATEUP: gate 0, 1, up 2, 3), lane row ln,
-    // columns 32 * (lane / 16) of each step
+    // columns 32 * (lane / 16) of each step; rows clamped to real rows (columns
+    // past N are computed from a repeated row and never stored)
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
         const int r = (MODE == GATEUP) ? n0 + 16 * (ns & 1) + ln : n0 + 16 * ns + ln;
@@ -690,15 +658,166 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
                                                               (st.qoff[ns] + (uint32_t)(col >> 1)));
         }
     }
+}
+
+// LDS of a work item: two A buffers, the row table, the low part's buffers (LO) and
+// the weight scale rows.
+template <int MT, bool LO>
+struct ItemLds {
+    uint8_t* alds;   // [2][MT][A_ROW]
+    int32_t* rperm;  // [MT] pair of each tile row
+    float* rw;       // [MT] its routing weight
+    uint8_t* llds;   // LO: [2][MT * LO_ROW + MT * 4]
+    uint8_t* slds;   // [TENSORS][rows][Kdim/32]
+    __device__ __forceinline__ explicit ItemLds(uint8_t* smem) {
+        alds = smem;
+        rperm = reinterpret_cast<int32_t*>(smem + 2 * MT * A_ROW);
+        rw = reinterpret_cast<float*>(rperm + MT);
+        llds = reinterpret_cast<uint8_t*>(rw + MT);
+        slds = llds + (LO ? 2 * MT * (LO_ROW + 4) : 0);
+    }
+};
+
+// Run the staged item (scales and row table in LDS) on the bf16 MFMA: its first
+// activation steps, the exact-path test, and the step body for its subtile count.
+// BODY B_BF16 (x, with the low part when LO) or B_CVT (fp16 h staged as bf16); H16:
+// h out in fp16.  Used by item_rest; the bf16 kernels write the same steps out.
+template <int MODE, int MT, int CW, int NBB, bool LO, int BODY, bool H16>
+__device__ __forceinline__ void item_bf16(const GemmArgs& a, GemmState<MODE, MT, CW, NBB, LO>& st,
+                                          const ItemLds<MT, LO>& L, int row0, int mrows, int nb0, int stotal,
+                                          const char* qb0, const char* qb1) {
+    using ST = GemmState<MODE, MT, CW, NBB, LO>;
+    constexpr int THREADS = CW * 64;
+    const int Kdim = a.Kdim, nsteps = (Kdim + KS - 1) / KS;
+    const int msub = min((mrows + 15) >> 4, MT / 16);
+    st.ap.load(a.A, st.areg[0], 0, Kdim);
+    if constexpr (ST::AS == 2) st.ap.load(a.A, st.areg[1], min(1, nsteps - 1), Kdim);
+    if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], 0);
+    st.ap.template store<BODY == B_CVT>(st.areg[0], L.alds, 0, Kdim);
+    if constexpr (LO) st.lp.store(st.lreg[0], st.lsreg[0], L.llds, L.llds + MT * LO_ROW);
+    if constexpr (ST::AS == 1) {  // step 1's activations into the one register set
+        st.ap.load(a.A, st.areg[0], min(1, nsteps - 1), Kdim);
+        if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(1, nsteps - 1));
+    }
+    __syncthreads();  // scales, the first A buffer and the row table are in LDS
+    const bool exact = __syncthreads_or(scales_have_255(L.slds, stotal, THREADS)) != 0 || (Kdim % KS) != 0;
+    if (exact) {
+        gemm_steps<MODE, MT, CW, NBB, LO, MT / 16, true, BODY, H16>(a, st, L.alds, L.llds, L.slds, qb0, qb1, L.rperm,
+                                                                    L.rw, row0, mrows, nb0, a.A);
+        return;
+    }
+#define K3_TILE_CASE(MSV)                                                                                    \
+    case MSV:                                                                                                \
+        if constexpr (MSV <= MT / 16)                                                                        \
+            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, BODY, H16>(a, st, L.alds, L.llds, L.slds, qb0, qb1, \
+                                                                     L.rperm, L.rw, row0, mrows, nb0, a.A);  \
+        break;
+    switch (msub) {
+        K3_TILE_CASE(1)
+        K3_TILE_CASE(2)
+        K3_TILE_CASE(3)
+        K3_TILE_CASE(4)
+        K3_TILE_CASE(5)
+        K3_TILE_CASE(6)
+        K3_TILE_CASE(7)
+        K3_TILE_CASE(8)
+        default: break;
+    }
+#undef K3_TILE_CASE
+}
+
+// The fp32-x kernels' items that the fp16 test rejected, on the bf16 MFMA with a
+// state of their own.  Not inlined: its registers stay out of the fp16 path, and
+// it redoes the per-item setup (the scales and the row table are already in LDS).
+// The launch's GemmArgs is read where the kernel's arguments lie (the kernarg
+// segment, whose first explicit argument sits at offset 0): handing the kernel
+// parameter itself to a call would copy it to private memory in every workgroup.
+template <int MODE, int MT, int CW, int NBB, bool LO>
+__device__ __attribute__((noinline)) void item_rest(const void* kargs, int e, int row0, int mrows, int nb0,
+                                                    int srows_real, int stotal) {
+    const GemmArgs& a = *static_cast<const GemmArgs*>(kargs);
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const ItemLds<MT, LO> L(smem);
+    const char* qb0 = reinterpret_cast<const char*>(a.q0 + (size_t)e * a.q0_stride);
+    const char* qb1 = (MODE == GATEUP) ? reinterpret_cast<const char*>(a.q1 + (size_t)e * a.q1_stride) : qb0;
+    GemmState<MODE, MT, CW, NBB, LO> st;
+    item_init(a, st, row0, mrows);
+    item_ring(a, st, nb0, srows_real, qb0, qb1);
+    item_bf16<MODE, MT, CW, NBB, LO, MODE == GATEUP ? B_BF16 : B_CVT, true>(a, st, L, row0, mrows, nb0, stotal, qb0,
+                                                                           qb1);
+}
+
+// One workgroup = one (tile of <= MT pair rows of one expert, block of BN output
+// columns), the whole reduction, in 128-column steps:
+//   - each of CW waves streams the 16-byte weight chunks of its four 16-row
+//     subtiles through an NBB-deep register ring and converts them in registers
+//     into MFMA B operands;
+//   - the tile's activation rows (shared by all waves) are loaded ahead into
+//     registers and stored into a double-buffered LDS tile, 16-byte pieces
+//     XOR-swizzled by row; A fragments are read from there;
+//   - one barrier per step; the scale bytes of the workgroup's weight rows are
+//     copied to LDS up front, while the first weight loads are already in flight.
+// KIND K_BF16: bf16 x (with the low part when LO) and bf16 h.  K_F16 (fp32 x, and
+// the down product after it): items whose weights are all fp16 normals run on the
+// fp16 MFMA; the others go to item_rest.
+template <int MODE, int MT, int CW, int NBB, bool LO, int KIND>
+__global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
+    using SH = GemmShape<MODE, CW>;
+    using ST = GemmState<MODE, MT, CW, NBB, LO>;
+    constexpr int BN = SH::BN;
+    constexpr int THREADS = CW * 64;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const ItemLds<MT, LO> L(smem);
+
+    // ---- work item (XCD-aware): XCD x walks items [x*per, (x+1)*per)
+    const int item = xcd_item(a.scalars[1] * a.nblk_n);
+    if (item < 0) return;  // block-uniform
+    const int tile = item / a.nblk_n, nblk = item % a.nblk_n;
+    const int4 td = a.tiles[tile];
+    const int e = td.x, row0 = td.y, mrows = td.z;  // 1 <= mrows <= MT
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Kdim = a.Kdim, N = a.N, sb = Kdim >> 5;
+    const int nb0 = nblk * BN;
+    const int nsteps = (Kdim + KS - 1) / KS;
+    const int srows_real = min(BN, N - nb0);
+    ST st;
+    item_init(a, st, row0, mrows);
+
+    // ---- scale bytes of the workgroup's rows: srows_real * sb contiguous bytes per
+    // tensor (a multiple of 32, 16-byte aligned), copied global -> LDS directly
+    // (global_load_lds) with tensor 1 right after tensor 0, so 16-byte piece c lands
+    // at byte 16*c.  A wave whose 64 pieces all lie past the end skips the copy;
+    // the lanes of the last wave that run past it re-copy the last piece into the
+    // rounded-up tail of the region.
+    const int spieces = (srows_real * sb) >> 4;
+    const int stotal = SH::TENSORS * spieces;
+    for (int c0 = 0; c0 < stotal; c0 += THREADS) {
+        if (c0 + wave * 64 < stotal) {  // wave-uniform
+            const int cc = min(c0 + tid, stotal - 1);
+            const int tsel = cc >= spieces ? 1 : 0, pc = cc - tsel * spieces;
+            const uint8_t* sbase = tsel == 0 ? a.s0 + (size_t)e * a.s0_stride : a.s1 + (size_t)e * a.s1_stride;
+            __builtin_amdgcn_global_load_lds((glb_ptr_t)(sbase + (size_t)nb0 * sb + 16 * pc),
+                                             (lds_ptr_t)(L.slds + 16 * (c0 + wave * 64)), 16, 0, 0);
+        }
+    }
+    // the expert's weight tensors: wave-uniform bases, per-lane 32-bit row offsets
+    const char* qb0 = reinterpret_cast<const char*>(a.q0 + (size_t)e * a.q0_stride);
+    const char* qb1 = (MODE == GATEUP) ? reinterpret_cast<const char*>(a.q1 + (size_t)e * a.q1_stride) : qb0;
+    item_ring(a, st, nb0, srows_real, qb0, qb1);  // first weight loads, behind the scale copy
     if (MODE == DOWN && tid < mrows) {  // pair id and routing weight of each tile row
         const int p = a.perm[row0 + tid];
-        rperm[tid] = p;
-        rw[tid] = a.wts[p];
+        L.rperm[tid] = p;
+        L.rw[tid] = a.wts[p];
     }
-    const int msub = min((mrows + 15) >> 4, MT / 16);
 
-    if constexpr (!F16K) {
-        // bf16 activations: their first steps go out before the scale check
+    if constexpr (KIND == K_BF16) {
+        // bf16 activations: their first steps go out before the scale check (the
+        // same steps as item_bf16, written out here: called, it costs spills)
+        uint8_t* const alds = L.alds;
+        uint8_t* const llds = L.llds;
+        uint8_t* const slds = L.slds;
+        const int msub = min((mrows + 15) >> 4, MT / 16);
         st.ap.load(a.A, st.areg[0], 0, Kdim);
         if constexpr (ST::AS == 2) st.ap.load(a.A, st.areg[1], min(1, nsteps - 1), Kdim);
         if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], 0);
@@ -711,15 +830,15 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
         __syncthreads();  // scales, the first A buffer and the row table are in LDS
         const bool exact = __syncthreads_or(scales_have_255(slds, stotal, THREADS)) != 0 || (Kdim % KS) != 0;
         if (exact) {
-            gemm_steps<MODE, MT, CW, NBB, LO, MT / 16, true, B_BF16, false>(a, st, alds, llds, slds, qb0, qb1, rperm,
-                                                                           rw, row0, mrows, nb0, a.A);
+            gemm_steps<MODE, MT, CW, NBB, LO, MT / 16, true, B_BF16, false>(a, st, alds, llds, slds, qb0, qb1, L.rperm,
+                                                                           L.rw, row0, mrows, nb0, a.A);
             return;
         }
-#define K3_TILE_CASE(MSV)                                                                                        \
-    case MSV:                                                                                                    \
-        if constexpr (MSV <= MT / 16)                                                                            \
-            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, B_BF16, false>(a, st, alds, llds, slds, qb0, qb1, rperm, \
-                                                                         rw, row0, mrows, nb0, a.A);             \
+#define K3_TILE_CASE(MSV)                                                                                          \
+    case MSV:                                                                                                      \
+        if constexpr (MSV <= MT / 16)                                                                              \
+            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, B_BF16, false>(a, st, alds, llds, slds, qb0, qb1, L.rperm, \
+                                                                         L.rw, row0, mrows, nb0, a.A);             \
         break;
         switch (msub) {
             K3_TILE_CASE(1)
@@ -734,62 +853,28 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
         }
 #undef K3_TILE_CASE
     } else {
-        // fp32 x (gate/up) or the fp16 h it produced (down): the item runs on the
-        // fp16 MFMA when every weight it reads is an fp16 normal (scale bytes 114..140),
-        // no |x| overflows fp16 and the steps are whole; else on bf16 (x: the bf16
-        // high part plus the MXFP4 low part; h: converted to bf16 as it is staged)
+        // the item runs on the fp16 MFMA when every weight it reads is an fp16
+        // normal (scale bytes 114..140), no |x| overflows fp16 and the steps are whole
         __syncthreads();  // the scales and the row table are in LDS
-        const bool f16 = __syncthreads_or(scales_outside(slds, stotal, THREADS, kF16ScaleLo, kF16ScaleHi)) == 0 &&
+        const bool f16 = __syncthreads_or(scales_outside(L.slds, stotal, THREADS, kF16ScaleLo, kF16ScaleHi)) == 0 &&
                          (Kdim % KS) == 0 && (MODE == DOWN || a.scalars[2] == 0);
-        if (f16) {
-            const uint16_t* src = MODE == GATEUP ? a.A16 : a.A;
-            st.ap.load(src, st.areg[0], 0, Kdim);
-            if constexpr (ST::AS == 2) st.ap.load(src, st.areg[1], min(1, nsteps - 1), Kdim);
-            st.ap.store(st.areg[0], alds, 0, Kdim);
-            if constexpr (ST::AS == 1) st.ap.load(src, st.areg[0], min(1, nsteps - 1), Kdim);
-            __syncthreads();
-#define K3_TILE_CASE(MSV)                                                                                      \
-    case MSV:                                                                                                  \
-        if constexpr (MSV <= MT / 16)                                                                          \
-            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, B_F16, true>(a, st, alds, llds, slds, qb0, qb1, rperm, \
-                                                                       rw, row0, mrows, nb0, src);             \
-        break;
-            switch (msub) {
-                K3_TILE_CASE(1)
-                K3_TILE_CASE(2)
-                K3_TILE_CASE(3)
-                K3_TILE_CASE(4)
-                K3_TILE_CASE(5)
-                K3_TILE_CASE(6)
-                K3_TILE_CASE(7)
-                K3_TILE_CASE(8)
-                default: break;
-            }
-#undef K3_TILE_CASE
+        if (!f16) {  // block-uniform; the loads already made are dropped
+            item_rest<MODE, MT, CW, NBB, LO>((const void*)__builtin_amdgcn_kernarg_segment_ptr(), e, row0, mrows,
+                                             nb0, srows_real, stotal);
             return;
         }
-        constexpr int BODY = MODE == GATEUP ? B_BF16 : B_CVT;
-        st.ap.load(a.A, st.areg[0], 0, Kdim);
-        if constexpr (ST::AS == 2) st.ap.load(a.A, st.areg[1], min(1, nsteps - 1), Kdim);
-        if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], 0);
-        st.ap.template store<BODY == B_CVT>(st.areg[0], alds, 0, Kdim);
-        if constexpr (LO) st.lp.store(st.lreg[0], st.lsreg[0], llds, llds + MT * LO_ROW);
-        if constexpr (ST::AS == 1) {
-            st.ap.load(a.A, st.areg[0], min(1, nsteps - 1), Kdim);
-            if constexpr (LO) st.lp.load(a, st.lreg[0], st.lsreg[0], min(1, nsteps - 1));
-        }
-        __syncthreads();  // the first A buffer is in LDS
-        const bool exact = __syncthreads_or(scales_have_255(slds, stotal, THREADS)) != 0 || (Kdim % KS) != 0;
-        if (exact) {
-            gemm_steps<MODE, MT, CW, NBB, LO, MT / 16, true, BODY, true>(a, st, alds, llds, slds, qb0, qb1, rperm, rw,
-                                                                        row0, mrows, nb0, a.A);
-            return;
-        }
-#define K3_TILE_CASE(MSV)                                                                                    \
-    case MSV:                                                                                                \
-        if constexpr (MSV <= MT / 16)                                                                        \
-            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, BODY, true>(a, st, alds, llds, slds, qb0, qb1, rperm, \
-                                                                      rw, row0, mrows, nb0, a.A);            \
+        const uint16_t* src = MODE == GATEUP ? a.A16 : a.A;
+        st.ap.load(src, st.areg[0], 0, Kdim);
+        if constexpr (ST::AS == 2) st.ap.load(src, st.areg[1], min(1, nsteps - 1), Kdim);
+        st.ap.store(st.areg[0], L.alds, 0, Kdim);
+        if constexpr (ST::AS == 1) st.ap.load(src, st.areg[0], min(1, nsteps - 1), Kdim);
+        __syncthreads();
+        const int msub = min((mrows + 15) >> 4, MT / 16);
+#define K3_TILE_CASE(MSV)                                                                                     \
+    case MSV:                                                                                                 \
+        if constexpr (MSV <= MT / 16)                                                                         \
+            gemm_steps<MODE, MT, CW, NBB, LO, MSV, false, B_F16, true>(a, st, L.alds, L.llds, L.slds, qb0, qb1, \
+                                                                       L.rperm, L.rw, row0, mrows, nb0, src); \
         break;
         switch (msub) {
             K3_TILE_CASE(1)
@@ -806,17 +891,17 @@ __global__ __launch_bounds__(CW * 64, 1) void gemm_kernel(GemmArgs a) {
     }
 }
 
-template <int MODE, int MT, int CW, int NBB, bool LO, bool F16K>
+template <int MODE, int MT, int CW, int NBB, bool LO, int KIND>
 hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
     using SH = GemmShape<MODE, CW>;
     a.nblk_n = (a.N + SH::BN - 1) / SH::BN;
     const size_t lds = gemm_lds_bytes(MT, 2, SH::SROWS, a.Kdim, LO);
     const long max_items = (long)max_tiles * a.nblk_n;
     const dim3 grid(xcd_grid(max_items));
-    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, NBB, LO, F16K>);
+    const void* fn = reinterpret_cast<const void*>(&gemm_kernel<MODE, MT, CW, NBB, LO, KIND>);
     hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, NBB, LO, F16K>), grid, dim3(CW * 64), lds, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<MODE, MT, CW, NBB, LO, KIND>), grid, dim3(CW * 64), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -825,13 +910,14 @@ hipError_t launch_gemm_t(GemmArgs a, int max_tiles, hipStream_t stream) {
 // waves per SIMD beside two sets of activation registers.  LDS: two A buffers plus
 // the staged scales; when the scales of eight waves' rows do not fit (long rows,
 // e.g. a gate/up reduction of 8192), four waves with half the rows.
-// F16K: the fp32-x kernels (fp16 items where the weights allow, h in fp16).
-template <int MODE, bool LO, bool F16K>
+// KIND: K_BF16 (bf16 x and h), K_F16 (fp32 x and the fp16 h it produces: fp16 items
+// where the weights allow, the rest on bf16).
+template <int MODE, bool LO, int KIND>
 hipError_t launch_gemm(const GemmArgs& a, int mt, int max_tiles, hipStream_t stream) {
-    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 4, LO, F16K>(a, max_tiles, stream);
+    if (mt == 16) return launch_gemm_t<MODE, 16, 8, 4, LO, KIND>(a, max_tiles, stream);
     if (gemm_lds_bytes(kTileRowsLarge, 2, GemmShape<MODE, 8>::SROWS, a.Kdim, LO) <= kLdsLimit)
-        return launch_gemm_t<MODE, kTileRowsLarge, 8, 2, LO, F16K>(a, max_tiles, stream);
-    return launch_gemm_t<MODE, kTileRowsLarge, 4, 2, LO, F16K>(a, max_tiles, stream);
+        return launch_gemm_t<MODE, kTileRowsLarge, 8, 2, LO, KIND>(a, max_tiles, stream);
+    return launch_gemm_t<MODE, kTileRowsLarge, 4, 2, LO, KIND>(a, max_tiles, stream);
 }
 
 // ------------------------------------------------------------------ x = hi + lo
@@ -1046,8 +1132,8 @@ hipError_t launch_chunk(const DevWeights& W, const float* x32, const uint16_t* x
     gu.tiles = ws.g.tiles;
     gu.scalars = ws.g.scalars;
     gu.h_out = ws.h_bf16;
-    err = lo ? launch_gemm<GATEUP, true, true>(gu, ws.g.mt, ws.g.max_tiles, stream)
-             : launch_gemm<GATEUP, false, false>(gu, ws.g.mt, ws.g.max_tiles, stream);
+    err = lo ? launch_gemm<GATEUP, true, K_F16>(gu, ws.g.mt, ws.g.max_tiles, stream)
+             : launch_gemm<GATEUP, false, K_BF16>(gu, ws.g.mt, ws.g.max_tiles, stream);
     if (err != hipSuccess) return err;
 
     GemmArgs dn{};
@@ -1062,8 +1148,8 @@ hipError_t launch_chunk(const DevWeights& W, const float* x32, const uint16_t* x
     dn.scalars = ws.g.scalars;
     dn.y_out = ws.ytk;
     dn.wts = w;
-    err = lo ? launch_gemm<DOWN, false, true>(dn, ws.g.mt, ws.g.max_tiles, stream)   // h in fp16
-             : launch_gemm<DOWN, false, false>(dn, ws.g.mt, ws.g.max_tiles, stream);
+    err = lo ? launch_gemm<DOWN, false, K_F16>(dn, ws.g.mt, ws.g.max_tiles, stream)   // h in fp16
+             : launch_gemm<DOWN, false, K_BF16>(dn, ws.g.mt, ws.g.max_tiles, stream);
     if (err != hipSuccess) return err;
 
     return launch_combine(ws.ytk, idx, T, K, W.D, ws.g.scalars, y, stream);
