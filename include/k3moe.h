@@ -301,12 +301,12 @@ typedef struct k3moe_latent {
  * x stays fp32 (the projection's fp32 accumulation) and the routed block is
  * k3moe_forward_decode's path for T = 1 and k3moe_forward_chunk's (fp32 x)
  * otherwise; RMSNorm and SiTU-GLU outputs are bf16; the dense products are bf16
- * x bf16 with fp32 accumulation (this library's GEMV kernels for T = 1, rocBLAS
- * GEMMs otherwise).
+ * x bf16 with fp32 accumulation (this library's GEMV kernels for T = 1, its MFMA
+ * GEMM kernels otherwise, whose split reductions are summed in a fixed order: the
+ * output does not depend on scheduling).
  * Requires d_hidden and d_shared multiples of 32 in [32, K3MOE_MAX_DIM], eps >= 0,
- * every pointer 16-byte aligned.  ws: k3moe_latent_workspace_size() bytes.  The
- * first call on a device creates that device's rocBLAS handle (rocBLAS allocates
- * its own workspace then); later calls allocate nothing.
+ * every pointer 16-byte aligned.  ws: k3moe_latent_workspace_size() bytes; the
+ * call allocates nothing.
  */
 int k3moe_latent_forward(const k3moe_latent_t *L, const k3moe_weights_t *W, const uint16_t *h, int32_t T,
                          const int32_t *idx, const float *w, int32_t K, float *out, void *ws, size_t ws_bytes,

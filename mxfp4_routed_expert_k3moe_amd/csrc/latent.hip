@@ -15,13 +15,11 @@
 //   s   = SiTU(g, u)                      [Fs]   bf16
 //   out += Sd s                           [Dh]
 // The five dense products are bf16 x bf16 with fp32 accumulation.  For one token
-// they are this file's GEMV kernels (x in one pass with g, u and s
-// in one pass, the norm folded into the pass that forms out); for a chunk they
-// are rocBLAS GEMMs (Tensile's MFMA kernels for gfx950) around the rmsnorm and
-// situ kernels.
-#include <rocblas/rocblas.h>
+// they are this file's GEMV kernels (x in one pass with g, u and s, the norm
+// folded into the pass that forms out); for a chunk, dense.hip's MFMA kernels
+// (x; s with SiTU-GLU in the epilogue; out = Wup r + Sd s as one reduction)
+// around the routed chunk path and the rmsnorm kernel.
 
-#include <mutex>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -70,14 +68,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
         out[i] = make_uint2(pack_bf16x2(g0 * (v[j].x * inv), g1 * (v[j].y * inv)),
                             pack_bf16x2(g2 * (v[j].z * inv), g3 * (v[j].w * inv)));
     }
-}
-
-// s = SiTU-GLU(g, u) elementwise, bf16 out.
-__global__ __launch_bounds__(256) void situ_kernel(const float* __restrict__ g, const float* __restrict__ u,
-                                                   size_t n, uint16_t* __restrict__ s) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        s[i] = (uint16_t)f32_to_bf16_bits(situ_fast(g[i], u[i]));
 }
 
 // ------------------------------------------------ one token: bf16 GEMVs
@@ -274,48 +264,17 @@ hipError_t launch_gemv_xs(const GemvArgs& gx, const GemvArgs& gs, hipStream_t st
     return hipGetLastError();
 }
 
-int grid_blocks(size_t n, int per_block) {
-    size_t b = (n + per_block - 1) / per_block;
-    return (int)(b < 65536 ? (b > 0 ? b : 1) : 65536);
-}
-
-// One rocBLAS handle per device, created on first use.
-std::mutex g_blas_mu;
-rocblas_handle g_blas[64] = {};
-
-hipError_t blas_for(hipStream_t stream, rocblas_handle* out) {
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(g_blas_mu);
-    if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) return hipErrorUnknown;
-    if (rocblas_set_stream(g_blas[dev], stream) != rocblas_status_success) return hipErrorUnknown;
-    *out = g_blas[dev];
-    return hipSuccess;
-}
-
-// out[T, N] (fp32 or bf16, row-major) = beta * out + in[T, Kd] (bf16) . W[N, Kd]^T (bf16):
-// in column-major terms out^T = W^T^T . in^T with W read transposed.
-hipError_t dense(rocblas_handle h, const uint16_t* in, int T, int Kd, const uint16_t* W, int N, void* out,
-                 bool out_f32, float beta) {
-    const float alpha = 1.0f;
-    const rocblas_datatype ot = out_f32 ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
-    const rocblas_status st =
-        rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, N, T, Kd, &alpha, W,
-                        rocblas_datatype_bf16_r, Kd, in, rocblas_datatype_bf16_r, Kd, &beta, out, ot, N, out, ot, N,
-                        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    return st == rocblas_status_success ? hipSuccess : hipErrorLaunchFailure;
-}
 
 }  // namespace
 
-// x (fp32), the routed block's workspace, a, r, g, u, s.
+// x (fp32), the routed block's workspace, a, r, s; for T >= 2 the dense products'
+// split partials and their counters (three launches).
 size_t latent_workspace_bytes(const LatentDims& L, int T, int K, int E) {
     const size_t t = (size_t)T;
     const size_t routed = T == 1 ? decode_workspace_bytes(K, L.Dl, L.F) : chunk_workspace_bytes(T, K, E, L.Dl, L.F);
+    const size_t dense = T == 1 ? 0 : align256(dense_part_bytes(T)) + 3 * align256(dense_cnt_bytes());
     return align256(t * L.Dl * 4) + align256(routed) + align256(t * L.Dl * 4) + align256(t * L.Dl * 2) +
-           2 * align256(t * L.Fs * 4) + align256(t * L.Fs * 2);
+           align256(t * L.Fs * 2) + dense;
 }
 
 hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t* h, int T, const int32_t* idx,
@@ -329,9 +288,7 @@ hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t
     void* rws = p; p += align256(routed);
     float* a = reinterpret_cast<float*>(p); p += align256(t * Dl * 4);
     uint16_t* r = reinterpret_cast<uint16_t*>(p); p += align256(t * Dl * 2);
-    float* g = reinterpret_cast<float*>(p); p += align256(t * Fs * 4);
-    float* u = reinterpret_cast<float*>(p); p += align256(t * Fs * 4);
-    uint16_t* s = reinterpret_cast<uint16_t*>(p);
+    uint16_t* s = reinterpret_cast<uint16_t*>(p); p += align256(t * Fs * 2);
 
     if (T == 1) {
         // one token: x = Wdn h (fp32), s = SiTU(Sg h, Su h), the routed decode path
@@ -349,30 +306,34 @@ hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t
         go.a = a; go.gn = L.norm; go.eps = L.eps; go.v1 = s; go.yf = out;
         return launch_gemv<GEMV_OUT>(go, stream);
     }
-    rocblas_handle blas = nullptr;
-    err = blas_for(stream, &blas);
+    // T >= 2: the dense products on this library's MFMA kernels (dense.hip)
+    float* part = reinterpret_cast<float*>(p); p += align256(dense_part_bytes(T));
+    int32_t* cnt = reinterpret_cast<int32_t*>(p);
+    const size_t cstride = align256(dense_cnt_bytes()) / sizeof(int32_t);
+    err = launch_dense_clear(cnt, 3, stream);
     if (err != hipSuccess) return err;
-    // x = Wdn h in fp32, then the routed block on x
-    err = dense(blas, h, T, Dh, L.w_down, Dl, x32, true, 0.0f);
+    // x = Wdn h in fp32, s = SiTU(Sg h, Su h) in bf16
+    DenseProblem px{};
+    px.epi = DENSE_F32; px.A[0] = h; px.W[0] = L.w_down; px.K[0] = Dh; px.T = T; px.N = Dl; px.outf = x32;
+    err = launch_dense(px, part, cnt, stream);
     if (err != hipSuccess) return err;
+    DenseProblem ps{};
+    ps.epi = DENSE_SITU; ps.A[0] = h; ps.W[0] = L.shared_gate; ps.Wu = L.shared_up; ps.K[0] = Dh; ps.T = T;
+    ps.N = Fs; ps.outb = s;
+    err = launch_dense(ps, part, cnt + cstride, stream);
+    if (err != hipSuccess) return err;
+    // the routed block on x
     err = launch_chunk(W, x32, nullptr, T, idx, w, K, a, nullptr, chunk_workspace_carve(rws, T, K, W.E, Dl, W.F),
                        stream);
     if (err != hipSuccess) return err;
-    // RMSNorm on the aggregate, then back to the full width
+    // RMSNorm on the aggregate, then out = Wup r + Sd s in one reduction
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(T), dim3(256), 0, stream, a, L.norm, Dl, L.eps, r);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    err = dense(blas, r, T, Dl, L.w_up, Dh, out, true, 0.0f);
-    if (err != hipSuccess) return err;
-    // the fused shared experts, added into out
-    err = dense(blas, h, T, Dh, L.shared_gate, Fs, g, true, 0.0f);
-    if (err != hipSuccess) return err;
-    err = dense(blas, h, T, Dh, L.shared_up, Fs, u, true, 0.0f);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(situ_kernel, dim3(grid_blocks(t * Fs, 256)), dim3(256), 0, stream, g, u, t * Fs, s);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    return dense(blas, s, T, Fs, L.shared_down, Dh, out, true, 1.0f);
+    DenseProblem po{};
+    po.epi = DENSE_F32; po.A[0] = r; po.W[0] = L.w_up; po.K[0] = Dl; po.A[1] = s; po.W[1] = L.shared_down;
+    po.K[1] = Fs; po.T = T; po.N = Dh; po.outf = out;
+    return launch_dense(po, part, cnt + 2 * cstride, stream);
 }
 
 }  // namespace k3moe

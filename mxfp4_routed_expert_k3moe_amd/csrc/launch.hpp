@@ -119,6 +119,33 @@ hipError_t launch_chunk_mx(const DevWeights& W, const float* x, int T, const int
                            int K, int parts, float* y, int32_t* n_unique_out, const ChunkMxWorkspace& ws,
                            hipStream_t stream);
 
+// ------------------------------------------------------------------ dense bf16 products (LatentMoE, T >= 2)
+enum { DENSE_F32 = 0, DENSE_SITU = 1 };
+constexpr int kDenseMaxSplits = 16;
+constexpr int kDenseMaxSplitItems = 1024;  // work items of a launch whose reduction is split
+// out[T, N] = A[0] W[0]^T (+ A[1] W[1]^T over a second segment when K[1] > 0), fp32
+// (DENSE_F32); or bf16 SiTU(A[0] W[0]^T, A[0] Wu^T) (DENSE_SITU, one segment).  A [T, K],
+// W [N, K] row-major bf16; N and each K multiples of 32.
+struct DenseProblem {
+    int epi;
+    const uint16_t* A[2];
+    const uint16_t* W[2];
+    const uint16_t* Wu;
+    int K[2];
+    int T, N;
+    float* outf;
+    uint16_t* outb;
+};
+struct DensePlan {
+    int ms, mtiles, ntiles, splits;
+};
+DensePlan dense_plan(const DenseProblem& p, int slots);
+size_t dense_part_bytes(int T);  // split partials of one launch
+size_t dense_cnt_bytes();        // counters of one launch
+// counters of ncnt launches (back to back, dense_cnt_bytes() apart) set to zero
+hipError_t launch_dense_clear(int32_t* cnt, int ncnt_launches, hipStream_t stream);
+hipError_t launch_dense(const DenseProblem& p, float* part, int32_t* cnt, hipStream_t stream);
+
 // ------------------------------------------------------------------ LatentMoE block
 struct LatentDims {
     int Dh, Dl, F, Fs;  // hidden width, latent width (= expert D), expert width, shared width

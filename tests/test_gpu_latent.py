@@ -75,10 +75,38 @@ def test_latent_deterministic():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("T", [5, 70])
+@pytest.mark.parametrize("T", [2, 5, 70, 300])
 def test_latent_ragged_token_counts(T):
-    """Token counts that are not multiples of the 64-token grouping block."""
+    """Token counts that are not multiples of the 64-token grouping block; 300 spans
+    three 128-row token tiles of the dense products, the last one ragged."""
     _run(synth.LATENT["latent_tiny"], T=T, what=f"tiny T={T}")
+
+
+def test_latent_widths_not_multiple_of_64():
+    """Hidden width 544 and shared width 288: reductions that end half-way through
+    a 64-column step and output widths that end inside a column tile."""
+    import dataclasses
+    lc = dataclasses.replace(synth.LATENT["latent_tiny"], name="latent_tiny_544", Dh=544, Fs=288)
+    _run(lc, T=40, what="tiny Dh=544 Fs=288 T=40")
+
+
+def test_latent_k3_chunk_deterministic():
+    """Split reductions of the K3-shaped dense products are summed in split order:
+    two runs give the same bits whichever split of a tile finishes last."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    lc = synth.LATENT["latent32"]
+    cfg = lc.experts
+    _, L = _dense_device(lc)
+    W = device_weights(cfg)
+    h, logits, bias = synth.latent_activations(lc, T=64)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    args = (L, W, torch.from_numpy(h).to(torch.bfloat16).cuda(), torch.from_numpy(idx).cuda(),
+            torch.from_numpy(w).cuda())
+    a = lib.latent_forward(*args).cpu().numpy()
+    b = lib.latent_forward(*args).cpu().numpy()
+    assert np.isfinite(a).all()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 def test_latent_single_expert_per_token():

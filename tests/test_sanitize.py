@@ -57,6 +57,6 @@ def test_host_code_under_asan_ubsan(tmp_path):
     san = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all"]
     _run([CLANGXX, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer"] + san +
          ["-I", os.path.join(ROOT, "include"), os.path.join(HERE, "host_driver.cpp")] + objs +
-         ["-o", exe, "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas", "-lamdhip64"])
+         ["-o", exe, "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lamdhip64"])
     r = _run([exe], env=ENV)
     assert "all checks passed" in r.stdout
