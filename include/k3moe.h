@@ -59,6 +59,10 @@ extern "C" {
 #define K3MOE_PRUNED (-1)       /* routing slot dropped by top-p (k3moe_route_topp)   */
 #define K3MOE_MAX_E 4096        /* experts per layer                                  */
 #define K3MOE_MAX_DIM 8192      /* latent width D and expert width F                  */
+#define K3MOE_MAX_ROW_ELEMS (1ll << 31) /* chunk paths: T*K*max(D, F) (and for the LatentMoE
+                                           block T*max(d_hidden, d_shared)) at most this many
+                                           elements: the GEMM kernels address their
+                                           activation rows with 32-bit byte offsets      */
 #define K3MOE_NOALLOC_SCRATCH_BYTES ((2u << 20) + (64u << 10)) /* per device, k3moe_forward_decode_noalloc */
 
 /* Workspace kinds for k3moe_workspace_size(). */
@@ -241,7 +245,8 @@ int k3moe_decode_down(const k3moe_weights_t *W, const float *h, const int32_t *i
  * x [T, D] fp32 (16-byte aligned), idx [T, K] int32 (K3MOE_PRUNED slots skipped),
  * w [T, K] fp32, y [T, D] fp32; n_unique (device int32, nullable) receives the
  * union size, or -1 for invalid routing, in which case every element of y is NaN.
- * ws: k3moe_workspace_size(K3MOE_OP_CHUNK, T, K, W) bytes.
+ * ws: k3moe_workspace_size(K3MOE_OP_CHUNK, T, K, W) bytes.  T*K <= 2^30 and
+ * T*K*max(D, F) <= K3MOE_MAX_ROW_ELEMS, else K3MOE_E_DIM.
  */
 int k3moe_forward_chunk(const k3moe_weights_t *W, const float *x, int32_t T, const int32_t *idx,
                         const float *w, int32_t K, float *y, int32_t *n_unique, void *ws,

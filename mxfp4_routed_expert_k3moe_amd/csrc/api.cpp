@@ -2,6 +2,8 @@
 // code, before anything is launched), the gfx950 device check, workspace carving
 // and the kernel launches on the caller's stream.  Nothing here allocates device
 // memory or synchronizes.
+#include <algorithm>
+
 #include "k3moe.h"
 
 #include <hip/hip_runtime.h>
@@ -218,6 +220,12 @@ int k3moe_decode_down(const k3moe_weights_t* W, const float* h, const int32_t* i
     return finish(k3moe::launch_decode_down(dw, h, idx, w, K, dws.ypart, y, static_cast<hipStream_t>(stream)));
 }
 
+// The chunk GEMMs address activation rows (x by token, h by pair) with 32-bit
+// byte offsets: T*K*max(D, F) 16-bit elements must stay within 2^32 bytes.
+static bool chunk_rows_ok(int32_t T, int32_t K, const k3moe_weights_t* W) {
+    return (long long)T * K * std::max(W->d_model, W->d_ff) <= K3MOE_MAX_ROW_ELEMS;
+}
+
 static int forward_chunk_any(const k3moe_weights_t* W, const float* x32, const uint16_t* xb16, int32_t T,
                              const int32_t* idx, const float* w, int32_t K, float* y, int32_t* n_unique, void* ws,
                              size_t ws_bytes, void* stream) {
@@ -226,7 +234,7 @@ static int forward_chunk_any(const k3moe_weights_t* W, const float* x32, const u
     if (rc != K3MOE_OK) return rc;
     if (!x || !idx || !w || !y || !ws) return K3MOE_E_NULL;
     if (T < 1 || K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return K3MOE_E_DIM;
-    if ((long long)T * K > (1ll << 30)) return K3MOE_E_DIM;
+    if ((long long)T * K > (1ll << 30) || !chunk_rows_ok(T, K, W)) return K3MOE_E_DIM;
     if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return K3MOE_E_ALIGN;
     if (ws_bytes < k3moe::chunk_workspace_bytes(T, K, W->n_experts, W->d_model, W->d_ff))
         return K3MOE_E_WORKSPACE;
@@ -260,7 +268,7 @@ int k3moe_forward_chunk_mx(const k3moe_weights_t* W, const float* x, int32_t T, 
     if (T < 1 || K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return K3MOE_E_DIM;
     if (parts != 1 && parts != 2) return K3MOE_E_DIM;
     if (W->d_model % 128 || W->d_ff % 128) return K3MOE_E_DIM;
-    if ((long long)T * K > (1ll << 30)) return K3MOE_E_DIM;
+    if ((long long)T * K > (1ll << 30) || !chunk_rows_ok(T, K, W)) return K3MOE_E_DIM;
     if (!aligned16(x) || !aligned16(y) || !aligned16(ws)) return K3MOE_E_ALIGN;
     if (ws_bytes < k3moe::chunk_mx_workspace_bytes(T, K, W->n_experts, W->d_model, W->d_ff))
         return K3MOE_E_WORKSPACE;
@@ -293,7 +301,9 @@ int k3moe_latent_forward(const k3moe_latent_t* L, const k3moe_weights_t* W, cons
         !L->shared_up || !L->shared_down)
         return K3MOE_E_NULL;
     if (!latent_ok(L, W) || T < 1 || K < 1 || K > K3MOE_MAX_K || K > W->n_experts) return K3MOE_E_DIM;
-    if ((long long)T * K > (1ll << 30)) return K3MOE_E_DIM;
+    if ((long long)T * K > (1ll << 30) || !chunk_rows_ok(T, K, W) ||
+        (long long)T * std::max(L->d_hidden, L->d_shared) > K3MOE_MAX_ROW_ELEMS)
+        return K3MOE_E_DIM;
     if (!aligned16(h) || !aligned16(out) || !aligned16(ws) || !aligned16(L->w_down) || !aligned16(L->w_up) ||
         !aligned16(L->norm) || !aligned16(L->shared_gate) || !aligned16(L->shared_up) || !aligned16(L->shared_down))
         return K3MOE_E_ALIGN;

@@ -196,6 +196,26 @@ def test_latent_validation():
     assert f(ctypes.byref(mis), ctypes.byref(s), vp, 32, vp, vp, 16, vp, vp, need, None) == k3.K3MOE_E_ALIGN
     assert f(ctypes.byref(L), ctypes.byref(s), vp, 0, vp, vp, 16, vp, vp, need, None) == k3.K3MOE_E_DIM
     assert f(ctypes.byref(L), ctypes.byref(s), vp, 32, vp, vp, 16, vp, vp, need - 1, None) == k3.K3MOE_E_WORKSPACE
+    # T*max(d_hidden, d_shared) beyond 2^31 elements (32-bit row offsets of the dense products)
+    assert f(ctypes.byref(L), ctypes.byref(_struct()), vp, (1 << 31) // 7168 + 1, vp, vp, 1, vp, vp, 1 << 62,
+             None) == k3.K3MOE_E_DIM
+
+
+def test_chunk_row_offsets_bound():
+    """T*K*max(D, F) above 2^31 elements is a size error on every chunk entry point (the
+    GEMM kernels address activation rows with 32-bit byte offsets); just under it the
+    dimensions pass and the small workspace is what is refused."""
+    lib = k3.load()
+    s = _struct()
+    p = 256
+    limit = (1 << 31) // (16 * 3584)  # K = 16, max(D, F) = 3584
+    over, under = limit + 1, limit
+    ck, cb, mx = lib.k3moe_forward_chunk, lib.k3moe_forward_chunk_bf16, lib.k3moe_forward_chunk_mx
+    for fn in (ck, cb):
+        assert fn(ctypes.byref(s), p, over, p, p, 16, p, None, p, 1 << 62, None) == k3.K3MOE_E_DIM
+        assert fn(ctypes.byref(s), p, under, p, p, 16, p, None, p, 100, None) == k3.K3MOE_E_WORKSPACE
+    assert mx(ctypes.byref(s), p, over, p, p, 16, 1, p, None, p, 1 << 62, None) == k3.K3MOE_E_DIM
+    assert mx(ctypes.byref(s), p, under, p, p, 16, 1, p, None, p, 100, None) == k3.K3MOE_E_WORKSPACE
 
 
 def test_binding_refuses_cpu_tensors():
