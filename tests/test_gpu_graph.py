@@ -1,4 +1,4 @@
-"""The decode path and the LatentMoE one-token block replayed from a HIP graph
+"""The decode path, the chunk path and the LatentMoE block replayed from a HIP graph
 (torch.cuda.CUDAGraph around the same library calls, as the benchmark times
 them): every replay, with eager work and synchronizations between replays, must
 reproduce the eager outputs bit for bit."""
@@ -95,3 +95,81 @@ def test_latent_one_token_graph_replays_equal_eager():
     assert np.all(np.isfinite(want.cpu().numpy()))
     log("latent one-token graph: 3 replays equal the eager outputs")
     del g
+
+
+def _replays_equal(torch, fn, outs, n_rep=3, what=""):
+    """Capture fn() once; each replay (outputs poisoned first, eager work on other data
+    between replays) must reproduce the eager outputs bit for bit."""
+    fn()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    g = _capture(torch, lambda i: fn(), 1)
+    for rep in range(n_rep):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for o, wnt in zip(outs, want):
+            assert torch.equal(o.view(torch.int32), wnt.view(torch.int32)), f"{what}: replay {rep} differs"
+        fn(eager_other=True)
+        torch.cuda.synchronize()
+    del g
+    return want
+
+
+def test_chunk_graph_replays_equal_eager():
+    """The fp32 chunk path at K3 shape (group, split of x, fp16 / bf16 GEMM items,
+    combine) replayed from a graph: no memset or host-side state in the capture."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = synth.CONFIGS["prefill32"]
+    W = device_weights(cfg)
+    x, lg, b = synth.activations(cfg)
+    x_d = torch.from_numpy(x).cuda()
+    x_other = torch.flip(x_d, dims=[0]).contiguous()
+    idx, w = lib.route(torch.from_numpy(lg).cuda(), torch.from_numpy(b).cuda(), cfg.K)
+    y = torch.empty((x.shape[0], cfg.D), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y)
+    ws = torch.empty(lib.workspace_size(lib.OP_CHUNK, x.shape[0], cfg.K, W), dtype=torch.uint8, device="cuda")
+
+    def fn(eager_other=False):
+        if eager_other:
+            lib.forward_chunk(W, x_other, idx, w, y=y2, ws=ws)
+        else:
+            lib.forward_chunk(W, x_d, idx, w, y=y, ws=ws)
+
+    want = _replays_equal(torch, fn, [y], what="chunk")
+    assert np.all(np.isfinite(want[0].cpu().numpy()))
+    log("chunk graph (prefill32, fp32 x): 3 replays equal the eager output")
+
+
+def test_latent_chunk_graph_replays_equal_eager():
+    """The LatentMoE block for 32 tokens at K3 shape (dense MFMA products with split
+    reductions whose counters the block clears itself, the routed chunk path, RMSNorm)
+    replayed from a graph."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    lc = synth.LATENT["latent32"]
+    cfg = lc.experts
+    W = device_weights(cfg)
+    dh = synth.latent_dense_host(lc)
+    L = lib.LatentWeights({k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in dh.items()}, lc.eps)
+    h, lg, b = synth.latent_activations(lc)
+    T = h.shape[0]
+    h_d = torch.from_numpy(h).to(torch.bfloat16).cuda()
+    h_other = torch.flip(h_d, dims=[0]).contiguous()
+    idx, w = lib.route(torch.from_numpy(lg).cuda(), torch.from_numpy(b).cuda(), cfg.K)
+    out = torch.empty((T, lc.Dh), dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out)
+    ws = torch.empty(lib.load().k3moe_latent_workspace_size(L.ref(), T, cfg.K, W.ref()), dtype=torch.uint8,
+                     device="cuda")
+
+    def fn(eager_other=False):
+        if eager_other:
+            lib.latent_forward(L, W, h_other, idx, w, out=out2, ws=ws)
+        else:
+            lib.latent_forward(L, W, h_d, idx, w, out=out, ws=ws)
+
+    want = _replays_equal(torch, fn, [out], what="latent chunk")
+    assert np.all(np.isfinite(want[0].cpu().numpy()))
+    log(f"latent chunk graph (T={T}, K3 shape): 3 replays equal the eager output")
