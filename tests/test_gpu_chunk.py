@@ -83,6 +83,23 @@ def test_chunk_tiles_and_tails(E, K, D, F, T):
     _full_case(cfg, f"E={E} K={K} D={D} F={F} T={T}", bf16=True)
 
 
+@pytest.mark.parametrize("scale_lo,scale_hi", [(120, 130), (100, 113)])
+def test_chunk_max_widths(scale_lo, scale_hi):
+    """D = F = 8192 (the largest widths) with 24 pairs per expert: 96-row tiles whose
+    scale rows for eight waves would not fit in LDS, so the four-wave kernels run;
+    scale bytes 120..130 put every item on the fp16 body, 100..113 (below the fp16
+    normals) every item on the bf16 + low-part fallback.  A CPU emulation of the two
+    roundings on these weights gives 2.3e-3 and 1.7e-3.  (Scale bytes up to 140 make
+    8192-term gate sums large enough that the SiTU-GLU transitions amplify either
+    rounding of x past the budget: 1.8e-2 for fp16 and for bf16 + low part alike, the
+    same in the emulation as on the GPU.)"""
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name=f"chmax{scale_lo}", E=4, K=2, D=8192, F=8192, T=48,
+                       weight_seed=870 + scale_lo, act_seed=871, scale_lo=scale_lo, scale_hi=scale_hi, path="chunk")
+    _full_case(cfg, f"D=F=8192 scales {scale_lo}..{scale_hi}")
+    if scale_lo == 120:
+        _full_case(cfg, "D=F=8192 bf16 x", bf16=True)
+
+
 def test_chunk_prefill32():
     """fp32 x: within the budget, and well inside what the bf16 entry reaches on the
     same tokens rounded to bf16 (measured against the exact block on the fp32 x),
