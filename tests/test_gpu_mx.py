@@ -134,6 +134,17 @@ def test_chunk_mx_tiles_and_tails(E, K, D, F, T, parts):
 
 
 @pytest.mark.parametrize("parts", [1, 2])
+def test_chunk_mx_max_widths(parts):
+    """D = F = 8192 with 24 pairs per expert: 96-row tiles on the four-wave MX
+    kernels (eight waves' scale rows would not fit in LDS); compared with the
+    oracle's MX variant only (the format's distance from the exact block depends on
+    the weights' conditioning, not on the kernel)."""
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name="mxmax", E=4, K=2, D=8192, F=8192, T=48, weight_seed=880,
+                       act_seed=881, scale_lo=120, scale_hi=130, path="chunk")
+    _case(cfg, "D=F=8192", parts, exact=False)
+
+
+@pytest.mark.parametrize("parts", [1, 2])
 def test_chunk_mx_prefill32(parts):
     _case(synth.CONFIGS["prefill32"], "prefill32", parts)
 
