@@ -90,6 +90,15 @@ def test_latent_widths_not_multiple_of_64():
     _run(lc, T=40, what="tiny Dh=544 Fs=288 T=40")
 
 
+@pytest.mark.parametrize("T", [1, 40])
+def test_latent_max_widths(T):
+    """Hidden and shared widths at the largest supported 8192: the one-token GEMV
+    kernels and the chunk's dense MFMA products (reductions of 8192 and of 256 + 8192)."""
+    import dataclasses
+    lc = dataclasses.replace(synth.LATENT["latent_tiny"], name="latent_tiny_8192", Dh=8192, Fs=8192)
+    _run(lc, T=T, what=f"tiny Dh=Fs=8192 T={T}")
+
+
 def test_latent_k3_chunk_deterministic():
     """Split reductions of the K3-shaped dense products are summed in split order:
     two runs give the same bits whichever split of a tile finishes last."""
