@@ -56,8 +56,8 @@ __host__ __device__ constexpr int item_floats(int ms) { return DWAVES * ms * DNS
 
 struct DenseArgs {
     const uint16_t* A[2];   // per segment: activations [T, K[s]] bf16, row-major
-    const uint16_t* W[2];   // per segment: weights [N, K[s]] bf16 (EPI_SITU: the gate half)
-    const uint16_t* Wu;     // EPI_SITU: the up half [N, K[0]]
+    const uint16_t* W[2];   // per segment: weights [N, K[s]] bf16 (DENSE_SITU: the gate half)
+    const uint16_t* Wu;     // DENSE_SITU: the up half [N, K[0]]
     int K[2];               // per segment reduction length (multiple of 32; K[1] = 0: one segment)
     int nst0, nst;          // steps of segment 0, of both
     int T, N;
