@@ -82,12 +82,52 @@ def test_latent_ragged_token_counts(T):
     _run(synth.LATENT["latent_tiny"], T=T, what=f"tiny T={T}")
 
 
+def test_latent_latent_width_not_multiple_of_64():
+    """A latent width of 288 (the routed experts' d_model): the out product's first
+    segment (W_up r) ends half-way through a step and the second (S_d s) starts on a
+    fresh one."""
+    import dataclasses
+    base = synth.LATENT["latent_tiny"]
+    lc = dataclasses.replace(base, name="latent_tiny_288", experts=synth.scaled(base.experts, D=288), Dh=544, Fs=288)
+    _run(lc, T=40, what="tiny Dl=288 Dh=544 Fs=288 T=40")
+    _run(lc, T=1, what="tiny Dl=288 Dh=544 Fs=288 T=1")
+
+
 def test_latent_widths_not_multiple_of_64():
     """Hidden width 544 and shared width 288: reductions that end half-way through
     a 64-column step and output widths that end inside a column tile."""
     import dataclasses
     lc = dataclasses.replace(synth.LATENT["latent_tiny"], name="latent_tiny_544", Dh=544, Fs=288)
     _run(lc, T=40, what="tiny Dh=544 Fs=288 T=40")
+
+
+def test_latent_k3_256_tokens_sampled():
+    """The 256-token block at K3 shape, in the configuration the benchmark times (the
+    decode1 experts, 128-row token tiles, split reductions), checked on 24 sampled
+    tokens: every output token depends only on its own inputs."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    lc = synth.LATENT["latent1"]
+    cfg = lc.experts
+    host, L = _dense_device(lc)
+    W = device_weights(cfg)
+    h, logits, bias = synth.latent_activations(lc, T=256)
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    log(f"latent K3 256 tokens: T=256 Dh={lc.Dh} Dl={cfg.D} Fs={lc.Fs}")
+    out = lib.latent_forward(L, W, torch.from_numpy(h).to(torch.bfloat16).cuda(), torch.from_numpy(idx).cuda(),
+                             torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    s = np.random.default_rng(256).choice(256, 24, replace=False)
+    s.sort()
+    used = np.unique(idx[s])
+    Wh = synth.weights_host(cfg, used)
+    local = np.searchsorted(used, idx[s]).astype(np.int32)
+    dense = {"w_dn": host["w_down"], "w_up": host["w_up"], "norm": host["norm"], "eps": lc.eps,
+             "sg": host["shared_gate"], "su": host["shared_up"], "sd": host["shared_down"]}
+    want = oracle.latent_forward(dense, Wh, h[s], local, w[s])
+    assert_close(got[s], want, TOL, "latent K3 256 tokens (24 sampled)")
+    assert np.isfinite(got).all()
 
 
 @pytest.mark.parametrize("T", [1, 40])
