@@ -167,6 +167,31 @@ def test_latent_single_expert_per_token():
 
 
 @pytest.mark.parametrize("T", [1, 6])
+def test_latent_every_slot_pruned(T):
+    """With every routing slot pruned the routed aggregate is 0, RMSNorm(0) = 0, and the
+    block's output is the shared experts alone (against the oracle, which skips the
+    pruned slots the same way)."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    lc = synth.LATENT["latent_tiny"]
+    cfg = lc.experts
+    host, L = _dense_device(lc)
+    W = device_weights(cfg)
+    h, logits, bias = synth.latent_activations(lc, T=T)
+    idx = np.full((T, cfg.K), -1, dtype=np.int32)
+    w = np.zeros((T, cfg.K), dtype=np.float32)
+    out = lib.latent_forward(L, W, torch.from_numpy(h).to(torch.bfloat16).cuda(), torch.from_numpy(idx).cuda(),
+                             torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    Wh = synth.weights_host(cfg, np.array([0]))
+    dense = {"w_dn": host["w_down"], "w_up": host["w_up"], "norm": host["norm"], "eps": lc.eps,
+             "sg": host["shared_gate"], "su": host["shared_up"], "sd": host["shared_down"]}
+    want = oracle.latent_forward(dense, Wh, h, idx, w)
+    assert_close(got, want, TOL, f"latent every slot pruned T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 6])
 def test_latent_invalid_routing_is_nan(T):
     """An expert id out of range makes the routed block's output NaN (decode: the
     token's row; chunk: the whole chunk, n_unique = -1), and the block's output with it."""

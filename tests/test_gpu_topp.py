@@ -136,3 +136,47 @@ def test_decode_pruned_anywhere(E, K, D, F):
                            torch.from_numpy(w[0]).cuda())
     torch.cuda.synchronize()
     assert np.isnan(y.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("entry", ["fp32", "bf16", "mx1", "mx2"])
+def test_chunk_pruned_tokens_and_empty_union(entry):
+    """Tokens with every slot pruned contribute y = 0 (the combine of no slot), the
+    others their kept slots; a chunk whose every slot is pruned has an empty union
+    (n_unique 0, no GEMM work item) and y = 0 throughout."""
+    torch = torch_cuda()
+    from mxfp4_routed_expert_k3moe_amd import lib
+    cfg = synth.scaled(synth.CONFIGS["tiny"], name="prune_chunk", E=8, K=2, D=256, F=128, T=70, path="chunk")
+    x, logits, bias = synth.activations(cfg, bf16=entry == "bf16")
+    idx, w, _ = oracle.route(logits, bias, cfg.K)
+    idx = idx.copy()
+    w = w.copy()
+    idx[:10] = -1  # tokens 0..9: every slot pruned
+    w[:10] = 0.0
+    idx[10:20, 1] = -1  # tokens 10..19: the second slot pruned, the weights renormalized to the first
+    w[10:20, 1] = 0.0
+    w[10:20, 0] = 1.0
+    W = device_weights(cfg)
+
+    def run(idx_, w_):
+        nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+        xd = torch.from_numpy(x).cuda()
+        args = (W, xd.to(torch.bfloat16) if entry == "bf16" else xd, torch.from_numpy(idx_).cuda(),
+                torch.from_numpy(w_).cuda())
+        if entry.startswith("mx"):
+            y = lib.forward_chunk_mx(*args, parts=int(entry[2]), n_unique=nu)
+        else:
+            y = lib.forward_chunk(*args, n_unique=nu)
+        torch.cuda.synchronize()
+        return y.cpu().numpy(), int(nu.item())
+
+    got, nu = run(idx, w)
+    assert nu == len(np.unique(idx[idx >= 0]))
+    assert np.all(got[:10] == 0.0)
+    mx = int(entry[2]) if entry.startswith("mx") else 0
+    want = oracle_forward_subset(cfg, x, idx, w, mx=mx)
+    assert_close(got, want, 5e-3, f"chunk {entry} with pruned tokens")
+    empty_idx = np.full_like(idx, -1)
+    got0, nu0 = run(empty_idx, np.zeros_like(w))
+    assert nu0 == 0
+    assert np.all(got0 == 0.0)
+    log(f"chunk {entry}: pruned tokens exact zeros, empty union y = 0")
