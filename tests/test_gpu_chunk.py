@@ -67,12 +67,20 @@ def test_chunk_tiny_ragged():
     _full_case(cfg, "tiny T=5")
 
 
+def test_chunk_one_token():
+    """A chunk of one token: one pair per touched expert, 16-row tiles."""
+    cfg = synth.scaled(synth.CONFIGS["tiny"], T=1, path="chunk")
+    _full_case(cfg, "tiny T=1")
+    _full_case(cfg, "tiny T=1 bf16 x", bf16=True)
+
+
 def test_chunk_tiny_bf16_entry():
     cfg = synth.scaled(synth.CONFIGS["tiny"], T=70, path="chunk", x_bf16=True)
     _full_case(cfg, "tiny T=70 bf16 x")
 
 
-@pytest.mark.parametrize("E,K,D,F,T", [(8, 4, 512, 384, 600), (16, 4, 352, 160, 100), (6, 6, 256, 128, 131)])
+@pytest.mark.parametrize("E,K,D,F,T", [(8, 4, 512, 384, 600), (16, 4, 352, 160, 100), (6, 6, 256, 128, 131),
+                                     (64, 64, 256, 128, 20), (4096, 16, 128, 64, 3)])
 def test_chunk_tiles_and_tails(E, K, D, F, T):
     """Several tiles per expert, a ragged last tile, and widths that are not
     multiples of the 128-wide steps and column blocks (the low part's rows are
