@@ -1015,10 +1015,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             const float nan = __builtin_nanf("");
             acc = make_float4(nan, nan, nan, nan);
         } else {
-            for (int k = 0; k < K; ++k) {
-                if (idx[t * K + k] == K3MOE_PRUNED) continue;
-                const float4 v = reinterpret_cast<const float4*>(ytk + ((t * K + k) * (size_t)D))[dd];
-                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            // eight slots' loads in flight at once (every pair row exists, so the
+            // loads need no branch); a pruned slot's row is read but not added
+            for (int k0 = 0; k0 < K; k0 += 8) {
+                float4 v[8];
+                bool live[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int k = min(k0 + j, K - 1);
+                    live[j] = k0 + j < K && idx[t * K + k] != K3MOE_PRUNED;
+                    v[j] = reinterpret_cast<const float4*>(ytk + ((t * K + k) * (size_t)D))[dd];
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (live[j]) {
+                        acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w;
+                    }
+                }
             }
         }
         reinterpret_cast<float4*>(y)[i] = acc;
