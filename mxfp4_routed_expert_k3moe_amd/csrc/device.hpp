@@ -131,19 +131,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// One DPP move of a 32-bit value (lanes outside ROW_MASK's rows keep their own).
+// max(v, v moved by one DPP pattern); lanes outside ROW_MASK's rows see 0, the
+// identity of the maximum, which lets the compiler fold the move into the max.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false));
 }
 
 // Maximum over each row of 16 lanes, returned to every lane of the row: swap
 // neighbours, swap pairs, rotate by 4, rotate by 8.
 __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-    v = max(v, dpp_u32<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
-    v = max(v, dpp_u32<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
-    v = max(v, dpp_u32<0x124, 0xF>(v));  // row_ror:4
-    v = max(v, dpp_u32<0x128, 0xF>(v));  // row_ror:8
+    v = dpp_max_u32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_u32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_u32<0x124, 0xF>(v);  // row_ror:4
+    v = dpp_max_u32<0x128, 0xF>(v);  // row_ror:8
     return v;
 }
 

@@ -22,12 +22,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     __shared__ RouteScratch rs;
     extern __shared__ double sig_e[];  // [E] double sigmoid of each expert's logit
     const int t = blockIdx.x;
-    route_block<PL>(logits + (size_t)t * E, bias, E, K, top_p, rs, sig_e);
-    if ((int)threadIdx.x < K) {
-        idx[(size_t)t * K + threadIdx.x] = rs.out_idx[threadIdx.x];
-        w[(size_t)t * K + threadIdx.x] = rs.out_w[threadIdx.x];
-    }
-    if (n_kept != nullptr && threadIdx.x == 0) n_kept[t] = rs.kept;
+    route_block<PL>(logits + (size_t)t * E, bias, E, K, top_p, rs, sig_e, idx + (size_t)t * K, w + (size_t)t * K,
+                    n_kept != nullptr ? n_kept + t : nullptr);
 }
 
 template <int PL>

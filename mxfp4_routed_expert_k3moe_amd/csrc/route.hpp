@@ -12,11 +12,13 @@
 // key and, among equal keys, the lower id.
 //
 // Wave w of the 4 holds experts [w*Q, (w+1)*Q) in registers.  A threshold pass
-// keeps the codes at or above a bound that provably admits the top K (a few dozen
-// of 896), and those rank themselves against each other in parallel.  When more
-// than kCandCap codes pass (flat or tied keys), each wave instead finds its top-K
-// with K rounds of a 32-bit wave max on the key (a second reduction on the id only
-// when keys tie) and the 4*K survivors rank themselves.
+// keeps the codes whose key is at or above a bound that provably admits the top K
+// (two to three dozen of 896): each wave finds the ceil(K/4)-th largest of its own
+// keys with a few rounds of a wave max, and the bound is the least of the four.
+// The candidates rank themselves against each other (wave 0 alone when there
+// are at most 64), and wave 0 writes the result.  When more than kCandCap codes pass (flat or tied keys), each wave
+// instead finds its top-K with K rounds of a 32-bit wave max on the key (a second
+// reduction on the id only when keys tie) and the 4*K survivors rank themselves.
 #pragma once
 
 #include "device.hpp"
@@ -41,8 +43,8 @@ __device__ __forceinline__ double sigmoid_d(float l) { return 1.0 / (1.0 + exp(-
 // keep their own value.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = row16_max_u32(v);
-    v = max(v, dpp_u32<0x142, 0xA>(v));  // row_bcast:15 into rows 1, 3
-    v = max(v, dpp_u32<0x143, 0xC>(v));  // row_bcast:31 into rows 2, 3
+    v = dpp_max_u32<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+    v = dpp_max_u32<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
@@ -94,24 +96,23 @@ constexpr int kCandCap = 128;  // candidates the threshold pass may keep
 
 // LDS of one token's routing; sig_e ([E] doubles) is passed separately.
 struct RouteScratch {
-    unsigned long long lmax[4][64];     // each lane's best code, per wave
-    unsigned long long kth[4];          // per wave: the K-th largest of its lane bests (0: fewer than K)
+    uint32_t tw[4];                     // per wave: the ceil(K/4)-th largest key word it holds (0: none)
     unsigned long long pool[kCandCap];  // codes at or above the threshold
     int npool;
     unsigned long long cand[4 * K3MOE_MAX_K_DEV];
-    double sel_sig[K3MOE_MAX_K_DEV];
+    double sel_sig[K3MOE_MAX_K_DEV];  // the selection by rank
     int sel_id[K3MOE_MAX_K_DEV];
-    int out_idx[K3MOE_MAX_K_DEV];  // the routing result, slot order
-    float out_w[K3MOE_MAX_K_DEV];
-    int kept;  // slots 0..kept-1 hold experts, the rest K3MOE_PRUNED
 };
 
-// Route token logits l [E] (bias [E]) into rs.out_idx / rs.out_w / rs.kept.  Called
-// by all 256 threads of the workgroup (4 waves); ends with a barrier, after which
-// the result is visible to every thread.  top_p outside (0, 1) keeps all K.
+
+// Route token logits l [E] (bias [E]); wave 0 writes the slot-order result to
+// idx [K], w [K] and, when given, n_kept.  Called by all 256 threads of the
+// workgroup (4 waves).  top_p outside (0, 1) keeps all K.
 template <int PL>
 __device__ __forceinline__ void route_block(const float* __restrict__ l, const float* __restrict__ bias, int E,
-                                            int K, double top_p, RouteScratch& rs, double* sig_e) {
+                                            int K, double top_p, RouteScratch& rs, double* sig_e,
+                                            int32_t* __restrict__ idx, float* __restrict__ w,
+                                            int32_t* __restrict__ n_kept) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int Q = (E + 3) / 4;  // experts per wave
 
@@ -137,42 +138,71 @@ __device__ __forceinline__ void route_block(const float* __restrict__ l, const f
             code[j] = make_code(key_order(key), e);
         }
     }
-    // Threshold pass.  T_w = the K-th largest of wave w's 64 lane bests (0 when the
-    // wave has fewer than K experts); T = max_w T_w.  The wave that attains T has K
-    // lanes whose best code is >= T, so at least K codes are >= T, hence the K-th
-    // largest code overall is >= T and every selected code is in the pool of codes
-    // >= T (about 54 of 896 for the 16-of-896 workloads).  Codes are unique, so
-    // ranking the pool gives the exact selection in order.
-    unsigned long long best = 0ull;
-#pragma unroll
-    for (int j = 0; j < PL; ++j) best = code[j] > best ? code[j] : best;
-    rs.lmax[wave][lane] = best;
-    if (lane == 0) rs.kth[wave] = 0ull;
-    if (threadIdx.x == 0) rs.npool = 0;
-    __syncthreads();
+    // Threshold pass.  Kw = ceil(K/4).  T_w = the Kw-th largest key word of wave w's
+    // codes, counting each lane once per round (a lane may hold several codes of
+    // one key, so the count is a lower bound), or 0 when the wave holds fewer.  Wave
+    // w has at least Kw codes with key >= T_w, so with T = min_w T_w at least 4 Kw
+    // >= K codes have key >= T: the K-th largest code overall has key >= T, and so
+    // has every selected code.  The pool of codes with key >= T is about 30 of 896
+    // for the 16-of-896 workloads; codes are unique, so ranking the pool gives the
+    // exact selection in order.
     {
-        int r = 0;  // lane bests of this wave above this lane's (a nonzero best is unique)
-#pragma unroll 16
-        for (int i = 0; i < 64; ++i) r += rs.lmax[wave][i] > best;
-        if (r == K - 1 && best != 0ull) rs.kth[wave] = best;
-    }
-    __syncthreads();
-    const unsigned long long T0 = rs.kth[0] > rs.kth[1] ? rs.kth[0] : rs.kth[1];
-    const unsigned long long T1 = rs.kth[2] > rs.kth[3] ? rs.kth[2] : rs.kth[3];
-    const unsigned long long T = T0 > T1 ? T0 : T1;
+        const int Kw = (K + 3) >> 2;
+        uint32_t kw[PL];
+        uint32_t head = 0u;
 #pragma unroll
-    for (int j = 0; j < PL; ++j) {
-        const bool in = code[j] != 0ull && code[j] >= T;
-        const unsigned long long m = __ballot(in);
-        int base = 0;
-        if (lane == 0 && m != 0ull) base = atomicAdd(&rs.npool, __popcll(m));
-        base = __shfl(base, 0);
-        const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-        if (in && pos < kCandCap) rs.pool[pos] = code[j];
+        for (int j = 0; j < PL; ++j) {
+            kw[j] = (uint32_t)(code[j] >> 32);
+            head = max(head, kw[j]);
+        }
+        uint32_t tw = 0u;
+        int counted = 0;
+        for (int r = 0; r < Kw; ++r) {  // every round retires at least one code
+            const uint32_t m = wave_max_u32(head);
+            if (m == 0u) break;  // fewer than Kw codes in this wave
+            counted += __popcll(__ballot(head == m));
+            if (counted >= Kw) {
+                tw = m;
+                break;
+            }
+            if (head == m) {
+                head = 0u;
+#pragma unroll
+                for (int j = 0; j < PL; ++j) {
+                    kw[j] = kw[j] == m ? 0u : kw[j];
+                    head = max(head, kw[j]);
+                }
+            }
+        }
+        if (lane == 0) rs.tw[wave] = tw;
     }
-    __syncthreads();
+    if (threadIdx.x == 0) rs.npool = 0;
+    __syncthreads();  // thresholds, sigmoids, npool
+    const uint32_t T = min(min(rs.tw[0], rs.tw[1]), min(rs.tw[2], rs.tw[3]));
+    {
+        unsigned long long bal[PL];
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < PL; ++j) {
+            bal[j] = __ballot(code[j] != 0ull && (uint32_t)(code[j] >> 32) >= T);
+            cnt += __popcll(bal[j]);
+        }
+        int base = 0;
+        if (lane == 0 && cnt != 0) base = atomicAdd(&rs.npool, cnt);
+        base = __builtin_amdgcn_readfirstlane(base);
+        const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int j = 0; j < PL; ++j) {
+            const int pos = base + __popcll(bal[j] & below);
+            if (((bal[j] >> lane) & 1ull) && pos < kCandCap) rs.pool[pos] = code[j];
+            base += __popcll(bal[j]);
+        }
+    }
+    __syncthreads();  // the pool
     const int npool = rs.npool;  // block-uniform
     if (npool <= kCandCap) {
+        // thread i ranks pool code i against the others (same-address LDS reads are
+        // broadcasts; unrolled so they overlap)
         if ((int)threadIdx.x < npool) {
             const unsigned long long c = rs.pool[threadIdx.x];
             int rank = 0;
@@ -184,6 +214,8 @@ __device__ __forceinline__ void route_block(const float* __restrict__ l, const f
                 rs.sel_sig[rank] = sig_e[e];
             }
         }
+        // up to 64 codes were ranked by wave 0 itself, which uses the selection next
+        if (npool > 64) __syncthreads();
     } else {
         // too many codes at the threshold (flat or tied keys): K rounds of wave maxima
         wave_topk<PL>(code, K, lane, rs.cand + wave * K);
@@ -206,8 +238,10 @@ __device__ __forceinline__ void route_block(const float* __restrict__ l, const f
                 }
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
+    // wave 0 forms the weights and writes the result (when it ranked the pool alone,
+    // it wrote the selection itself, and a wave's LDS accesses complete in order)
     if (wave == 0) {
         double S = 0.0;  // slot order, as in the definition (reads unrolled, sum in order)
 #pragma unroll 16
@@ -246,16 +280,15 @@ __device__ __forceinline__ void route_block(const float* __restrict__ l, const f
         const unsigned long long km = __ballot(kept);
         if (kept) {  // kept slots, compacted in slot order
             const int slot = __popcll(km & ((1ull << lane) - 1ull));
-            rs.out_idx[slot] = rs.sel_id[lane];
-            rs.out_w[slot] = (float)(sig / Sk);
+            idx[slot] = rs.sel_id[lane];
+            w[slot] = (float)(sig / Sk);
         }
         if (lane >= m && lane < K) {  // the pruned tail (lane here is the output slot)
-            rs.out_idx[lane] = K3MOE_PRUNED;
-            rs.out_w[lane] = 0.0f;
+            idx[lane] = K3MOE_PRUNED;
+            w[lane] = 0.0f;
         }
-        if (lane == 0) rs.kept = m;
+        if (lane == 0 && n_kept != nullptr) *n_kept = m;
     }
-    __syncthreads();
 }
 
 // Candidates per lane in each of the 4 waves for E experts (the PL template argument).

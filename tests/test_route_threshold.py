@@ -1,10 +1,14 @@
-"""The router's threshold pass, restated on the host: the pool of codes at or above
-T = max over the 4 waves of (the K-th largest lane best in that wave) always holds
-the exact top K, and at least K codes.  Brute force over random, tied, flat and
-adversarial key sets with the kernel's expert-to-lane layout (wave w holds experts
-[w*Q, (w+1)*Q), lane l of it the ones with (e - w*Q) % 64 == l), plus the pool
-sizes the 16-of-896 workloads see (the kernel ranks at most 128 codes and falls
-back to K rounds of wave maxima beyond that)."""
+"""The router's threshold pass, restated on the host: with Kw = ceil(K/4), each of
+the 4 waves takes T_w = the Kw-th largest key it holds, found in rounds of a wave
+maximum over the lanes' best remaining keys (each round counts every lane whose
+best equals the maximum once, then retires all of those lanes' codes of that key;
+0 when the wave runs out), and T = min_w T_w.  The pool of codes with key >= T
+always holds the exact top K, and at least K codes.  Brute force over random,
+tied, flat and adversarial key sets with the kernel's expert-to-lane layout (wave
+w holds experts [w*Q, (w+1)*Q), lane l of it the ones with (e - w*Q) % 64 == l),
+plus the pool sizes the 16-of-896 workloads see (the kernel ranks at most 128
+codes, with one wave when there are at most 64, and falls back to K rounds of wave
+maxima beyond 128)."""
 import numpy as np
 import pytest
 
@@ -19,25 +23,37 @@ def codes_of(keys):
     return code
 
 
-def threshold_pool(code, K):
-    E = len(code)
+def threshold_pool(keys, K):
+    E = len(keys)
     Q = (E + 3) // 4
-    kth = []
+    Kw = (K + 3) // 4
+    tws = []
     for w in range(4):
-        best = np.zeros(64, np.int64)
-        for i in range(Q):
-            e = w * Q + i
-            if e < E:
-                best[i % 64] = max(best[i % 64], code[e])
-        nz = np.sort(best[best > 0])[::-1]
-        kth.append(nz[K - 1] if len(nz) >= K else 0)
-    T = max(kth)
-    return np.nonzero((code > 0) & (code >= T))[0]
+        lanes = [[keys[e] for e in range(w * Q + l, min(E, (w + 1) * Q), 64)] for l in range(64)]
+        tw, counted = None, 0
+        for _ in range(Kw):
+            heads = [max(v) if v else None for v in lanes]
+            live = [h for h in heads if h is not None]
+            if not live:
+                break  # fewer than Kw codes in this wave: no bound
+            m = max(live)
+            hit = [l for l in range(64) if heads[l] is not None and heads[l] == m]
+            counted += len(hit)
+            if counted >= Kw:
+                tw = m
+                break
+            for l in hit:
+                lanes[l] = [v for v in lanes[l] if v != m]
+        tws.append(tw)
+    if any(t is None for t in tws):
+        return np.arange(E)
+    T = min(tws)
+    return np.nonzero(keys >= T)[0]
 
 
 def check(keys, K):
     code = codes_of(keys)
-    pool = threshold_pool(code, K)
+    pool = threshold_pool(keys, K)
     top = np.argsort(-code, kind="stable")[:K]
     assert len(pool) >= K
     assert set(top.tolist()) <= set(pool.tolist())
