@@ -82,11 +82,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 // Layout: W row-major [O, I] bf16, I a multiple of 32.  A workgroup stages its
 // input vectors in LDS as bf16 (zero-padded to whole 512-column chunks); wave w
 // owns kGemvRows consecutive rows; lane l reads columns 8l + 512c (16 bytes) of
-// each row, eight chunks per batch, and accumulates fp32 products in column
+// each row, four chunks per batch, and accumulates fp32 products in column
 // order; a wave sum (fixed order) finishes each dot product.
 enum { GEMV_X = 0, GEMV_SITU = 1, GEMV_OUT = 2 };
-constexpr int kGemvRows = 2;     // rows per wave
-constexpr int kGemvBatch = 8;    // 16-byte chunks per row in flight per lane
+constexpr int kGemvRows = 1;     // rows per wave
+constexpr int kGemvBatch = 4;    // 16-byte chunks per row in flight per lane
 constexpr int kGemvRowsPerBlock = 4 * kGemvRows;
 
 struct GemvArgs {
