@@ -69,3 +69,18 @@ def test_route_ties_nan_and_signed_zero():
     logits2 = np.full((1, 8), -200.0, np.float32)
     bias2 = np.array([-0.0, 0.0, -0.0, 0.0, -0.0, 0.0, -0.0, 0.0], np.float32)
     _compare(logits2, bias2, 5, "signed zeros")
+
+
+@pytest.mark.parametrize("E,K", [(896, 16), (4096, 64)])
+def test_route_flat_keys(E, K):
+    """Keys tied across most experts, so more than 128 codes reach the threshold and
+    the router takes its K-rounds fallback: all logits equal (the order is by id
+    alone), two values, and equal logits under a bias that ties in groups."""
+    rng = np.random.default_rng(E + K)
+    logits = np.zeros((3, E), np.float32)
+    logits[1] = rng.integers(0, 2, E).astype(np.float32)
+    bias = np.zeros(E, np.float32)
+    logits2 = np.full((1, E), 0.25, np.float32)
+    bias2 = (0.01 * rng.integers(0, 3, E)).astype(np.float32)
+    _compare(logits, bias, K, f"flat keys {E}/{K}")
+    _compare(logits2, bias2, K, f"grouped ties {E}/{K}")

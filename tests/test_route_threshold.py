@@ -97,3 +97,30 @@ def test_pool_size_at_the_decode_workloads():
         sizes.append(check(keys, 16))
     assert max(sizes) <= 128, max(sizes)
     assert 16 <= min(sizes)
+
+
+def _kernel_keys(logits, bias):
+    sd = 1.0 / (1.0 + np.exp(-logits.astype(np.float64)))
+    key = (sd.astype(np.float32) + bias).astype(np.float32).astype(np.float64)
+    key[np.isnan(key)] = -np.inf
+    return key
+
+
+def test_gpu_route_inputs_reach_every_rank_path():
+    """The router ranks the pool in wave 0 alone (at most 64 codes), with every wave
+    (65..128), or falls back to K rounds of wave maxima (more than 128).  The GPU
+    router tests' own inputs (same generators) must reach all three."""
+    sizes = []
+    for T, E, K in [(3, 100, 7), (5, 64, 64), (2, 4096, 64), (4, 33, 1), (7, 16, 16)]:  # test_route_shapes
+        rng = np.random.default_rng(T * 1000 + E)
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+        sizes += [len(threshold_pool(_kernel_keys(logits[t], bias), K)) for t in range(T)]
+    for E, K in [(896, 16), (4096, 64)]:  # test_route_flat_keys
+        rng = np.random.default_rng(E + K)
+        logits = np.zeros((3, E), np.float32)
+        logits[1] = rng.integers(0, 2, E).astype(np.float32)
+        bias = np.zeros(E, np.float32)
+        sizes += [len(threshold_pool(_kernel_keys(logits[t], bias), K)) for t in range(3)]
+    sizes = np.array(sizes)
+    assert np.any(sizes <= 64) and np.any((sizes > 64) & (sizes <= 128)) and np.any(sizes > 128), sizes
