@@ -132,20 +132,38 @@ __device__ __forceinline__ float dot8_bf16(const u32x4& w, const uint4& v, float
 // the row (the batch's tail, or a lane past a width that is not a multiple of
 // 512) load an in-range address and are replaced by zeros on both sides, so the
 // body has no branches.
+typedef u32x4 GemvBatch[kGemvRows][kGemvBatch];
+
+// Issue the loads of batch c0 (chunks c0 .. c0 + kGemvBatch - 1) of the rows.
+__device__ __forceinline__ void gemv_issue(const uint16_t* __restrict__ W, int I, const int (&rows)[kGemvRows],
+                                           int c0, GemvBatch& w) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r)
+#pragma unroll
+        for (int b = 0; b < kGemvBatch; ++b) {
+            const int col = 8 * lane + 512 * (c0 + b);
+            const u32x4 q = *reinterpret_cast<const u32x4*>(W + (size_t)rows[r] * I + min(col, I - 8));
+            w[r][b] = col < I ? q : u32x4{0u, 0u, 0u, 0u};
+        }
+}
+
+// acc[r] += W[rows[r], :] . v; the first batch's loads were issued by the caller
+// (pre), before it staged v, so the weight stream starts with the kernel.
 __device__ __forceinline__ void gemv_rows(const uint16_t* __restrict__ W, int I, const int (&rows)[kGemvRows],
-                                          const uint16_t* v, float (&acc)[kGemvRows]) {
+                                          const uint16_t* v, float (&acc)[kGemvRows], const GemvBatch& pre) {
     const int lane = threadIdx.x & 63;
     const int nch = gemv_pad(I) / 512;
     for (int c0 = 0; c0 < nch; c0 += kGemvBatch) {
-        u32x4 w[kGemvRows][kGemvBatch];
+        GemvBatch w;
+        if (c0 == 0) {
 #pragma unroll
-        for (int r = 0; r < kGemvRows; ++r)
+            for (int r = 0; r < kGemvRows; ++r)
 #pragma unroll
-            for (int b = 0; b < kGemvBatch; ++b) {
-                const int col = 8 * lane + 512 * (c0 + b);
-                const u32x4 q = *reinterpret_cast<const u32x4*>(W + (size_t)rows[r] * I + min(col, I - 8));
-                w[r][b] = col < I ? q : u32x4{0u, 0u, 0u, 0u};
-            }
+                for (int b = 0; b < kGemvBatch; ++b) w[r][b] = pre[r][b];
+        } else {
+            gemv_issue(W, I, rows, c0, w);
+        }
 #pragma unroll
         for (int b = 0; b < kGemvBatch; ++b) {
             const bool in = c0 + b < nch;
@@ -159,18 +177,33 @@ __device__ __forceinline__ void gemv_rows(const uint16_t* __restrict__ W, int I,
 
 // One GEMV workgroup's rows [blk * kGemvRowsPerBlock, ...) once its inputs are in
 // LDS (vs: v0 padded; vs1: v1 padded).
-template <int EPI>
-__device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_t* vs, const uint16_t* vs1, int blk) {
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int o0 = blk * kGemvRowsPerBlock + wave * kGemvRows;
-    if (o0 >= g.O) return;  // wave-uniform; no barrier follows
+// The wave's rows of workgroup blk (clamped to real rows) and the first batch of
+// their W0 chunks, issued before the workgroup stages its inputs.
+struct GemvRows {
+    int o0;
     int rows[kGemvRows];
+    GemvBatch pre;
+};
+__device__ __forceinline__ void gemv_prefetch(const GemvArgs& g, int blk, GemvRows& wr) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    wr.o0 = blk * kGemvRowsPerBlock + wave * kGemvRows;
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) rows[r] = min(o0 + r, g.O - 1);
+    for (int r = 0; r < kGemvRows; ++r) wr.rows[r] = min(wr.o0 + r, g.O - 1);
+    gemv_issue(g.W0, g.I0, wr.rows, 0, wr.pre);
+}
+
+template <int EPI>
+__device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_t* vs, const uint16_t* vs1,
+                                                const GemvRows& wr) {
+    const int o0 = wr.o0;
+    if (o0 >= g.O) return;  // wave-uniform; no barrier follows
     float acc0[kGemvRows] = {}, acc1[kGemvRows] = {};
-    gemv_rows(g.W0, g.I0, rows, vs, acc0);
-    if (EPI == GEMV_SITU) gemv_rows(g.W1, g.I0, rows, vs, acc1);
-    if (EPI == GEMV_OUT) gemv_rows(g.W1, g.I1, rows, vs1, acc1);
+    gemv_rows(g.W0, g.I0, wr.rows, vs, acc0, wr.pre);
+    if (EPI != GEMV_X) {
+        GemvBatch p1;
+        gemv_issue(g.W1, EPI == GEMV_SITU ? g.I0 : g.I1, wr.rows, 0, p1);
+        gemv_rows(g.W1, EPI == GEMV_SITU ? g.I0 : g.I1, wr.rows, EPI == GEMV_SITU ? vs : vs1, acc1, p1);
+    }
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int r = 0; r < kGemvRows; ++r) {
@@ -194,13 +227,18 @@ __device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_
 // rows of x.
 __global__ __launch_bounds__(256) void gemv_xs_kernel(GemvArgs gx, GemvArgs gs, int nbs) {
     extern __shared__ __attribute__((aligned(16))) uint16_t vs[];
+    const int b = blockIdx.x;
+    GemvRows wr;
+    if (b < nbs)
+        gemv_prefetch(gs, b, wr);
+    else
+        gemv_prefetch(gx, b - nbs, wr);
     gemv_stage(gx.v0, gx.I0, vs);
     __syncthreads();
-    const int b = blockIdx.x;
     if (b < nbs)
-        gemv_block_rows<GEMV_SITU>(gs, vs, vs, b);
+        gemv_block_rows<GEMV_SITU>(gs, vs, vs, wr);
     else
-        gemv_block_rows<GEMV_X>(gx, vs, vs, b - nbs);
+        gemv_block_rows<GEMV_X>(gx, vs, vs, wr);
 }
 
 template <int EPI>
@@ -208,6 +246,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint16_t vs[];  // v0 (padded), then v1 (padded)
     __shared__ float part[256 / kWave];
     uint16_t* vs1 = vs + gemv_pad(g.I0);
+    GemvRows wr;
+    gemv_prefetch(g, blockIdx.x, wr);
     if (EPI == GEMV_OUT) {
         // RMSNorm of a, exactly as rmsnorm_kernel: sum of squares in the same order,
         // r = bf16(gn * (a * inv))
@@ -245,7 +285,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
         gemv_stage(g.v0, g.I0, vs);
     }
     __syncthreads();
-    gemv_block_rows<EPI>(g, vs, vs1, blockIdx.x);
+    gemv_block_rows<EPI>(g, vs, vs1, wr);
 }
 
 template <int EPI>
