@@ -127,14 +127,12 @@ __device__ __forceinline__ float dot8_bf16(const u32x4& w, const uint4& v, float
     return acc;
 }
 
-// acc[r] += W[rows[r], :] . v over the lane's chunks (v in LDS, zero-padded to
-// whole chunks).  Each batch issues all of its loads before any use; chunks past
-// the row (the batch's tail, or a lane past a width that is not a multiple of
-// 512) load an in-range address and are replaced by zeros on both sides, so the
-// body has no branches.
 typedef u32x4 GemvBatch[kGemvRows][kGemvBatch];
 
-// Issue the loads of batch c0 (chunks c0 .. c0 + kGemvBatch - 1) of the rows.
+// Issue the loads of batch c0 (chunks c0 .. c0 + kGemvBatch - 1) of the rows, all
+// before any use.  Chunks past the row (the batch's tail, or a lane past a width
+// that is not a multiple of 512) load an in-range address and are replaced by
+// zeros, so the body has no branches.
 __device__ __forceinline__ void gemv_issue(const uint16_t* __restrict__ W, int I, const int (&rows)[kGemvRows],
                                            int c0, GemvBatch& w) {
     const int lane = threadIdx.x & 63;
@@ -148,8 +146,10 @@ __device__ __forceinline__ void gemv_issue(const uint16_t* __restrict__ W, int I
         }
 }
 
-// acc[r] += W[rows[r], :] . v; the first batch's loads were issued by the caller
-// (pre), before it staged v, so the weight stream starts with the kernel.
+// acc[r] += W[rows[r], :] . v over the lane's chunks (v in LDS, zero-padded to
+// whole chunks, so chunks past the row meet zeros on both sides).  The first
+// batch's loads were issued by the caller (pre), before it staged v, so the
+// weight stream starts with the kernel.
 __device__ __forceinline__ void gemv_rows(const uint16_t* __restrict__ W, int I, const int (&rows)[kGemvRows],
                                           const uint16_t* v, float (&acc)[kGemvRows], const GemvBatch& pre) {
     const int lane = threadIdx.x & 63;
@@ -175,8 +175,6 @@ __device__ __forceinline__ void gemv_rows(const uint16_t* __restrict__ W, int I,
     }
 }
 
-// One GEMV workgroup's rows [blk * kGemvRowsPerBlock, ...) once its inputs are in
-// LDS (vs: v0 padded; vs1: v1 padded).
 // The wave's rows of workgroup blk (clamped to real rows) and the first batch of
 // their W0 chunks, issued before the workgroup stages its inputs.
 struct GemvRows {
@@ -192,6 +190,8 @@ __device__ __forceinline__ void gemv_prefetch(const GemvArgs& g, int blk, GemvRo
     gemv_issue(g.W0, g.I0, wr.rows, 0, wr.pre);
 }
 
+// One GEMV workgroup's rows [blk * kGemvRowsPerBlock, ...) once its inputs are in
+// LDS (vs: v0 padded; vs1: v1 padded).
 template <int EPI>
 __device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_t* vs, const uint16_t* vs1,
                                                 const GemvRows& wr) {
