@@ -204,24 +204,41 @@ struct RowStream {
         const int astep = (ln < 3) ? 128 : 0;
         const int jstep = (ln < 3) ? 8 : 0;
         int s0 = 0;
-        // steady state: every refill is in range, so the body has no branches
+        // Slots are refilled in pairs, after the odd step of each pair: an even step
+        // and the next one are the two 64-byte halves of each row's 128-byte line, so
+        // both halves are requested together (the line is fetched once, whole).
+        // Steady state: every refill is in range, so the body has no branches.
+        static_assert(PD % 2 == 0, "slots refill in pairs");
         for (; s0 + 2 * PD <= nsteps; s0 += PD) {
 #pragma unroll
             for (int u = 0; u < PD; ++u) {
                 step(u, s0 + u, abase, astep, jstep, true, acc);
+                if (u & 1) {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) buf[u][t] = load_row_chunk(qrow[t], (s0 + u + PD) * 128 + 32 * lg, kdim);
+                    for (int v = u - 1; v <= u; ++v)
+#pragma unroll
+                        for (int t = 0; t < NT; ++t)
+                            buf[v][t] = load_row_chunk(qrow[t], (s0 + v + PD) * 128 + 32 * lg, kdim);
+                }
             }
         }
-        // tail: the last PD..2PD-1 steps (only the final step can be partial)
+        // tail: the last PD..2PD-1 steps (only the final step can be partial).  A
+        // refill of an even slot needs its odd neighbour's step to exist, which
+        // s + PD < nsteps guarantees.
 #pragma unroll
         for (int u = 0; u < PD; ++u) {
             const int s = s0 + u;
             if (s < nsteps) {
                 step(u, s, abase, astep, jstep, s * 128 + 32 * lg < kdim, acc);
-                if (s + PD < nsteps) {
+                if (u & 1) {
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) buf[u][t] = load_row_chunk(qrow[t], (s + PD) * 128 + 32 * lg, kdim);
+                    for (int v = u - 1; v <= u; ++v) {
+                        if (s0 + v + PD < nsteps) {
+#pragma unroll
+                            for (int t = 0; t < NT; ++t)
+                                buf[v][t] = load_row_chunk(qrow[t], (s0 + v + PD) * 128 + 32 * lg, kdim);
+                        }
+                    }
                 }
             }
         }
