@@ -77,14 +77,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 //   GEMV_X    x = Wdn h in fp32
 //   GEMV_SITU s = SiTU(Sg h, Su h) in bf16 (both shared projections in one pass)
 //   (the two above run as one launch, gemv_xs_kernel: both read h)
-//   GEMV_OUT  out = Wup r + Sd s in fp32, r = RMSNorm(a) computed by every
-//             workgroup (same arithmetic as rmsnorm_kernel) while staging
+//   out = Wup r + Sd s in fp32, r = RMSNorm(a) computed by every workgroup
+//             (same arithmetic as rmsnorm_kernel), in gemv_out_kernel
 // Layout: W row-major [O, I] bf16, I a multiple of 32.  A workgroup stages its
 // input vectors in LDS as bf16 (zero-padded to whole 512-column chunks); wave w
 // owns kGemvRows consecutive rows; lane l reads columns 8l + 512c (16 bytes) of
 // each row, four chunks per batch, and accumulates fp32 products in column
 // order; a wave sum (fixed order) finishes each dot product.
-enum { GEMV_X = 0, GEMV_SITU = 1, GEMV_OUT = 2 };
+enum { GEMV_X = 0, GEMV_SITU = 1 };
 constexpr int kGemvRows = 1;     // rows per wave
 constexpr int kGemvBatch = 4;    // 16-byte chunks per row in flight per lane
 constexpr int kGemvRowsPerBlock = 4 * kGemvRows;
@@ -190,19 +190,18 @@ __device__ __forceinline__ void gemv_prefetch(const GemvArgs& g, int blk, GemvRo
     gemv_issue(g.W0, g.I0, wr.rows, 0, wr.pre);
 }
 
-// One GEMV workgroup's rows [blk * kGemvRowsPerBlock, ...) once its inputs are in
-// LDS (vs: v0 padded; vs1: v1 padded).
+// One GEMV workgroup's rows [blk * kGemvRowsPerBlock, ...) once its input is in
+// LDS (vs: v0 padded).
 template <int EPI>
-__device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_t* vs, const uint16_t* vs1,
-                                                const GemvRows& wr) {
+__device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_t* vs, const GemvRows& wr) {
     const int o0 = wr.o0;
     if (o0 >= g.O) return;  // wave-uniform; no barrier follows
     float acc0[kGemvRows] = {}, acc1[kGemvRows] = {};
     gemv_rows(g.W0, g.I0, wr.rows, vs, acc0, wr.pre);
-    if (EPI != GEMV_X) {
+    if (EPI == GEMV_SITU) {
         GemvBatch p1;
-        gemv_issue(g.W1, EPI == GEMV_SITU ? g.I0 : g.I1, wr.rows, 0, p1);
-        gemv_rows(g.W1, EPI == GEMV_SITU ? g.I0 : g.I1, wr.rows, EPI == GEMV_SITU ? vs : vs1, acc1, p1);
+        gemv_issue(g.W1, g.I0, wr.rows, 0, p1);
+        gemv_rows(g.W1, g.I0, wr.rows, vs, acc1, p1);
     }
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -211,13 +210,10 @@ __device__ __forceinline__ void gemv_block_rows(const GemvArgs& g, const uint16_
         const float d1 = (EPI == GEMV_X) ? 0.f : wave_sum(acc1[r]);
         const int o = o0 + r;
         if (lane != 0 || o >= g.O) continue;
-        if (EPI == GEMV_X) {
+        if (EPI == GEMV_X)
             g.yf[o] = d0;
-        } else if (EPI == GEMV_SITU) {
+        else
             g.yb[o] = (uint16_t)f32_to_bf16_bits(situ_fast(d0, d1));
-        } else {
-            g.yf[o] = d0 + d1;
-        }
     }
 }
 
@@ -236,63 +232,81 @@ __global__ __launch_bounds__(256) void gemv_xs_kernel(GemvArgs gx, GemvArgs gs, 
     gemv_stage(gx.v0, gx.I0, vs);
     __syncthreads();
     if (b < nbs)
-        gemv_block_rows<GEMV_SITU>(gs, vs, vs, wr);
+        gemv_block_rows<GEMV_SITU>(gs, vs, wr);
     else
-        gemv_block_rows<GEMV_X>(gx, vs, vs, wr);
+        gemv_block_rows<GEMV_X>(gx, vs, wr);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs g) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t vs[];  // v0 (padded), then v1 (padded)
+// out = Wup r + Sd s with r = RMSNorm(a), computed by every workgroup with the
+// same arithmetic as rmsnorm_kernel.  The S_d product needs only s, so it runs
+// first, while the loads of a are in flight; the norm, its barriers and the W_up
+// product follow, the first W_up batch issued before them.  d0 (W_up r) and d1
+// (S_d s) are each summed exactly as before and added as d0 + d1.
+__global__ __launch_bounds__(256) void gemv_out_kernel(GemvArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t vs[];  // r (padded), then s (padded)
     __shared__ float part[256 / kWave];
     uint16_t* vs1 = vs + gemv_pad(g.I0);
-    GemvRows wr;
-    gemv_prefetch(g, blockIdx.x, wr);
-    if (EPI == GEMV_OUT) {
-        // RMSNorm of a, exactly as rmsnorm_kernel: sum of squares in the same order,
-        // r = bf16(gn * (a * inv))
-        const float4* row = reinterpret_cast<const float4*>(g.a);
-        const int n4 = g.I0 >> 2;
-        float4 v[8];
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int o0 = blockIdx.x * kGemvRowsPerBlock + wave * kGemvRows;
+    int rows[kGemvRows];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = (int)threadIdx.x + 256 * j;
-            v[j] = i < n4 ? row[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        float ss = 0.f;
+    for (int r = 0; r < kGemvRows; ++r) rows[r] = min(o0 + r, g.O - 1);
+    GemvBatch pre1;
+    gemv_issue(g.W1, g.I1, rows, 0, pre1);
+    const float4* arow = reinterpret_cast<const float4*>(g.a);
+    const int n4 = g.I0 >> 2;
+    float4 v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-        ss = wave_sum(ss);
-        if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = ss;
-        __syncthreads();
-        float tot = 0.f;
-#pragma unroll
-        for (int j = 0; j < 256 / kWave; ++j) tot += part[j];
-        const float inv = 1.0f / sqrtf(tot / (float)g.I0 + g.eps);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = (int)threadIdx.x + 256 * j;
-            if (i >= n4) break;
-            const uint2 gw = reinterpret_cast<const uint2*>(g.gn)[i];
-            const float g0 = __uint_as_float(gw.x << 16), g1 = __uint_as_float(gw.x & 0xFFFF0000u);
-            const float g2 = __uint_as_float(gw.y << 16), g3 = __uint_as_float(gw.y & 0xFFFF0000u);
-            reinterpret_cast<uint2*>(vs)[i] = make_uint2(pack_bf16x2(g0 * (v[j].x * inv), g1 * (v[j].y * inv)),
-                                                         pack_bf16x2(g2 * (v[j].z * inv), g3 * (v[j].w * inv)));
-        }
-        for (int i = g.I0 + (int)threadIdx.x; i < gemv_pad(g.I0); i += 256) vs[i] = 0;
-        gemv_stage(g.v1, g.I1, vs1);
-    } else {
-        gemv_stage(g.v0, g.I0, vs);
+    for (int j = 0; j < 8; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        v[j] = i < n4 ? arow[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    gemv_stage(g.v1, g.I1, vs1);
     __syncthreads();
-    gemv_block_rows<EPI>(g, vs, vs1, wr);
+    float acc0[kGemvRows] = {}, acc1[kGemvRows] = {};
+    if (o0 < g.O) gemv_rows(g.W1, g.I1, rows, vs1, acc1, pre1);  // wave-uniform
+    GemvBatch pre0;
+    gemv_issue(g.W0, g.I0, rows, 0, pre0);
+    // RMSNorm of a, exactly as rmsnorm_kernel: sum of squares in the same order,
+    // r = bf16(gn * (a * inv))
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    ss = wave_sum(ss);
+    if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 256 / kWave; ++j) tot += part[j];
+    const float inv = 1.0f / sqrtf(tot / (float)g.I0 + g.eps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        if (i >= n4) break;
+        const uint2 gw = reinterpret_cast<const uint2*>(g.gn)[i];
+        const float g0 = __uint_as_float(gw.x << 16), g1 = __uint_as_float(gw.x & 0xFFFF0000u);
+        const float g2 = __uint_as_float(gw.y << 16), g3 = __uint_as_float(gw.y & 0xFFFF0000u);
+        reinterpret_cast<uint2*>(vs)[i] = make_uint2(pack_bf16x2(g0 * (v[j].x * inv), g1 * (v[j].y * inv)),
+                                                     pack_bf16x2(g2 * (v[j].z * inv), g3 * (v[j].w * inv)));
+    }
+    for (int i = g.I0 + (int)threadIdx.x; i < gemv_pad(g.I0); i += 256) vs[i] = 0;
+    __syncthreads();
+    if (o0 >= g.O) return;  // wave-uniform; no barrier follows
+    gemv_rows(g.W0, g.I0, rows, vs, acc0, pre0);
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < kGemvRows; ++r) {
+        const float d0 = wave_sum(acc0[r]);
+        const float d1 = wave_sum(acc1[r]);
+        const int o = o0 + r;
+        if (lane == 0 && o < g.O) g.yf[o] = d0 + d1;
+    }
 }
 
-template <int EPI>
-hipError_t launch_gemv(const GemvArgs& g, hipStream_t stream) {
-    const size_t lds = (size_t)(gemv_pad(g.I0) + (EPI == GEMV_OUT ? gemv_pad(g.I1) : 0)) * 2;
+hipError_t launch_gemv_out(const GemvArgs& g, hipStream_t stream) {
+    const size_t lds = (size_t)(gemv_pad(g.I0) + gemv_pad(g.I1)) * 2;
     const dim3 grid((g.O + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock);
-    hipLaunchKernelGGL(gemv_kernel<EPI>, grid, dim3(256), lds, stream, g);
+    hipLaunchKernelGGL(gemv_out_kernel, grid, dim3(256), lds, stream, g);
     return hipGetLastError();
 }
 
@@ -344,7 +358,7 @@ hipError_t launch_latent(const DevLatent& L, const DevWeights& W, const uint16_t
         GemvArgs go{};
         go.W0 = L.w_up; go.W1 = L.shared_down; go.I0 = Dl; go.I1 = Fs; go.O = Dh;
         go.a = a; go.gn = L.norm; go.eps = L.eps; go.v1 = s; go.yf = out;
-        return launch_gemv<GEMV_OUT>(go, stream);
+        return launch_gemv_out(go, stream);
     }
     // T >= 2: the dense products on this library's MFMA kernels (dense.hip)
     float* part = reinterpret_cast<float*>(p); p += align256(dense_part_bytes(T));
